@@ -1,0 +1,247 @@
+/*
+ * kvq.h -- C ABI of an MI355X (gfx950) library for decode-step attention over
+ * a low-bit quantized KV cache.
+ *
+ * What is computed (the sources of the method):
+ *   - KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache
+ *     (papercache.org note on arXiv 2402.02750): asymmetric round-to-nearest
+ *     Q(X) = round((X - z)/s), X' = Q*s + z; keys quantized per channel over
+ *     groups of G tokens, values per token over groups of G channels; the most
+ *     recent tokens stay in an fp16 residual; decode logits are the
+ *     concatenation of the grouped part and the residual part under one
+ *     softmax (sections "How it works", "Method details", Algorithm 1).
+ *   - WindowQuant: Mixed-Precision KV Cache Quantization Based on Window-Level
+ *     Similarity for VLMs Inference Optimization (ACM TACO): windows of S
+ *     tokens get 8/4/2 bits (or stay fp16), windows of equal width are
+ *     reordered to sit together, decode runs Q.K^T per width block, one
+ *     softmax, per-block A.V summed (Sec. 3.1, 3.3.1, Eq. 12-16).
+ *   - The split of the context across workgroups with a final merge of the
+ *     partial softmax states follows the FlashDecoding dataflow that the
+ *     VQ-LLM note (arXiv 2503.02236, reference [10]) describes.
+ *
+ * Conventions for every call:
+ *   - All device pointers are plain HIP device addresses; the caller allocates
+ *     and frees every buffer (cache arenas, residuals, query, output,
+ *     workspace).  The library never allocates, frees or synchronizes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on that stream and returns.
+ *   - Arguments are checked on the host before anything is enqueued; on any
+ *     error the call returns a status other than KVQ_OK and no device memory
+ *     is touched.  Nothing aborts and nothing is thrown across the ABI.
+ *   - No global mutable state: calls are re-entrant.  Calls that write the
+ *     same buffers must be ordered by the caller (same stream or events).
+ *   - A "stream" of the cache (not to be confused with a HIP stream) is one
+ *     (batch b, kv head h) sequence; its index is b * n_kv_heads + h.
+ *   - fp16 means IEEE binary16 stored as 16-bit words.
+ *
+ * Cache layout (not given by the pages; fixed here and part of the ABI).
+ * The cache of each stream is a list of runs ("segments"), each holding
+ * consecutive tokens at one bit width b, plus an fp16 residual.
+ *   Code arena, keys, b in {2,4,8}: one row of RB = d_h*b/8 bytes per token,
+ *     row t of the run at byte code_off + t*RB.  The code of channel c sits in
+ *     byte floor(c*b/8) at bit (c*b) mod 8, low bits first.
+ *   Code arena, values, b in {2,4,8}: tokens 2p and 2p+1 of the run share a
+ *     block of 2*RB bytes at byte code_off + p*2*RB, made of RB/2
+ *     little-endian 32-bit words; word w holds bytes 2w, 2w+1 of token 2p's
+ *     row (the key row format) in its low 16 bits and the same two bytes of
+ *     token 2p+1's row in its high 16 bits.
+ *   Code arena, b = 16 (keys and values): rows of d_h fp16 values.
+ *   Meta arena: (scale, zero) pairs of two fp16 values, 4 bytes per pair,
+ *     starting at byte meta_off of the run.  Keys: the pair of group j
+ *     (tokens jG..jG+G-1 of the run) and channel c has index j*d_h + c.
+ *     Values: the pair of token t and channel group g (channels gG..gG+G-1)
+ *     has index ((t/2)*(d_h/G) + g)*2 + (t mod 2).  b = 16 runs have no meta.
+ *   Residual: fp16 rows of d_h values, row i of a stream at element
+ *     stream*res_stride + i*d_h.
+ *
+ * Quantizer (bit-exact contract): for each group, in IEEE fp32 on the fp16
+ * inputs, mn = min, mx = max, s32 = (mx - mn) / (2^b - 1) (one correctly
+ * rounded division), s = fp16(s32) (round to nearest even), z = fp16(mn)
+ * (exact); codes are 0 when s == 0, else clamp(rint((x - z) / s), 0, 2^b - 1)
+ * with z, s widened from fp16, one fp32 subtraction and one correctly rounded
+ * fp32 division, rint rounding half to even.  The stored (s, z) are the ones
+ * used to encode, so X' = Q*s + z decodes what was encoded.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,       /* argument out of range or inconsistent */
+  KVQ_EALIGN = 2,       /* pointer, offset or stride not aligned as required */
+  KVQ_EUNSUPPORTED = 3, /* well-formed, but not a shape this library runs */
+  KVQ_EWORKSPACE = 4,   /* workspace missing or smaller than required */
+  KVQ_ELAUNCH = 5       /* the HIP runtime refused a kernel launch */
+} kvq_status;
+
+/* Which half of the cache a quantize call writes. */
+enum { KVQ_KEYS = 0, KVQ_VALUES = 1 };
+
+/* One run of consecutive cache tokens at one bit width.  The runs of a cache
+ * are listed in token order: run i starts at the token where run i-1 ends. */
+typedef struct kvq_segment {
+  int32_t bits;      /* 16, 8, 4 or 2                                          */
+  int32_t tok_begin; /* first token of the run, in attention (stored) order    */
+  int32_t n_tok;     /* tokens in the run                                      */
+  int32_t reserved;  /* must be 0                                              */
+  int64_t code_off;  /* byte offset of the run in each stream's code arena     */
+  int64_t meta_off;  /* byte offset of the run in each stream's meta arena     */
+} kvq_segment;
+
+/* ABI version of the loaded library (KVQ_ABI_VERSION at build time). */
+int32_t kvq_abi_version(void);
+
+/* Static, human-readable name of a status; never NULL. */
+const char* kvq_strerror(int32_t status);
+
+/*
+ * kvq_quantize_append -- quantize n_tok fp16 rows of every stream, pack them
+ * and append them to one run of the cache (KIVI GroupQuant / KeyQuant and the
+ * decode-time flushes of Algorithm 1; WindowQuant per-window quantization of
+ * reordered windows, Sec. 3.3.1 and Eq. 14-16).
+ *
+ *   which      KVQ_KEYS: per-channel groups of `group` consecutive tokens;
+ *              requires n_tok % group == 0 and dst_tok % group == 0.
+ *              KVQ_VALUES: per-token groups of `group` consecutive channels;
+ *              any n_tok >= 1 and any dst_tok >= 0.
+ *   bits       2, 4 or 8; or 16 = copy the rows unchanged (no meta written).
+ *   group      G in {32, 64, 128}; values need G <= d_h.
+ *   n_streams  B * Hkv (>= 1).     d_h  64 or 128.     n_tok >= 0 (0 = no-op).
+ *   src        fp16 rows; row i of stream s at element
+ *              s*src_stream_stride + r*src_row_stride, r = src_rows ? src_rows[i] : i.
+ *              Both strides are multiples of 8 elements, src_row_stride >= d_h.
+ *   src_rows   NULL, or device int32 [n_tok] of source row indices (gather, e.g.
+ *              the row list of kvq_reorder_windows).  Indices are not checked
+ *              on the device: each must address a row inside the caller's
+ *              buffer.
+ *   codes      device pointer to the run's first byte (arena + code_off) of
+ *              stream 0; stream s at codes + s*codes_stream_stride bytes.
+ *   meta       same for the (scale, zero) pairs (ignored for bits 16).
+ *   dst_tok    tokens already in the run; new token i becomes run token
+ *              dst_tok + i.  For values, a token sharing a pair block with an
+ *              existing token only writes its own 16-bit halves.
+ * Alignment: src, codes, meta and the stream strides are multiples of 16 bytes.
+ * Writes exactly the bytes of the appended tokens (and their meta pairs).
+ */
+kvq_status kvq_quantize_append(int32_t which, int32_t bits, int32_t group,
+                               int32_t n_streams, int32_t d_h, int32_t n_tok,
+                               const void* src, int64_t src_stream_stride,
+                               int64_t src_row_stride, const int32_t* src_rows,
+                               void* codes, int64_t codes_stream_stride,
+                               void* meta, int64_t meta_stream_stride,
+                               int32_t dst_tok, void* stream);
+
+/*
+ * kvq_residual_append -- copy n_rows fp16 rows of every stream into the fp16
+ * residual at rows dst_row..dst_row+n_rows-1 (KIVI Algorithm 1, Decoding: the
+ * new key and value rows are appended to the full-precision residuals).
+ *   src: row r of stream s at element s*src_stream_stride + r*src_row_stride.
+ *   dst: row i of stream s at element s*dst_stream_stride + i*d_h.
+ * Strides are in fp16 elements, multiples of 8; pointers 16-byte aligned.
+ */
+kvq_status kvq_residual_append(int32_t n_streams, int32_t d_h, int32_t n_rows,
+                               const void* src, int64_t src_stream_stride,
+                               int64_t src_row_stride, void* dst,
+                               int64_t dst_stream_stride, int32_t dst_row,
+                               void* stream);
+
+/*
+ * kvq_reorder_windows -- WindowQuant window reorder (Sec. 3.3.1-3.3.2): a
+ * stable sort of the windows by bit width, widest first (16, 8, 4, 2; equal
+ * widths keep their original order), and the run table of the reordered cache.
+ *
+ *   win_bits       device uint8 [n_windows], each 16, 8, 4 or 2.
+ *   n_windows      1..65536.   window_tokens  S, a multiple of `group`
+ *                  (and even).   group, d_h   as for kvq_quantize_append.
+ *   perm           device int32 [n_windows]: perm[new] = old window index.
+ *   segs           device kvq_segment [4]: one run per width present, in the
+ *                  order 16, 8, 4, 2; tok_begin = first reordered token of the
+ *                  run; code_off / meta_off: runs are laid out one after the
+ *                  other in each stream's arena, each starting at the previous
+ *                  run's end rounded up to 256 bytes (codes and meta
+ *                  separately).  Code bytes of a run: n_tok*d_h*b/8 (b < 16) or
+ *                  n_tok*d_h*2 (b = 16); meta bytes: n_tok*(d_h/G)*4 (b < 16)
+ *                  or 0.
+ *   n_segs         device int32 [1]: number of runs, or -1 when a window
+ *                  width is not one of 16/8/4/2 (then perm, segs and
+ *                  row_gather hold no result).
+ *   row_gather     NULL, or device int32 [n_windows*window_tokens]: the source
+ *                  token of every reordered token, perm[w]*S + i at w*S + i.
+ * The decode step applies no mask, so the reorder does not change its output
+ * (Eq. 12-13); the prefill (masked) must run before it (Sec. 3.3.4).
+ */
+kvq_status kvq_reorder_windows(const uint8_t* win_bits, int32_t n_windows,
+                               int32_t window_tokens, int32_t group, int32_t d_h,
+                               int32_t* perm, kvq_segment* segs, int32_t* n_segs,
+                               int32_t* row_gather, void* stream);
+
+/*
+ * Decode attention arguments.  For every batch row b and query head hq (kv
+ * head h = hq / (n_q_heads / n_kv_heads), contiguous grouping), with the N
+ * cache tokens of stream (b, h):
+ *   logit_t = sm_scale * <q[b][hq], K'_t>,  p = softmax(logit) over all N,
+ *   out[b][hq] = sum_t p_t V'_t,
+ * where K'_t is the dequantized key of token t when t lies in a key run
+ * (Q*s + z) or the fp16 residual key row t - n_Kq otherwise (n_Kq = tokens
+ * in all key runs), and likewise V'_t with the value runs and residual.  This
+ * is KIVI's A = Concat([A_g, A_r]) under one softmax, t_O = A_g Q(X_Vg) +
+ * A_r X_Vr, with keys and values flushed at different token counts, and
+ * WindowQuant's per-width block decode (Sec. 3.3.1).  No mask is applied.
+ */
+typedef struct kvq_decode_args {
+  int32_t batch;          /* B >= 1                                              */
+  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads, Hq/Hkv <= 8           */
+  int32_t n_kv_heads;     /* Hkv >= 1                                            */
+  int32_t d_h;            /* 64 or 128                                           */
+  int32_t group;          /* G of the quantized runs (32, 64, 128; <= d_h)       */
+  float sm_scale;         /* logit scale, e.g. 1/sqrt(d_h)                       */
+  const void* q;          /* fp16 [B][Hq][d_h], contiguous                       */
+  const kvq_segment* k_segs; /* HOST array of key runs, in token order          */
+  int32_t n_k_segs;       /* 0..8                                                */
+  const kvq_segment* v_segs; /* HOST array of value runs, in token order        */
+  int32_t n_v_segs;       /* 0..8                                                */
+  const void* k_codes;  int64_t k_codes_stride;  /* arena base, bytes/stream    */
+  const void* k_meta;   int64_t k_meta_stride;
+  const void* v_codes;  int64_t v_codes_stride;
+  const void* v_meta;   int64_t v_meta_stride;
+  const void* k_res;    int32_t n_k_res;  int64_t k_res_stride; /* fp16 elems  */
+  const void* v_res;    int32_t n_v_res;  int64_t v_res_stride;
+  float* out;             /* fp32 [B][Hq][d_h]                                   */
+  void* workspace;        /* device scratch, see kvq_decode_attn_workspace       */
+  size_t workspace_bytes;
+  int32_t split_tokens;   /* tokens per workgroup; 0 = chosen by the library     */
+} kvq_decode_args;
+
+/*
+ * Bytes of workspace kvq_decode_attn needs for these arguments (it depends
+ * on the shapes, the runs and split_tokens, not on the pointers).  The
+ * workspace holds per-split partial softmax states; it needs no
+ * initialization and its contents are scratch after the call.
+ */
+kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes);
+
+/*
+ * kvq_decode_attn -- one decode step of attention for every (b, hq).
+ * Checks (all before any launch): shapes as documented above; runs in token
+ * order with sum(k n_tok) + n_k_res == sum(v n_tok) + n_v_res = N >= 1;
+ * key runs with b < 16 hold whole groups (n_tok % G == 0); code_off and
+ * meta_off multiples of 16; pointers and byte strides multiples of 16;
+ * residual strides multiples of 8 elements; workspace large enough.
+ * Reads the cache, q and the residuals; writes out and the workspace only.
+ */
+kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */
