@@ -1,0 +1,218 @@
+"""Benchmark: one KIVI decode step over a 2-bit KV cache, Llama-2-7B shape.
+
+Workload (the default): batch 16, 32 heads (MHA), d_h 128, 4096 cached tokens,
+G 32, R 128, int2; the step appends token 4096 and attends 4097 tokens.  A
+step is the whole path: the new key/value rows go into the fp16 residuals,
+the value that leaves the 128-token window is quantized and appended, and
+decode attention runs over [quantized | residual] keys and values.
+
+Timing: the cache is built (prefill, on the GPU) in several independent
+copies whose total exceeds twice the 256 MB Infinity Cache, and each timed
+step uses the next copy, so the reads come from HBM.  One step per copy is
+captured in a HIP graph; W warm-up and then K timed steps are replayed, with
+a synchronize on both sides.  The host integers of every copy are restored
+before each step, so every step does identical work on identical data.
+
+Prints one JSON line.  `value` is the effective bandwidth of the step
+(algorithmic bytes / step time); `roofline` covers the decode-attention
+kernels (split + merge) timed live the same way; `cpu_baseline` times the
+CPU oracle's decode step on a sample of streams on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+
+
+def step_bytes(w: workloads.Workload, state):
+    """Algorithmic HBM bytes of decode attention and of the whole step."""
+    n_kq, r_k, n_vq, r_v = state
+    streams = w.batch * w.n_kv_heads
+    d, b, G = w.d_h, w.bits, w.group
+    k_codes = n_kq * d * b / 8
+    k_meta = n_kq // G * d * 4
+    v_codes = n_vq * d * b / 8
+    v_meta = n_vq * (d // G) * 4
+    res = (r_k + r_v) * d * 2
+    attn = streams * (k_codes + k_meta + v_codes + v_meta + res) + w.batch * w.n_q_heads * d * (2 + 4)
+    # append: read 2 new rows, write 2 rows; quantize 1 value row: read it, write codes + meta
+    extra = streams * (4 * d * 2 + d * 2 + d * b / 8 + (d // G) * 4)
+    return attn, attn + extra
+
+
+def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0):
+    """Oracle decode step (append + float64 attention) on a sample of streams."""
+    from threadpoolctl import threadpool_limits
+    from oracle.kivi import KiviStream
+    q = workloads.queries(w)
+    L = w.context
+    g = w.gqa
+    times, n = 0.0, 0
+    units = workloads.sample_units(w, 64, seed=99)
+    with threadpool_limits(limits=1):
+        for (b, h) in units:
+            k, v = workloads.unit_kv(w, b, h)
+            st = KiviStream(w.d_h, w.bits, w.group, w.residual)
+            st.prefill(k[:L], v[:L])                           # cache state, not timed
+            t0 = time.perf_counter()
+            st.decode_append(k[L], v[L])
+            st.attend(q[b, h * g:(h + 1) * g], w.sm_scale)
+            times += time.perf_counter() - t0
+            n += 1
+            if times > budget_s:
+                break
+    attn_b, step_b = step_bytes(w, st.lengths)
+    per_stream = step_b / (w.batch * w.n_kv_heads)
+    return {"value": round(per_stream * n / times / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} of {w.batch * w.n_kv_heads} (batch, kv-head) streams of the same "
+                      f"workload, decode-step append + float64 attention per stream, "
+                      f"{times:.1f} s single-threaded"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama2_7b")
+    ap.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough for 2x 256 MB)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+
+    import torch
+    from decode_attention_kivi_amd.cache import KiviCache
+    lib = os.path.join(ROOT, "decode_attention_kivi_amd", "libkvq.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    w = workloads.get(args.workload)
+    assert not w.mixed, "bench runs the uniform KIVI workloads"
+    dev = torch.device("cuda:0")
+    L = w.context
+    k, v = workloads.full_kv(w)
+    q = torch.from_numpy(workloads.queries(w)).to(dev)
+    kt = torch.from_numpy(k).to(dev)
+    vt = torch.from_numpy(v).to(dev)
+    del k, v
+
+    attn_probe = None
+    caches = []
+    copies = args.copies
+    t_build = time.perf_counter()
+    while True:
+        c = KiviCache(w.batch, w.n_kv_heads, w.d_h, w.bits, w.group, w.residual, w.n_tokens, dev)
+        c.prefill(kt[:, :, :L], vt[:, :, :L])
+        caches.append(c)
+        if attn_probe is None:
+            st0 = c.lengths, c.v_start
+            c.append(kt[:, :, L:L + 1], vt[:, :, L:L + 1])
+            attn_probe = c.lengths
+            (c.n_kq, c.r_k, c.n_vq, c.r_v), c.v_start = st0
+        attn_b, total_b = step_bytes(w, attn_probe)
+        if copies and len(caches) >= copies:
+            break
+        if not copies and len(caches) >= 4 and len(caches) * attn_b > 2 * 256e6:
+            break
+    torch.cuda.synchronize()
+    t_build = time.perf_counter() - t_build
+    saved = [(c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start) for c in caches]
+    outs = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in caches]
+    k_new, v_new = kt[:, :, L:L + 1], vt[:, :, L:L + 1]
+
+    def restore():
+        for c, s in zip(caches, saved):
+            c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start = s
+
+    # prepare workspaces outside capture
+    for c, o in zip(caches, outs):
+        c.append(k_new, v_new)
+        c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+    restore()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    step_graph = torch.cuda.CUDAGraph()
+    attn_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(step_graph, stream=stream):
+            for c, o in zip(caches, outs):
+                c.append(k_new, v_new)
+                c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+        restore()
+        for c in caches:           # attention-only graph on the post-step state
+            c.append(k_new, v_new)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(attn_graph, stream=stream):
+            for c, o in zip(caches, outs):
+                c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+    restore()
+    torch.cuda.synchronize()
+    n_copies = len(caches)
+
+    def timed(graph, steps, warmup):
+        reps_w = max(1, -(-warmup // n_copies))
+        reps = max(1, -(-steps // n_copies))
+        for _ in range(reps_w):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * n_copies), reps * n_copies
+
+    with torch.cuda.stream(stream):
+        attn_ms, _ = timed(attn_graph, args.steps, args.warmup)
+        step_ms, n_steps = timed(step_graph, args.steps, args.warmup)
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+
+    achieved = attn_b / (attn_ms * 1e-3) / 1e9
+    value = total_b / (step_ms * 1e-3) / 1e9
+    result = {
+        "metric": "decode-attn effective KV GB/s (% of HBM peak) + us/step, int2 Llama-2-7B shape",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "us_per_step": round(step_ms * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_context_per_s": round(w.batch * w.n_tokens / (step_ms * 1e-3), 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u2/f16/f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "d_h": w.d_h, "context": w.context,
+                   "attended_tokens": w.n_tokens, "group": w.group, "residual": w.residual,
+                   "bits": w.bits, "cache_copies": n_copies,
+                   "cache_state_nKq_rK_nVq_rV": list(attn_probe),
+                   "algorithmic_bytes_step": int(total_b), "algorithmic_bytes_attention": int(attn_b)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_split_kernel + decode_merge_kernel (one kvq_decode_attn call)",
+                     "us_per_launch": round(attn_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

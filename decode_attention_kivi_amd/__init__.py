@@ -1,0 +1,199 @@
+"""kvq -- decode attention over a low-bit quantized KV cache on MI355X (gfx950).
+
+Python binding of the C ABI in ``include/kvq.h``.  Every function here has
+the name and argument list of the C entry point; the binding only turns torch
+tensors into device pointers, picks torch's current HIP stream when none is
+given, and raises :class:`KvqError` on a non-zero status.  All computation
+happens in the HIP kernels of ``libkvq.so``; there is no fallback: if the
+library is missing, importing a function that needs it raises.
+
+``decode_attention_kivi_amd.cache`` holds the cache bookkeeping (KIVI's
+residual / flush rules and the WindowQuant reorder flow) built on these calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "KVQ_KEYS", "KVQ_VALUES", "KvqError", "Segment", "DecodeArgs", "library_path",
+    "kvq_abi_version", "kvq_strerror", "kvq_quantize_append", "kvq_residual_append",
+    "kvq_reorder_windows", "kvq_decode_attn_workspace", "kvq_decode_attn",
+]
+
+KVQ_KEYS = 0
+KVQ_VALUES = 1
+ABI_VERSION = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvq.so")
+_lib = None
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {kvq_strerror(status)} (status {status})")
+
+
+class Segment(ctypes.Structure):
+    """kvq_segment: one run of consecutive cache tokens at one bit width."""
+    _fields_ = [("bits", ctypes.c_int32), ("tok_begin", ctypes.c_int32),
+                ("n_tok", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("code_off", ctypes.c_int64), ("meta_off", ctypes.c_int64)]
+
+    def astuple(self):
+        return (self.bits, self.tok_begin, self.n_tok, self.code_off, self.meta_off)
+
+
+class DecodeArgs(ctypes.Structure):
+    """kvq_decode_args (field order and types of include/kvq.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("d_h", ctypes.c_int32),
+        ("group", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("q", ctypes.c_void_p),
+        ("k_segs", ctypes.POINTER(Segment)), ("n_k_segs", ctypes.c_int32),
+        ("v_segs", ctypes.POINTER(Segment)), ("n_v_segs", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("k_codes_stride", ctypes.c_int64),
+        ("k_meta", ctypes.c_void_p), ("k_meta_stride", ctypes.c_int64),
+        ("v_codes", ctypes.c_void_p), ("v_codes_stride", ctypes.c_int64),
+        ("v_meta", ctypes.c_void_p), ("v_meta_stride", ctypes.c_int64),
+        ("k_res", ctypes.c_void_p), ("n_k_res", ctypes.c_int32), ("k_res_stride", ctypes.c_int64),
+        ("v_res", ctypes.c_void_p), ("n_v_res", ctypes.c_int32), ("v_res_stride", ctypes.c_int64),
+        ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("split_tokens", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.kvq_abi_version.restype = i32
+    lib.kvq_abi_version.argtypes = []
+    lib.kvq_strerror.restype = ctypes.c_char_p
+    lib.kvq_strerror.argtypes = [i32]
+    lib.kvq_quantize_append.restype = i32
+    lib.kvq_quantize_append.argtypes = [i32, i32, i32, i32, i32, i32, vp, i64, i64, vp,
+                                        vp, i64, vp, i64, i32, vp]
+    lib.kvq_residual_append.restype = i32
+    lib.kvq_residual_append.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, i32, vp]
+    lib.kvq_reorder_windows.restype = i32
+    lib.kvq_reorder_windows.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.kvq_decode_attn_workspace.restype = i32
+    lib.kvq_decode_attn_workspace.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_decode_attn.restype = i32
+    lib.kvq_decode_attn.argtypes = [ctypes.POINTER(DecodeArgs), vp]
+    if lib.kvq_abi_version() != ABI_VERSION:
+        raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _dev(x) -> Optional[int]:
+    """Device pointer of a CUDA tensor (None -> NULL); ints pass through."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not getattr(x, "is_cuda", False):
+        raise ValueError("device buffer expected (a CUDA tensor or an int address)")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KvqError(status, where)
+
+
+def kvq_abi_version() -> int:
+    return int(_load().kvq_abi_version())
+
+
+def kvq_strerror(status: int) -> str:
+    return _load().kvq_strerror(int(status)).decode()
+
+
+def kvq_quantize_append(which, bits, group, n_streams, d_h, n_tok, src, src_stream_stride,
+                        src_row_stride, src_rows, codes, codes_stream_stride, meta,
+                        meta_stream_stride, dst_tok, stream=None):
+    """See include/kvq.h.  Strides: src in fp16 elements, codes/meta in bytes."""
+    _check(_load().kvq_quantize_append(
+        which, bits, group, n_streams, d_h, n_tok, _dev(src), src_stream_stride, src_row_stride,
+        _dev(src_rows), _dev(codes), codes_stream_stride, _dev(meta), meta_stream_stride,
+        dst_tok, _stream(stream)), "kvq_quantize_append")
+
+
+def kvq_residual_append(n_streams, d_h, n_rows, src, src_stream_stride, src_row_stride, dst,
+                        dst_stream_stride, dst_row, stream=None):
+    """See include/kvq.h.  Strides in fp16 elements."""
+    _check(_load().kvq_residual_append(
+        n_streams, d_h, n_rows, _dev(src), src_stream_stride, src_row_stride, _dev(dst),
+        dst_stream_stride, dst_row, _stream(stream)), "kvq_residual_append")
+
+
+def kvq_reorder_windows(win_bits, n_windows, window_tokens, group, d_h, perm, segs, n_segs,
+                        row_gather, stream=None):
+    """See include/kvq.h.  ``segs`` is a device buffer of 4 kvq_segment (128 bytes)."""
+    _check(_load().kvq_reorder_windows(
+        _dev(win_bits), n_windows, window_tokens, group, d_h, _dev(perm), _dev(segs),
+        _dev(n_segs), _dev(row_gather), _stream(stream)), "kvq_reorder_windows")
+
+
+def segments(rows: Sequence) -> ctypes.Array:
+    """Host kvq_segment array from (bits, tok_begin, n_tok, code_off, meta_off) rows."""
+    arr = (Segment * max(1, len(rows)))()
+    for i, r in enumerate(rows):
+        arr[i] = Segment(int(r[0]), int(r[1]), int(r[2]), 0, int(r[3]), int(r[4]))
+    return arr
+
+
+def make_decode_args(*, batch, n_q_heads, n_kv_heads, d_h, group, sm_scale, q,
+                     k_segs=(), v_segs=(), k_codes=None, k_codes_stride=0, k_meta=None,
+                     k_meta_stride=0, v_codes=None, v_codes_stride=0, v_meta=None,
+                     v_meta_stride=0, k_res=None, n_k_res=0, k_res_stride=0, v_res=None,
+                     n_v_res=0, v_res_stride=0, out=None, workspace=None, workspace_bytes=0,
+                     split_tokens=0) -> DecodeArgs:
+    """Fill a kvq_decode_args; segments are (bits, tok_begin, n_tok, code_off, meta_off)."""
+    ks, vs = segments(k_segs), segments(v_segs)
+    a = DecodeArgs(
+        batch, n_q_heads, n_kv_heads, d_h, group, float(sm_scale), _dev(q),
+        ks, len(k_segs), vs, len(v_segs),
+        _dev(k_codes), k_codes_stride, _dev(k_meta), k_meta_stride,
+        _dev(v_codes), v_codes_stride, _dev(v_meta), v_meta_stride,
+        _dev(k_res), n_k_res, k_res_stride, _dev(v_res), n_v_res, v_res_stride,
+        _dev(out), _dev(workspace), int(workspace_bytes), int(split_tokens))
+    a._keep = (ks, vs)          # the segment arrays must outlive the call
+    return a
+
+
+def kvq_decode_attn_workspace(args: DecodeArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().kvq_decode_attn_workspace(ctypes.byref(args), ctypes.byref(n)),
+           "kvq_decode_attn_workspace")
+    return int(n.value)
+
+
+def kvq_decode_attn(args: DecodeArgs, stream=None):
+    _check(_load().kvq_decode_attn(ctypes.byref(args), _stream(stream)), "kvq_decode_attn")

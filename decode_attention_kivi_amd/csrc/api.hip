@@ -1,0 +1,289 @@
+// extern "C" entry points of include/kvq.h: argument checks on the host,
+// launch planning, kernel launches.  No allocation, no synchronization.
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::Cell;
+using kvq::DecodeParams;
+using kvq::Run;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool valid_d(int d) { return d == 64 || d == 128; }
+bool valid_group(int g) { return g == 32 || g == 64 || g == 128; }
+bool valid_bits(int b) { return b == 2 || b == 4 || b == 8 || b == 16; }
+
+kvq_status from_hip(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ELAUNCH; }
+
+// The launch plan of one decode call, derived from the arguments alone.
+struct Plan {
+  DecodeParams p;
+  int GQ = 1;
+  size_t ws_bytes = 0;
+};
+
+kvq_status check_runs(const kvq_segment* segs, int n, int d, int G, bool keys, int64_t* n_total) {
+  if (n < 0 || n > kvq::kMaxRuns) return KVQ_EINVAL;
+  if (n > 0 && !segs) return KVQ_EINVAL;
+  int64_t tok = 0;
+  for (int i = 0; i < n; ++i) {
+    const kvq_segment& s = segs[i];
+    if (!valid_bits(s.bits) || s.reserved != 0) return KVQ_EINVAL;
+    if (s.n_tok < 0 || s.tok_begin != tok) return KVQ_EINVAL;
+    if (s.code_off < 0 || s.meta_off < 0) return KVQ_EINVAL;
+    if ((s.code_off & 15) || (s.meta_off & 15)) return KVQ_EALIGN;
+    if (keys && s.bits != 16 && s.n_tok % G != 0) return KVQ_EINVAL;
+    (void)d;
+    tok += s.n_tok;
+  }
+  *n_total = tok;
+  return KVQ_OK;
+}
+
+int64_t count_splits(const std::vector<Cell>& cells, int st) {
+  int64_t n = 0;
+  for (const Cell& c : cells) n += (c.n + st - 1) / st;
+  return n;
+}
+
+kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
+  if (!a) return KVQ_EINVAL;
+  if (a->batch < 1 || a->n_kv_heads < 1 || a->n_q_heads < 1) return KVQ_EINVAL;
+  if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_EINVAL;
+  const int gq = a->n_q_heads / a->n_kv_heads;
+  if (!valid_d(a->d_h) || !valid_group(a->group) || a->group > a->d_h) return KVQ_EUNSUPPORTED;
+  if (gq > 8) return KVQ_EUNSUPPORTED;
+  if (int64_t(a->batch) * a->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  if (!(std::isfinite(a->sm_scale))) return KVQ_EINVAL;
+  if (!a->q || !a->out) return KVQ_EINVAL;
+  if (a->n_k_res < 0 || a->n_v_res < 0 || a->split_tokens < 0) return KVQ_EINVAL;
+  const int D = a->d_h, G = a->group;
+
+  int64_t nk = 0, nv = 0;
+  kvq_status st = check_runs(a->k_segs, a->n_k_segs, D, G, true, &nk);
+  if (st != KVQ_OK) return st;
+  st = check_runs(a->v_segs, a->n_v_segs, D, G, false, &nv);
+  if (st != KVQ_OK) return st;
+  const int64_t N = nk + a->n_k_res;
+  if (N < 1 || N != nv + a->n_v_res || N > (int64_t(1) << 30)) return KVQ_EINVAL;
+  bool k_quant = false, v_quant = false;
+  for (int i = 0; i < a->n_k_segs; ++i) k_quant |= a->k_segs[i].bits != 16 && a->k_segs[i].n_tok > 0;
+  for (int i = 0; i < a->n_v_segs; ++i) v_quant |= a->v_segs[i].bits != 16 && a->v_segs[i].n_tok > 0;
+  if ((nk > 0 && !a->k_codes) || (k_quant && !a->k_meta)) return KVQ_EINVAL;
+  if ((nv > 0 && !a->v_codes) || (v_quant && !a->v_meta)) return KVQ_EINVAL;
+  if (a->n_k_res > 0 && !a->k_res) return KVQ_EINVAL;
+  if (a->n_v_res > 0 && !a->v_res) return KVQ_EINVAL;
+  for (const void* ptr : {a->q, static_cast<const void*>(a->out), a->k_codes, a->k_meta,
+                          a->v_codes, a->v_meta, a->k_res, a->v_res, static_cast<const void*>(a->workspace)})
+    if (ptr && !aligned16(ptr)) return KVQ_EALIGN;
+  for (int64_t s : {a->k_codes_stride, a->k_meta_stride, a->v_codes_stride, a->v_meta_stride})
+    if (s < 0 || (s & 15)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
+  for (int64_t s : {a->k_res_stride, a->v_res_stride})
+    if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
+
+  // cells: maximal token ranges with one key source and one value source
+  std::vector<int64_t> cuts = {0, N, nk, nv};
+  for (int i = 0; i < a->n_k_segs; ++i) cuts.push_back(a->k_segs[i].tok_begin);
+  for (int i = 0; i < a->n_v_segs; ++i) cuts.push_back(a->v_segs[i].tok_begin);
+  std::sort(cuts.begin(), cuts.end());
+  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  std::vector<Cell> cells;
+  for (size_t i = 0; i + 1 < cuts.size(); ++i) {
+    const int64_t t0 = cuts[i], t1 = cuts[i + 1];
+    if (t1 <= t0) continue;
+    Cell c{};
+    c.t0 = int32_t(t0);
+    c.n = int32_t(t1 - t0);
+    c.k_src = -1;
+    c.v_src = -1;
+    for (int k = 0; k < a->n_k_segs; ++k)
+      if (t0 >= a->k_segs[k].tok_begin && t0 < a->k_segs[k].tok_begin + a->k_segs[k].n_tok) c.k_src = k;
+    for (int k = 0; k < a->n_v_segs; ++k)
+      if (t0 >= a->v_segs[k].tok_begin && t0 < a->v_segs[k].tok_begin + a->v_segs[k].n_tok) c.v_src = k;
+    cells.push_back(c);
+  }
+  if (cells.empty() || cells.size() > size_t(kvq::kMaxCells)) return KVQ_EUNSUPPORTED;
+
+  int GQ = 1;
+  while (GQ < gq) GQ *= 2;
+  const int64_t streams = int64_t(a->batch) * a->n_kv_heads;
+  int st_tokens = a->split_tokens;
+  if (st_tokens == 0) {
+    st_tokens = 1024;
+    while (st_tokens > 64 && kvq::decode_lds_bytes(D, GQ, st_tokens, G) > kvq::kLdsLimit) st_tokens /= 2;
+    while (st_tokens > 128 && streams * count_splits(cells, st_tokens) < 2048) st_tokens /= 2;
+  }
+  if (kvq::decode_lds_bytes(D, GQ, st_tokens, G) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
+  int64_t n_splits = 0;
+  for (Cell& c : cells) {
+    c.split0 = int32_t(n_splits);
+    n_splits += (c.n + st_tokens - 1) / st_tokens;
+  }
+  if (n_splits > (int64_t(1) << 31) - 1) return KVQ_EUNSUPPORTED;
+
+  Plan& pl = *out;
+  DecodeParams& p = pl.p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.out = a->out;
+  p.ws = static_cast<float*>(a->workspace);
+  p.k_codes = static_cast<const uint8_t*>(a->k_codes);
+  p.k_meta = static_cast<const uint8_t*>(a->k_meta);
+  p.v_codes = static_cast<const uint8_t*>(a->v_codes);
+  p.v_meta = static_cast<const uint8_t*>(a->v_meta);
+  p.k_res = static_cast<const uint16_t*>(a->k_res);
+  p.v_res = static_cast<const uint16_t*>(a->v_res);
+  p.k_codes_stride = a->k_codes_stride;
+  p.k_meta_stride = a->k_meta_stride;
+  p.v_codes_stride = a->v_codes_stride;
+  p.v_meta_stride = a->v_meta_stride;
+  p.k_res_stride = a->k_res_stride;
+  p.v_res_stride = a->v_res_stride;
+  p.B = a->batch;
+  p.Hq = a->n_q_heads;
+  p.Hkv = a->n_kv_heads;
+  p.D = D;
+  p.G = G;
+  p.gq = gq;
+  p.n_kq = int32_t(nk);
+  p.n_vq = int32_t(nv);
+  p.n_splits = int32_t(n_splits);
+  p.split_tokens = st_tokens;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  p.n_cells = int32_t(cells.size());
+  p.n_k_runs = a->n_k_segs;
+  p.n_v_runs = a->n_v_segs;
+  for (int i = 0; i < a->n_k_segs; ++i)
+    p.k_runs[i] = Run{a->k_segs[i].bits, a->k_segs[i].tok_begin, a->k_segs[i].n_tok, 0,
+                      a->k_segs[i].code_off, a->k_segs[i].meta_off};
+  for (int i = 0; i < a->n_v_segs; ++i)
+    p.v_runs[i] = Run{a->v_segs[i].bits, a->v_segs[i].tok_begin, a->v_segs[i].n_tok, 0,
+                      a->v_segs[i].code_off, a->v_segs[i].meta_off};
+  for (size_t i = 0; i < cells.size(); ++i) p.cells[i] = cells[i];
+  pl.GQ = GQ;
+  pl.ws_bytes = size_t(streams) * size_t(n_splits) * size_t(gq) * size_t(D + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_strerror(int32_t status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_EALIGN: return "misaligned pointer, offset or stride";
+    case KVQ_EUNSUPPORTED: return "unsupported shape";
+    case KVQ_EWORKSPACE: return "workspace missing or too small";
+    case KVQ_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+kvq_status kvq_quantize_append(int32_t which, int32_t bits, int32_t group, int32_t n_streams,
+                               int32_t d_h, int32_t n_tok, const void* src,
+                               int64_t src_stream_stride, int64_t src_row_stride,
+                               const int32_t* src_rows, void* codes,
+                               int64_t codes_stream_stride, void* meta,
+                               int64_t meta_stream_stride, int32_t dst_tok, void* stream) {
+  if (which != KVQ_KEYS && which != KVQ_VALUES) return KVQ_EINVAL;
+  if (!valid_bits(bits)) return KVQ_EINVAL;
+  if (!valid_group(group) || !valid_d(d_h)) return KVQ_EUNSUPPORTED;
+  if (which == KVQ_VALUES && bits != 16 && group > d_h) return KVQ_EUNSUPPORTED;
+  if (n_streams < 1 || n_tok < 0 || dst_tok < 0) return KVQ_EINVAL;
+  if (n_streams > 65535) return KVQ_EUNSUPPORTED;
+  if (which == KVQ_KEYS && bits != 16 && (n_tok % group != 0 || dst_tok % group != 0))
+    return KVQ_EINVAL;
+  if (!src || !codes || (bits != 16 && !meta)) return KVQ_EINVAL;
+  if (src_stream_stride < 0 || src_row_stride < d_h || codes_stream_stride < 0 ||
+      meta_stream_stride < 0)
+    return KVQ_EINVAL;
+  if (!aligned16(src) || !aligned16(codes) || (meta && !aligned16(meta))) return KVQ_EALIGN;
+  if ((src_stream_stride & 7) || (src_row_stride & 7) || (codes_stream_stride & 15) ||
+      (meta_stream_stride & 15))
+    return KVQ_EALIGN;
+  if (int64_t(dst_tok) + n_tok > (int64_t(1) << 30)) return KVQ_EINVAL;
+  if (n_tok == 0) return KVQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (bits == 16)
+    return from_hip(kvq::launch_copy_rows(static_cast<const uint16_t*>(src), src_stream_stride,
+                                          src_row_stride, src_rows, static_cast<uint8_t*>(codes),
+                                          codes_stream_stride, dst_tok, n_streams, d_h, n_tok, s));
+  kvq::QuantParams p{};
+  p.src = static_cast<const uint16_t*>(src);
+  p.src_rows = src_rows;
+  p.codes = static_cast<uint8_t*>(codes);
+  p.meta = static_cast<uint8_t*>(meta);
+  p.src_stream_stride = src_stream_stride;
+  p.src_row_stride = src_row_stride;
+  p.codes_stream_stride = codes_stream_stride;
+  p.meta_stream_stride = meta_stream_stride;
+  p.bits = bits;
+  p.G = group;
+  p.D = d_h;
+  p.n_streams = n_streams;
+  p.n_tok = n_tok;
+  p.dst_tok = dst_tok;
+  return from_hip(which == KVQ_KEYS ? kvq::launch_quantize_keys(p, s)
+                                    : kvq::launch_quantize_values(p, s));
+}
+
+kvq_status kvq_residual_append(int32_t n_streams, int32_t d_h, int32_t n_rows, const void* src,
+                               int64_t src_stream_stride, int64_t src_row_stride, void* dst,
+                               int64_t dst_stream_stride, int32_t dst_row, void* stream) {
+  if (!valid_d(d_h)) return KVQ_EUNSUPPORTED;
+  if (n_streams < 1 || n_rows < 0 || dst_row < 0) return KVQ_EINVAL;
+  if (!src || !dst) return KVQ_EINVAL;
+  if (src_stream_stride < 0 || src_row_stride < d_h || dst_stream_stride < 0) return KVQ_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return KVQ_EALIGN;
+  if ((src_stream_stride & 7) || (src_row_stride & 7) || (dst_stream_stride & 7)) return KVQ_EALIGN;
+  if (n_rows == 0) return KVQ_OK;
+  return from_hip(kvq::launch_copy_rows(static_cast<const uint16_t*>(src), src_stream_stride,
+                                        src_row_stride, nullptr, static_cast<uint8_t*>(dst),
+                                        dst_stream_stride * 2, dst_row, n_streams, d_h, n_rows,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_reorder_windows(const uint8_t* win_bits, int32_t n_windows, int32_t window_tokens,
+                               int32_t group, int32_t d_h, int32_t* perm, kvq_segment* segs,
+                               int32_t* n_segs, int32_t* row_gather, void* stream) {
+  if (!valid_group(group) || !valid_d(d_h) || group > d_h) return KVQ_EUNSUPPORTED;
+  if (n_windows < 1 || n_windows > 65536) return KVQ_EINVAL;
+  if (window_tokens < 1 || window_tokens % group != 0 || (window_tokens & 1)) return KVQ_EINVAL;
+  if (int64_t(n_windows) * window_tokens > (int64_t(1) << 30)) return KVQ_EINVAL;
+  if (!win_bits || !perm || !segs || !n_segs) return KVQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(perm) & 3) || (reinterpret_cast<uintptr_t>(n_segs) & 3) ||
+      (reinterpret_cast<uintptr_t>(row_gather) & 3) || (reinterpret_cast<uintptr_t>(segs) & 7))
+    return KVQ_EALIGN;
+  return from_hip(kvq::launch_reorder(win_bits, n_windows, window_tokens, group, d_h, perm, segs,
+                                      n_segs, row_gather, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes) {
+  if (!bytes) return KVQ_EINVAL;
+  Plan pl;
+  const kvq_status st = make_plan(args, &pl);
+  if (st != KVQ_OK) return st;
+  *bytes = pl.ws_bytes;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream) {
+  Plan pl;
+  const kvq_status st = make_plan(args, &pl);
+  if (st != KVQ_OK) return st;
+  if (!args->workspace || args->workspace_bytes < pl.ws_bytes) return KVQ_EWORKSPACE;
+  return from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Device helpers for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+}
+
+// fp32 -> fp16, round to nearest even (v_cvt_f16_f32 in the default mode).
+__device__ __forceinline__ uint32_t f2h(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// a.lo*b.lo + a.hi*b.hi + c with fp16 pairs and an fp32 accumulator.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
+                                __builtin_bit_cast(half2_t, b), c, false);
+}
+
+// Unpacking one 32-bit word of codes into fp16 pairs without conversions:
+// a b-bit code moved into the fp16 mantissa under a fixed exponent reads as
+// (offset + code).  Pair k of a word combines the code at bit b*k of the low
+// half with the code at bit 16 + b*k of the high half.  The offsets are chosen
+// small (at most 64 for 2- and 4-bit codes) so that the fp32 accumulation of
+// (offset + code) * weight loses little against the later subtraction of
+// offset * sum(weight).
+template <int BITS> struct Unpack;
+
+template <> struct Unpack<2> {
+  static constexpr int NP = 8;   // pairs per word
+  __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
+    const uint32_t a = w << 4, c = w >> 6;
+    v[0] = (a & 0x00300030u) | 0x54005400u;  // mantissa bits 4-5: 64 + code
+    v[1] = (a & 0x00C000C0u) | 0x4C004C00u;  // bits 6-7: 16 + code
+    v[2] = (a & 0x03000300u) | 0x44004400u;  // bits 8-9: 4 + code
+    v[3] = (w & 0x00C000C0u) | 0x4C004C00u;
+    v[4] = (w & 0x03000300u) | 0x44004400u;
+    v[5] = (c & 0x00300030u) | 0x54005400u;
+    v[6] = (c & 0x00C000C0u) | 0x4C004C00u;
+    v[7] = (c & 0x03000300u) | 0x44004400u;
+  }
+  __device__ static __forceinline__ float offset(int k) {
+    return (k == 0 || k == 5) ? 64.f : ((k == 1 || k == 3 || k == 6) ? 16.f : 4.f);
+  }
+};
+
+template <> struct Unpack<4> {
+  static constexpr int NP = 4;
+  __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
+    v[0] = ((w << 4) & 0x00F000F0u) | 0x54005400u;  // mantissa bits 4-7: 64 + code
+    v[1] = (w & 0x00F000F0u) | 0x54005400u;
+    v[2] = ((w >> 4) & 0x00F000F0u) | 0x54005400u;
+    v[3] = ((w >> 8) & 0x00F000F0u) | 0x54005400u;
+  }
+  __device__ static __forceinline__ float offset(int) { return 64.f; }
+};
+
+template <> struct Unpack<8> {
+  static constexpr int NP = 2;
+  __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
+    v[0] = (w & 0x00FF00FFu) | 0x64006400u;         // mantissa bits 0-7: 1024 + code
+    v[1] = ((w >> 8) & 0x00FF00FFu) | 0x64006400u;
+  }
+  __device__ static __forceinline__ float offset(int) { return 1024.f; }
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+  return x;
+}
+
+}  // namespace kvq

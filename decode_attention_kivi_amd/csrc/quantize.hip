@@ -1,0 +1,189 @@
+// Group quantize + pack + append kernels, and the fp16 row copy.
+//
+// Quantizer: asymmetric round-to-nearest, Q = round((x - z)/s), x' = Q*s + z
+// (KIVI note, "How it works"; WindowQuant Sec. 3.3.3, Eq. 14-16), with
+// s = (max - min)/(2^b - 1) and z = min stored as fp16 and the stored values
+// used to encode.  Keys: one group per channel over G consecutive tokens;
+// values: one group per token over G consecutive channels (KIVI note,
+// "Method details" and Algorithm 1).
+//
+// Bit-exact contract (include/kvq.h): every step is one IEEE fp32 operation
+// on fp16-exact inputs -- subtract, correctly rounded divide, round half to
+// even -- so this file is built without FMA contraction and with correctly
+// rounded fp32 division.
+
+#include "kvq_internal.h"
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+// One group's scale and zero point.  The minimum is canonicalized to +0 when
+// it is a zero (min of {-0, +0} is not ordered), so z has a single encoding.
+struct GroupScale {
+  uint32_t s16, z16;
+  float s, z;
+};
+
+template <int BITS>
+__device__ __forceinline__ GroupScale group_scale(float mn, float mx) {
+  constexpr float kQmax = float((1 << BITS) - 1);
+  GroupScale g;
+  mn = mn + 0.0f;
+  g.s16 = f2h(__fdiv_rn(mx - mn, kQmax));
+  g.z16 = f2h(mn);
+  g.s = h2f(g.s16);
+  g.z = h2f(g.z16);
+  return g;
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t encode(float x, const GroupScale& g) {
+  constexpr float kQmax = float((1 << BITS) - 1);
+  if (g.s == 0.0f) return 0u;
+  float t = rintf(__fdiv_rn(x - g.z, g.s));
+  t = fminf(fmaxf(t, 0.0f), kQmax);
+  return static_cast<uint32_t>(t);
+}
+
+// Keys: block = one group of G tokens of one stream, thread = channel.
+template <int BITS>
+__global__ void __launch_bounds__(128) quantize_keys_kernel(QuantParams p) {
+  __shared__ uint8_t codes[128 * 128];  // [token in group][channel]
+  const int c = threadIdx.x;
+  const int j = blockIdx.x;
+  const int64_t s = blockIdx.y;
+  const int G = p.G, D = p.D;
+  const uint16_t* src = p.src + s * p.src_stream_stride;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = 0; i < G; ++i) {
+    const int tok = j * G + i;
+    const int64_t row = p.src_rows ? p.src_rows[tok] : tok;
+    const float x = h2f(src[row * p.src_row_stride + c]);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  const GroupScale g = group_scale<BITS>(mn, mx);
+  uint32_t* meta = reinterpret_cast<uint32_t*>(p.meta + s * p.meta_stream_stride);
+  meta[int64_t(p.dst_tok / G + j) * D + c] = g.s16 | (g.z16 << 16);
+  for (int i = 0; i < G; ++i) {
+    const int tok = j * G + i;
+    const int64_t row = p.src_rows ? p.src_rows[tok] : tok;
+    codes[i * D + c] = static_cast<uint8_t>(encode<BITS>(h2f(src[row * p.src_row_stride + c]), g));
+  }
+  __syncthreads();
+  constexpr int kCpw = 32 / BITS;       // channels per 32-bit word
+  const int wpr = D / kCpw;             // words per row
+  const int64_t rb = int64_t(D) * BITS / 8;
+  uint8_t* out = p.codes + s * p.codes_stream_stride;
+  for (int wi = c; wi < G * wpr; wi += blockDim.x) {
+    const int i = wi / wpr, wr = wi % wpr;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < kCpw; ++k)
+      word |= uint32_t(codes[i * D + wr * kCpw + k]) << (k * BITS);
+    *reinterpret_cast<uint32_t*>(out + int64_t(p.dst_tok + j * G + i) * rb + wr * 4) = word;
+  }
+}
+
+// Values: thread = one group (G channels) of one token of one stream.  The
+// codes go to the token's 16-bit halves of its pair block.
+template <int BITS>
+__global__ void __launch_bounds__(256) quantize_values_kernel(QuantParams p, int NG) {
+  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = int64_t(p.n_streams) * p.n_tok * NG;
+  if (item >= total) return;
+  const int g = int(item % NG);
+  const int64_t rest = item / NG;
+  const int i = int(rest % p.n_tok);
+  const int64_t s = rest / p.n_tok;
+  const int G = p.G;
+  const int64_t row = p.src_rows ? p.src_rows[i] : i;
+  const uint16_t* x = p.src + s * p.src_stream_stride + row * p.src_row_stride + int64_t(g) * G;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int k = 0; k < G; k += 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + k);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = h2f(w[e] & 0xffffu), b = h2f(w[e] >> 16);
+      mn = fminf(mn, fminf(a, b));
+      mx = fmaxf(mx, fmaxf(a, b));
+    }
+  }
+  const GroupScale gs = group_scale<BITS>(mn, mx);
+  const int te = p.dst_tok + i;
+  const int64_t pair = te >> 1;
+  const int par = te & 1;
+  const int64_t rb = int64_t(p.D) * BITS / 8;
+  uint8_t* blk = p.codes + s * p.codes_stream_stride + pair * 2 * rb;
+  constexpr int kPerUnit = 16 / BITS;   // codes per 16-bit unit
+  const int units = G / kPerUnit;
+  const int u0 = g * units;
+  for (int u = 0; u < units; ++u) {
+    uint32_t unit = 0;
+#pragma unroll
+    for (int k = 0; k < kPerUnit; ++k)
+      unit |= encode<BITS>(h2f(x[u * kPerUnit + k]), gs) << (k * BITS);
+    *reinterpret_cast<uint16_t*>(blk + 4 * (u0 + u) + 2 * par) = static_cast<uint16_t>(unit);
+  }
+  uint32_t* meta = reinterpret_cast<uint32_t*>(p.meta + s * p.meta_stream_stride);
+  meta[(pair * NG + g) * 2 + par] = gs.s16 | (gs.z16 << 16);
+}
+
+// fp16 row copy, 16 bytes per thread.
+__global__ void __launch_bounds__(256) copy_rows_kernel(
+    const uint16_t* src, int64_t sss, int64_t srs, const int32_t* rows, uint8_t* dst,
+    int64_t dss, int32_t row0, int32_t n_streams, int32_t D, int32_t n_rows) {
+  const int cpr = D / 8;
+  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = int64_t(n_streams) * n_rows * cpr;
+  if (item >= total) return;
+  const int c = int(item % cpr);
+  const int64_t rest = item / cpr;
+  const int i = int(rest % n_rows);
+  const int64_t s = rest / n_rows;
+  const int64_t r = rows ? rows[i] : i;
+  const uint4 v = *reinterpret_cast<const uint4*>(src + s * sss + r * srs + c * 8);
+  *reinterpret_cast<uint4*>(dst + s * dss + int64_t(row0 + i) * D * 2 + c * 16) = v;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_keys(const QuantParams& p, hipStream_t s) {
+  const dim3 grid(p.n_tok / p.G, p.n_streams), block(p.D);
+  switch (p.bits) {
+    case 2: hipLaunchKernelGGL(quantize_keys_kernel<2>, grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL(quantize_keys_kernel<4>, grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL(quantize_keys_kernel<8>, grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_values(const QuantParams& p, hipStream_t s) {
+  const int NG = p.D / p.G;
+  const int64_t total = int64_t(p.n_streams) * p.n_tok * NG;
+  const dim3 grid(unsigned((total + 255) / 256)), block(256);
+  switch (p.bits) {
+    case 2: hipLaunchKernelGGL(quantize_values_kernel<2>, grid, block, 0, s, p, NG); break;
+    case 4: hipLaunchKernelGGL(quantize_values_kernel<4>, grid, block, 0, s, p, NG); break;
+    case 8: hipLaunchKernelGGL(quantize_values_kernel<8>, grid, block, 0, s, p, NG); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const uint16_t* src, int64_t src_stream_stride,
+                            int64_t src_row_stride, const int32_t* rows,
+                            uint8_t* dst, int64_t dst_stream_bytes, int32_t dst_row0,
+                            int32_t n_streams, int32_t D, int32_t n_rows, hipStream_t s) {
+  const int64_t total = int64_t(n_streams) * n_rows * (D / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s,
+                     src, src_stream_stride, src_row_stride, rows, dst, dst_stream_bytes,
+                     dst_row0, n_streams, D, n_rows);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

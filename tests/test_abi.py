@@ -1,0 +1,143 @@
+"""The C-ABI library loads, exports every symbol include/kvq.h declares, and
+rejects bad arguments on the host with the documented status codes (before
+any HIP call, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.helpers import ROOT, ensure_built
+
+ensure_built()
+import decode_attention_kivi_amd as kvq  # noqa: E402
+from decode_attention_kivi_amd import KVQ_KEYS, KVQ_VALUES, KvqError  # noqa: E402
+
+EINVAL, EALIGN, EUNSUP, EWS = 1, 2, 3, 4
+A = 1 << 20        # a fake, 16-byte aligned device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(kvq.library_path())
+    names = declared_functions()
+    assert {"kvq_quantize_append", "kvq_reorder_windows", "kvq_decode_attn"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings():
+    assert kvq.kvq_abi_version() == 1
+    assert kvq.kvq_strerror(0) == "ok"
+    assert "workspace" in kvq.kvq_strerror(4)
+    assert kvq.kvq_strerror(99) == "unknown status"
+
+
+def _q(**kw):
+    args = dict(which=KVQ_KEYS, bits=2, group=32, n_streams=2, d_h=128, n_tok=64, src=A,
+                src_stream_stride=128 * 64, src_row_stride=128, src_rows=None, codes=A,
+                codes_stream_stride=4096, meta=A, meta_stream_stride=4096, dst_tok=0, stream=0)
+    args.update(kw)
+    return kvq.kvq_quantize_append(**args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(which=7), EINVAL), (dict(bits=3), EINVAL), (dict(group=16), EUNSUP),
+    (dict(d_h=96), EUNSUP), (dict(n_tok=33), EINVAL), (dict(dst_tok=16), EINVAL),
+    (dict(src=None), EINVAL), (dict(meta=None), EINVAL), (dict(src=A + 2), EALIGN),
+    (dict(codes=A + 8), EALIGN), (dict(src_row_stride=132), EALIGN),
+    (dict(src_row_stride=64), EINVAL), (dict(codes_stream_stride=4100), EALIGN),
+    (dict(n_streams=0), EINVAL), (dict(n_streams=70000), EUNSUP),
+    (dict(which=KVQ_VALUES, group=128, d_h=64), EUNSUP),
+])
+def test_quantize_rejects(kw, code):
+    with pytest.raises(KvqError) as e:
+        _q(**kw)
+    assert e.value.status == code
+
+
+def test_quantize_empty_is_a_noop():
+    _q(n_tok=0)                      # returns OK without launching anything
+    _q(which=KVQ_VALUES, n_tok=0, dst_tok=3)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_h=32), EUNSUP), (dict(n_rows=-1), EINVAL), (dict(dst=A + 4), EALIGN),
+    (dict(src_stream_stride=12), EALIGN), (dict(src=None), EINVAL),
+])
+def test_residual_append_rejects(kw, code):
+    args = dict(n_streams=2, d_h=64, n_rows=1, src=A, src_stream_stride=64, src_row_stride=64,
+                dst=A, dst_stream_stride=64 * 8, dst_row=0, stream=0)
+    args.update(kw)
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_residual_append(**args)
+    assert e.value.status == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_windows=0), EINVAL), (dict(n_windows=70000), EINVAL), (dict(window_tokens=48), EINVAL),
+    (dict(group=16), EUNSUP), (dict(perm=None), EINVAL), (dict(perm=A + 2), EALIGN),
+])
+def test_reorder_rejects(kw, code):
+    args = dict(win_bits=A, n_windows=8, window_tokens=64, group=32, d_h=128, perm=A, segs=A,
+                n_segs=A, row_gather=None, stream=0)
+    args.update(kw)
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_reorder_windows(**args)
+    assert e.value.status == code
+
+
+def _decode(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, d_h=128, group=32, sm_scale=0.0884, q=A,
+                k_segs=[(2, 0, 256, 0, 0)], v_segs=[(2, 0, 200, 0, 0)],
+                k_codes=A, k_codes_stride=1 << 16, k_meta=A, k_meta_stride=1 << 16,
+                v_codes=A, v_codes_stride=1 << 16, v_meta=A, v_meta_stride=1 << 16,
+                k_res=A, n_k_res=3, k_res_stride=128 * 128, v_res=A, n_v_res=59,
+                v_res_stride=128 * 128, out=A, split_tokens=64)
+    base.update(kw)
+    return kvq.make_decode_args(**base)
+
+
+def test_workspace_size_follows_the_split_plan():
+    a = _decode()
+    # cells: [0,200) K run + V run, [200,256) K run + V residual, [256,259) residual
+    # splits of 64: 4 + 1 + 1 = 6; workspace = streams*splits*gq*(d+2)*4
+    assert kvq.kvq_decode_attn_workspace(a) == 2 * 2 * 6 * 4 * 130 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_q_heads=7), EINVAL), (dict(n_q_heads=2 * 16), EUNSUP), (dict(d_h=96), EUNSUP),
+    (dict(n_k_res=4), EINVAL), (dict(k_segs=[(2, 0, 250, 0, 0)], n_k_res=9), EINVAL),
+    (dict(k_segs=[(3, 0, 256, 0, 0)]), EINVAL), (dict(k_segs=[(2, 0, 256, 8, 0)]), EALIGN),
+    (dict(v_segs=[(2, 5, 200, 0, 0)]), EINVAL), (dict(q=A + 2), EALIGN),
+    (dict(k_codes_stride=100), EALIGN), (dict(k_res_stride=12), EALIGN),
+    (dict(sm_scale=float("nan")), EINVAL), (dict(k_codes=None), EINVAL),
+    (dict(split_tokens=1 << 20), EUNSUP), (dict(group=128, d_h=64), EUNSUP),
+])
+def test_decode_rejects(kw, code):
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_decode_attn_workspace(_decode(**kw))
+    assert e.value.status == code
+
+
+def test_decode_needs_workspace():
+    a = _decode()
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_decode_attn(a, 0)
+    assert e.value.status == EWS
+    a.workspace = A
+    a.workspace_bytes = kvq.kvq_decode_attn_workspace(a) - 4
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_decode_attn(a, 0)
+    assert e.value.status == EWS
+
+
+def test_binding_refuses_host_tensors_as_device_buffers():
+    import torch
+    with pytest.raises(ValueError):
+        _q(src=torch.zeros(16, dtype=torch.float16))

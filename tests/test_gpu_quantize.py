@@ -1,0 +1,107 @@
+"""GPU parity of kvq_quantize_append against the oracle: codes, scales and
+zero points bit-exact, packed in the header's layout."""
+import numpy as np
+import pytest
+
+from tests.helpers import ensure_built
+from oracle import pack
+from oracle.quant import quantize_keys, quantize_values
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    ensure_built()
+    import decode_attention_kivi_amd as m
+    return m
+
+
+def _data(rng, n_streams, n, d, kind="normal"):
+    x = rng.standard_normal((n_streams, n, d)).astype(np.float32)
+    x[:, :, rng.choice(d, 3, replace=False)] *= 9.0
+    if kind == "special":
+        x[:, : min(n, 40), :16] = 0.5                  # constant groups: scale 0
+        x[:, :, 20] = -0.0                             # negative zeros
+        x[0, 3, :] = 1e-6                              # subnormal-range values
+    return x.astype(np.float16)
+
+
+def _run(kvq, which, bits, G, d, n_tok, dst_tok, gather, kind="normal", seed=0):
+    import torch
+    rng = np.random.default_rng([seed, which, bits, G, d, n_tok, dst_tok])
+    S = 3
+    n_src = n_tok + 5
+    x = _data(rng, S, n_src, d, kind)
+    rows = rng.permutation(n_src)[:n_tok].astype(np.int32) if gather else np.arange(n_tok, dtype=np.int32)
+    total = dst_tok + n_tok
+    if which == kvq.KVQ_KEYS:
+        cb, mb = total * d * bits // 8, total // G * d * 4
+    else:
+        cb, mb = (total + 1) // 2 * d * bits // 4, (total + 1) // 2 * (d // G) * 8
+    cb, mb = (cb + 15) // 16 * 16, (mb + 15) // 16 * 16
+    dev = torch.device("cuda")
+    xt = torch.from_numpy(x).to(dev)
+    codes = torch.zeros(S, cb, dtype=torch.uint8, device=dev)
+    meta = torch.zeros(S, mb, dtype=torch.uint8, device=dev)
+    rt = torch.from_numpy(rows).to(dev) if gather else None
+    print(f"quantize which={which} bits={bits} G={G} d={d} n={n_tok} dst={dst_tok} gather={gather}", flush=True)
+    kvq.kvq_quantize_append(which, bits, G, S, d, n_tok, xt, n_src * d, d, rt, codes, cb, meta, mb, dst_tok)
+    torch.cuda.synchronize()
+    got_c, got_m = codes.cpu().numpy(), meta.cpu().numpy()
+    for s in range(S):
+        src = x[s][rows]
+        if which == kvq.KVQ_KEYS:
+            c, sc, z = quantize_keys(src, bits, G)
+            full = np.zeros((total, d), np.uint8)
+            full[dst_tok:] = c
+            exp_c = pack.pack_rows(full, bits).reshape(-1)
+            ms, mz = np.zeros((total // G, d), np.float16), np.zeros((total // G, d), np.float16)
+            ms[dst_tok // G:], mz[dst_tok // G:] = sc, z
+            exp_m = pack.pack_key_meta(ms, mz).view(np.uint8)
+        else:
+            c, sc, z = quantize_values(src, bits, G)
+            full = np.zeros((total, d), np.uint8)
+            full[dst_tok:] = c
+            exp_c = pack.pack_values(full, bits).reshape(-1)
+            ms, mz = np.zeros((total, d // G), np.float16), np.zeros((total, d // G), np.float16)
+            ms[dst_tok:], mz[dst_tok:] = sc, z
+            exp_m = pack.pack_value_meta(ms, mz).view(np.uint8)
+        assert np.array_equal(got_c[s, :exp_c.size], exp_c), f"codes differ (stream {s})"
+        assert not got_c[s, exp_c.size:].any()
+        assert np.array_equal(got_m[s, :exp_m.size], exp_m), f"scale/zero differ (stream {s})"
+        assert not got_m[s, exp_m.size:].any()
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_keys_bit_exact(kvq, bits, d, G):
+    _run(kvq, kvq.KVQ_KEYS, bits, G, d, n_tok=2 * G, dst_tok=G, gather=False)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("d,G", [(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)])
+def test_values_bit_exact_odd_offsets(kvq, bits, d, G):
+    _run(kvq, kvq.KVQ_VALUES, bits, G, d, n_tok=37, dst_tok=5, gather=False)
+    _run(kvq, kvq.KVQ_VALUES, bits, G, d, n_tok=1, dst_tok=0, gather=False)
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_gather_and_special_values(kvq, which, bits):
+    _run(kvq, which, bits, 32, 128, n_tok=96, dst_tok=0, gather=True, kind="special")
+
+
+def test_fp16_run_is_a_copy(kvq):
+    import torch
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 40, 64)).astype(np.float16)
+    rows = rng.permutation(40)[:32].astype(np.int32)
+    dev = torch.device("cuda")
+    out = torch.zeros(2, 48 * 64 * 2, dtype=torch.uint8, device=dev)
+    print("quantize bits=16 copy", flush=True)
+    kvq.kvq_quantize_append(kvq.KVQ_VALUES, 16, 32, 2, 64, 32, torch.from_numpy(x).to(dev), 40 * 64,
+                            64, torch.from_numpy(rows).to(dev), out, out.stride(0), None, 0, 16)
+    got = out.cpu().numpy().view(np.float16).reshape(2, 48, 64)
+    assert np.array_equal(got[:, 16:], x[:, rows]) and not got[:, :16].view(np.uint16).any()
