@@ -14,7 +14,9 @@ with these further readings where the pages are silent:
   z, so the encoder and the decoder use the same numbers;
 * rounding is round-half-even (the pages only say "nearest");
 * codes are clamped to [0, 2^b - 1] (WindowQuant Eq. 14 clamps);
-* a group whose fp16 scale is 0 gets all codes 0 (it dequantizes to z).
+* a group whose fp16 scale is 0 gets all codes 0 (it dequantizes to z);
+* zero extrema are taken as +0 (min + 0 and max + 0 in fp32): the minimum
+  of {-0, +0} is not ordered, and z and s each need a single encoding.
 
 Arithmetic is IEEE fp32: fp16 inputs are widened exactly, the range and the
 division are single fp32 operations, nothing is fused.
@@ -44,8 +46,8 @@ def quantize_groups(x: np.ndarray, bits: int):
     assert x.dtype == np.float16 and bits in (2, 4, 8)
     qmax = (1 << bits) - 1
     x32 = x.astype(np.float32)
-    mn = x32.min(axis=-1)
-    mx = x32.max(axis=-1)
+    mn = x32.min(axis=-1) + np.float32(0)        # -0 -> +0
+    mx = x32.max(axis=-1) + np.float32(0)        # -0 -> +0
     s32 = (mx - mn) / np.float32(qmax)           # fp32 subtract, fp32 divide
     s16 = s32.astype(np.float16)                 # round to nearest even
     z16 = mn.astype(np.float16)                  # exact: mn is an fp16 value

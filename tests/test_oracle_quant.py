@@ -41,8 +41,9 @@ def test_worked_examples():
         x = np.array(ex["x"], dtype=np.float16)[None, :]
         codes, s16, z16 = quantize_groups(x, ex["bits"])
         assert codes[0].tolist() == ex["codes"], ex["why"]
-        assert float(s16[0]) == ex["s16"], ex["why"]
-        assert float(z16[0]) == ex["z16"], ex["why"]
+        # compare bit patterns: the sign of a zero matters
+        assert s16[:1].view(np.uint16)[0] == np.float16(ex["s16"]).view(np.uint16), ex["why"]
+        assert z16[:1].view(np.uint16)[0] == np.float16(ex["z16"]).view(np.uint16), ex["why"]
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
