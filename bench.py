@@ -91,6 +91,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough for 2x 256 MB)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one fp16 row copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -107,6 +109,16 @@ def main():
     w = workloads.get(args.workload)
     assert not w.mixed, "bench runs the uniform KIVI workloads"
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        # a plain copy of known size through the library's row-copy kernel:
+        # its FETCH_SIZE / WRITE_SIZE per byte calibrate the traffic counters
+        import decode_attention_kivi_amd as kvq
+        rows = args.copy_probe_mib * (1 << 20) // 256
+        src = torch.ones(rows, 128, dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        kvq.kvq_residual_append(1, 128, rows, src, 0, 128, dst, 0, 0)
+        torch.cuda.synchronize()
+        del src, dst
     L = w.context
     k, v = workloads.full_kv(w)
     q = torch.from_numpy(workloads.queries(w)).to(dev)

@@ -114,13 +114,16 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   int GQ = 1;
   while (GQ < gq) GQ *= 2;
   const int64_t streams = int64_t(a->batch) * a->n_kv_heads;
+  // a workgroup covers up to kWaves * wave_tokens(GQ) tokens; smaller splits
+  // only when the grid would otherwise leave most of the GPU idle
+  const int st_max = kvq::kWaves * kvq::wave_tokens(GQ);
   int st_tokens = a->split_tokens;
   if (st_tokens == 0) {
-    st_tokens = 1024;
-    while (st_tokens > 64 && kvq::decode_lds_bytes(D, GQ, st_tokens, G) > kvq::kLdsLimit) st_tokens /= 2;
-    while (st_tokens > 128 && streams * count_splits(cells, st_tokens) < 2048) st_tokens /= 2;
+    st_tokens = st_max;
+    while (st_tokens > 64 && streams * count_splits(cells, st_tokens) < 1024) st_tokens /= 2;
   }
-  if (kvq::decode_lds_bytes(D, GQ, st_tokens, G) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
+  if (st_tokens > st_max) return KVQ_EUNSUPPORTED;
+  if (kvq::decode_lds(D, GQ).total > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
   int64_t n_splits = 0;
   for (Cell& c : cells) {
     c.split0 = int32_t(n_splits);
@@ -151,6 +154,7 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   p.Hkv = a->n_kv_heads;
   p.D = D;
   p.G = G;
+  p.lg_g = G == 32 ? 5 : G == 64 ? 6 : 7;
   p.gq = gq;
   p.n_kq = int32_t(nk);
   p.n_vq = int32_t(nv);

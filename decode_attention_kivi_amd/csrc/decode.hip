@@ -1,23 +1,27 @@
 // Decode-step attention over a low-bit quantized KV cache, split over the
-// context (FlashDecoding dataflow, as the VQ-LLM note's reference [10]
+// context (the FlashDecoding dataflow that the VQ-LLM note's reference [10]
 // describes) with a final cross-split softmax merge.
 //
-// Per workgroup: one cache stream (batch b, kv head h), the GQ query heads
+// A workgroup takes one cache stream (batch b, kv head h), the GQ query heads
 // that share it, and a range of tokens whose keys come from one source (a
 // quantized run or the fp16 residual) and whose values come from one source.
-//   1. q*s per key group and channel (fp16 pairs) and the group's bias
-//      sum_c q_c z_c are staged in LDS (per-channel key scales: KIVI note,
-//      "Method details");
-//   2. logits: 16-byte loads of packed codes, in-register unpack of code
-//      pairs into fp16 (offset + code), v_dot2_f32_f16 against q*s; the
-//      residual part is q . K_r over fp16 rows (A = Concat([A_g, A_r]));
-//   3. the split's max and sum of exp2(logit - max), one softmax over the
+// Each of its four waves streams its own sub-range independently; the only
+// workgroup barrier is the final combine.  Per wave:
+//   1. q*s for every key group of the range (per-channel key scales, KIVI
+//      note "Method details"), as fp16 hi + lo pairs, and the group bias
+//      sum_c q_c z_c, into the wave's LDS area;
+//   2. logits: prefetched 16-byte loads of packed codes, unpack of code pairs
+//      into fp16 (offset + code) by mask-and-or with an exponent constant,
+//      v_dot2_f32_f16 against q*s; residual rows dot q directly
+//      (A = Concat([A_g, A_r]));
+//   3. the range's max and sum of exp2(logit - max): one softmax over the
 //      concatenation (KIVI Algorithm 1; WindowQuant Sec. 3.3.1);
-//   4. A.V: value codes are stored as token pairs, so one fp16 pair holds the
-//      same channel of two tokens and v_dot2 accumulates p*s over two tokens
-//      per instruction; the per-token zero points are summed separately;
-//   5. partial (max, sum, o[d]) per query head go to the workspace; the merge
-//      kernel rescales and adds them.
+//   4. A.V over token-pair value blocks: one fp16 pair holds the same channel
+//      of two tokens, so v_dot2 applies both tokens' p*s at once; sum(p*z) and
+//      sum(p*s) per group are kept apart and folded in at the end; partials
+//      are reduced with DPP row rotations and a 4-row LDS stage;
+//   5. the four waves' (max, sum, o[d]) are combined and written as the
+//      split's partial; the merge kernel rescales and adds the splits.
 // Logits are kept in base 2 (q is pre-scaled by sm_scale * log2 e).
 
 #include "kvq_internal.h"
@@ -27,211 +31,298 @@ namespace kvq {
 namespace {
 
 constexpr int NT = kThreads;
-constexpr int U = 2;   // 16-byte loads in flight per thread
+constexpr int NB = 8;    // loads per batch in the key streaming loops (wave instructions)
+constexpr int NBV = 4;   // loads per batch in the value streaming loops
 
-struct Lds {
-  float* qf;        // [GQ][D]     q * scale_log2 (fp32)
-  uint32_t* qh;     // [GQ][D/2]   q as fp16 pairs
-  uint32_t* qs;     // [NGMAX][GQ][D/2]  fp16(q*s) pairs per key group
-  float* bias;      // [NGMAX][GQ] sum_c q_c z_c - sum_c (q*s)_c * offset_c
-  float* p;         // [GQ][ST]    logits, then probabilities
-  float* red;       // [kRedFloats] value-partial reduction
-  float* scratch;   // [64]
+// Make this wave's LDS writes visible to its own later LDS reads.  LDS
+// operations of one wave execute in order; this only keeps the compiler from
+// moving memory operations across the point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// v + rotate_right(v, s) within each row of 16 lanes.
+template <int S>
+__device__ __forceinline__ float row_ror_add(float v) {
+  return v + __builtin_amdgcn_update_dpp(0.f, v, 0x120 + S, 0xF, 0xF, false);
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16) with
+// DPP: quad permutations, then half-row and row mirrors.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if (N >= 2) x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+  if (N >= 4) x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+  if (N >= 8) x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // half mirror
+  if (N >= 16) x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false); // mirror
+  return x;
+}
+
+struct WaveLds {
+  float* logit;      // [GQ][LT] logits by token slot; later the [4][D] value rows
+  uint16_t* p16;     // [GQ][LT] fp16 probabilities, zero outside the wave's tokens
+  uint32_t* qs;      // [NGW][GQ][2][D/2] q*s fp16 hi pairs then lo pairs
+  float* bias;       // [NGW][GQ]
+  float* ow;         // [GQ][D+2] (m, l, o[D]) of the wave (aliases qs/bias)
 };
 
 template <int D, int GQ>
-__device__ __forceinline__ Lds carve(unsigned char* smem, int ST, int G) {
-  const int ngmax = (ST + G - 1) / G + 1;
-  Lds L;
-  unsigned char* ptr = smem;
-  L.qf = reinterpret_cast<float*>(ptr);       ptr += GQ * D * 4;
-  L.qh = reinterpret_cast<uint32_t*>(ptr);    ptr += GQ * D * 2;
-  L.qs = reinterpret_cast<uint32_t*>(ptr);    ptr += size_t(ngmax) * GQ * D * 2;
-  L.bias = reinterpret_cast<float*>(ptr);     ptr += size_t(ngmax) * GQ * 4;
-  L.p = reinterpret_cast<float*>(ptr);        ptr += size_t(GQ) * ST * 4;
-  L.red = reinterpret_cast<float*>(ptr);      ptr += size_t(kRedFloats) * 4;
-  L.scratch = reinterpret_cast<float*>(ptr);
-  return L;
+__device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
+  constexpr int NGW = wave_tokens(GQ) / 32 + 1;
+  constexpr DecodeLds lay = decode_lds(D, GQ);
+  unsigned char* base = smem + lay.block + int64_t(wave) * lay.wave;
+  WaveLds W;
+  W.logit = reinterpret_cast<float*>(base);
+  W.p16 = reinterpret_cast<uint16_t*>(base + lay.logit);
+  W.qs = reinterpret_cast<uint32_t*>(base + lay.logit + lay.p16);
+  W.bias = reinterpret_cast<float*>(base + lay.logit + lay.p16 + int64_t(NGW) * GQ * D * 4);
+  W.ow = reinterpret_cast<float*>(base + lay.logit + lay.p16);
+  return W;
 }
 
+__device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
+__device__ __forceinline__ uint32_t as_u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
 // ---------------------------------------------------------------------------
-// Keys from a quantized run (bits 2/4/8), tokens [t0, t1) of the split.
+// Keys of run tokens [r0, r1) (bits 2/4/8) -> logits at slots slot0 + (t - r0).
+//
+// Per key group: hi = fp16(q'*s), lo = fp16(q'*s - hi) with packed fp16 ops
+// (q' = q * 2^-8 exactly, so no product can overflow fp16); a single fp16
+// q*s is too coarse for outlier channels, whose large logits would carry its
+// 2^-11 relative error into the softmax, while hi + lo keeps ~22 bits.  The
+// bias sum_c q'_c z_c - sum_c (hi + lo)_c * offset_c comes from three dot2.
 template <int D, int GQ, int BITS>
-__device__ void keys_quantized(const DecodeParams& P, const Lds& L, int64_t stream,
-                               const Run& run, int t0, int t1) {
+__device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qh16,
+                               int64_t stream, const Run& run, int r0, int r1, int slot0,
+                               int lane) {
+  constexpr int LT = wave_tokens(GQ) + 4;
   constexpr int RB = D * BITS / 8;       // bytes per token row
   constexpr int CPR = RB / 16;           // 16-byte chunks per row
+  constexpr int TPI = 64 / CPR;          // tokens per wave instruction
   constexpr int PPC = 64 / BITS;         // fp16 pairs per chunk
   constexpr int NP = Unpack<BITS>::NP;   // pairs per 32-bit word
   constexpr int CPW = 32 / BITS;         // channels per 32-bit word
   constexpr int HD = D / 2;              // pairs per row
-  const int ST = P.split_tokens;
-  const int G = P.G;
-  const int tid = threadIdx.x;
-  const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
-  const int j0 = r0 / G;
-  const int ng = (r1 - 1) / G - j0 + 1;
+  constexpr int GPI = 64 / HD;           // key groups per meta iteration
+  constexpr int NGW = wave_tokens(GQ) / 32 + 1;
+  constexpr int MI = (NGW + GPI - 1) / GPI;
+  const int lg = P.lg_g;
+  const int j0 = r0 >> lg;
+  const int ng = ((r1 - 1) >> lg) - j0 + 1;
+  const int rofs = r0 & (P.G - 1);
+  const int n = r1 - r0;
   const uint8_t* codes = P.k_codes + stream * P.k_codes_stride + run.code_off;
   const uint32_t* meta = reinterpret_cast<const uint32_t*>(
       P.k_meta + stream * P.k_meta_stride + run.meta_off);
+  const int n_inst = (n + TPI - 1) / TPI;
+  const int my_t = lane / CPR, my_c = lane % CPR;
 
-  // 1. q*s pairs and bias of every group the split touches.  Pair pi of a
-  //    row is word w = pi/NP, position k = pi%NP: channels (w*CPW + k) and
-  //    (w*CPW + k + NP), the two codes one unpacked word pair holds.
-  const int nm = ng * HD;
-  for (int base = 0; base < nm; base += NT) {
-    const int item = base + tid;
-    const bool valid = item < nm;
-    const int jl = valid ? item / HD : 0;
-    const int pi = item % HD;
-    const int w = pi / NP, k = pi % NP;
-    const int clo = w * CPW + k, chi = clo + NP;
-    uint32_t mlo = 0, mhi = 0;
-    if (valid) {
-      const uint32_t* m = meta + int64_t(j0 + jl) * D;
-      mlo = m[clo];
-      mhi = m[chi];
-    }
-    const float slo = h2f(mlo & 0xffffu), zlo = h2f(mlo >> 16);
-    const float shi = h2f(mhi & 0xffffu), zhi = h2f(mhi >> 16);
-    const float off = Unpack<BITS>::offset(k);
+  // the first batch of code loads is in flight during the meta work; every
+  // load address is clamped into the range, so no load sits behind a branch
+  auto load = [&](int i) {
+    const int r = r0 + min(i * TPI + my_t, n - 1);
+    return *reinterpret_cast<const uint4*>(codes + int64_t(r) * RB + my_c * 16);
+  };
+  uint4 buf[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) buf[u] = load(u);
+
+  // meta work: lane -> pair pi of a row (word pi/NP, position pi%NP, i.e.
+  // channels clo and clo + NP) of group it*GPI + lane/HD
+  const int pi = lane % HD, gsub = lane / HD;
+  const int kq = pi % NP;
+  const int clo = (pi / NP) * CPW + kq, chi = clo + NP;
+  uint32_t mlo[MI], mhi[MI];
+#pragma unroll
+  for (int it = 0; it < MI; ++it) {
+    const int j = min(it * GPI + gsub, ng - 1);
+    const uint32_t* m = meta + int64_t(j0 + j) * D;
+    mlo[it] = m[clo];
+    mhi[it] = m[chi];
+  }
+  half2_t qk[GQ];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+    qk[h] = as_h2(uint32_t(qh16[h * D + clo]) | (uint32_t(qh16[h * D + chi]) << 16)) *
+            as_h2(0x1C001C00u);                                   // * 2^-8, exact
+  const _Float16 off = static_cast<_Float16>(Unpack<BITS>::offset(kq));
+  const half2_t nego = {-off, -off};
+#pragma unroll
+  for (int it = 0; it < MI; ++it) {
+    const int j = it * GPI + gsub;
+    const bool valid = j < ng;
+    if (it * GPI >= ng) continue;          // uniform; keeps the loop fully unrolled
+    const half2_t s2 = as_h2((mlo[it] & 0xffffu) | (mhi[it] << 16));
+    const half2_t z2 = as_h2((mlo[it] >> 16) | (mhi[it] & 0xffff0000u));
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      const float qlo = L.qf[h * D + clo], qhi = L.qf[h * D + chi];
-      const uint32_t a = f2h(qlo * slo), c = f2h(qhi * shi);
-      float bp = qlo * zlo + qhi * zhi - (h2f(a) + h2f(c)) * off;
-#pragma unroll
-      for (int m = HD / 2; m >= 1; m >>= 1) bp += __shfl_xor(bp, m);
+      const half2_t hi = qk[h] * s2;
+      const half2_t lo = __builtin_elementwise_fma(qk[h], s2, -hi);
+      float bp = __builtin_amdgcn_fdot2(qk[h], z2, 0.f, false);
+      bp = __builtin_amdgcn_fdot2(hi, nego, bp, false);
+      bp = __builtin_amdgcn_fdot2(lo, nego, bp, false);
+      bp = group_sum<16>(bp);
+      bp += __shfl_xor(bp, 16);
+      if (HD == 64) bp += __shfl_xor(bp, 32);
       if (valid) {
-        L.qs[(jl * GQ + h) * HD + pi] = a | (c << 16);
-        if (pi == 0) L.bias[jl * GQ + h] = bp;
+        uint32_t* qs = W.qs + (j * GQ + h) * (2 * HD);
+        qs[pi] = as_u32(hi);
+        qs[HD + pi] = as_u32(lo);
+        if (pi == 0) W.bias[j * GQ + h] = bp;
       }
     }
   }
-  __syncthreads();
+  wave_lds_sync();
 
-  // 2. logits: item = (token, 16-byte chunk of its row).
-  const int ni = (r1 - r0) * CPR;
-  for (int base = 0; base < ni; base += NT * U) {
-    uint4 cw[U];
+  const float sc = P.scale_log2 * 256.f;   // undo the 2^-8
+  for (int i0 = 0;;) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int item = base + u * NT + tid;
-      if (item < ni) {
-        const int r = r0 + item / CPR, c = item % CPR;
-        cw[u] = *reinterpret_cast<const uint4*>(codes + int64_t(r) * RB + c * 16);
-      } else {
-        cw[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int item = base + u * NT + tid;
-      const bool valid = item < ni;
-      const int tl = valid ? item / CPR : 0;
-      const int c = item % CPR;
-      const int r = r0 + tl;
-      const int jl = r / G - j0;
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      const uint4 cw = buf[u];
+      const int tl = i * TPI + my_t;
+      const bool valid = tl < n;
+      const int jl = (min(tl, n - 1) + rofs) >> lg;
       uint32_t v[4][NP];
-      Unpack<BITS>::run(cw[u].x, v[0]);
-      Unpack<BITS>::run(cw[u].y, v[1]);
-      Unpack<BITS>::run(cw[u].z, v[2]);
-      Unpack<BITS>::run(cw[u].w, v[3]);
+      Unpack<BITS>::run(cw.x, v[0]);
+      Unpack<BITS>::run(cw.y, v[1]);
+      Unpack<BITS>::run(cw.z, v[2]);
+      Unpack<BITS>::run(cw.w, v[3]);
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const uint32_t* qs = L.qs + (jl * GQ + h) * HD + c * PPC;
+        const uint32_t* qb = W.qs + (jl * GQ + h) * (2 * HD) + my_c * PPC;
+        const uint4* qhi = reinterpret_cast<const uint4*>(qb);
+        const uint4* qlo = reinterpret_cast<const uint4*>(qb + HD);
         float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
+        for (int w = 0; w < 4; ++w) {
 #pragma unroll
-          for (int k = 0; k < NP; ++k) acc = dot2(qs[w * NP + k], v[w][k], acc);
+          for (int q4 = 0; q4 < NP / 4 + (NP < 4 ? 1 : 0); ++q4) {
+            const int pbase = w * NP + q4 * 4;   // the NP pairs of word w
+            uint32_t hi[4], lo[4];
+            if (NP >= 4) {
+              const uint4 x = qhi[pbase / 4], y = qlo[pbase / 4];
+              hi[0] = x.x; hi[1] = x.y; hi[2] = x.z; hi[3] = x.w;
+              lo[0] = y.x; lo[1] = y.y; lo[2] = y.z; lo[3] = y.w;
+            } else {
+              const uint2 x = reinterpret_cast<const uint2*>(qb)[pbase / 2];
+              const uint2 y = reinterpret_cast<const uint2*>(qb + HD)[pbase / 2];
+              hi[0] = x.x; hi[1] = x.y; lo[0] = y.x; lo[1] = y.y;
+            }
 #pragma unroll
-        for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-        if (valid && c == 0) L.p[h * ST + (r + run.tok_begin - t0)] = acc + L.bias[jl * GQ + h];
+            for (int e = 0; e < (NP >= 4 ? 4 : NP); ++e) {
+              acc = dot2(hi[e], v[w][q4 * 4 + e], acc);
+              acc = dot2(lo[e], v[w][q4 * 4 + e], acc);
+            }
+          }
+        }
+        acc = group_sum<CPR>(acc);
+        if (valid && my_c == 0) W.logit[h * LT + slot0 + tl] = (acc + W.bias[jl * GQ + h]) * sc;
       }
     }
+    i0 += NB;
+    if (i0 >= n_inst) break;
+    // the whole batch is consumed before the next one is issued, so no load
+    // is in flight across the loop edge and the wait counts stay exact
+#pragma unroll
+    for (int u = 0; u < NB; ++u) buf[u] = load(i0 + u);
   }
 }
 
-// Keys from fp16 rows (the residual, or a 16-bit run): rows[row0 + i], i < nt.
+// Keys from fp16 rows rows[row0 + i], i < n -> logits at slots slot0 + i.
 template <int D, int GQ>
-__device__ void keys_fp16(const DecodeParams& P, const Lds& L, const uint16_t* rows,
-                          int row0, int nt) {
+__device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qh16,
+                          const uint16_t* rows, int row0, int n, int slot0, int lane) {
+  constexpr int LT = wave_tokens(GQ) + 4;
   constexpr int CPR = D / 8;             // 16-byte chunks per row
-  const int ST = P.split_tokens;
-  const int tid = threadIdx.x;
-  const int ni = nt * CPR;
-  for (int base = 0; base < ni; base += NT * U) {
-    uint4 x[U];
+  constexpr int TPI = 64 / CPR;
+  const int n_inst = (n + TPI - 1) / TPI;
+  const int my_t = lane / CPR, my_c = lane % CPR;
+  auto load = [&](int i) {
+    const int t = min(i * TPI + my_t, n - 1);
+    return *reinterpret_cast<const uint4*>(rows + int64_t(row0 + t) * D + my_c * 8);
+  };
+  uint4 buf[NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int item = base + u * NT + tid;
-      if (item < ni) {
-        x[u] = *reinterpret_cast<const uint4*>(rows + int64_t(row0 + item / CPR) * D + (item % CPR) * 8);
-      } else {
-        x[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
+  for (int u = 0; u < NB; ++u) buf[u] = load(u);
+  for (int i0 = 0;;) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int item = base + u * NT + tid;
-      const bool valid = item < ni;
-      const int tl = valid ? item / CPR : 0;
-      const int c = item % CPR;
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      const uint4 x = buf[u];
+      const int t = i * TPI + my_t;
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const uint32_t* qh = L.qh + h * (D / 2) + c * 4;
-        float acc = dot2(qh[0], x[u].x, 0.f);
-        acc = dot2(qh[1], x[u].y, acc);
-        acc = dot2(qh[2], x[u].z, acc);
-        acc = dot2(qh[3], x[u].w, acc);
-#pragma unroll
-        for (int m = CPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-        if (valid && c == 0) L.p[h * ST + tl] = acc * P.scale_log2;
+        const uint4 qq = reinterpret_cast<const uint4*>(qh16 + h * D)[my_c];
+        float acc = dot2(qq.x, x.x, 0.f);
+        acc = dot2(qq.y, x.y, acc);
+        acc = dot2(qq.z, x.z, acc);
+        acc = dot2(qq.w, x.w, acc);
+        acc = group_sum<CPR>(acc);
+        if (t < n && my_c == 0) W.logit[h * LT + slot0 + t] = acc * P.scale_log2;
       }
     }
+    i0 += NB;
+    if (i0 >= n_inst) break;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) buf[u] = load(i0 + u);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Sum the value partials of all threads (slot = threads sharing a channel
-// range) and write o[h][:] of this split.
-template <int D, int CH>
-__device__ __forceinline__ void reduce_write(const Lds& L, const float* vals, int slot,
-                                             int ch0, int nslot, float* o) {
-  __syncthreads();
+// Reduce the per-lane value partials vals[CH] (lanes l with l % CPL == c own
+// channels c*CH .. c*CH+CH-1) across the wave into o[0..D).  The four rows of
+// 16 lanes are combined through W.logit, whose logits are dead by now.
+template <int D, int CPL, int CH>
+__device__ __forceinline__ void wave_reduce_values(const WaveLds& W, float* vals, int lane,
+                                                   float* o) {
 #pragma unroll
-  for (int j = 0; j < CH; ++j) L.red[slot * D + ch0 + j] = vals[j];
-  __syncthreads();
-  for (int ch = threadIdx.x; ch < D; ch += NT) {
-    float s = 0.f;
-    for (int sl = 0; sl < nslot; ++sl) s += L.red[sl * D + ch];
-    o[ch] = s;
+  for (int j = 0; j < CH; ++j) {
+    float x = vals[j];
+    if (CPL <= 8) x = row_ror_add<8>(x);
+    if (CPL <= 4) x = row_ror_add<4>(x);
+    if (CPL <= 2) x = row_ror_add<2>(x);
+    if (CPL <= 1) x = row_ror_add<1>(x);
+    vals[j] = x;
   }
+  // lanes (lane % 16) < CPL of each row of 16 now hold their row's sums
+  float* red = W.logit;
+  const int row = lane >> 4, c = lane & 15;
+  if (c < CPL) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) red[row * D + c * CH + j] = vals[j];
+  }
+  wave_lds_sync();
+  for (int ch = lane; ch < D; ch += 64)
+    o[ch] = (red[ch] + red[D + ch]) + (red[2 * D + ch] + red[3 * D + ch]);
+  wave_lds_sync();
 }
 
-// Values from a quantized run (bits 2/4/8), tokens [t0, t1) of the split.
+// Values of run tokens [r0, r1) (bits 2/4/8).  Pair block P of the run holds
+// run tokens 2P and 2P+1, whose probabilities are the fp16 pair P - r0/2 of
+// W.p16 (slot 2(P - r0/2) is token 2P); the pair after the last is zero.
 template <int D, int GQ, int BITS>
-__device__ void values_quantized(const DecodeParams& P, const Lds& L, int64_t stream,
-                                 const Run& run, int t0, int t1, float* ws) {
+__device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_t stream,
+                                 const Run& run, int r0, int r1, int lane) {
+  constexpr int LT = wave_tokens(GQ) + 4;
   constexpr int RB = D * BITS / 8;
   constexpr int CPP = 2 * RB / 16;        // 16-byte chunks per pair block
+  constexpr int PPI = 64 / CPP;           // pair blocks per wave instruction
   constexpr int CPCV = 64 / BITS;         // channels per chunk
   constexpr int NP = Unpack<BITS>::NP;    // channels per 16-bit unit
   constexpr int HPP = (GQ * CPCV <= 64) ? GQ : ((64 / CPCV) > 0 ? (64 / CPCV) : 1);
-  const int ST = P.split_tokens;
-  const int G = P.G;
-  const int NG = D / G;
-  const int tid = threadIdx.x;
-  const int c = tid % CPP;                // fixed chunk of this thread
-  const int slot = tid / CPP;
-  const int g = (c * CPCV) / G;
-  const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
+  const int NG = D >> P.lg_g;
+  const int my_p = lane / CPP, my_c = lane % CPP;
+  const int g = (my_c * CPCV) >> P.lg_g;
   const int p0 = r0 >> 1;
   const int np = ((r1 - 1) >> 1) - p0 + 1;
-  const int ni = np * CPP;
+  const int n_inst = (np + PPI - 1) / PPI;
   const uint8_t* codes = P.v_codes + stream * P.v_codes_stride + run.code_off;
   const uint8_t* meta = P.v_meta + stream * P.v_meta_stride + run.meta_off;
+  const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16);
+  const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
   for (int hp = 0; hp < GQ; hp += HPP) {
     float acc[HPP][CPCV];
@@ -243,96 +334,89 @@ __device__ void values_quantized(const DecodeParams& P, const Lds& L, int64_t st
 #pragma unroll
       for (int j = 0; j < CPCV; ++j) acc[hh][j] = 0.f;
     }
-    for (int base = 0; base < ni; base += NT * U) {
-      uint4 cw[U];
-      uint2 mw[U];
+    auto load = [&](int i, uint4& c4, uint2& m2) {
+      const int64_t pr = p0 + min(i * PPI + my_p, np - 1);
+      c4 = *reinterpret_cast<const uint4*>(codes + pr * (2 * RB) + my_c * 16);
+      m2 = *reinterpret_cast<const uint2*>(meta + (pr * NG + g) * 8);
+    };
+    uint4 cb[NBV];
+    uint2 mb[NBV];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int item = base + u * NT + tid;
-        if (item < ni) {
-          const int64_t pr = p0 + item / CPP;
-          cw[u] = *reinterpret_cast<const uint4*>(codes + pr * (2 * RB) + c * 16);
-          mw[u] = *reinterpret_cast<const uint2*>(meta + (pr * NG + g) * 8);
-        } else {
-          cw[u] = make_uint4(0u, 0u, 0u, 0u);
-          mw[u] = make_uint2(0u, 0u);
-        }
-      }
+    for (int u = 0; u < NBV; ++u) load(u, cb[u], mb[u]);
+    for (int i0 = 0;;) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int item = base + u * NT + tid;
-        const bool valid = item < ni;
-        const int te0 = 2 * (p0 + item / CPP), te1 = te0 + 1;
-        const bool ok0 = valid && te0 >= r0 && te0 < r1;
-        const bool ok1 = valid && te1 >= r0 && te1 < r1;
-        const float s0 = ok0 ? h2f(mw[u].x & 0xffffu) : 0.f, z0 = ok0 ? h2f(mw[u].x >> 16) : 0.f;
-        const float s1 = ok1 ? h2f(mw[u].y & 0xffffu) : 0.f, z1 = ok1 ? h2f(mw[u].y >> 16) : 0.f;
-        uint32_t v[4][NP];
-        Unpack<BITS>::run(cw[u].x, v[0]);
-        Unpack<BITS>::run(cw[u].y, v[1]);
-        Unpack<BITS>::run(cw[u].z, v[2]);
-        Unpack<BITS>::run(cw[u].w, v[3]);
+      for (int u = 0; u < NBV; ++u) {
+        const int i = i0 + u;
+        const uint4 cw = cb[u];
+        const uint2 mw = mb[u];
+        const int plc = min(i * PPI + my_p, np);      // pair np reads as zero
+        const half2_t s2 = as_h2((mw.x & 0xffffu) | (mw.y << 16));
+        const half2_t z2 = as_h2((mw.x >> 16) | (mw.y & 0xffff0000u));
+        uint32_t ps[HPP];
 #pragma unroll
         for (int hh = 0; hh < HPP; ++hh) {
-          const int h = hp + hh;
-          const float pa = ok0 ? L.p[h * ST + te0 - r0] : 0.f;
-          const float pb = ok1 ? L.p[h * ST + te1 - r0] : 0.f;
-          const uint32_t a = f2h(pa * s0), b = f2h(pb * s1);
-          const uint32_t ps = a | (b << 16);
-          sps[hh] += h2f(a) + h2f(b);
-          pz[hh] += pa * z0 + pb * z1;
+          const half2_t p2 = as_h2(pp[(hp + hh) * (LT / 2) + plc]);
+          const half2_t psh = p2 * s2;
+          ps[hh] = as_u32(psh);
+          sps[hh] = __builtin_amdgcn_fdot2(psh, one2, sps[hh], false);
+          pz[hh] = __builtin_amdgcn_fdot2(p2, z2, pz[hh], false);
+        }
+        // one word at a time: unpack, then apply it to every head
+        const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
+        for (int w = 0; w < 4; ++w) {
+          uint32_t v[NP];
+          Unpack<BITS>::run(words[w], v);
 #pragma unroll
-            for (int k = 0; k < NP; ++k) acc[hh][w * NP + k] = dot2(ps, v[w][k], acc[hh][w * NP + k]);
+          for (int hh = 0; hh < HPP; ++hh)
+#pragma unroll
+            for (int k = 0; k < NP; ++k) acc[hh][w * NP + k] = dot2(ps[hh], v[k], acc[hh][w * NP + k]);
         }
       }
+      i0 += NBV;
+      if (i0 >= n_inst) break;
+#pragma unroll
+      for (int u = 0; u < NBV; ++u) load(i0 + u, cb[u], mb[u]);
     }
 #pragma unroll
     for (int hh = 0; hh < HPP; ++hh) {
-      const int h = hp + hh;
       float vals[CPCV];
 #pragma unroll
       for (int j = 0; j < CPCV; ++j)
         vals[j] = acc[hh][j] - Unpack<BITS>::offset(j % NP) * sps[hh] + pz[hh];
-      float* o = ws + int64_t(h) * (D + 2) + 2;
-      if (h < P.gq) reduce_write<D, CPCV>(L, vals, slot, c * CPCV, NT / CPP, o);
+      wave_reduce_values<D, CPP, CPCV>(W, vals, lane, W.ow + (hp + hh) * (D + 2) + 2);
     }
   }
 }
 
-// Values from fp16 rows: rows[row0 + i], i < nt.
+// Values from fp16 rows rows[row0 + i], i < n, probabilities at slots i.
 template <int D, int GQ>
-__device__ void values_fp16(const DecodeParams& P, const Lds& L, const uint16_t* rows,
-                            int row0, int nt, float* ws) {
+__device__ void values_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* rows,
+                            int row0, int n, int lane) {
+  constexpr int LT = wave_tokens(GQ) + 4;
   constexpr int CPR = D / 8;
-  const int ST = P.split_tokens;
-  const int tid = threadIdx.x;
-  const int c = tid % CPR;
-  const int slot = tid / CPR;
-  const int ni = nt * CPR;
+  constexpr int TPI = 64 / CPR;
+  const int my_t = lane / CPR, my_c = lane % CPR;
+  const int n_inst = (n + TPI - 1) / TPI;
   float acc[GQ][8];
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-  for (int base = 0; base < ni; base += NT * U) {
-    uint4 x[U];
+  auto load = [&](int i) {
+    const int t = min(i * TPI + my_t, n - 1);
+    return *reinterpret_cast<const uint4*>(rows + int64_t(row0 + t) * D + my_c * 8);
+  };
+  uint4 buf[NB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int item = base + u * NT + tid;
-      if (item < ni) {
-        x[u] = *reinterpret_cast<const uint4*>(rows + int64_t(row0 + item / CPR) * D + c * 8);
-      } else {
-        x[u] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
+  for (int u = 0; u < NB; ++u) buf[u] = load(u);
+  for (int i0 = 0;;) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int item = base + u * NT + tid;
-      if (item >= ni) continue;
-      const int tl = item / CPR;
-      const uint32_t wv[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      const uint4 x = buf[u];
+      const int t = min(i * TPI + my_t, LT - 1);     // slots past the tokens are zero
+      const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
       float f[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -341,26 +425,32 @@ __device__ void values_fp16(const DecodeParams& P, const Lds& L, const uint16_t*
       }
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const float p = L.p[h * ST + tl];
+        const float p = h2f(W.p16[h * LT + t]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] += p * f[j];
       }
     }
+    i0 += NB;
+    if (i0 >= n_inst) break;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) buf[u] = load(i0 + u);
   }
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    float* o = ws + int64_t(h) * (D + 2) + 2;
-    if (h < P.gq) reduce_write<D, 8>(L, acc[h], slot, c * 8, NT / CPR, o);
-  }
+  for (int h = 0; h < GQ; ++h) wave_reduce_values<D, CPR, 8>(W, acc[h], lane, W.ow + h * (D + 2) + 2);
 }
 
 // ---------------------------------------------------------------------------
+// Four waves per SIMD (<= 128 VGPRs) for one query head per kv head: 16
+// resident waves per CU keep enough loads in flight to cover HBM latency.
+// Grouped heads do GQ times the arithmetic per byte and get 256 VGPRs.
 template <int D, int GQ>
-__global__ void __launch_bounds__(NT) decode_split_kernel(const DecodeParams P) {
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(GQ == 1 ? 4 : 2)))
+decode_split_kernel(const DecodeParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int ST = P.split_tokens;
-  const Lds L = carve<D, GQ>(smem, ST, P.G);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int LT = wave_tokens(GQ) + 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (scalar) so that every loop bound derived from it is scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = blockIdx.x;
   const int64_t stream = blockIdx.y;
   const int b = int(stream / P.Hkv), hkv = int(stream % P.Hkv);
@@ -368,84 +458,116 @@ __global__ void __launch_bounds__(NT) decode_split_kernel(const DecodeParams P) 
   int ci = 0;
   while (ci + 1 < P.n_cells && P.cells[ci + 1].split0 <= split) ++ci;
   const Cell cell = P.cells[ci];
+  const int ST = P.split_tokens;
   const int t0 = cell.t0 + (split - cell.split0) * ST;
   const int t1 = min(t0 + ST, cell.t0 + cell.n);
-  const int nt = t1 - t0;
+  const int wt = (ST + kWaves - 1) / kWaves;      // tokens per wave (<= wave_tokens(GQ))
+  const int a = min(t0 + wave * wt, t1);
+  const int e = min(a + wt, t1);
+  const int n = e - a;
 
+  uint16_t* qh16 = reinterpret_cast<uint16_t*>(smem);
   const int64_t qrow = (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;
   for (int i = tid; i < GQ * D; i += NT) {
-    const int h = i / D, ch = i % D;
-    L.qf[i] = h < P.gq ? h2f(P.q[qrow + int64_t(h) * D + ch]) * P.scale_log2 : 0.f;
-  }
-  const uint32_t* q32 = reinterpret_cast<const uint32_t*>(P.q);
-  for (int i = tid; i < GQ * (D / 2); i += NT) {
-    const int h = i / (D / 2), c2 = i % (D / 2);
-    L.qh[i] = h < P.gq ? q32[(qrow + int64_t(h) * D) / 2 + c2] : 0u;
+    const int h = i / D;
+    qh16[i] = h < P.gq ? P.q[qrow + i] : uint16_t(0);
   }
   __syncthreads();
 
-  if (cell.k_src >= 0) {
-    const Run& run = P.k_runs[cell.k_src];
-    switch (run.bits) {
-      case 2: keys_quantized<D, GQ, 2>(P, L, stream, run, t0, t1); break;
-      case 4: keys_quantized<D, GQ, 4>(P, L, stream, run, t0, t1); break;
-      case 8: keys_quantized<D, GQ, 8>(P, L, stream, run, t0, t1); break;
-      default:
-        keys_fp16<D, GQ>(P, L,
-                         reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off),
-                         t0 - run.tok_begin, nt);
+  const WaveLds W = carve_wave<D, GQ>(smem, wave);
+  // token t of the wave sits at slot slot0 + (t - a); for quantized value runs
+  // slot0 makes every value pair block start at an even slot
+  int slot0 = 0;
+  if (cell.v_src >= 0 && P.v_runs[cell.v_src].bits != 16)
+    slot0 = (a - P.v_runs[cell.v_src].tok_begin) & 1;
+  if (n > 0) {
+    if (cell.k_src >= 0) {
+      const Run& run = P.k_runs[cell.k_src];
+      const int r0 = a - run.tok_begin, r1 = e - run.tok_begin;
+      switch (run.bits) {
+        case 2: keys_quantized<D, GQ, 2>(P, W, qh16, stream, run, r0, r1, slot0, lane); break;
+        case 4: keys_quantized<D, GQ, 4>(P, W, qh16, stream, run, r0, r1, slot0, lane); break;
+        case 8: keys_quantized<D, GQ, 8>(P, W, qh16, stream, run, r0, r1, slot0, lane); break;
+        default:
+          keys_fp16<D, GQ>(P, W, qh16,
+                           reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off),
+                           r0, n, slot0, lane);
+      }
+    } else {
+      keys_fp16<D, GQ>(P, W, qh16, P.k_res + stream * P.k_res_stride, a - P.n_kq, n, slot0, lane);
     }
-  } else {
-    keys_fp16<D, GQ>(P, L, P.k_res + stream * P.k_res_stride, t0 - P.n_kq, nt);
-  }
-  __syncthreads();
+    wave_lds_sync();
 
-  // split-local softmax state per head (base-2 logits)
-  float mh[GQ], lh[GQ];
+    // softmax state of this wave's range, per head (base-2 logits); every slot
+    // of p16 is written, zero outside the wave's tokens
+    float mh[GQ], lh[GQ];
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    float mx = -INFINITY;
-    for (int i = tid; i < nt; i += NT) mx = fmaxf(mx, L.p[h * ST + i]);
-    mx = wave_max(mx);
-    if (lane == 0) L.scratch[wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(L.scratch[0], L.scratch[1]), fmaxf(L.scratch[2], L.scratch[3]));
-    __syncthreads();
-    float sum = 0.f;
-    for (int i = tid; i < nt; i += NT) {
-      const float e = exp2f(L.p[h * ST + i] - mx);
-      L.p[h * ST + i] = e;
-      sum += e;
+    for (int h = 0; h < GQ; ++h) {
+      float mx = -INFINITY;
+      for (int i = lane; i < n; i += 64) mx = fmaxf(mx, W.logit[h * LT + slot0 + i]);
+      mx = wave_max(mx);
+      float sum = 0.f;
+      for (int sl = lane; sl < LT; sl += 64) {
+        const int i = sl - slot0;
+        const float x = (i >= 0 && i < n) ? exp2f(W.logit[h * LT + sl] - mx) : 0.f;
+        const uint32_t x16 = f2h(x);
+        W.p16[h * LT + sl] = static_cast<uint16_t>(x16);
+        sum += h2f(x16);              // the same rounded values the A.V uses
+      }
+      mh[h] = mx;
+      lh[h] = wave_sum(sum);
     }
-    sum = wave_sum(sum);
-    if (lane == 0) L.scratch[wave] = sum;
-    __syncthreads();
-    sum = L.scratch[0] + L.scratch[1] + L.scratch[2] + L.scratch[3];
-    __syncthreads();
-    mh[h] = mx;
-    lh[h] = sum;
-  }
+    wave_lds_sync();
 
-  float* ws = P.ws + (stream * P.n_splits + split) * int64_t(P.gq) * (D + 2);
-  if (cell.v_src >= 0) {
-    const Run& run = P.v_runs[cell.v_src];
-    switch (run.bits) {
-      case 2: values_quantized<D, GQ, 2>(P, L, stream, run, t0, t1, ws); break;
-      case 4: values_quantized<D, GQ, 4>(P, L, stream, run, t0, t1, ws); break;
-      case 8: values_quantized<D, GQ, 8>(P, L, stream, run, t0, t1, ws); break;
-      default:
-        values_fp16<D, GQ>(P, L,
-                           reinterpret_cast<const uint16_t*>(P.v_codes + stream * P.v_codes_stride + run.code_off),
-                           t0 - run.tok_begin, nt, ws);
+    if (cell.v_src >= 0) {
+      const Run& run = P.v_runs[cell.v_src];
+      const int r0 = a - run.tok_begin, r1 = e - run.tok_begin;
+      switch (run.bits) {
+        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, lane); break;
+        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, lane); break;
+        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, lane); break;
+        default:
+          values_fp16<D, GQ>(P, W,
+                             reinterpret_cast<const uint16_t*>(P.v_codes + stream * P.v_codes_stride + run.code_off),
+                             r0, n, lane);
+      }
+    } else {
+      values_fp16<D, GQ>(P, W, P.v_res + stream * P.v_res_stride, a - P.n_vq, n, lane);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        W.ow[h * (D + 2)] = mh[h];
+        W.ow[h * (D + 2) + 1] = lh[h];
+      }
     }
   } else {
-    values_fp16<D, GQ>(P, L, P.v_res + stream * P.v_res_stride, t0 - P.n_vq, nt, ws);
-  }
-  if (tid == 0) {
-    for (int h = 0; h < GQ && h < P.gq; ++h) {
-      ws[int64_t(h) * (D + 2)] = mh[h];
-      ws[int64_t(h) * (D + 2) + 1] = lh[h];
+    for (int i = lane; i < GQ * (D + 2); i += 64) {
+      const int j = i % (D + 2);
+      W.ow[i] = j == 0 ? -INFINITY : 0.f;
     }
+  }
+  __syncthreads();
+
+  // combine the waves' states and write this split's partial
+  float* ws = P.ws + (stream * P.n_splits + split) * int64_t(P.gq) * (D + 2);
+  constexpr DecodeLds lay = decode_lds(D, GQ);
+  for (int i = tid; i < P.gq * (D + 2); i += NT) {
+    const int h = i / (D + 2), j = i % (D + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* ow = reinterpret_cast<const float*>(smem + lay.block + w * lay.wave + lay.logit + lay.p16);
+      M = fmaxf(M, ow[h * (D + 2)]);
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* ow = reinterpret_cast<const float*>(smem + lay.block + w * lay.wave + lay.logit + lay.p16);
+      const float f = exp2f(ow[h * (D + 2)] - M);
+      r += f * ow[h * (D + 2) + (j == 0 ? 1 : j)];
+    }
+    ws[i] = j == 0 ? M : r;
   }
 }
 
@@ -472,7 +594,7 @@ __global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeParams P) {
 
 template <int D, int GQ>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t s) {
-  const size_t lds = size_t(decode_lds_bytes(D, GQ, p.split_tokens, p.G));
+  const size_t lds = size_t(decode_lds(D, GQ).total);
   hipLaunchKernelGGL((decode_split_kernel<D, GQ>), dim3(p.n_splits, p.B * p.Hkv), dim3(NT),
                      lds, s, p);
   hipError_t e = hipGetLastError();

@@ -23,6 +23,26 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                 __builtin_bit_cast(half2_t, b), c, false);
 }
 
+// (x & mask) | magic in one VALU op (v_and_or_b32).  The gfx9-family VOP3
+// encoding takes no literal constant, so with literal masks the compiler
+// splits this into and + or.  Routing the constants through a trivial
+// (non-volatile, so hoistable) register move makes them opaque register
+// operands, and instruction selection then forms v_and_or_b32 while the
+// scheduler stays free to move the operation.
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t c) {
+  uint32_t r;
+  asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t c) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+  return (x & opaque_sgpr(mask)) | opaque_vgpr(magic);
+}
+
 // Unpacking one 32-bit word of codes into fp16 pairs without conversions:
 // a b-bit code moved into the fp16 mantissa under a fixed exponent reads as
 // (offset + code).  Pair k of a word combines the code at bit b*k of the low
@@ -36,14 +56,14 @@ template <> struct Unpack<2> {
   static constexpr int NP = 8;   // pairs per word
   __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
     const uint32_t a = w << 4, c = w >> 6;
-    v[0] = (a & 0x00300030u) | 0x54005400u;  // mantissa bits 4-5: 64 + code
-    v[1] = (a & 0x00C000C0u) | 0x4C004C00u;  // bits 6-7: 16 + code
-    v[2] = (a & 0x03000300u) | 0x44004400u;  // bits 8-9: 4 + code
-    v[3] = (w & 0x00C000C0u) | 0x4C004C00u;
-    v[4] = (w & 0x03000300u) | 0x44004400u;
-    v[5] = (c & 0x00300030u) | 0x54005400u;
-    v[6] = (c & 0x00C000C0u) | 0x4C004C00u;
-    v[7] = (c & 0x03000300u) | 0x44004400u;
+    v[0] = and_or(a, 0x00300030u, 0x54005400u);  // mantissa bits 4-5: 64 + code
+    v[1] = and_or(a, 0x00C000C0u, 0x4C004C00u);  // bits 6-7: 16 + code
+    v[2] = and_or(a, 0x03000300u, 0x44004400u);  // bits 8-9: 4 + code
+    v[3] = and_or(w, 0x00C000C0u, 0x4C004C00u);
+    v[4] = and_or(w, 0x03000300u, 0x44004400u);
+    v[5] = and_or(c, 0x00300030u, 0x54005400u);
+    v[6] = and_or(c, 0x00C000C0u, 0x4C004C00u);
+    v[7] = and_or(c, 0x03000300u, 0x44004400u);
   }
   __device__ static __forceinline__ float offset(int k) {
     return (k == 0 || k == 5) ? 64.f : ((k == 1 || k == 3 || k == 6) ? 16.f : 4.f);
@@ -53,10 +73,10 @@ template <> struct Unpack<2> {
 template <> struct Unpack<4> {
   static constexpr int NP = 4;
   __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
-    v[0] = ((w << 4) & 0x00F000F0u) | 0x54005400u;  // mantissa bits 4-7: 64 + code
-    v[1] = (w & 0x00F000F0u) | 0x54005400u;
-    v[2] = ((w >> 4) & 0x00F000F0u) | 0x54005400u;
-    v[3] = ((w >> 8) & 0x00F000F0u) | 0x54005400u;
+    v[0] = and_or(w << 4, 0x00F000F0u, 0x54005400u);  // mantissa bits 4-7: 64 + code
+    v[1] = and_or(w, 0x00F000F0u, 0x54005400u);
+    v[2] = and_or(w >> 4, 0x00F000F0u, 0x54005400u);
+    v[3] = and_or(w >> 8, 0x00F000F0u, 0x54005400u);
   }
   __device__ static __forceinline__ float offset(int) { return 64.f; }
 };
@@ -64,8 +84,8 @@ template <> struct Unpack<4> {
 template <> struct Unpack<8> {
   static constexpr int NP = 2;
   __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
-    v[0] = (w & 0x00FF00FFu) | 0x64006400u;         // mantissa bits 0-7: 1024 + code
-    v[1] = ((w >> 8) & 0x00FF00FFu) | 0x64006400u;
+    v[0] = and_or(w, 0x00FF00FFu, 0x64006400u);       // mantissa bits 0-7: 1024 + code
+    v[1] = and_or(w >> 8, 0x00FF00FFu, 0x64006400u);
   }
   __device__ static __forceinline__ float offset(int) { return 1024.f; }
 };

@@ -9,10 +9,14 @@
 namespace kvq {
 
 constexpr int kThreads = 256;          // threads per decode / quantize workgroup
+constexpr int kWaves = 4;              // waves per decode workgroup
 constexpr int kMaxRuns = 8;            // runs per half of the cache
 constexpr int kMaxCells = 20;          // token ranges with one key and one value source
-constexpr int kRedFloats = kThreads * 32;  // value-reduction buffer (floats)
 constexpr int kLdsLimit = 64 * 1024;   // dynamic LDS budget per decode workgroup
+
+// Tokens each wave of a decode workgroup streams; a workgroup covers
+// kWaves * wave_tokens(GQ) tokens.  Larger GQ needs more LDS per token.
+__host__ __device__ constexpr int wave_tokens(int GQ) { return GQ <= 1 ? 256 : GQ == 2 ? 128 : GQ == 4 ? 64 : 32; }
 
 struct Run {            // device copy of kvq_segment
   int32_t bits, tok_begin, n_tok, pad;
@@ -38,8 +42,9 @@ struct DecodeParams {
   int64_t k_codes_stride, k_meta_stride, v_codes_stride, v_meta_stride;
   int64_t k_res_stride, v_res_stride;   // fp16 elements
   int32_t B, Hq, Hkv, D, G, gq;
+  int32_t lg_g;                         // log2(G)
   int32_t n_kq, n_vq;                   // tokens held in key runs / value runs
-  int32_t n_splits, split_tokens;
+  int32_t n_splits, split_tokens;       // split_tokens = kWaves * wave_tokens(GQ)
   float scale_log2;                     // sm_scale * log2(e)
   int32_t n_cells, n_k_runs, n_v_runs;
   Run k_runs[kMaxRuns];
@@ -47,18 +52,29 @@ struct DecodeParams {
   Cell cells[kMaxCells];
 };
 
-// Dynamic LDS bytes of one decode workgroup (same carve-up on the device).
-inline int64_t decode_lds_bytes(int D, int GQ, int split_tokens, int G) {
-  const int64_t ngmax = (split_tokens + G - 1) / G + 1;
-  int64_t bytes = 0;
-  bytes += int64_t(GQ) * D * 4;            // q * scale, fp32
-  bytes += int64_t(GQ) * D * 2;            // q, fp16 pairs
-  bytes += ngmax * GQ * D * 2;             // q*s per key group, fp16 pairs
-  bytes += ngmax * GQ * 4;                 // bias per key group
-  bytes += int64_t(GQ) * split_tokens * 4; // logits / probabilities
-  bytes += int64_t(kRedFloats) * 4;        // value reduction
-  bytes += 64 * 4;                         // block-reduction scratch
-  return bytes;
+// LDS carve-up of one decode workgroup (the device uses the same numbers).
+// Block part: q of the GQ heads as fp16.  Per wave, for LT = wave_tokens + 4
+// token slots (a leading slot keeps value pairs aligned, the tail is zero):
+//   logit  fp32 [GQ][LT]  logits; reused afterwards for the [4][D] value
+//                          reduction rows
+//   p16    fp16 [GQ][LT]  probabilities, zero outside the wave's tokens
+//   area   q*s hi/lo pairs [NGW][GQ][2][D/2] and bias [NGW][GQ] per key group
+//          (NGW groups, sized for G = 32); afterwards the wave's partial
+//          (m, l, o[D]) per head
+struct DecodeLds {
+  int64_t block, logit, p16, area, wave, total;
+};
+__host__ __device__ constexpr int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
+__host__ __device__ constexpr int64_t cmax(int64_t a, int64_t b) { return a > b ? a : b; }
+__host__ __device__ constexpr DecodeLds decode_lds(int D, int GQ) {
+  const int64_t lt = wave_tokens(GQ) + 4;
+  const int64_t ngw = wave_tokens(GQ) / 32 + 1;
+  const int64_t block = round16(int64_t(GQ) * D * 2);
+  const int64_t logit = round16(cmax(int64_t(GQ) * lt * 4, int64_t(4) * D * 4));
+  const int64_t p16 = round16(int64_t(GQ) * lt * 2);
+  const int64_t area = round16(cmax(ngw * GQ * D * 4 + ngw * GQ * 4, int64_t(GQ) * (D + 2) * 4));
+  const int64_t wave = logit + p16 + area;
+  return DecodeLds{block, logit, p16, area, wave, block + kWaves * wave};
 }
 
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s);

@@ -18,8 +18,8 @@
 namespace kvq {
 namespace {
 
-// One group's scale and zero point.  The minimum is canonicalized to +0 when
-// it is a zero (min of {-0, +0} is not ordered), so z has a single encoding.
+// One group's scale and zero point.  Zero extrema are canonicalized to +0
+// (min/max of {-0, +0} are not ordered), so z and s have single encodings.
 struct GroupScale {
   uint32_t s16, z16;
   float s, z;
@@ -30,6 +30,7 @@ __device__ __forceinline__ GroupScale group_scale(float mn, float mx) {
   constexpr float kQmax = float((1 << BITS) - 1);
   GroupScale g;
   mn = mn + 0.0f;
+  mx = mx + 0.0f;
   g.s16 = f2h(__fdiv_rn(mx - mn, kQmax));
   g.z16 = f2h(mn);
   g.s = h2f(g.s16);
@@ -100,13 +101,17 @@ __global__ void __launch_bounds__(256) quantize_values_kernel(QuantParams p, int
   const int G = p.G;
   const int64_t row = p.src_rows ? p.src_rows[i] : i;
   const uint16_t* x = p.src + s * p.src_stream_stride + row * p.src_row_stride + int64_t(g) * G;
+  // the group's G fp16 values stay in registers (G <= 128: 16 loads of 16 B)
+  uint32_t xw[64];
   float mn = INFINITY, mx = -INFINITY;
-  for (int k = 0; k < G; k += 8) {
-    const uint4 u = *reinterpret_cast<const uint4*>(x + k);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    if (k * 8 >= G) break;
+    const uint4 u = *reinterpret_cast<const uint4*>(x + k * 8);
+    xw[4 * k] = u.x; xw[4 * k + 1] = u.y; xw[4 * k + 2] = u.z; xw[4 * k + 3] = u.w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float a = h2f(w[e] & 0xffffu), b = h2f(w[e] >> 16);
+      const float a = h2f(xw[4 * k + e] & 0xffffu), b = h2f(xw[4 * k + e] >> 16);
       mn = fminf(mn, fminf(a, b));
       mx = fmaxf(mx, fmaxf(a, b));
     }
@@ -120,15 +125,28 @@ __global__ void __launch_bounds__(256) quantize_values_kernel(QuantParams p, int
   constexpr int kPerUnit = 16 / BITS;   // codes per 16-bit unit
   const int units = G / kPerUnit;
   const int u0 = g * units;
-  for (int u = 0; u < units; ++u) {
+#pragma unroll
+  for (int u = 0; u < 128 / kPerUnit; ++u) {
+    if (u >= units) break;
     uint32_t unit = 0;
 #pragma unroll
-    for (int k = 0; k < kPerUnit; ++k)
-      unit |= encode<BITS>(h2f(x[u * kPerUnit + k]), gs) << (k * BITS);
+    for (int k = 0; k < kPerUnit; ++k) {
+      const int e = u * kPerUnit + k;                 // element of the group
+      const uint32_t h = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      unit |= encode<BITS>(h2f(h), gs) << (k * BITS);
+    }
     *reinterpret_cast<uint16_t*>(blk + 4 * (u0 + u) + 2 * par) = static_cast<uint16_t>(unit);
   }
   uint32_t* meta = reinterpret_cast<uint32_t*>(p.meta + s * p.meta_stream_stride);
   meta[(pair * NG + g) * 2 + par] = gs.s16 | (gs.z16 << 16);
+  // the last appended token at an even index leaves its pair partner unwritten:
+  // zero the partner's halves and (scale, zero) so decode reads finite values
+  // (the next append overwrites them)
+  if (par == 0 && i == p.n_tok - 1) {
+    for (int u = 0; u < units; ++u)
+      *reinterpret_cast<uint16_t*>(blk + 4 * (u0 + u) + 2) = 0;
+    meta[(pair * NG + g) * 2 + 1] = 0u;
+  }
 }
 
 // fp16 row copy, 16 bytes per thread.

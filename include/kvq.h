@@ -55,10 +55,10 @@
  *     stream*res_stride + i*d_h.
  *
  * Quantizer (bit-exact contract): for each group, in IEEE fp32 on the fp16
- * inputs, mn = min, mx = max, s32 = (mx - mn) / (2^b - 1) (one correctly
- * rounded division), s = fp16(s32) (round to nearest even), z = fp16(mn)
- * (exact); codes are 0 when s == 0, else clamp(rint((x - z) / s), 0, 2^b - 1)
- * with z, s widened from fp16, one fp32 subtraction and one correctly rounded
+ * inputs, mn = min + 0, mx = max + 0 (zero extrema are +0), s32 = (mx - mn) /
+ * (2^b - 1) (one correctly rounded division), s = fp16(s32) (round to
+ * nearest even), z = fp16(mn) (exact); codes are 0 when s == 0, else
+ * clamp(rint((x - z) / s), 0, 2^b - 1) with z, s widened from fp16, one fp32 subtraction and one correctly rounded
  * fp32 division, rint rounding half to even.  The stored (s, z) are the ones
  * used to encode, so X' = Q*s + z decodes what was encoded.
  */
@@ -128,9 +128,13 @@ const char* kvq_strerror(int32_t status);
  *   meta       same for the (scale, zero) pairs (ignored for bits 16).
  *   dst_tok    tokens already in the run; new token i becomes run token
  *              dst_tok + i.  For values, a token sharing a pair block with an
- *              existing token only writes its own 16-bit halves.
+ *              existing token only writes its own 16-bit halves; when the last
+ *              appended token has an even index, the halves and (scale, zero)
+ *              pair of the next (not yet written) token are set to zero, so a
+ *              run of odd length never exposes uninitialized bytes to decode.
  * Alignment: src, codes, meta and the stream strides are multiples of 16 bytes.
- * Writes exactly the bytes of the appended tokens (and their meta pairs).
+ * Writes the bytes of the appended tokens and their meta pairs (and, as
+ * above, zeroes the unwritten pair partner of a last even-index value token).
  */
 kvq_status kvq_quantize_append(int32_t which, int32_t bits, int32_t group,
                                int32_t n_streams, int32_t d_h, int32_t n_tok,
@@ -231,6 +235,8 @@ kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes)
 
 /*
  * kvq_decode_attn -- one decode step of attention for every (b, hq).
+ * A value run of odd length must have the missing pair partner's (scale,
+ * zero) finite (kvq_quantize_append leaves it zero).
  * Checks (all before any launch): shapes as documented above; runs in token
  * order with sum(k n_tok) + n_k_res == sum(v n_tok) + n_v_res = N >= 1;
  * key runs with b < 16 hold whole groups (n_tok % G == 0); code_off and
