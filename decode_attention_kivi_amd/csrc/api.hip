@@ -11,7 +11,6 @@
 
 namespace {
 
-using kvq::Cell;
 using kvq::DecodeParams;
 using kvq::Run;
 
@@ -40,17 +39,15 @@ kvq_status check_runs(const kvq_segment* segs, int n, int d, int G, bool keys, i
     if (s.code_off < 0 || s.meta_off < 0) return KVQ_EINVAL;
     if ((s.code_off & 15) || (s.meta_off & 15)) return KVQ_EALIGN;
     if (keys && s.bits != 16 && s.n_tok % G != 0) return KVQ_EINVAL;
+    // quantized key runs start on a group boundary, quantized value runs on
+    // a pair boundary (true of every run the library's own calls produce)
+    if (keys && s.bits != 16 && s.tok_begin % G != 0) return KVQ_EUNSUPPORTED;
+    if (!keys && s.bits != 16 && (s.tok_begin & 1)) return KVQ_EUNSUPPORTED;
     (void)d;
     tok += s.n_tok;
   }
   *n_total = tok;
   return KVQ_OK;
-}
-
-int64_t count_splits(const std::vector<Cell>& cells, int st) {
-  int64_t n = 0;
-  for (const Cell& c : cells) n += (c.n + st - 1) / st;
-  return n;
 }
 
 kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
@@ -88,48 +85,28 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   for (int64_t s : {a->k_res_stride, a->v_res_stride})
     if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
 
-  // cells: maximal token ranges with one key source and one value source
-  std::vector<int64_t> cuts = {0, N, nk, nv};
-  for (int i = 0; i < a->n_k_segs; ++i) cuts.push_back(a->k_segs[i].tok_begin);
-  for (int i = 0; i < a->n_v_segs; ++i) cuts.push_back(a->v_segs[i].tok_begin);
-  std::sort(cuts.begin(), cuts.end());
-  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
-  std::vector<Cell> cells;
-  for (size_t i = 0; i + 1 < cuts.size(); ++i) {
-    const int64_t t0 = cuts[i], t1 = cuts[i + 1];
-    if (t1 <= t0) continue;
-    Cell c{};
-    c.t0 = int32_t(t0);
-    c.n = int32_t(t1 - t0);
-    c.k_src = -1;
-    c.v_src = -1;
-    for (int k = 0; k < a->n_k_segs; ++k)
-      if (t0 >= a->k_segs[k].tok_begin && t0 < a->k_segs[k].tok_begin + a->k_segs[k].n_tok) c.k_src = k;
-    for (int k = 0; k < a->n_v_segs; ++k)
-      if (t0 >= a->v_segs[k].tok_begin && t0 < a->v_segs[k].tok_begin + a->v_segs[k].n_tok) c.v_src = k;
-    cells.push_back(c);
-  }
-  if (cells.empty() || cells.size() > size_t(kvq::kMaxCells)) return KVQ_EUNSUPPORTED;
-
   int GQ = 1;
   while (GQ < gq) GQ *= 2;
+  if (kvq::decode_lds_bytes(D, GQ, 4) < 0) return KVQ_EUNSUPPORTED;
   const int64_t streams = int64_t(a->batch) * a->n_kv_heads;
-  // a workgroup covers up to kWaves * wave_tokens(GQ) tokens; smaller splits
-  // only when the grid would otherwise leave most of the GPU idle
-  const int st_max = kvq::kWaves * kvq::wave_tokens(GQ);
-  int st_tokens = a->split_tokens;
-  if (st_tokens == 0) {
-    st_tokens = st_max;
-    while (st_tokens > 64 && streams * count_splits(cells, st_tokens) < 1024) st_tokens /= 2;
+  // Each stream's N tokens are cut into 4 * n_wg wave ranges of about equal
+  // length, four waves per workgroup.  The automatic choice aims at
+  // wave_tokens(GQ) tokens per wave and shortens the ranges while the grid
+  // would leave most of the GPU idle; split_tokens > 0 asks for workgroups of
+  // that many tokens.
+  const int WT = kvq::wave_tokens(GQ);
+  int64_t n_wg;
+  if (a->split_tokens > 0) {
+    n_wg = (N + a->split_tokens - 1) / a->split_tokens;
+  } else {
+    n_wg = std::max<int64_t>(1, (N + 2 * WT) / (4 * WT));
+    while (streams * n_wg < 1024 && (N + 8 * n_wg - 1) / (8 * n_wg) >= 64) n_wg *= 2;
   }
-  if (st_tokens > st_max) return KVQ_EUNSUPPORTED;
-  if (kvq::decode_lds(D, GQ).total > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
-  int64_t n_splits = 0;
-  for (Cell& c : cells) {
-    c.split0 = int32_t(n_splits);
-    n_splits += (c.n + st_tokens - 1) / st_tokens;
-  }
-  if (n_splits > (int64_t(1) << 31) - 1) return KVQ_EUNSUPPORTED;
+  const int nw = kvq::kWaves;
+  const int64_t nws = nw * n_wg;
+  if (n_wg > (int64_t(1) << 28)) return KVQ_EUNSUPPORTED;
+  if ((N + nws - 1) / nws + kvq::kWaveAlign - 1 > kvq::wave_cap(GQ)) return KVQ_EUNSUPPORTED;
+  if (kvq::decode_lds_bytes(D, GQ, nw) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
 
   Plan& pl = *out;
   DecodeParams& p = pl.p;
@@ -156,12 +133,13 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   p.G = G;
   p.lg_g = G == 32 ? 5 : G == 64 ? 6 : 7;
   p.gq = gq;
+  p.n_tok = int32_t(N);
   p.n_kq = int32_t(nk);
   p.n_vq = int32_t(nv);
-  p.n_splits = int32_t(n_splits);
-  p.split_tokens = st_tokens;
+  p.waves_per_stream = int32_t(nws);
+  p.waves_per_wg = nw;
+  p.wg_per_stream = int32_t(n_wg);
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
-  p.n_cells = int32_t(cells.size());
   p.n_k_runs = a->n_k_segs;
   p.n_v_runs = a->n_v_segs;
   for (int i = 0; i < a->n_k_segs; ++i)
@@ -170,9 +148,11 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   for (int i = 0; i < a->n_v_segs; ++i)
     p.v_runs[i] = Run{a->v_segs[i].bits, a->v_segs[i].tok_begin, a->v_segs[i].n_tok, 0,
                       a->v_segs[i].code_off, a->v_segs[i].meta_off};
-  for (size_t i = 0; i < cells.size(); ++i) p.cells[i] = cells[i];
   pl.GQ = GQ;
-  pl.ws_bytes = size_t(streams) * size_t(n_splits) * size_t(gq) * size_t(D + 2) * sizeof(float);
+  // the per-workgroup partial states; one workgroup per stream writes the
+  // output directly and needs no workspace
+  pl.ws_bytes = n_wg == 1 ? 0
+                          : size_t(streams) * size_t(n_wg) * size_t(gq) * size_t(D + 2) * sizeof(float);
   return KVQ_OK;
 }
 
@@ -286,7 +266,8 @@ kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream) {
   Plan pl;
   const kvq_status st = make_plan(args, &pl);
   if (st != KVQ_OK) return st;
-  if (!args->workspace || args->workspace_bytes < pl.ws_bytes) return KVQ_EWORKSPACE;
+  if (pl.ws_bytes > 0 && (!args->workspace || args->workspace_bytes < pl.ws_bytes))
+    return KVQ_EWORKSPACE;
   return from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
 }
 

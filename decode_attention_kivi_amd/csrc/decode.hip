@@ -1,27 +1,28 @@
 // Decode-step attention over a low-bit quantized KV cache, split over the
 // context (the FlashDecoding dataflow that the VQ-LLM note's reference [10]
-// describes) with a final cross-split softmax merge.
+// describes) with a cross-split softmax merge.
 //
-// A workgroup takes one cache stream (batch b, kv head h), the GQ query heads
-// that share it, and a range of tokens whose keys come from one source (a
-// quantized run or the fp16 residual) and whose values come from one source.
-// Each of its four waves streams its own sub-range independently; the only
-// workgroup barrier is the final combine.  Per wave:
-//   1. q*s for every key group of the range (per-channel key scales, KIVI
-//      note "Method details"), as fp16 hi + lo pairs, and the group bias
-//      sum_c q_c z_c, into the wave's LDS area;
-//   2. logits: prefetched 16-byte loads of packed codes, unpack of code pairs
-//      into fp16 (offset + code) by mask-and-or with an exponent constant,
-//      v_dot2_f32_f16 against q*s; residual rows dot q directly
-//      (A = Concat([A_g, A_r]));
-//   3. the range's max and sum of exp2(logit - max): one softmax over the
+// The N tokens of a cache stream (batch b, kv head h) are cut into
+// waves_per_stream ranges of about equal length (starts at multiples of 32);
+// a workgroup holds four consecutive ranges of one stream and the GQ query
+// heads that share it.  A wave's range may cross run boundaries: it walks the
+// key pieces (quantized runs, fp16 runs, the fp16 residual) and then the value
+// pieces in token order.  Per wave:
+//   1. logits, one load batch at a time: 8- or 16-byte code loads, the batch's
+//      key groups' q*s (per-channel key scales, KIVI note "Method details") as
+//      fp16 hi + lo pairs and the group bias sum_c q_c z_c into LDS; each lane
+//      keeps its pairs' q*s in registers for all tokens of a group, unpacks
+//      code pairs into fp16 (offset + code) by mask-and-or with an exponent
+//      constant and accumulates with v_dot2_f32_f16; residual rows dot q
+//      directly (A = Concat([A_g, A_r]));
+//   2. the range's max and sum of exp2(logit - max): one softmax over the
 //      concatenation (KIVI Algorithm 1; WindowQuant Sec. 3.3.1);
-//   4. A.V over token-pair value blocks: one fp16 pair holds the same channel
-//      of two tokens, so v_dot2 applies both tokens' p*s at once; sum(p*z) and
-//      sum(p*s) per group are kept apart and folded in at the end; partials
-//      are reduced with DPP row rotations and a 4-row LDS stage;
-//   5. the four waves' (max, sum, o[d]) are combined and written as the
-//      split's partial; the merge kernel rescales and adds the splits.
+//   3. A.V over token-pair value blocks: one fp16 pair holds the same channel
+//      of two tokens, so v_dot2 applies both tokens' p*s at once; sum(p*s) and
+//      sum(p*z) of a lane are kept apart and folded in after the cross-lane
+//      reduction;
+//   4. the four waves' (max, sum, o[d]) are combined into the workgroup's
+//      partial state; a second kernel merges a stream's partials.
 // Logits are kept in base 2 (q is pre-scaled by sm_scale * log2 e).
 
 #include "kvq_internal.h"
@@ -31,8 +32,7 @@ namespace kvq {
 namespace {
 
 constexpr int NT = kThreads;
-constexpr int NB = 8;    // loads per batch in the key streaming loops (wave instructions)
-constexpr int NBV = 4;   // loads per batch in the value streaming loops
+constexpr int NBV = 2;   // loads per batch in the value streaming loops (two batches in flight)
 
 // Make this wave's LDS writes visible to its own later LDS reads.  LDS
 // operations of one wave execute in order; this only keeps the compiler from
@@ -43,6 +43,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+
 // v + rotate_right(v, s) within each row of 16 lanes.
 template <int S>
 __device__ __forceinline__ float row_ror_add(float v) {
@@ -50,7 +53,8 @@ __device__ __forceinline__ float row_ror_add(float v) {
 }
 
 // Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16) with
-// DPP: quad permutations, then half-row and row mirrors.
+// DPP: quad permutations, then half-row and row mirrors.  Every lane of a
+// group ends with the group's sum.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   if (N >= 2) x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
@@ -60,88 +64,142 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-struct WaveLds {
-  float* logit;      // [GQ][LT] logits by token slot; later the [4][D] value rows
-  uint16_t* p16;     // [GQ][LT] fp16 probabilities, zero outside the wave's tokens
-  uint32_t* qs;      // [NGW][GQ][2][D/2] q*s fp16 hi pairs then lo pairs
-  float* bias;       // [NGW][GQ]
-  float* ow;         // [GQ][D+2] (m, l, o[D]) of the wave (aliases qs/bias)
-};
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if (N >= 2) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+  if (N >= 4) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+  if (N >= 8) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+  if (N >= 16) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
+  return x;
+}
 
-template <int D, int GQ>
-__device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
-  constexpr int NGW = wave_tokens(GQ) / 32 + 1;
-  constexpr DecodeLds lay = decode_lds(D, GQ);
-  unsigned char* base = smem + lay.block + int64_t(wave) * lay.wave;
-  WaveLds W;
-  W.logit = reinterpret_cast<float*>(base);
-  W.p16 = reinterpret_cast<uint16_t*>(base + lay.logit);
-  W.qs = reinterpret_cast<uint32_t*>(base + lay.logit + lay.p16);
-  W.bias = reinterpret_cast<float*>(base + lay.logit + lay.p16 + int64_t(NGW) * GQ * D * 4);
-  W.ow = reinterpret_cast<float*>(base + lay.logit + lay.p16);
-  return W;
+// For x uniform within each row of 16 lanes: the sum over row pairs (0,1) and
+// (2,3) [ROWS == 2] or over all four rows [ROWS == 4], in every lane.
+template <int ROWS>
+__device__ __forceinline__ float xrow_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+  x = bitsf(a[0]) + bitsf(a[1]);
+  if (ROWS == 4) {
+    const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+    x = bitsf(b[0]) + bitsf(b[1]);
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum64(float x) { return xrow_sum<4>(group_sum<16>(x)); }
+
+__device__ __forceinline__ float wave_max64(float x) {
+  x = group_max<16>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+  x = fmaxf(bitsf(a[0]), bitsf(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return fmaxf(bitsf(b[0]), bitsf(b[1]));
 }
 
 __device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ __forceinline__ uint32_t as_u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
+template <int W> struct LoadType;
+template <> struct LoadType<1> { typedef uint32_t T; };
+template <> struct LoadType<2> { typedef uint2 T; };
+template <> struct LoadType<4> { typedef uint4 T; };
+
+template <int W>
+__device__ __forceinline__ uint32_t word(const typename LoadType<W>::T& x, int i) {
+  if constexpr (W == 1) {
+    return x;
+  } else if constexpr (W == 2) {
+    return i == 0 ? x.x : x.y;
+  } else {
+    return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+  }
+}
+
+// Range-checked loads: a raw buffer resource over [base, base + bytes);
+// reads at or past the end return zeros (no clamping, no fault).  Offsets
+// stay in the per-lane register and the instruction's immediate.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
+}
+template <int W>
+__device__ __forceinline__ typename LoadType<W>::T bload(Rsrc r, uint32_t off) {
+  if constexpr (W == 1) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (W == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return make_uint2(v[0], v[1]);
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+struct WaveLds {
+  float* logit;      // [GQ][LT] logits by token slot; later the value row sums
+  uint16_t* p16;     // [GQ][LT] fp16 probabilities, zero outside the wave's tokens
+  uint32_t* qs;      // [NGB][GQ][QHEAD] q*s hi/lo chunks of one load batch
+  float* bias;       // [NGB][GQ][LPR] per-chunk biases (after the largest q*s block)
+  float* ow;         // [GQ][D+2] (m, l, o[D]) of the wave (aliases qs/bias)
+};
+
+template <int D, int GQ>
+__device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
+  constexpr DecodeLds lay = decode_lds<D, GQ>();
+  constexpr int64_t QSMAX = kQsMax<D, GQ>();
+  unsigned char* base = smem + lay.block + int64_t(wave) * lay.wave;
+  WaveLds W;
+  W.logit = reinterpret_cast<float*>(base);
+  W.p16 = reinterpret_cast<uint16_t*>(base + lay.logit);
+  W.qs = reinterpret_cast<uint32_t*>(base + lay.logit + lay.p16);
+  W.bias = reinterpret_cast<float*>(W.qs + QSMAX);
+  W.ow = reinterpret_cast<float*>(base + lay.logit + lay.p16);
+  return W;
+}
+
 // ---------------------------------------------------------------------------
-// Keys of run tokens [r0, r1) (bits 2/4/8) -> logits at slots slot0 + (t - r0).
+// Keys of run tokens [r0, r1) (bits 2/4/8) -> raw logits q'.k (q' = q * 2^-8)
+// at slots slot0 + (t - r0).  r0 is a multiple of 32, so every item
+// (TPI <= 32 tokens) lies in one key group.  Whole items are written: slots
+// past r1 get values that a later piece overwrites or the softmax ignores.
 //
 // Per key group: hi = fp16(q'*s), lo = fp16(q'*s - hi) with packed fp16 ops
 // (q' = q * 2^-8 exactly, so no product can overflow fp16); a single fp16
 // q*s is too coarse for outlier channels, whose large logits would carry its
 // 2^-11 relative error into the softmax, while hi + lo keeps ~22 bits.  The
-// bias sum_c q'_c z_c - sum_c (hi + lo)_c * offset_c comes from three dot2.
+// bias sum_c q'_c z_c - sum_c (hi + lo)_c * offset_c of each lane chunk comes
+// from three dot2 and a DPP sum over the chunk; it seeds the accumulator of
+// the lane that owns the chunk, so the row sum adds the whole bias.
 template <int D, int GQ, int BITS>
 __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qh16,
                                int64_t stream, const Run& run, int r0, int r1, int slot0,
                                int lane) {
-  constexpr int LT = wave_tokens(GQ) + 4;
-  constexpr int RB = D * BITS / 8;       // bytes per token row
-  constexpr int CPR = RB / 16;           // 16-byte chunks per row
-  constexpr int TPI = 64 / CPR;          // tokens per wave instruction
-  constexpr int PPC = 64 / BITS;         // fp16 pairs per chunk
-  constexpr int NP = Unpack<BITS>::NP;   // pairs per 32-bit word
-  constexpr int CPW = 32 / BITS;         // channels per 32-bit word
-  constexpr int HD = D / 2;              // pairs per row
-  constexpr int GPI = 64 / HD;           // key groups per meta iteration
-  constexpr int NGW = wave_tokens(GQ) / 32 + 1;
-  constexpr int MI = (NGW + GPI - 1) / GPI;
+  using KG = KeyGeo<D, GQ, BITS>;
+  constexpr int LT = wave_slots(GQ);
+  constexpr int RB = KG::RB, LB = KG::LB, LPR = KG::LPR, TPI = KG::TPI, WPL = KG::WPL;
+  constexpr int NP = KG::NP, CPW = KG::CPW, PPL = KG::PPL, HD = KG::HD;
+  constexpr int NB = KG::NB, NGB = KG::NGB, QSTR = KG::QSTR, QHEAD = KG::QHEAD;
+  constexpr int GPI = 64 / HD;                         // key groups per meta iteration
+  constexpr int MI = (NGB + GPI - 1) / GPI;
   const int lg = P.lg_g;
-  const int j0 = r0 >> lg;
-  const int ng = ((r1 - 1) >> lg) - j0 + 1;
-  const int rofs = r0 & (P.G - 1);
   const int n = r1 - r0;
-  const uint8_t* codes = P.k_codes + stream * P.k_codes_stride + run.code_off;
-  const uint32_t* meta = reinterpret_cast<const uint32_t*>(
-      P.k_meta + stream * P.k_meta_stride + run.meta_off);
-  const int n_inst = (n + TPI - 1) / TPI;
-  const int my_t = lane / CPR, my_c = lane % CPR;
+  const int n_items = (n + TPI - 1) / TPI;
+  const int jp = r0 >> lg;                             // first key group of the piece
+  const int n_groups = ((r1 - 1) >> lg) - jp + 1;
+  const Rsrc crs = make_rsrc(P.k_codes + stream * P.k_codes_stride + run.code_off + int64_t(r0) * RB,
+                             uint32_t(n) * RB);
+  const Rsrc mrs = make_rsrc(P.k_meta + stream * P.k_meta_stride + run.meta_off + int64_t(jp) * D * 4,
+                             uint32_t(n_groups) * D * 4);
+  const int tt = lane / LPR, tq = lane % LPR;
+  const uint32_t lane_off = uint32_t(tt * RB + tq * LB);
 
-  // the first batch of code loads is in flight during the meta work; every
-  // load address is clamped into the range, so no load sits behind a branch
-  auto load = [&](int i) {
-    const int r = r0 + min(i * TPI + my_t, n - 1);
-    return *reinterpret_cast<const uint4*>(codes + int64_t(r) * RB + my_c * 16);
-  };
-  uint4 buf[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) buf[u] = load(u);
-
-  // meta work: lane -> pair pi of a row (word pi/NP, position pi%NP, i.e.
-  // channels clo and clo + NP) of group it*GPI + lane/HD
+  // meta role of the lane: pair pi of a row (word pi/NP, position pi%NP, i.e.
+  // channels clo and clo + NP) of the iteration's group gsub
   const int pi = lane % HD, gsub = lane / HD;
   const int kq = pi % NP;
   const int clo = (pi / NP) * CPW + kq, chi = clo + NP;
-  uint32_t mlo[MI], mhi[MI];
-#pragma unroll
-  for (int it = 0; it < MI; ++it) {
-    const int j = min(it * GPI + gsub, ng - 1);
-    const uint32_t* m = meta + int64_t(j0 + j) * D;
-    mlo[it] = m[clo];
-    mhi[it] = m[chi];
-  }
+  const int qpos = (pi / PPL) * QSTR + pi % PPL;       // LDS dword of the pair's hi in its chunk
+  const uint32_t meta_off = uint32_t((gsub * D + clo) * 4);
   half2_t qk[GQ];
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
@@ -149,220 +207,247 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
             as_h2(0x1C001C00u);                                   // * 2^-8, exact
   const _Float16 off = static_cast<_Float16>(Unpack<BITS>::offset(kq));
   const half2_t nego = {-off, -off};
+
+  // Software pipeline over load batches: the loads of batch b+1 are in
+  // flight while batch b is consumed.  A batch past the end is still issued:
+  // its reads fall outside the buffer ranges and return zeros without
+  // touching memory, and issuing unconditionally keeps the wait counts exact.
+  struct Batch {
+    typename LoadType<WPL>::T buf[NB];
+    uint32_t mlo[MI], mhi[MI];
+  };
+  auto issue = [&](Batch& B, int i0) {
+    const uint32_t cb = lane_off + uint32_t(i0 * TPI * RB);
 #pragma unroll
-  for (int it = 0; it < MI; ++it) {
-    const int j = it * GPI + gsub;
-    const bool valid = j < ng;
-    if (it * GPI >= ng) continue;          // uniform; keeps the loop fully unrolled
-    const half2_t s2 = as_h2((mlo[it] & 0xffffu) | (mhi[it] << 16));
-    const half2_t z2 = as_h2((mlo[it] >> 16) | (mhi[it] & 0xffff0000u));
+    for (int u = 0; u < NB; ++u) B.buf[u] = bload<WPL>(crs, cb + u * TPI * RB);
+    const uint32_t mb = meta_off + uint32_t((((r0 + i0 * TPI) >> lg) - jp) * D * 4);
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      const half2_t hi = qk[h] * s2;
-      const half2_t lo = __builtin_elementwise_fma(qk[h], s2, -hi);
-      float bp = __builtin_amdgcn_fdot2(qk[h], z2, 0.f, false);
-      bp = __builtin_amdgcn_fdot2(hi, nego, bp, false);
-      bp = __builtin_amdgcn_fdot2(lo, nego, bp, false);
-      bp = group_sum<16>(bp);
-      bp += __shfl_xor(bp, 16);
-      if (HD == 64) bp += __shfl_xor(bp, 32);
-      if (valid) {
-        uint32_t* qs = W.qs + (j * GQ + h) * (2 * HD);
-        qs[pi] = as_u32(hi);
-        qs[HD + pi] = as_u32(lo);
-        if (pi == 0) W.bias[j * GQ + h] = bp;
+    for (int it = 0; it < MI; ++it) {
+      B.mlo[it] = bload<1>(mrs, mb + it * GPI * D * 4);
+      B.mhi[it] = bload<1>(mrs, mb + it * GPI * D * 4 + NP * 4);
+    }
+  };
+  auto consume = [&](const Batch& B, int i0) {
+    const int jb0 = ((r0 + i0 * TPI) >> lg) - jp;      // batch groups, relative to the piece
+    const int ng = min(((r0 + min((i0 + NB) * TPI, n) - 1) >> lg) - jp - jb0 + 1, NGB);
+#pragma unroll
+    for (int it = 0; it < MI; ++it) {
+      if (it * GPI >= ng) continue;          // uniform; keeps the loop fully unrolled
+      const int js = it * GPI + gsub;
+      const half2_t s2 = as_h2(__builtin_amdgcn_perm(B.mhi[it], B.mlo[it], 0x05040100u));
+      const half2_t z2 = as_h2(__builtin_amdgcn_perm(B.mhi[it], B.mlo[it], 0x07060302u));
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        const half2_t hi = qk[h] * s2;
+        const half2_t lo = __builtin_elementwise_fma(qk[h], s2, -hi);
+        float bp = __builtin_amdgcn_fdot2(qk[h], z2, 0.f, false);
+        bp = __builtin_amdgcn_fdot2(hi, nego, bp, false);
+        bp = __builtin_amdgcn_fdot2(lo, nego, bp, false);
+        bp = group_sum<PPL>(bp);
+        if (js < ng) {
+          uint32_t* qs = W.qs + (js * GQ + h) * QHEAD;
+          qs[qpos] = as_u32(hi);
+          qs[LPR * QSTR + qpos] = as_u32(lo);
+          if (pi % PPL == 0) W.bias[(js * GQ + h) * LPR + pi / PPL] = bp;
+        }
       }
     }
-  }
-  wave_lds_sync();
+    wave_lds_sync();
 
-  const float sc = P.scale_log2 * 256.f;   // undo the 2^-8
-  for (int i0 = 0;;) {
+    uint32_t qhi[GQ][PPL], qlo[GQ][PPL];
+    float bias[GQ];
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int i = i0 + u;
-      const uint4 cw = buf[u];
-      const int tl = i * TPI + my_t;
-      const bool valid = tl < n;
-      const int jl = (min(tl, n - 1) + rofs) >> lg;
-      uint32_t v[4][NP];
-      Unpack<BITS>::run(cw.x, v[0]);
-      Unpack<BITS>::run(cw.y, v[1]);
-      Unpack<BITS>::run(cw.z, v[2]);
-      Unpack<BITS>::run(cw.w, v[3]);
+      if (i >= n_items) continue;            // uniform
+      const int rt = r0 + i * TPI;           // first run token of the item
+      if (u == 0 || (rt & (P.G - 1)) == 0) {
+        // (uniform) the item starts a group: fetch the lane's q*s pairs
+        const int js = min((rt >> lg) - jp - jb0, NGB - 1);
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        const uint32_t* qb = W.qs + (jl * GQ + h) * (2 * HD) + my_c * PPC;
-        const uint4* qhi = reinterpret_cast<const uint4*>(qb);
-        const uint4* qlo = reinterpret_cast<const uint4*>(qb + HD);
-        float acc = 0.f;
+        for (int h = 0; h < GQ; ++h) {
+          const uint32_t* qs = W.qs + (js * GQ + h) * QHEAD + tq * QSTR;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-#pragma unroll
-          for (int q4 = 0; q4 < NP / 4 + (NP < 4 ? 1 : 0); ++q4) {
-            const int pbase = w * NP + q4 * 4;   // the NP pairs of word w
-            uint32_t hi[4], lo[4];
-            if (NP >= 4) {
-              const uint4 x = qhi[pbase / 4], y = qlo[pbase / 4];
-              hi[0] = x.x; hi[1] = x.y; hi[2] = x.z; hi[3] = x.w;
-              lo[0] = y.x; lo[1] = y.y; lo[2] = y.z; lo[3] = y.w;
-            } else {
-              const uint2 x = reinterpret_cast<const uint2*>(qb)[pbase / 2];
-              const uint2 y = reinterpret_cast<const uint2*>(qb + HD)[pbase / 2];
-              hi[0] = x.x; hi[1] = x.y; lo[0] = y.x; lo[1] = y.y;
-            }
-#pragma unroll
-            for (int e = 0; e < (NP >= 4 ? 4 : NP); ++e) {
-              acc = dot2(hi[e], v[w][q4 * 4 + e], acc);
-              acc = dot2(lo[e], v[w][q4 * 4 + e], acc);
-            }
+          for (int p = 0; p < PPL; p += 4) {
+            const uint4 x = *reinterpret_cast<const uint4*>(qs + p);
+            const uint4 y = *reinterpret_cast<const uint4*>(qs + LPR * QSTR + p);
+            qhi[h][p] = x.x; qhi[h][p + 1] = x.y; qhi[h][p + 2] = x.z; qhi[h][p + 3] = x.w;
+            qlo[h][p] = y.x; qlo[h][p + 1] = y.y; qlo[h][p + 2] = y.z; qlo[h][p + 3] = y.w;
           }
+          bias[h] = W.bias[(js * GQ + h) * LPR + tq];
         }
-        acc = group_sum<CPR>(acc);
-        if (valid && my_c == 0) W.logit[h * LT + slot0 + tl] = (acc + W.bias[jl * GQ + h]) * sc;
       }
-    }
-    i0 += NB;
-    if (i0 >= n_inst) break;
-    // the whole batch is consumed before the next one is issued, so no load
-    // is in flight across the loop edge and the wait counts stay exact
+      float acc[GQ];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) buf[u] = load(i0 + u);
+      for (int h = 0; h < GQ; ++h) acc[h] = bias[h];
+#pragma unroll
+      for (int w = 0; w < WPL; ++w) {
+        uint32_t v[NP];
+        Unpack<BITS>::run(word<WPL>(B.buf[u], w), v);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h)
+#pragma unroll
+          for (int k = 0; k < NP; ++k) {
+            acc[h] = dot2(qhi[h][w * NP + k], v[k], acc[h]);
+            acc[h] = dot2(qlo[h][w * NP + k], v[k], acc[h]);
+          }
+      }
+      // every lane of the row holds the row sum; all of them store it
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) W.logit[h * LT + slot0 + i * TPI + tt] = group_sum<LPR>(acc[h]);
+    }
+    wave_lds_sync();                         // the next batch rewrites q*s
+  };
+
+  Batch A, Bb;
+  issue(A, 0);
+  for (int i0 = 0; i0 < n_items; i0 += 2 * NB) {
+    issue(Bb, i0 + NB);
+    consume(A, i0);
+    issue(A, i0 + 2 * NB);
+    if (i0 + NB < n_items) consume(Bb, i0 + NB);
   }
 }
 
-// Keys from fp16 rows rows[row0 + i], i < n -> logits at slots slot0 + i.
+// Keys from fp16 rows rows[0..n) -> raw logits q'.k at slots slot0 + i
+// (whole items are written, as above).
 template <int D, int GQ>
 __device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qh16,
-                          const uint16_t* rows, int row0, int n, int slot0, int lane) {
-  constexpr int LT = wave_tokens(GQ) + 4;
+                          const uint16_t* rows, int n, int slot0, int lane) {
+  constexpr int LT = wave_slots(GQ);
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int TPI = 64 / CPR;
+  constexpr int NB = 8;
   const int n_inst = (n + TPI - 1) / TPI;
   const int my_t = lane / CPR, my_c = lane % CPR;
-  auto load = [&](int i) {
-    const int t = min(i * TPI + my_t, n - 1);
-    return *reinterpret_cast<const uint4*>(rows + int64_t(row0 + t) * D + my_c * 8);
-  };
-  uint4 buf[NB];
+  const Rsrc rs = make_rsrc(rows, uint32_t(n) * D * 2);
+  uint32_t qq[GQ][4];
 #pragma unroll
-  for (int u = 0; u < NB; ++u) buf[u] = load(u);
-  for (int i0 = 0;;) {
+  for (int h = 0; h < GQ; ++h) {
+    const uint4 x = reinterpret_cast<const uint4*>(qh16 + h * D)[my_c];
+    const half2_t s8 = as_h2(0x1C001C00u);                        // * 2^-8, exact
+    qq[h][0] = as_u32(as_h2(x.x) * s8);
+    qq[h][1] = as_u32(as_h2(x.y) * s8);
+    qq[h][2] = as_u32(as_h2(x.z) * s8);
+    qq[h][3] = as_u32(as_h2(x.w) * s8);
+  }
+  const uint32_t lane_off = uint32_t((my_t * D + my_c * 8) * 2);
+  for (int i0 = 0; i0 < n_inst; i0 += NB) {
+    uint4 buf[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) buf[u] = bload<4>(rs, lane_off + uint32_t((i0 + u) * TPI * D * 2));
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int i = i0 + u;
+      if (i >= n_inst) continue;
       const uint4 x = buf[u];
-      const int t = i * TPI + my_t;
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const uint4 qq = reinterpret_cast<const uint4*>(qh16 + h * D)[my_c];
-        float acc = dot2(qq.x, x.x, 0.f);
-        acc = dot2(qq.y, x.y, acc);
-        acc = dot2(qq.z, x.z, acc);
-        acc = dot2(qq.w, x.w, acc);
-        acc = group_sum<CPR>(acc);
-        if (t < n && my_c == 0) W.logit[h * LT + slot0 + t] = acc * P.scale_log2;
+        float acc = dot2(qq[h][0], x.x, 0.f);
+        acc = dot2(qq[h][1], x.y, acc);
+        acc = dot2(qq[h][2], x.z, acc);
+        acc = dot2(qq[h][3], x.w, acc);
+        W.logit[h * LT + slot0 + i * TPI + my_t] = group_sum<CPR>(acc);
       }
     }
-    i0 += NB;
-    if (i0 >= n_inst) break;
-#pragma unroll
-    for (int u = 0; u < NB; ++u) buf[u] = load(i0 + u);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Reduce the per-lane value partials vals[CH] (lanes l with l % CPL == c own
-// channels c*CH .. c*CH+CH-1) across the wave into o[0..D).  The four rows of
-// 16 lanes are combined through W.logit, whose logits are dead by now.
-template <int D, int CPL, int CH>
-__device__ __forceinline__ void wave_reduce_values(const WaveLds& W, float* vals, int lane,
-                                                   float* o) {
+// Cross-lane reduction of value partials.  Lane l holds x[0..NX) for chunk
+// c = l % CPL; lanes with equal l % CPL are summed.  Within each row of 16
+// lanes the sums come from DPP rotations; the four rows' sums are left in
+// W.logit (dead by now) as red[(row * CPL + c) * NX + j].
+template <int CPL, int NX>
+__device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], int lane) {
 #pragma unroll
-  for (int j = 0; j < CH; ++j) {
-    float x = vals[j];
-    if (CPL <= 8) x = row_ror_add<8>(x);
-    if (CPL <= 4) x = row_ror_add<4>(x);
-    if (CPL <= 2) x = row_ror_add<2>(x);
-    if (CPL <= 1) x = row_ror_add<1>(x);
-    vals[j] = x;
+  for (int j = 0; j < NX; ++j) {
+    float y = x[j];
+    if (CPL <= 8) y = row_ror_add<8>(y);
+    if (CPL <= 4) y = row_ror_add<4>(y);
+    if (CPL <= 2) y = row_ror_add<2>(y);
+    if (CPL <= 1) y = row_ror_add<1>(y);
+    x[j] = y;
   }
-  // lanes (lane % 16) < CPL of each row of 16 now hold their row's sums
+  // lanes (lane % 16) < CPL now hold their row's sums
   float* red = W.logit;
   const int row = lane >> 4, c = lane & 15;
   if (c < CPL) {
 #pragma unroll
-    for (int j = 0; j < CH; ++j) red[row * D + c * CH + j] = vals[j];
+    for (int j = 0; j < NX; ++j) red[(row * CPL + c) * NX + j] = x[j];
   }
-  wave_lds_sync();
-  for (int ch = lane; ch < D; ch += 64)
-    o[ch] = (red[ch] + red[D + ch]) + (red[2 * D + ch] + red[3 * D + ch]);
   wave_lds_sync();
 }
 
-// Values of run tokens [r0, r1) (bits 2/4/8).  Pair block P of the run holds
-// run tokens 2P and 2P+1, whose probabilities are the fp16 pair P - r0/2 of
-// W.p16 (slot 2(P - r0/2) is token 2P); the pair after the last is zero.
+// Values of run tokens [r0, r1) (bits 2/4/8).  Pair block p of the run holds
+// run tokens 2p and 2p+1, whose probabilities are fp16 pair p - r0/2 of W.p16
+// counted from dword ps0 (r0 is even).  The partner after an odd run's last
+// token has probability zero (the caller clears its slot) and finite meta;
+// pair blocks past the range read zero codes and zero meta, so they add 0.
 template <int D, int GQ, int BITS>
 __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_t stream,
-                                 const Run& run, int r0, int r1, int lane) {
-  constexpr int LT = wave_tokens(GQ) + 4;
+                                 const Run& run, int r0, int r1, int ps0, int lane) {
+  constexpr int LT = wave_slots(GQ);
   constexpr int RB = D * BITS / 8;
   constexpr int CPP = 2 * RB / 16;        // 16-byte chunks per pair block
   constexpr int PPI = 64 / CPP;           // pair blocks per wave instruction
   constexpr int CPCV = 64 / BITS;         // channels per chunk
   constexpr int NP = Unpack<BITS>::NP;    // channels per 16-bit unit
   constexpr int HPP = (GQ * CPCV <= 64) ? GQ : ((64 / CPCV) > 0 ? (64 / CPCV) : 1);
+  constexpr int NX = CPCV + 2;
   const int NG = D >> P.lg_g;
   const int my_p = lane / CPP, my_c = lane % CPP;
   const int g = (my_c * CPCV) >> P.lg_g;
   const int p0 = r0 >> 1;
   const int np = ((r1 - 1) >> 1) - p0 + 1;
   const int n_inst = (np + PPI - 1) / PPI;
-  const uint8_t* codes = P.v_codes + stream * P.v_codes_stride + run.code_off;
-  const uint8_t* meta = P.v_meta + stream * P.v_meta_stride + run.meta_off;
-  const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16);
+  const Rsrc crs = make_rsrc(P.v_codes + stream * P.v_codes_stride + run.code_off + int64_t(p0) * 2 * RB,
+                             uint32_t(np) * 2 * RB);
+  const Rsrc mrs = make_rsrc(P.v_meta + stream * P.v_meta_stride + run.meta_off + int64_t(p0) * NG * 8,
+                             uint32_t(np) * NG * 8);
+  const uint32_t c_off = uint32_t(my_p * 2 * RB + my_c * 16);
+  const uint32_t m_off = uint32_t((my_p * NG + g) * 8);
+  const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16) + ps0;
   const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
   for (int hp = 0; hp < GQ; hp += HPP) {
-    float acc[HPP][CPCV];
-    float sps[HPP], pz[HPP];
+    float acc[HPP][NX];                   // [CPCV] channel sums, then sum(p*s), sum(p*z)
 #pragma unroll
-    for (int hh = 0; hh < HPP; ++hh) {
-      sps[hh] = 0.f;
-      pz[hh] = 0.f;
+    for (int hh = 0; hh < HPP; ++hh)
 #pragma unroll
-      for (int j = 0; j < CPCV; ++j) acc[hh][j] = 0.f;
-    }
-    auto load = [&](int i, uint4& c4, uint2& m2) {
-      const int64_t pr = p0 + min(i * PPI + my_p, np - 1);
-      c4 = *reinterpret_cast<const uint4*>(codes + pr * (2 * RB) + my_c * 16);
-      m2 = *reinterpret_cast<const uint2*>(meta + (pr * NG + g) * 8);
+      for (int j = 0; j < NX; ++j) acc[hh][j] = 0.f;
+    // software pipeline as in keys_quantized: batch b+1 in flight while b is
+    // consumed; batches past the end read zeros and touch no memory
+    struct Batch {
+      uint4 cb[NBV];
+      uint2 mb[NBV];
     };
-    uint4 cb[NBV];
-    uint2 mb[NBV];
-#pragma unroll
-    for (int u = 0; u < NBV; ++u) load(u, cb[u], mb[u]);
-    for (int i0 = 0;;) {
+    auto issue = [&](Batch& B, int i0) {
 #pragma unroll
       for (int u = 0; u < NBV; ++u) {
-        const int i = i0 + u;
-        const uint4 cw = cb[u];
-        const uint2 mw = mb[u];
-        const int plc = min(i * PPI + my_p, np);      // pair np reads as zero
-        const half2_t s2 = as_h2((mw.x & 0xffffu) | (mw.y << 16));
-        const half2_t z2 = as_h2((mw.x >> 16) | (mw.y & 0xffff0000u));
+        B.cb[u] = bload<4>(crs, c_off + uint32_t((i0 + u) * PPI * 2 * RB));
+        B.mb[u] = bload<2>(mrs, m_off + uint32_t((i0 + u) * PPI * NG * 8));
+      }
+    };
+    auto consume = [&](const Batch& B, int i0) {
+#pragma unroll
+      for (int u = 0; u < NBV; ++u) {
+        if (i0 + u >= n_inst) continue;     // uniform
+        const half2_t s2 = as_h2(__builtin_amdgcn_perm(B.mb[u].y, B.mb[u].x, 0x05040100u));
+        const half2_t z2 = as_h2(__builtin_amdgcn_perm(B.mb[u].y, B.mb[u].x, 0x07060302u));
         uint32_t ps[HPP];
 #pragma unroll
         for (int hh = 0; hh < HPP; ++hh) {
-          const half2_t p2 = as_h2(pp[(hp + hh) * (LT / 2) + plc]);
+          // pair np (a zero slot, or a probability of the next piece whose
+          // meta here reads as zero) stands in for every pair past the range
+          const half2_t p2 = as_h2(pp[(hp + hh) * (LT / 2) + min((i0 + u) * PPI + my_p, np)]);
           const half2_t psh = p2 * s2;
           ps[hh] = as_u32(psh);
-          sps[hh] = __builtin_amdgcn_fdot2(psh, one2, sps[hh], false);
-          pz[hh] = __builtin_amdgcn_fdot2(p2, z2, pz[hh], false);
+          acc[hh][CPCV] = __builtin_amdgcn_fdot2(psh, one2, acc[hh][CPCV], false);
+          acc[hh][CPCV + 1] = __builtin_amdgcn_fdot2(p2, z2, acc[hh][CPCV + 1], false);
         }
         // one word at a time: unpack, then apply it to every head
-        const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+        const uint32_t words[4] = {B.cb[u].x, B.cb[u].y, B.cb[u].z, B.cb[u].w};
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t v[NP];
@@ -373,49 +458,65 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
             for (int k = 0; k < NP; ++k) acc[hh][w * NP + k] = dot2(ps[hh], v[k], acc[hh][w * NP + k]);
         }
       }
-      i0 += NBV;
-      if (i0 >= n_inst) break;
-#pragma unroll
-      for (int u = 0; u < NBV; ++u) load(i0 + u, cb[u], mb[u]);
+    };
+    Batch A, Bb;
+    issue(A, 0);
+    for (int i0 = 0; i0 < n_inst; i0 += 2 * NBV) {
+      issue(Bb, i0 + NBV);
+      consume(A, i0);
+      issue(A, i0 + 2 * NBV);
+      if (i0 + NBV < n_inst) consume(Bb, i0 + NBV);
     }
 #pragma unroll
     for (int hh = 0; hh < HPP; ++hh) {
-      float vals[CPCV];
+      reduce_rows<CPP, NX>(W, acc[hh], lane);
+      const float* red = W.logit;
 #pragma unroll
-      for (int j = 0; j < CPCV; ++j)
-        vals[j] = acc[hh][j] - Unpack<BITS>::offset(j % NP) * sps[hh] + pz[hh];
-      wave_reduce_values<D, CPP, CPCV>(W, vals, lane, W.ow + (hp + hh) * (D + 2) + 2);
+      for (int k = 0; k < D / 64; ++k) {
+        const int ch = lane + 64 * k;
+        const int c = ch / CPCV, j = ch % CPCV;
+        float a = 0.f, s = 0.f, z = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float* e = red + (r * CPP + c) * NX;
+          a += e[j];
+          s += e[CPCV];
+          z += e[CPCV + 1];
+        }
+        W.ow[(hp + hh) * (D + 2) + 2 + ch] += a - Unpack<BITS>::offset(j % NP) * s + z;
+      }
+      wave_lds_sync();
     }
   }
 }
 
-// Values from fp16 rows rows[row0 + i], i < n, probabilities at slots i.
+// Values from fp16 rows rows[0..n), probabilities at slots slot0 + i
+// (slots past the range are zero or belong to other pieces; rows past the
+// range read as zero).
 template <int D, int GQ>
 __device__ void values_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* rows,
-                            int row0, int n, int lane) {
-  constexpr int LT = wave_tokens(GQ) + 4;
+                            int n, int slot0, int lane) {
+  constexpr int LT = wave_slots(GQ);
   constexpr int CPR = D / 8;
   constexpr int TPI = 64 / CPR;
+  constexpr int NB = 8;
   const int my_t = lane / CPR, my_c = lane % CPR;
   const int n_inst = (n + TPI - 1) / TPI;
+  const Rsrc rs = make_rsrc(rows, uint32_t(n) * D * 2);
+  const uint32_t lane_off = uint32_t((my_t * D + my_c * 8) * 2);
   float acc[GQ][8];
 #pragma unroll
   for (int h = 0; h < GQ; ++h)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[h][j] = 0.f;
-  auto load = [&](int i) {
-    const int t = min(i * TPI + my_t, n - 1);
-    return *reinterpret_cast<const uint4*>(rows + int64_t(row0 + t) * D + my_c * 8);
-  };
-  uint4 buf[NB];
+  for (int i0 = 0; i0 < n_inst; i0 += NB) {
+    uint4 buf[NB];
 #pragma unroll
-  for (int u = 0; u < NB; ++u) buf[u] = load(u);
-  for (int i0 = 0;;) {
+    for (int u = 0; u < NB; ++u) buf[u] = bload<4>(rs, lane_off + uint32_t((i0 + u) * TPI * D * 2));
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      const int i = i0 + u;
+      const int t = (i0 + u) * TPI + my_t;
       const uint4 x = buf[u];
-      const int t = min(i * TPI + my_t, LT - 1);     // slots past the tokens are zero
       const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
       float f[8];
 #pragma unroll
@@ -425,182 +526,264 @@ __device__ void values_fp16(const DecodeParams& P, const WaveLds& W, const uint1
       }
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const float p = h2f(W.p16[h * LT + t]);
+        const float p = t < n ? h2f(W.p16[h * LT + slot0 + t]) : 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[h][j] += p * f[j];
       }
     }
-    i0 += NB;
-    if (i0 >= n_inst) break;
-#pragma unroll
-    for (int u = 0; u < NB; ++u) buf[u] = load(i0 + u);
   }
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) wave_reduce_values<D, CPR, 8>(W, acc[h], lane, W.ow + h * (D + 2) + 2);
+  for (int h = 0; h < GQ; ++h) {
+    reduce_rows<CPR, 8>(W, acc[h], lane);
+    const float* red = W.logit;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int ch = lane + 64 * k;
+      const int c = ch / 8, j = ch % 8;
+      float a = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a += red[(r * CPR + c) * 8 + j];
+      W.ow[h * (D + 2) + 2 + ch] += a;
+    }
+    wave_lds_sync();
+  }
+}
+
+// First token of wave range w of a stream of N tokens cut into NW ranges.
+__device__ __forceinline__ int wave_bound(int w, int N, int NW) {
+  if (w >= NW) return N;
+  return int((int64_t(w) * N / NW) & ~int64_t(kWaveAlign - 1));
 }
 
 // ---------------------------------------------------------------------------
 // Four waves per SIMD (<= 128 VGPRs) for one query head per kv head: 16
 // resident waves per CU keep enough loads in flight to cover HBM latency.
 // Grouped heads do GQ times the arithmetic per byte and get 256 VGPRs.
-template <int D, int GQ>
-__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(GQ == 1 ? 4 : 2)))
-decode_split_kernel(const DecodeParams P) {
+template <int D, int GQ, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQ == 1 ? 4 : 2)))
+decode_kernel(const DecodeParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int LT = wave_tokens(GQ) + 4;
+  constexpr int LT = wave_slots(GQ);
+  constexpr int DK = D / 64;
+  constexpr DecodeLds lay = decode_lds<D, GQ>();
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (scalar) so that every loop bound derived from it is scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int split = blockIdx.x;
+  const int wg = blockIdx.x;
   const int64_t stream = blockIdx.y;
   const int b = int(stream / P.Hkv), hkv = int(stream % P.Hkv);
-
-  int ci = 0;
-  while (ci + 1 < P.n_cells && P.cells[ci + 1].split0 <= split) ++ci;
-  const Cell cell = P.cells[ci];
-  const int ST = P.split_tokens;
-  const int t0 = cell.t0 + (split - cell.split0) * ST;
-  const int t1 = min(t0 + ST, cell.t0 + cell.n);
-  const int wt = (ST + kWaves - 1) / kWaves;      // tokens per wave (<= wave_tokens(GQ))
-  const int a = min(t0 + wave * wt, t1);
-  const int e = min(a + wt, t1);
+  const int N = P.n_tok;
+  const int gw = wg * NW + wave;
+  const int a = wave_bound(gw, N, P.waves_per_stream);
+  const int e = wave_bound(gw + 1, N, P.waves_per_stream);
   const int n = e - a;
 
   uint16_t* qh16 = reinterpret_cast<uint16_t*>(smem);
   const int64_t qrow = (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;
-  for (int i = tid; i < GQ * D; i += NT) {
+  for (int i = tid; i < GQ * D; i += NW * 64) {
     const int h = i / D;
     qh16[i] = h < P.gq ? P.q[qrow + i] : uint16_t(0);
   }
   __syncthreads();
 
   const WaveLds W = carve_wave<D, GQ>(smem, wave);
-  // token t of the wave sits at slot slot0 + (t - a); for quantized value runs
-  // slot0 makes every value pair block start at an even slot
-  int slot0 = 0;
-  if (cell.v_src >= 0 && P.v_runs[cell.v_src].bits != 16)
-    slot0 = (a - P.v_runs[cell.v_src].tok_begin) & 1;
+  // token t of the wave sits at slot t - a; a is even and quantized value
+  // runs start at even tokens, so every value pair block starts at an even slot
   if (n > 0) {
-    if (cell.k_src >= 0) {
-      const Run& run = P.k_runs[cell.k_src];
-      const int r0 = a - run.tok_begin, r1 = e - run.tok_begin;
+    // key pieces in token order
+    for (int k = 0; k < P.n_k_runs; ++k) {
+      const Run& run = P.k_runs[k];
+      const int t0 = max(a, run.tok_begin), t1 = min(e, run.tok_begin + run.n_tok);
+      if (t0 >= t1) continue;
+      const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
       switch (run.bits) {
-        case 2: keys_quantized<D, GQ, 2>(P, W, qh16, stream, run, r0, r1, slot0, lane); break;
-        case 4: keys_quantized<D, GQ, 4>(P, W, qh16, stream, run, r0, r1, slot0, lane); break;
-        case 8: keys_quantized<D, GQ, 8>(P, W, qh16, stream, run, r0, r1, slot0, lane); break;
+        case 2: keys_quantized<D, GQ, 2>(P, W, qh16, stream, run, r0, r1, t0 - a, lane); break;
+        case 4: keys_quantized<D, GQ, 4>(P, W, qh16, stream, run, r0, r1, t0 - a, lane); break;
+        case 8: keys_quantized<D, GQ, 8>(P, W, qh16, stream, run, r0, r1, t0 - a, lane); break;
         default:
           keys_fp16<D, GQ>(P, W, qh16,
-                           reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off),
-                           r0, n, slot0, lane);
+                           reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off) +
+                               int64_t(r0) * D,
+                           r1 - r0, t0 - a, lane);
       }
-    } else {
-      keys_fp16<D, GQ>(P, W, qh16, P.k_res + stream * P.k_res_stride, a - P.n_kq, n, slot0, lane);
+    }
+    if (e > P.n_kq) {
+      const int t0 = max(a, P.n_kq);
+      keys_fp16<D, GQ>(P, W, qh16, P.k_res + stream * P.k_res_stride + int64_t(t0 - P.n_kq) * D, e - t0,
+                       t0 - a, lane);
     }
     wave_lds_sync();
+  }
 
-    // softmax state of this wave's range, per head (base-2 logits); every slot
-    // of p16 is written, zero outside the wave's tokens
-    float mh[GQ], lh[GQ];
+  // softmax state of this wave's range, per head: raw logits x = q'.k, base-2
+  // logits x * sc; every slot of p16 is written, zero outside the tokens
+  float mh[GQ], lh[GQ];
+  const float sc = P.scale_log2 * 256.f;        // undoes q' = q * 2^-8
 #pragma unroll
-    for (int h = 0; h < GQ; ++h) {
-      float mx = -INFINITY;
-      for (int i = lane; i < n; i += 64) mx = fmaxf(mx, W.logit[h * LT + slot0 + i]);
-      mx = wave_max(mx);
-      float sum = 0.f;
-      for (int sl = lane; sl < LT; sl += 64) {
-        const int i = sl - slot0;
-        const float x = (i >= 0 && i < n) ? exp2f(W.logit[h * LT + sl] - mx) : 0.f;
-        const uint32_t x16 = f2h(x);
-        W.p16[h * LT + sl] = static_cast<uint16_t>(x16);
-        sum += h2f(x16);              // the same rounded values the A.V uses
-      }
-      mh[h] = mx;
-      lh[h] = wave_sum(sum);
+  for (int h = 0; h < GQ; ++h) {
+    float mx = -INFINITY;
+    for (int s = lane * 4; s < n; s += 256) {
+      const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
+      mx = fmaxf(mx, x.x * sc);
+      if (s + 1 < n) mx = fmaxf(mx, x.y * sc);
+      if (s + 2 < n) mx = fmaxf(mx, x.z * sc);
+      if (s + 3 < n) mx = fmaxf(mx, x.w * sc);
     }
-    wave_lds_sync();
+    mx = wave_max64(mx);
+    const float nm = -mx;
+    float sum = 0.f;
+#pragma unroll
+    for (int s = lane * 4; s < LT; s += 256) {
+      const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
+      const float xs[4] = {x.x, x.y, x.z, x.w};
+      uint32_t p16[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        p16[k] = s + k < n ? f2h(exp2f(__builtin_fmaf(xs[k], sc, nm))) : 0u;
+        sum += h2f(p16[k]);             // the same rounded values the A.V uses
+      }
+      *reinterpret_cast<uint2*>(W.p16 + h * LT + s) =
+          make_uint2(p16[0] | (p16[1] << 16), p16[2] | (p16[3] << 16));
+    }
+    mh[h] = mx;
+    lh[h] = wave_sum64(sum);
+  }
+  wave_lds_sync();
 
-    if (cell.v_src >= 0) {
-      const Run& run = P.v_runs[cell.v_src];
-      const int r0 = a - run.tok_begin, r1 = e - run.tok_begin;
+  // the wave's output o[D] per head accumulates in its (m, l, o) block, which
+  // the value pieces add into (lane l owns channels l + 64k)
+#pragma unroll
+  for (int h = 0; h < GQ; ++h)
+#pragma unroll
+    for (int k = 0; k < DK; ++k) W.ow[h * (D + 2) + 2 + lane + 64 * k] = 0.f;
+  wave_lds_sync();
+  if (n > 0) {
+    // value pieces in token order
+    for (int k = 0; k < P.n_v_runs; ++k) {
+      const Run& run = P.v_runs[k];
+      const int t0 = max(a, run.tok_begin), t1 = min(e, run.tok_begin + run.n_tok);
+      if (t0 >= t1) continue;
+      const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
+      // the pair partner after an odd run's last token belongs to the next
+      // piece: its probability is zero while this run is read
+      const int ph = (run.bits != 16 && (r1 & 1) && t1 < e) ? t1 - a : -1;
+      uint16_t keep[GQ];
+      if (ph >= 0) {
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+          keep[h] = W.p16[h * LT + ph];
+          wave_lds_sync();
+          if (lane == 0) W.p16[h * LT + ph] = 0;
+        }
+        wave_lds_sync();
+      }
       switch (run.bits) {
-        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, lane); break;
-        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, lane); break;
-        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, lane); break;
+        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane); break;
+        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane); break;
+        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane); break;
         default:
           values_fp16<D, GQ>(P, W,
-                             reinterpret_cast<const uint16_t*>(P.v_codes + stream * P.v_codes_stride + run.code_off),
-                             r0, n, lane);
+                             reinterpret_cast<const uint16_t*>(P.v_codes + stream * P.v_codes_stride + run.code_off) +
+                                 int64_t(r0) * D,
+                             r1 - r0, t0 - a, lane);
       }
-    } else {
-      values_fp16<D, GQ>(P, W, P.v_res + stream * P.v_res_stride, a - P.n_vq, n, lane);
-    }
-    if (lane == 0) {
+      if (ph >= 0) {
+        wave_lds_sync();
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) {
-        W.ow[h * (D + 2)] = mh[h];
-        W.ow[h * (D + 2) + 1] = lh[h];
+        for (int h = 0; h < GQ; ++h)
+          if (lane == 0) W.p16[h * LT + ph] = keep[h];
+        wave_lds_sync();
       }
     }
-  } else {
-    for (int i = lane; i < GQ * (D + 2); i += 64) {
-      const int j = i % (D + 2);
-      W.ow[i] = j == 0 ? -INFINITY : 0.f;
+    if (e > P.n_vq) {
+      const int t0 = max(a, P.n_vq);
+      values_fp16<D, GQ>(P, W, P.v_res + stream * P.v_res_stride + int64_t(t0 - P.n_vq) * D, e - t0,
+                         t0 - a, lane);
+    }
+  }
+  // the wave's state (an empty wave has m = -inf, l = 0, o = 0)
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      W.ow[h * (D + 2)] = mh[h];
+      W.ow[h * (D + 2) + 1] = lh[h];
     }
   }
   __syncthreads();
 
-  // combine the waves' states and write this split's partial
-  float* ws = P.ws + (stream * P.n_splits + split) * int64_t(P.gq) * (D + 2);
-  constexpr DecodeLds lay = decode_lds(D, GQ);
-  for (int i = tid; i < P.gq * (D + 2); i += NT) {
+  // combine the four waves; with one workgroup per stream that is the output
+  // (and there is no merge kernel)
+  const int gq = P.gq;
+  const int64_t step = int64_t(gq) * (D + 2);
+  const bool single = P.wg_per_stream == 1;
+  const float* ow0 = reinterpret_cast<const float*>(smem + lay.block + lay.logit + lay.p16);
+  constexpr int WSTEP = int(lay.wave / 4);
+  for (int i = tid; i < gq * (D + 2); i += NW * 64) {
     const int h = i / (D + 2), j = i % (D + 2);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* ow = reinterpret_cast<const float*>(smem + lay.block + w * lay.wave + lay.logit + lay.p16);
-      M = fmaxf(M, ow[h * (D + 2)]);
-    }
-    float r = 0.f;
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, ow0[w * WSTEP + h * (D + 2)]);
+    float r = 0.f, l = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* ow = reinterpret_cast<const float*>(smem + lay.block + w * lay.wave + lay.logit + lay.p16);
-      const float f = exp2f(ow[h * (D + 2)] - M);
-      r += f * ow[h * (D + 2) + (j == 0 ? 1 : j)];
+    for (int w = 0; w < NW; ++w) {
+      const float* ow = ow0 + w * WSTEP + h * (D + 2);
+      const float f = ow[0] == M ? 1.f : exp2f(ow[0] - M);   // also -inf == -inf
+      r += f * ow[j == 0 ? 1 : j];
+      l += f * ow[1];
     }
-    ws[i] = j == 0 ? M : r;
+    if (single) {
+      if (j >= 2) P.out[(int64_t(b) * P.Hq + int64_t(hkv) * gq + h) * D + (j - 2)] = r / l;
+    } else {
+      P.ws[(stream * P.wg_per_stream + wg) * step + i] = j == 0 ? M : r;
+    }
   }
 }
 
-// Cross-split merge: out = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+// Cross-split merge, one thread per output element:
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the stream's
+// workgroup partials, folded in one pass with a running maximum.
 template <int D>
-__global__ void __launch_bounds__(D) decode_merge_kernel(const DecodeParams P) {
-  const int bh = blockIdx.x;
-  const int b = bh / P.Hq, hq = bh % P.Hq;
+__global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
+  const int64_t idx = int64_t(blockIdx.x) * NT + threadIdx.x;
+  if (idx >= int64_t(P.B) * P.Hq * D) return;
+  const int c = int(idx % D);
+  const int64_t bhq = idx / D;
+  const int b = int(bhq / P.Hq), hq = int(bhq % P.Hq);
   const int hkv = hq / P.gq, h = hq % P.gq;
   const int64_t stream = int64_t(b) * P.Hkv + hkv;
   const int64_t step = int64_t(P.gq) * (D + 2);
-  const float* w = P.ws + stream * P.n_splits * step + int64_t(h) * (D + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < P.n_splits; ++s) M = fmaxf(M, w[s * step]);
-  float den = 0.f, num = 0.f;
-  const int c = threadIdx.x;
-  for (int s = 0; s < P.n_splits; ++s) {
-    const float f = exp2f(w[s * step] - M);
-    den += f * w[s * step + 1];
-    num += f * w[s * step + 2 + c];
+  const float* w0 = P.ws + stream * P.wg_per_stream * step + h * (D + 2);
+  float M = -INFINITY, L = 0.f, O = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < P.wg_per_stream; ++s) {
+    const float* w = w0 + s * step;
+    const float m = w[0], l = w[1], o = w[2 + c];
+    const float Mn = fmaxf(M, m);
+    const float fa = M == Mn ? 1.f : exp2f(M - Mn);   // also -inf == -inf
+    const float fb = m == Mn ? 1.f : exp2f(m - Mn);
+    L = L * fa + l * fb;
+    O = O * fa + o * fb;
+    M = Mn;
   }
-  P.out[(int64_t(b) * P.Hq + hq) * D + c] = num / den;
+  P.out[idx] = O / L;
+}
+
+template <int D, int GQ, int NW>
+hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
+  const size_t lds = size_t(lds_bytes(decode_lds<D, GQ>(), NW));
+  hipLaunchKernelGGL((decode_kernel<D, GQ, NW>), dim3(p.wg_per_stream, p.B * p.Hkv), dim3(NW * 64),
+                     lds, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.wg_per_stream == 1) return e;
+  const int64_t n = int64_t(p.B) * p.Hq * D;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(unsigned((n + NT - 1) / NT)), dim3(NT), 0, s, p);
+  return hipGetLastError();
 }
 
 template <int D, int GQ>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t s) {
-  const size_t lds = size_t(decode_lds(D, GQ).total);
-  hipLaunchKernelGGL((decode_split_kernel<D, GQ>), dim3(p.n_splits, p.B * p.Hkv), dim3(NT),
-                     lds, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.B * p.Hq), dim3(D), 0, s, p);
-  return hipGetLastError();
+  if (p.waves_per_wg != kWaves) return hipErrorInvalidValue;
+  return launch_dgw<D, GQ, kWaves>(p, s);
 }
 
 template <int D>
@@ -621,6 +804,20 @@ hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s) {
     case 64: return launch_d<64>(p, GQ, s);
     case 128: return launch_d<128>(p, GQ, s);
     default: return hipErrorInvalidValue;
+  }
+}
+
+int64_t decode_lds_bytes(int D, int GQ, int waves) {
+  switch (D * 16 + GQ) {
+    case 64 * 16 + 1: return lds_bytes(decode_lds<64, 1>(), waves);
+    case 64 * 16 + 2: return lds_bytes(decode_lds<64, 2>(), waves);
+    case 64 * 16 + 4: return lds_bytes(decode_lds<64, 4>(), waves);
+    case 64 * 16 + 8: return lds_bytes(decode_lds<64, 8>(), waves);
+    case 128 * 16 + 1: return lds_bytes(decode_lds<128, 1>(), waves);
+    case 128 * 16 + 2: return lds_bytes(decode_lds<128, 2>(), waves);
+    case 128 * 16 + 4: return lds_bytes(decode_lds<128, 4>(), waves);
+    case 128 * 16 + 8: return lds_bytes(decode_lds<128, 8>(), waves);
+    default: return -1;
   }
 }
 

@@ -11,28 +11,98 @@ namespace kvq {
 constexpr int kThreads = 256;          // threads per decode / quantize workgroup
 constexpr int kWaves = 4;              // waves per decode workgroup
 constexpr int kMaxRuns = 8;            // runs per half of the cache
-constexpr int kMaxCells = 20;          // token ranges with one key and one value source
-constexpr int kLdsLimit = 64 * 1024;   // dynamic LDS budget per decode workgroup
+constexpr int kLdsLimit = 160 * 1024;  // LDS of one gfx950 CU: the most a workgroup can use
+constexpr int kWaveAlign = 32;         // wave token ranges start at multiples of this
 
-// Tokens each wave of a decode workgroup streams; a workgroup covers
-// kWaves * wave_tokens(GQ) tokens.  Larger GQ needs more LDS per token.
+// Target tokens per wave; a wave may get up to wave_cap(GQ) tokens.  Larger
+// GQ needs more LDS per token.
 __host__ __device__ constexpr int wave_tokens(int GQ) { return GQ <= 1 ? 256 : GQ == 2 ? 128 : GQ == 4 ? 64 : 32; }
+__host__ __device__ constexpr int wave_cap(int GQ) { return wave_tokens(GQ) * 3 / 2 + kWaveAlign; }
+// token slots per wave in LDS: the cap plus 32, since the streaming loops
+// read and write whole items (up to 32 tokens) past a range's last token
+__host__ __device__ constexpr int wave_slots(int GQ) { return wave_cap(GQ) + 32; }
+
+// Geometry of the quantized-key loop for (D, GQ, BITS).  Each lane takes LB
+// bytes (WPL words, PPL fp16 code pairs) of one token row; LPR lanes share a
+// row, so one wave instruction covers TPI tokens, all of one key group.  The
+// q*s hi/lo pairs of the lane's PPL pairs for the GQ heads stay in registers
+// for all items of a group: LB is the widest load that keeps 2*GQ*PPL within
+// the register budget.
+template <int D, int GQ, int BITS>
+struct KeyGeo {
+  static constexpr int RB = D * BITS / 8;       // bytes per token row
+  static constexpr int NP = 16 / BITS;          // fp16 code pairs per 32-bit word
+  static constexpr int CPW = 32 / BITS;         // channels per 32-bit word
+  static constexpr int PPL_MAX = GQ >= 8 ? 8 : 16;
+  static constexpr int LB0 = 4 * PPL_MAX / NP;
+  static constexpr int LB = LB0 > 16 ? (RB < 16 ? RB : 16) : (LB0 > RB ? RB : LB0);
+  static constexpr int LPR = RB / LB;           // lanes per row
+  static constexpr int TPI = 64 / LPR;          // tokens per wave instruction (item)
+  static constexpr int WPL = LB / 4;            // code words per lane
+  static constexpr int PPL = WPL * NP;          // code pairs per lane
+  static constexpr int HD = D / 2;              // code pairs per row
+  static constexpr int NB = 4;                  // items per load batch (two batches in flight)
+  static constexpr int NGB = NB * TPI / 32 > 1 ? NB * TPI / 32 : 1;  // key groups per batch
+  static constexpr int QSTR = PPL + 4;          // LDS dwords per chunk (padded against bank conflicts)
+  static constexpr int QHEAD = 2 * LPR * QSTR;  // LDS dwords per (group, head): hi chunks, lo chunks
+  static_assert(LPR * PPL == HD, "lanes of a row cover its pairs");
+  static_assert(TPI <= 32 && (NB * TPI) % 32 == 0, "items never straddle a key group");
+};
+
+__host__ __device__ constexpr int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
+__host__ __device__ constexpr int64_t cmax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// LDS dwords of the q*s blocks and of the per-chunk key biases of one load
+// batch, over the three code widths.
+template <int D, int GQ>
+__host__ __device__ constexpr int64_t kQsMax() {
+  return cmax(cmax(KeyGeo<D, GQ, 2>::NGB * GQ * KeyGeo<D, GQ, 2>::QHEAD,
+                   KeyGeo<D, GQ, 4>::NGB * GQ * KeyGeo<D, GQ, 4>::QHEAD),
+              KeyGeo<D, GQ, 8>::NGB * GQ * KeyGeo<D, GQ, 8>::QHEAD);
+}
+template <int D, int GQ>
+__host__ __device__ constexpr int64_t kBiasMax() {
+  return cmax(cmax(KeyGeo<D, GQ, 2>::NGB * GQ * KeyGeo<D, GQ, 2>::LPR,
+                   KeyGeo<D, GQ, 4>::NGB * GQ * KeyGeo<D, GQ, 4>::LPR),
+              KeyGeo<D, GQ, 8>::NGB * GQ * KeyGeo<D, GQ, 8>::LPR);
+}
+
+// Per-wave LDS of a decode workgroup (the device uses the same numbers).
+// Block part: q of the GQ heads as fp16.  Per
+// wave, with LT = wave_slots(GQ):
+//   logit  fp32 [GQ][LT]  logits by token slot; reused afterwards for the
+//                          row sums of the value reduction (at most 640 floats)
+//   p16    fp16 [GQ][LT]  probabilities, zero outside the wave's tokens
+//   area   q*s hi/lo pairs and per-chunk biases of the key groups of one load batch;
+//          afterwards the wave's (m, l, o[D]) per head
+struct DecodeLds {
+  int64_t block, logit, p16, area, wave, total;   // total: for kWaves waves
+};
+__host__ __device__ constexpr int64_t lds_bytes(const DecodeLds& l, int waves) {
+  return l.block + waves * l.wave;
+}
+template <int D, int GQ>
+__host__ __device__ constexpr DecodeLds decode_lds() {
+  const int64_t lt = wave_slots(GQ);
+  const int64_t block = round16(int64_t(GQ) * D * 2);
+  const int64_t logit = round16(cmax(int64_t(GQ) * lt * 4, 640 * 4));
+  const int64_t p16 = round16(int64_t(GQ) * lt * 2);
+  // q*s blocks of the widest layout, then the per-chunk biases (see carve_wave)
+  const int64_t qs = (kQsMax<D, GQ>() + kBiasMax<D, GQ>()) * 4;
+  const int64_t area = round16(cmax(qs, int64_t(GQ) * (D + 2) * 4));
+  const int64_t wave = logit + p16 + area;
+  return DecodeLds{block, logit, p16, area, wave, block + kWaves * wave};
+}
 
 struct Run {            // device copy of kvq_segment
   int32_t bits, tok_begin, n_tok, pad;
   int64_t code_off, meta_off;
 };
 
-// A maximal token range [t0, t0+n) whose keys come from one source and whose
-// values come from one source.  k_src / v_src: run index, or -1 = residual.
-struct Cell {
-  int32_t t0, n, k_src, v_src, split0, pad0, pad1, pad2;
-};
-
 struct DecodeParams {
   const uint16_t* q;
   float* out;
-  float* ws;
+  float* ws;                            // per-workgroup partials [stream][wg][gq][D+2]
   const uint8_t* k_codes;
   const uint8_t* k_meta;
   const uint8_t* v_codes;
@@ -43,41 +113,21 @@ struct DecodeParams {
   int64_t k_res_stride, v_res_stride;   // fp16 elements
   int32_t B, Hq, Hkv, D, G, gq;
   int32_t lg_g;                         // log2(G)
+  int32_t n_tok;                        // N, tokens attended per stream
   int32_t n_kq, n_vq;                   // tokens held in key runs / value runs
-  int32_t n_splits, split_tokens;       // split_tokens = kWaves * wave_tokens(GQ)
+  int32_t waves_per_stream;             // a multiple of waves_per_wg
+  int32_t waves_per_wg;                 // kWaves
+  int32_t wg_per_stream;
   float scale_log2;                     // sm_scale * log2(e)
-  int32_t n_cells, n_k_runs, n_v_runs;
+  int32_t n_k_runs, n_v_runs;
   Run k_runs[kMaxRuns];
   Run v_runs[kMaxRuns];
-  Cell cells[kMaxCells];
 };
-
-// LDS carve-up of one decode workgroup (the device uses the same numbers).
-// Block part: q of the GQ heads as fp16.  Per wave, for LT = wave_tokens + 4
-// token slots (a leading slot keeps value pairs aligned, the tail is zero):
-//   logit  fp32 [GQ][LT]  logits; reused afterwards for the [4][D] value
-//                          reduction rows
-//   p16    fp16 [GQ][LT]  probabilities, zero outside the wave's tokens
-//   area   q*s hi/lo pairs [NGW][GQ][2][D/2] and bias [NGW][GQ] per key group
-//          (NGW groups, sized for G = 32); afterwards the wave's partial
-//          (m, l, o[D]) per head
-struct DecodeLds {
-  int64_t block, logit, p16, area, wave, total;
-};
-__host__ __device__ constexpr int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
-__host__ __device__ constexpr int64_t cmax(int64_t a, int64_t b) { return a > b ? a : b; }
-__host__ __device__ constexpr DecodeLds decode_lds(int D, int GQ) {
-  const int64_t lt = wave_tokens(GQ) + 4;
-  const int64_t ngw = wave_tokens(GQ) / 32 + 1;
-  const int64_t block = round16(int64_t(GQ) * D * 2);
-  const int64_t logit = round16(cmax(int64_t(GQ) * lt * 4, int64_t(4) * D * 4));
-  const int64_t p16 = round16(int64_t(GQ) * lt * 2);
-  const int64_t area = round16(cmax(ngw * GQ * D * 4 + ngw * GQ * 4, int64_t(GQ) * (D + 2) * 4));
-  const int64_t wave = logit + p16 + area;
-  return DecodeLds{block, logit, p16, area, wave, block + kWaves * wave};
-}
 
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s);
+// LDS bytes of a decode workgroup of `waves` waves; -1 if (D, GQ) is unsupported
+// LDS bytes of a decode workgroup of `waves` waves; -1 if (D, GQ) is unsupported
+int64_t decode_lds_bytes(int D, int GQ, int waves);
 
 struct QuantParams {
   const uint16_t* src;

@@ -227,9 +227,11 @@ typedef struct kvq_decode_args {
 
 /*
  * Bytes of workspace kvq_decode_attn needs for these arguments (it depends
- * on the shapes, the runs and split_tokens, not on the pointers).  The
- * workspace holds per-split partial softmax states; it needs no
- * initialization and its contents are scratch after the call.
+ * on the shapes, the runs and split_tokens, not on the pointers; 0 when each
+ * stream fits one workgroup, and then workspace may be NULL).  The workspace
+ * holds per-workgroup partial softmax states; it needs no initialization,
+ * its contents are scratch after the call, and calls that share one must
+ * not overlap.
  */
 kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes);
 

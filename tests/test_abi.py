@@ -105,9 +105,11 @@ def _decode(**kw):
 
 def test_workspace_size_follows_the_split_plan():
     a = _decode()
-    # cells: [0,200) K run + V run, [200,256) K run + V residual, [256,259) residual
-    # splits of 64: 4 + 1 + 1 = 6; workspace = streams*splits*gq*(d+2)*4
-    assert kvq.kvq_decode_attn_workspace(a) == 2 * 2 * 6 * 4 * 130 * 4
+    # N = 256 + 3 = 259 tokens, 64 per workgroup: 5 workgroups per stream;
+    # workspace = partial states, streams * workgroups * gq * (d + 2) floats
+    assert kvq.kvq_decode_attn_workspace(a) == 2 * 2 * 5 * 4 * 130 * 4
+    # one workgroup per stream writes the output directly: no workspace
+    assert kvq.kvq_decode_attn_workspace(_decode(split_tokens=512)) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -117,7 +119,11 @@ def test_workspace_size_follows_the_split_plan():
     (dict(v_segs=[(2, 5, 200, 0, 0)]), EINVAL), (dict(q=A + 2), EALIGN),
     (dict(k_codes_stride=100), EALIGN), (dict(k_res_stride=12), EALIGN),
     (dict(sm_scale=float("nan")), EINVAL), (dict(k_codes=None), EINVAL),
-    (dict(split_tokens=1 << 20), EUNSUP), (dict(group=128, d_h=64), EUNSUP),
+    (dict(k_segs=[(2, 0, 2048, 0, 0)], v_segs=[(2, 0, 1992, 0, 0)], split_tokens=1 << 20), EUNSUP),
+    (dict(group=128, d_h=64), EUNSUP),
+    # a quantized key run must start on a group boundary, a quantized value run on a pair
+    (dict(k_segs=[(16, 0, 16, 0, 0), (2, 16, 256, 4096, 0)], v_segs=[(2, 0, 216, 0, 0)]), EUNSUP),
+    (dict(v_segs=[(16, 0, 11, 0, 0), (2, 11, 189, 4096, 0)]), EUNSUP),
 ])
 def test_decode_rejects(kw, code):
     with pytest.raises(KvqError) as e:
