@@ -8,10 +8,13 @@ decode attention runs over [quantized | residual] keys and values.
 
 Timing: the cache is built (prefill, on the GPU) in several independent
 copies whose total exceeds twice the 256 MB Infinity Cache, and each timed
-step uses the next copy, so the reads come from HBM.  One step per copy is
-captured in a HIP graph; W warm-up and then K timed steps are replayed, with
-a synchronize on both sides.  The host integers of every copy are restored
-before each step, so every step does identical work on identical data.
+step uses the next copy, so the reads come from HBM.  A HIP graph holds
+`rounds` passes over the copies, one step per copy per pass (a step repeated
+on a copy rewrites the same rows and reads the same state, so every step does
+identical work on identical data); W warm-up and then K timed steps are
+replayed, with a synchronize on both sides, after about a second of untimed
+replays that lets the clocks settle.  The host integers of every copy are
+restored before each capture.
 
 Prints one JSON line.  `value` is the effective bandwidth of the step
 (algorithmic bytes / step time); `roofline` covers the decode-attention
@@ -103,6 +106,9 @@ def main():
     ap.add_argument("--workload", default="llama2_7b")
     ap.add_argument("--copies", type=int, default=0, help="cache copies (0 = enough for 2x 256 MB)")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--rounds", type=int, default=4, help="passes over the cache copies per graph")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
@@ -179,19 +185,22 @@ def main():
     attn_graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         with torch.cuda.graph(step_graph, stream=stream):
-            for c, o in zip(caches, outs):
-                c.append(k_new, v_new)
-                c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+            for _ in range(args.rounds):
+                restore()
+                for c, o in zip(caches, outs):
+                    c.append(k_new, v_new)
+                    c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
         restore()
         for c in caches:           # attention-only graph on the post-step state
             c.append(k_new, v_new)
         torch.cuda.synchronize()
         with torch.cuda.graph(attn_graph, stream=stream):
-            for c, o in zip(caches, outs):
-                c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+            for _ in range(args.rounds):
+                for c, o in zip(caches, outs):
+                    c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
     restore()
     torch.cuda.synchronize()
-    n_copies = len(caches)
+    n_copies = len(caches) * args.rounds       # steps per graph replay
 
     def timed(graph, steps, warmup):
         reps_w = max(1, -(-warmup // n_copies))
@@ -208,6 +217,12 @@ def main():
         return e0.elapsed_time(e1) / (reps * n_copies), reps * n_copies
 
     with torch.cuda.stream(stream):
+        # let the clocks settle (both graphs, untimed) before either is timed
+        t_settle = time.perf_counter()
+        while time.perf_counter() - t_settle < args.settle_s:
+            step_graph.replay()
+            attn_graph.replay()
+            torch.cuda.synchronize()
         attn_ms, _ = timed(attn_graph, args.steps, args.warmup)
         step_ms, n_steps = timed(step_graph, args.steps, args.warmup)
     t0 = time.perf_counter()
@@ -226,12 +241,12 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "d_h": w.d_h, "context": w.context,
                    "attended_tokens": w.n_tokens, "group": w.group, "residual": w.residual,
-                   "bits": w.bits, "cache_copies": n_copies,
+                   "bits": w.bits, "cache_copies": len(caches), "steps_per_graph": n_copies,
                    "cache_state_nKq_rK_nVq_rV": list(attn_probe),
                    "algorithmic_bytes_step": int(total_b), "algorithmic_bytes_attention": int(attn_b)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel (one kvq_decode_attn call)",
+                     "kernel": "decode_kernel: one kvq_decode_attn call (one workgroup per stream here, so no merge kernel)",
                      "us_per_launch": round(attn_ms * 1e3, 2)},
     }
     if not args.no_cpu_baseline:

@@ -19,6 +19,7 @@ from typing import Optional, Sequence
 __all__ = [
     "KVQ_KEYS", "KVQ_VALUES", "KvqError", "Segment", "DecodeArgs", "library_path",
     "kvq_abi_version", "kvq_strerror", "kvq_quantize_append", "kvq_residual_append",
+    "kvq_decode_append",
     "kvq_reorder_windows", "kvq_decode_attn_workspace", "kvq_decode_attn",
 ]
 
@@ -90,6 +91,9 @@ def _load():
                                         vp, i64, vp, i64, i32, vp]
     lib.kvq_residual_append.restype = i32
     lib.kvq_residual_append.argtypes = [i32, i32, i32, vp, i64, i64, vp, i64, i32, vp]
+    lib.kvq_decode_append.restype = i32
+    lib.kvq_decode_append.argtypes = [i32, i32, i32, i32, vp, i64, vp, i64, vp, i64, i32,
+                                      vp, i64, i32, i32, vp, i64, vp, i64, i32, vp]
     lib.kvq_reorder_windows.restype = i32
     lib.kvq_reorder_windows.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.kvq_decode_attn_workspace.restype = i32
@@ -151,6 +155,17 @@ def kvq_residual_append(n_streams, d_h, n_rows, src, src_stream_stride, src_row_
     _check(_load().kvq_residual_append(
         n_streams, d_h, n_rows, _dev(src), src_stream_stride, src_row_stride, _dev(dst),
         dst_stream_stride, dst_row, _stream(stream)), "kvq_residual_append")
+
+
+def kvq_decode_append(bits, group, n_streams, d_h, k_new, k_new_stride, v_new, v_new_stride,
+                      k_res, k_res_stride, k_row, v_res, v_res_stride, v_row, v_quant_row,
+                      v_codes, v_codes_stride, v_meta, v_meta_stride, v_dst_tok, stream=None):
+    """See include/kvq.h.  Row strides in fp16 elements, code/meta strides in bytes."""
+    _check(_load().kvq_decode_append(
+        bits, group, n_streams, d_h, _dev(k_new), k_new_stride, _dev(v_new), v_new_stride,
+        _dev(k_res), k_res_stride, k_row, _dev(v_res), v_res_stride, v_row, v_quant_row,
+        _dev(v_codes), v_codes_stride, _dev(v_meta), v_meta_stride, v_dst_tok, _stream(stream)),
+        "kvq_decode_append")
 
 
 def kvq_reorder_windows(win_bits, n_windows, window_tokens, group, d_h, perm, segs, n_segs,

@@ -23,8 +23,9 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (KVQ_KEYS, KVQ_VALUES, Segment, kvq_decode_attn, kvq_decode_attn_workspace,
-               kvq_quantize_append, kvq_reorder_windows, kvq_residual_append, make_decode_args)
+from . import (KVQ_KEYS, KVQ_VALUES, Segment, kvq_decode_append, kvq_decode_attn,
+               kvq_decode_attn_workspace, kvq_quantize_append, kvq_reorder_windows,
+               kvq_residual_append, make_decode_args)
 
 __all__ = ["KiviCache", "WindowCache", "arena_bytes"]
 
@@ -117,34 +118,40 @@ class KiviCache:
         self.n_kq, self.r_k, self.n_vq, self.r_v, self.v_start = n_kq, l - n_kq, n_vq, l - n_vq, 0
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
-        """Decode-step append of one token per stream ([B][Hkv][1][d] fp16)."""
+        """Decode-step append of one token per stream ([B][Hkv][1][d] fp16).
+
+        One kvq_decode_append call writes the key residual row and the value
+        window row and quantizes the oldest value beyond R; the rare key flush
+        (every R steps) and window compaction are separate calls.
+        """
         assert self.n_tokens + 1 <= self.capacity
-        n, ss, rs = _streams(k_new)
-        n2, ss2, rs2 = _streams(v_new)
-        # keys: residual append, flush R tokens as whole groups when full
-        kvq_residual_append(n, self.d, 1, k_new, ss, rs, self.k_res, self.k_res.stride(0),
-                            self.r_k, stream)
+        n, ss, _ = _streams(k_new)
+        n2, ss2, _ = _streams(v_new)
+        assert n == n2 == self.n_streams
+        if self.v_start + self.r_v + 1 > self.v_win_rows:
+            kvq_residual_append(n, self.d, self.r_v, self.v_res[:, self.v_start:], self.v_res.stride(0),
+                                self.d, self.v_res, self.v_res.stride(0), 0, stream)
+            self.v_start = 0
+        v_row = self.v_start + self.r_v
+        quant = self.r_v + 1 > self.R            # the window then holds R + 1 values
+        kvq_decode_append(self.bits, self.G, n, self.d, k_new, ss, v_new, ss2,
+                          self.k_res, self.k_res.stride(0), self.r_k,
+                          self.v_res, self.v_res.stride(0), v_row,
+                          self.v_start if quant else -1,
+                          self.v_codes, self.v_codes.stride(0), self.v_meta, self.v_meta.stride(0),
+                          self.n_vq, stream)
         self.r_k += 1
+        self.r_v += 1
+        if quant:
+            self.n_vq += 1
+            self.v_start += 1
+            self.r_v -= 1
+        # keys: flush R tokens as whole groups when the residual is full
         if self.r_k == self.R:
             self._quant(KVQ_KEYS, self.k_res.unsqueeze(1), self.R, self.k_res.stride(0), self.d,
                         self.n_kq, stream)
             self.n_kq += self.R
             self.r_k = 0
-        # values: window append, quantize the oldest tokens beyond R
-        if self.v_start + self.r_v + 1 > self.v_win_rows:
-            kvq_residual_append(n, self.d, self.r_v, self.v_res[:, self.v_start:], self.v_res.stride(0),
-                                self.d, self.v_res, self.v_res.stride(0), 0, stream)
-            self.v_start = 0
-        kvq_residual_append(n, self.d, 1, v_new, ss2, rs2, self.v_res, self.v_res.stride(0),
-                            self.v_start + self.r_v, stream)
-        self.r_v += 1
-        if self.r_v > self.R:
-            over = self.r_v - self.R
-            self._quant(KVQ_VALUES, self.v_res[:, self.v_start:].unsqueeze(1), over,
-                        self.v_res.stride(0), self.d, self.n_vq, stream)
-            self.n_vq += over
-            self.v_start += over
-            self.r_v = self.R
 
     def decode_args(self, q: torch.Tensor, out: torch.Tensor, sm_scale: float,
                     split_tokens: int = 0):

@@ -89,18 +89,20 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   while (GQ < gq) GQ *= 2;
   if (kvq::decode_lds_bytes(D, GQ, 4) < 0) return KVQ_EUNSUPPORTED;
   const int64_t streams = int64_t(a->batch) * a->n_kv_heads;
-  // Each stream's N tokens are cut into 4 * n_wg wave ranges of about equal
-  // length, four waves per workgroup.  The automatic choice aims at
-  // wave_tokens(GQ) tokens per wave and shortens the ranges while the grid
-  // would leave most of the GPU idle; split_tokens > 0 asks for workgroups of
-  // that many tokens.
-  const int WT = kvq::wave_tokens(GQ);
+  // Each stream's N tokens are cut into kWaves * n_wg wave ranges of about
+  // equal length, kWaves waves per workgroup.  The automatic choice aims at
+  // wave_tokens(GQ) tokens per wave (one workgroup per stream when that
+  // covers it: no partial states, no merge kernel) and shortens the ranges
+  // while the grid has fewer than two workgroups per CU; split_tokens > 0
+  // asks for workgroups of that many tokens.
+  const int64_t wg_tok = int64_t(kvq::kWaves) * kvq::wave_tokens(GQ);
   int64_t n_wg;
   if (a->split_tokens > 0) {
     n_wg = (N + a->split_tokens - 1) / a->split_tokens;
   } else {
-    n_wg = std::max<int64_t>(1, (N + 2 * WT) / (4 * WT));
-    while (streams * n_wg < 1024 && (N + 8 * n_wg - 1) / (8 * n_wg) >= 64) n_wg *= 2;
+    n_wg = std::max<int64_t>(1, (N + wg_tok / 2) / wg_tok);
+    while (streams * n_wg < 512 && (N + 2 * kvq::kWaves * n_wg - 1) / (2 * kvq::kWaves * n_wg) >= 64)
+      n_wg *= 2;
   }
   const int nw = kvq::kWaves;
   const int64_t nws = nw * n_wg;
@@ -236,6 +238,56 @@ kvq_status kvq_residual_append(int32_t n_streams, int32_t d_h, int32_t n_rows, c
                                         src_row_stride, nullptr, static_cast<uint8_t*>(dst),
                                         dst_stream_stride * 2, dst_row, n_streams, d_h, n_rows,
                                         static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_append(int32_t bits, int32_t group, int32_t n_streams, int32_t d_h,
+                             const void* k_new, int64_t k_new_stride,
+                             const void* v_new, int64_t v_new_stride,
+                             void* k_res, int64_t k_res_stride, int32_t k_row,
+                             void* v_res, int64_t v_res_stride, int32_t v_row,
+                             int32_t v_quant_row,
+                             void* v_codes, int64_t v_codes_stride,
+                             void* v_meta, int64_t v_meta_stride, int32_t v_dst_tok,
+                             void* stream) {
+  if (bits != 2 && bits != 4 && bits != 8) return KVQ_EINVAL;
+  if (!valid_group(group) || !valid_d(d_h) || group > d_h) return KVQ_EUNSUPPORTED;
+  if (n_streams < 1 || k_row < 0 || v_row < 0 || v_quant_row < -1) return KVQ_EINVAL;
+  if (n_streams > (1 << 24)) return KVQ_EUNSUPPORTED;
+  if (!k_new || !v_new || !k_res || !v_res) return KVQ_EINVAL;
+  if (k_new_stride < d_h || v_new_stride < d_h || k_res_stride < 0 || v_res_stride < 0)
+    return KVQ_EINVAL;
+  for (const void* ptr : {k_new, v_new, static_cast<const void*>(k_res), static_cast<const void*>(v_res)})
+    if (!aligned16(ptr)) return KVQ_EALIGN;
+  if ((k_new_stride & 7) || (v_new_stride & 7) || (k_res_stride & 7) || (v_res_stride & 7))
+    return KVQ_EALIGN;
+  if (v_quant_row >= 0) {
+    if (!v_codes || !v_meta || v_dst_tok < 0 || v_codes_stride < 0 || v_meta_stride < 0)
+      return KVQ_EINVAL;
+    if (!aligned16(v_codes) || !aligned16(v_meta) || (v_codes_stride & 15) || (v_meta_stride & 15))
+      return KVQ_EALIGN;
+  }
+  kvq::AppendParams p{};
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.k_res = static_cast<uint16_t*>(k_res);
+  p.v_res = static_cast<uint16_t*>(v_res);
+  p.v_codes = static_cast<uint8_t*>(v_codes);
+  p.v_meta = static_cast<uint8_t*>(v_meta);
+  p.k_new_stride = k_new_stride;
+  p.v_new_stride = v_new_stride;
+  p.k_res_stride = k_res_stride;
+  p.v_res_stride = v_res_stride;
+  p.v_codes_stride = v_codes_stride;
+  p.v_meta_stride = v_meta_stride;
+  p.bits = bits;
+  p.G = group;
+  p.D = d_h;
+  p.n_streams = n_streams;
+  p.k_row = k_row;
+  p.v_row = v_row;
+  p.v_quant_row = v_quant_row;
+  p.v_dst_tok = v_dst_tok;
+  return from_hip(kvq::launch_decode_append(p, static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_reorder_windows(const uint8_t* win_bits, int32_t n_windows, int32_t window_tokens,

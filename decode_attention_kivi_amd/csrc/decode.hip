@@ -4,7 +4,7 @@
 //
 // The N tokens of a cache stream (batch b, kv head h) are cut into
 // waves_per_stream ranges of about equal length (starts at multiples of 32);
-// a workgroup holds four consecutive ranges of one stream and the GQ query
+// a workgroup holds eight consecutive ranges of one stream and the GQ query
 // heads that share it.  A wave's range may cross run boundaries: it walks the
 // key pieces (quantized runs, fp16 runs, the fp16 residual) and then the value
 // pieces in token order.  Per wave:
@@ -21,9 +21,11 @@
 //      of two tokens, so v_dot2 applies both tokens' p*s at once; sum(p*s) and
 //      sum(p*z) of a lane are kept apart and folded in after the cross-lane
 //      reduction;
-//   4. the four waves' (max, sum, o[d]) are combined into the workgroup's
-//      partial state; a second kernel merges a stream's partials.
-// Logits are kept in base 2 (q is pre-scaled by sm_scale * log2 e).
+//   4. the eight waves' (max, sum, o[d]) are combined: into the output when
+//      one workgroup covers the stream, otherwise into the workgroup's
+//      partial state, which a second kernel merges with the stream's others.
+// Logits stay raw q'.k (q' = q * 2^-8, exact) until the softmax scales them
+// by sm_scale * log2(e) * 2^8 into base-2 logits.
 
 #include "kvq_internal.h"
 #include "kvq_device.h"
@@ -41,59 +43,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
-__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
-
-// v + rotate_right(v, s) within each row of 16 lanes.
-template <int S>
-__device__ __forceinline__ float row_ror_add(float v) {
-  return v + __builtin_amdgcn_update_dpp(0.f, v, 0x120 + S, 0xF, 0xF, false);
-}
-
-// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16) with
-// DPP: quad permutations, then half-row and row mirrors.  Every lane of a
-// group ends with the group's sum.
-template <int N>
-__device__ __forceinline__ float group_sum(float x) {
-  if (N >= 2) x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
-  if (N >= 4) x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
-  if (N >= 8) x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // half mirror
-  if (N >= 16) x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false); // mirror
-  return x;
-}
-
-template <int N>
-__device__ __forceinline__ float group_max(float x) {
-  if (N >= 2) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
-  if (N >= 4) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
-  if (N >= 8) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
-  if (N >= 16) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
-  return x;
-}
-
-// For x uniform within each row of 16 lanes: the sum over row pairs (0,1) and
-// (2,3) [ROWS == 2] or over all four rows [ROWS == 4], in every lane.
-template <int ROWS>
-__device__ __forceinline__ float xrow_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
-  x = bitsf(a[0]) + bitsf(a[1]);
-  if (ROWS == 4) {
-    const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
-    x = bitsf(b[0]) + bitsf(b[1]);
-  }
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum64(float x) { return xrow_sum<4>(group_sum<16>(x)); }
-
-__device__ __forceinline__ float wave_max64(float x) {
-  x = group_max<16>(x);
-  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
-  x = fmaxf(bitsf(a[0]), bitsf(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
-  return fmaxf(bitsf(b[0]), bitsf(b[1]));
 }
 
 __device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
@@ -171,7 +120,7 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 // from three dot2 and a DPP sum over the chunk; it seeds the accumulator of
 // the lane that owns the chunk, so the row sum adds the whole bias.
 template <int D, int GQ, int BITS>
-__device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qh16,
+__device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
                                int64_t stream, const Run& run, int r0, int r1, int slot0,
                                int lane) {
   using KG = KeyGeo<D, GQ, BITS>;
@@ -200,13 +149,10 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
   const int clo = (pi / NP) * CPW + kq, chi = clo + NP;
   const int qpos = (pi / PPL) * QSTR + pi % PPL;       // LDS dword of the pair's hi in its chunk
   const uint32_t meta_off = uint32_t((gsub * D + clo) * 4);
-  half2_t qk[GQ];
-#pragma unroll
-  for (int h = 0; h < GQ; ++h)
-    qk[h] = as_h2(uint32_t(qh16[h * D + clo]) | (uint32_t(qh16[h * D + chi]) << 16)) *
-            as_h2(0x1C001C00u);                                   // * 2^-8, exact
   const _Float16 off = static_cast<_Float16>(Unpack<BITS>::offset(kq));
   const half2_t nego = {-off, -off};
+
+  half2_t qk[GQ];
 
   // Software pipeline over load batches: the loads of batch b+1 are in
   // flight while batch b is consumed.  A batch past the end is still issued:
@@ -301,6 +247,13 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
 
   Batch A, Bb;
   issue(A, 0);
+  // q of the lane's meta pair for the GQ heads (global, cached), loaded while
+  // the first batch is in flight; padded heads are zero
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const uint32_t q2 = h < P.gq ? uint32_t(qg[h * D + clo]) | (uint32_t(qg[h * D + chi]) << 16) : 0u;
+    qk[h] = as_h2(q2) * as_h2(0x1C001C00u);                       // * 2^-8, exact
+  }
   for (int i0 = 0; i0 < n_items; i0 += 2 * NB) {
     issue(Bb, i0 + NB);
     consume(A, i0);
@@ -312,7 +265,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
 // Keys from fp16 rows rows[0..n) -> raw logits q'.k at slots slot0 + i
 // (whole items are written, as above).
 template <int D, int GQ>
-__device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qh16,
+__device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
                           const uint16_t* rows, int n, int slot0, int lane) {
   constexpr int LT = wave_slots(GQ);
   constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -324,7 +277,7 @@ __device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_
   uint32_t qq[GQ][4];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    const uint4 x = reinterpret_cast<const uint4*>(qh16 + h * D)[my_c];
+    const uint4 x = h < P.gq ? reinterpret_cast<const uint4*>(qg + h * D)[my_c] : make_uint4(0, 0, 0, 0);
     const half2_t s8 = as_h2(0x1C001C00u);                        // * 2^-8, exact
     qq[h][0] = as_u32(as_h2(x.x) * s8);
     qq[h][1] = as_u32(as_h2(x.y) * s8);
@@ -381,12 +334,15 @@ __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], in
 
 // Values of run tokens [r0, r1) (bits 2/4/8).  Pair block p of the run holds
 // run tokens 2p and 2p+1, whose probabilities are fp16 pair p - r0/2 of W.p16
-// counted from dword ps0 (r0 is even).  The partner after an odd run's last
-// token has probability zero (the caller clears its slot) and finite meta;
-// pair blocks past the range read zero codes and zero meta, so they add 0.
-template <int D, int GQ, int BITS>
+// counted from dword ps0 (r0 is even).  Slot ph >= 0 (the partner after an
+// odd run's last token, a token of the next piece) reads as zero while the
+// run is read; the partner's meta is finite.  Pair blocks past the range read
+// zero codes and zero meta, so they add 0.  Unless softmax_done, `softmax`
+// runs after the first loads are issued (it writes W.p16).
+template <int D, int GQ, int BITS, class Softmax>
 __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_t stream,
-                                 const Run& run, int r0, int r1, int ps0, int lane) {
+                                 const Run& run, int r0, int r1, int ps0, int lane,
+                                 Softmax& softmax, bool softmax_done, int ph) {
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = D * BITS / 8;
   constexpr int CPP = 2 * RB / 16;        // 16-byte chunks per pair block
@@ -410,6 +366,7 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
   const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16) + ps0;
   const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
 
+  uint16_t keep[GQ];
   for (int hp = 0; hp < GQ; hp += HPP) {
     float acc[HPP][NX];                   // [CPCV] channel sums, then sum(p*s), sum(p*z)
 #pragma unroll
@@ -461,6 +418,20 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
     };
     Batch A, Bb;
     issue(A, 0);
+    if (hp == 0) {
+      // the probabilities are made while the first loads are in flight
+      if (!softmax_done) softmax();
+      if (ph >= 0) {
+        // (uniform) clear the partner slot after an odd run end for this run
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+          keep[h] = W.p16[h * LT + ph];
+          wave_lds_sync();
+          if (lane == 0) W.p16[h * LT + ph] = 0;
+        }
+        wave_lds_sync();
+      }
+    }
     for (int i0 = 0; i0 < n_inst; i0 += 2 * NBV) {
       issue(Bb, i0 + NBV);
       consume(A, i0);
@@ -487,6 +458,12 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
       }
       wave_lds_sync();
     }
+  }
+  if (ph >= 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+      if (lane == 0) W.p16[h * LT + ph] = keep[h];
+    wave_lds_sync();
   }
 }
 
@@ -557,8 +534,9 @@ __device__ __forceinline__ int wave_bound(int w, int N, int NW) {
 
 // ---------------------------------------------------------------------------
 // Four waves per SIMD (<= 128 VGPRs) for one query head per kv head: 16
-// resident waves per CU keep enough loads in flight to cover HBM latency.
-// Grouped heads do GQ times the arithmetic per byte and get 256 VGPRs.
+// resident waves per CU (two workgroups) keep enough loads in flight to
+// cover HBM latency.  Grouped heads do GQ times the arithmetic per byte and
+// get 256 VGPRs (one workgroup per CU).
 template <int D, int GQ, int NW>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQ == 1 ? 4 : 2)))
 decode_kernel(const DecodeParams P) {
@@ -578,13 +556,7 @@ decode_kernel(const DecodeParams P) {
   const int e = wave_bound(gw + 1, N, P.waves_per_stream);
   const int n = e - a;
 
-  uint16_t* qh16 = reinterpret_cast<uint16_t*>(smem);
-  const int64_t qrow = (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;
-  for (int i = tid; i < GQ * D; i += NW * 64) {
-    const int h = i / D;
-    qh16[i] = h < P.gq ? P.q[qrow + i] : uint16_t(0);
-  }
-  __syncthreads();
+  const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;   // [gq][D]
 
   const WaveLds W = carve_wave<D, GQ>(smem, wave);
   // token t of the wave sits at slot t - a; a is even and quantized value
@@ -597,11 +569,11 @@ decode_kernel(const DecodeParams P) {
       if (t0 >= t1) continue;
       const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
       switch (run.bits) {
-        case 2: keys_quantized<D, GQ, 2>(P, W, qh16, stream, run, r0, r1, t0 - a, lane); break;
-        case 4: keys_quantized<D, GQ, 4>(P, W, qh16, stream, run, r0, r1, t0 - a, lane); break;
-        case 8: keys_quantized<D, GQ, 8>(P, W, qh16, stream, run, r0, r1, t0 - a, lane); break;
+        case 2: keys_quantized<D, GQ, 2>(P, W, qg, stream, run, r0, r1, t0 - a, lane); break;
+        case 4: keys_quantized<D, GQ, 4>(P, W, qg, stream, run, r0, r1, t0 - a, lane); break;
+        case 8: keys_quantized<D, GQ, 8>(P, W, qg, stream, run, r0, r1, t0 - a, lane); break;
         default:
-          keys_fp16<D, GQ>(P, W, qh16,
+          keys_fp16<D, GQ>(P, W, qg,
                            reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off) +
                                int64_t(r0) * D,
                            r1 - r0, t0 - a, lane);
@@ -609,46 +581,52 @@ decode_kernel(const DecodeParams P) {
     }
     if (e > P.n_kq) {
       const int t0 = max(a, P.n_kq);
-      keys_fp16<D, GQ>(P, W, qh16, P.k_res + stream * P.k_res_stride + int64_t(t0 - P.n_kq) * D, e - t0,
+      keys_fp16<D, GQ>(P, W, qg, P.k_res + stream * P.k_res_stride + int64_t(t0 - P.n_kq) * D, e - t0,
                        t0 - a, lane);
     }
     wave_lds_sync();
   }
 
   // softmax state of this wave's range, per head: raw logits x = q'.k, base-2
-  // logits x * sc; every slot of p16 is written, zero outside the tokens
+  // logits x * sc; every slot of p16 is written, zero outside the tokens.
+  // It runs once, after the first value piece has issued its first loads
+  // (or before any other value piece, or on its own for an empty range).
   float mh[GQ], lh[GQ];
-  const float sc = P.scale_log2 * 256.f;        // undoes q' = q * 2^-8
+  bool softmax_done = false;
+  auto softmax = [&]() {
+    const float sc = P.scale_log2 * 256.f;      // undoes q' = q * 2^-8
 #pragma unroll
-  for (int h = 0; h < GQ; ++h) {
-    float mx = -INFINITY;
-    for (int s = lane * 4; s < n; s += 256) {
-      const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
-      mx = fmaxf(mx, x.x * sc);
-      if (s + 1 < n) mx = fmaxf(mx, x.y * sc);
-      if (s + 2 < n) mx = fmaxf(mx, x.z * sc);
-      if (s + 3 < n) mx = fmaxf(mx, x.w * sc);
-    }
-    mx = wave_max64(mx);
-    const float nm = -mx;
-    float sum = 0.f;
-#pragma unroll
-    for (int s = lane * 4; s < LT; s += 256) {
-      const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
-      const float xs[4] = {x.x, x.y, x.z, x.w};
-      uint32_t p16[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        p16[k] = s + k < n ? f2h(exp2f(__builtin_fmaf(xs[k], sc, nm))) : 0u;
-        sum += h2f(p16[k]);             // the same rounded values the A.V uses
+    for (int h = 0; h < GQ; ++h) {
+      float mx = -INFINITY;
+      for (int s = lane * 4; s < n; s += 256) {
+        const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
+        mx = fmaxf(mx, x.x * sc);
+        if (s + 1 < n) mx = fmaxf(mx, x.y * sc);
+        if (s + 2 < n) mx = fmaxf(mx, x.z * sc);
+        if (s + 3 < n) mx = fmaxf(mx, x.w * sc);
       }
-      *reinterpret_cast<uint2*>(W.p16 + h * LT + s) =
-          make_uint2(p16[0] | (p16[1] << 16), p16[2] | (p16[3] << 16));
+      mx = wave_max64(mx);
+      const float nm = -mx;
+      float sum = 0.f;
+#pragma unroll
+      for (int s = lane * 4; s < LT; s += 256) {
+        const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+        uint32_t p16[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          p16[k] = s + k < n ? f2h(exp2f(__builtin_fmaf(xs[k], sc, nm))) : 0u;
+          sum += h2f(p16[k]);           // the same rounded values the A.V uses
+        }
+        *reinterpret_cast<uint2*>(W.p16 + h * LT + s) =
+            make_uint2(p16[0] | (p16[1] << 16), p16[2] | (p16[3] << 16));
+      }
+      mh[h] = mx;
+      lh[h] = wave_sum64(sum);
     }
-    mh[h] = mx;
-    lh[h] = wave_sum64(sum);
-  }
-  wave_lds_sync();
+    wave_lds_sync();
+    softmax_done = true;
+  };
 
   // the wave's output o[D] per head accumulates in its (m, l, o) block, which
   // the value pieces add into (lane l owns channels l + 64k)
@@ -666,41 +644,27 @@ decode_kernel(const DecodeParams P) {
       const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
       // the pair partner after an odd run's last token belongs to the next
       // piece: its probability is zero while this run is read
-      const int ph = (run.bits != 16 && (r1 & 1) && t1 < e) ? t1 - a : -1;
-      uint16_t keep[GQ];
-      if (ph >= 0) {
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-          keep[h] = W.p16[h * LT + ph];
-          wave_lds_sync();
-          if (lane == 0) W.p16[h * LT + ph] = 0;
-        }
-        wave_lds_sync();
-      }
+      const int ph = ((r1 & 1) && t1 < e) ? t1 - a : -1;
       switch (run.bits) {
-        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane); break;
-        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane); break;
-        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane); break;
+        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph); break;
+        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph); break;
+        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph); break;
         default:
+          if (!softmax_done) softmax();
           values_fp16<D, GQ>(P, W,
                              reinterpret_cast<const uint16_t*>(P.v_codes + stream * P.v_codes_stride + run.code_off) +
                                  int64_t(r0) * D,
                              r1 - r0, t0 - a, lane);
       }
-      if (ph >= 0) {
-        wave_lds_sync();
-#pragma unroll
-        for (int h = 0; h < GQ; ++h)
-          if (lane == 0) W.p16[h * LT + ph] = keep[h];
-        wave_lds_sync();
-      }
     }
     if (e > P.n_vq) {
+      if (!softmax_done) softmax();
       const int t0 = max(a, P.n_vq);
       values_fp16<D, GQ>(P, W, P.v_res + stream * P.v_res_stride + int64_t(t0 - P.n_vq) * D, e - t0,
                          t0 - a, lane);
     }
   }
+  if (!softmax_done) softmax();
   // the wave's state (an empty wave has m = -inf, l = 0, o = 0)
   if (lane == 0) {
 #pragma unroll
@@ -711,7 +675,7 @@ decode_kernel(const DecodeParams P) {
   }
   __syncthreads();
 
-  // combine the four waves; with one workgroup per stream that is the output
+  // combine the waves; with one workgroup per stream that is the output
   // (and there is no merge kernel)
   const int gq = P.gq;
   const int64_t step = int64_t(gq) * (D + 2);

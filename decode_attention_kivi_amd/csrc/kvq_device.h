@@ -90,15 +90,108 @@ template <> struct Unpack<8> {
   __device__ static __forceinline__ float offset(int) { return 1024.f; }
 };
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+// ---------------------------------------------------------------------------
+// Cross-lane reductions of a wave64 (DPP within rows of 16 lanes, permlane
+// swaps across rows; no LDS).
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// v + rotate_right(v, s) within each row of 16 lanes.
+template <int S>
+__device__ __forceinline__ float row_ror_add(float v) {
+  return v + __builtin_amdgcn_update_dpp(0.f, v, 0x120 + S, 0xF, 0xF, false);
+}
+
+// Sum over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16) with
+// DPP: quad permutations, then half-row and row mirrors.  Every lane of a
+// group ends with the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if (N >= 2) x += __builtin_amdgcn_update_dpp(0.f, x, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+  if (N >= 4) x += __builtin_amdgcn_update_dpp(0.f, x, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+  if (N >= 8) x += __builtin_amdgcn_update_dpp(0.f, x, 0x141, 0xF, 0xF, false);  // half mirror
+  if (N >= 16) x += __builtin_amdgcn_update_dpp(0.f, x, 0x140, 0xF, 0xF, false); // mirror
   return x;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  if (N >= 2) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+  if (N >= 4) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+  if (N >= 8) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+  if (N >= 16) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// For x uniform within each row of 16 lanes: the sum over row pairs (0,1) and
+// (2,3) [ROWS == 2] or over all four rows [ROWS == 4], in every lane.
+template <int ROWS>
+__device__ __forceinline__ float xrow_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+  x = bitsf(a[0]) + bitsf(a[1]);
+  if (ROWS == 4) {
+    const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+    x = bitsf(b[0]) + bitsf(b[1]);
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum64(float x) { return xrow_sum<4>(group_sum<16>(x)); }
+
+__device__ __forceinline__ float wave_max64(float x) {
+  x = group_max<16>(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+  x = fmaxf(bitsf(a[0]), bitsf(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+  return fmaxf(bitsf(b[0]), bitsf(b[1]));
+}
+
+
+// Bitwise OR over aligned groups of N consecutive lanes (N = 1, 2, 4, 8, 16).
+template <int N>
+__device__ __forceinline__ uint32_t group_or(uint32_t x) {
+  if (N >= 2) x |= __builtin_amdgcn_update_dpp(0u, x, 0xB1, 0xF, 0xF, false);
+  if (N >= 4) x |= __builtin_amdgcn_update_dpp(0u, x, 0x4E, 0xF, 0xF, false);
+  if (N >= 8) x |= __builtin_amdgcn_update_dpp(0u, x, 0x141, 0xF, 0xF, false);
+  if (N >= 16) x |= __builtin_amdgcn_update_dpp(0u, x, 0x140, 0xF, 0xF, false);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_min(float x) {
+  if (N >= 2) x = fminf(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+  if (N >= 4) x = fminf(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+  if (N >= 8) x = fminf(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+  if (N >= 16) x = fminf(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// min / max over aligned groups of N lanes, N = 16, 32 or 64 (every lane of
+// a group gets the group's value).
+template <int N>
+__device__ __forceinline__ float span_min(float x) {
+  x = group_min<16>(x);
+  if (N >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+    x = fminf(bitsf(a[0]), bitsf(a[1]));
+  }
+  if (N >= 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+    x = fminf(bitsf(b[0]), bitsf(b[1]));
+  }
+  return x;
+}
+template <int N>
+__device__ __forceinline__ float span_max(float x) {
+  x = group_max<16>(x);
+  if (N >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+    x = fmaxf(bitsf(a[0]), bitsf(a[1]));
+  }
+  if (N >= 64) {
+    const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+    x = fmaxf(bitsf(b[0]), bitsf(b[1]));
+  }
   return x;
 }
 

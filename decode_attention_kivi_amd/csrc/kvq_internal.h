@@ -9,14 +9,14 @@
 namespace kvq {
 
 constexpr int kThreads = 256;          // threads per decode / quantize workgroup
-constexpr int kWaves = 4;              // waves per decode workgroup
+constexpr int kWaves = 8;              // waves per decode workgroup
 constexpr int kMaxRuns = 8;            // runs per half of the cache
 constexpr int kLdsLimit = 160 * 1024;  // LDS of one gfx950 CU: the most a workgroup can use
 constexpr int kWaveAlign = 32;         // wave token ranges start at multiples of this
 
 // Target tokens per wave; a wave may get up to wave_cap(GQ) tokens.  Larger
-// GQ needs more LDS per token.
-__host__ __device__ constexpr int wave_tokens(int GQ) { return GQ <= 1 ? 256 : GQ == 2 ? 128 : GQ == 4 ? 64 : 32; }
+// GQ needs more LDS per token (logits and probabilities of GQ heads).
+__host__ __device__ constexpr int wave_tokens(int GQ) { return 512 / GQ; }
 __host__ __device__ constexpr int wave_cap(int GQ) { return wave_tokens(GQ) * 3 / 2 + kWaveAlign; }
 // token slots per wave in LDS: the cap plus 32, since the streaming loops
 // read and write whole items (up to 32 tokens) past a range's last token
@@ -68,7 +68,7 @@ __host__ __device__ constexpr int64_t kBiasMax() {
 }
 
 // Per-wave LDS of a decode workgroup (the device uses the same numbers).
-// Block part: q of the GQ heads as fp16.  Per
+// Block part: none (q is read from global memory by each wave).  Per
 // wave, with LT = wave_slots(GQ):
 //   logit  fp32 [GQ][LT]  logits by token slot; reused afterwards for the
 //                          row sums of the value reduction (at most 640 floats)
@@ -84,7 +84,7 @@ __host__ __device__ constexpr int64_t lds_bytes(const DecodeLds& l, int waves) {
 template <int D, int GQ>
 __host__ __device__ constexpr DecodeLds decode_lds() {
   const int64_t lt = wave_slots(GQ);
-  const int64_t block = round16(int64_t(GQ) * D * 2);
+  const int64_t block = 0;
   const int64_t logit = round16(cmax(int64_t(GQ) * lt * 4, 640 * 4));
   const int64_t p16 = round16(int64_t(GQ) * lt * 2);
   // q*s blocks of the widest layout, then the per-chunk biases (see carve_wave)
@@ -139,8 +139,22 @@ struct QuantParams {
   int32_t bits, G, D, n_streams, n_tok, dst_tok;
 };
 
+struct AppendParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_res;
+  uint16_t* v_res;
+  uint8_t* v_codes;
+  uint8_t* v_meta;
+  int64_t k_new_stride, v_new_stride, k_res_stride, v_res_stride;   // fp16 elements
+  int64_t v_codes_stride, v_meta_stride;                            // bytes
+  int32_t bits, G, D, n_streams;
+  int32_t k_row, v_row, v_quant_row, v_dst_tok;
+};
+
 hipError_t launch_quantize_keys(const QuantParams& p, hipStream_t s);
 hipError_t launch_quantize_values(const QuantParams& p, hipStream_t s);
+hipError_t launch_decode_append(const AppendParams& p, hipStream_t s);
 
 // fp16 row copy: dst row (dst_row0 + i) of stream s at byte
 // s*dst_stream_bytes + (dst_row0+i)*D*2, source row (rows ? rows[i] : i).

@@ -87,20 +87,16 @@ __global__ void __launch_bounds__(128) quantize_keys_kernel(QuantParams p) {
   }
 }
 
-// Values: thread = one group (G channels) of one token of one stream.  The
-// codes go to the token's 16-bit halves of its pair block.
+// Values: one group (G channels at x) of the token with index te of a value
+// run.  The codes go to the token's 16-bit halves of its pair block in
+// `codes` (the run's arena of this stream), the (scale, zero) pair to `meta`.
+// `last`: the token is the last one appended; at an even index its pair
+// partner is not written yet, so the partner's halves and (scale, zero) are
+// zeroed and decode reads finite values (the next append overwrites them).
 template <int BITS>
-__global__ void __launch_bounds__(256) quantize_values_kernel(QuantParams p, int NG) {
-  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = int64_t(p.n_streams) * p.n_tok * NG;
-  if (item >= total) return;
-  const int g = int(item % NG);
-  const int64_t rest = item / NG;
-  const int i = int(rest % p.n_tok);
-  const int64_t s = rest / p.n_tok;
-  const int G = p.G;
-  const int64_t row = p.src_rows ? p.src_rows[i] : i;
-  const uint16_t* x = p.src + s * p.src_stream_stride + row * p.src_row_stride + int64_t(g) * G;
+__device__ __forceinline__ void quantize_value_group(const uint16_t* x, int G, int g, int NG, int D,
+                                                     int64_t te, bool last, uint8_t* codes,
+                                                     uint32_t* meta) {
   // the group's G fp16 values stay in registers (G <= 128: 16 loads of 16 B)
   uint32_t xw[64];
   float mn = INFINITY, mx = -INFINITY;
@@ -117,11 +113,10 @@ __global__ void __launch_bounds__(256) quantize_values_kernel(QuantParams p, int
     }
   }
   const GroupScale gs = group_scale<BITS>(mn, mx);
-  const int te = p.dst_tok + i;
   const int64_t pair = te >> 1;
-  const int par = te & 1;
-  const int64_t rb = int64_t(p.D) * BITS / 8;
-  uint8_t* blk = p.codes + s * p.codes_stream_stride + pair * 2 * rb;
+  const int par = int(te & 1);
+  const int64_t rb = int64_t(D) * BITS / 8;
+  uint8_t* blk = codes + pair * 2 * rb;
   constexpr int kPerUnit = 16 / BITS;   // codes per 16-bit unit
   const int units = G / kPerUnit;
   const int u0 = g * units;
@@ -137,15 +132,96 @@ __global__ void __launch_bounds__(256) quantize_values_kernel(QuantParams p, int
     }
     *reinterpret_cast<uint16_t*>(blk + 4 * (u0 + u) + 2 * par) = static_cast<uint16_t>(unit);
   }
-  uint32_t* meta = reinterpret_cast<uint32_t*>(p.meta + s * p.meta_stream_stride);
   meta[(pair * NG + g) * 2 + par] = gs.s16 | (gs.z16 << 16);
-  // the last appended token at an even index leaves its pair partner unwritten:
-  // zero the partner's halves and (scale, zero) so decode reads finite values
-  // (the next append overwrites them)
-  if (par == 0 && i == p.n_tok - 1) {
+  if (par == 0 && last) {
     for (int u = 0; u < units; ++u)
       *reinterpret_cast<uint16_t*>(blk + 4 * (u0 + u) + 2) = 0;
     meta[(pair * NG + g) * 2 + 1] = 0u;
+  }
+}
+
+// Values: thread = one group (G channels) of one token of one stream.
+template <int BITS>
+__global__ void __launch_bounds__(256) quantize_values_kernel(QuantParams p, int NG) {
+  const int64_t item = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t total = int64_t(p.n_streams) * p.n_tok * NG;
+  if (item >= total) return;
+  const int g = int(item % NG);
+  const int64_t rest = item / NG;
+  const int i = int(rest % p.n_tok);
+  const int64_t s = rest / p.n_tok;
+  const int64_t row = p.src_rows ? p.src_rows[i] : i;
+  const uint16_t* x = p.src + s * p.src_stream_stride + row * p.src_row_stride + int64_t(g) * p.G;
+  quantize_value_group<BITS>(x, p.G, g, NG, p.D, int64_t(p.dst_tok) + i, i == p.n_tok - 1,
+                             p.codes + s * p.codes_stream_stride,
+                             reinterpret_cast<uint32_t*>(p.meta + s * p.meta_stream_stride));
+}
+
+// One decode step's append (KIVI note, Algorithm 1, Decoding), one launch,
+// one wave per stream: the new key and value rows are copied (16 bytes per
+// lane), and (v_quant_row >= 0) one value-window row is quantized with each
+// lane holding D/64 channels: group min/max by cross-lane reductions, codes
+// from the same group_scale/encode as quantize_value_group, 16-bit units
+// assembled by OR across the lanes of a unit.
+template <int BITS, int D, int G>
+__global__ void __launch_bounds__(256) decode_append_kernel(AppendParams p) {
+  constexpr int CPL = D / 64;            // channels per lane
+  constexpr int LPG = G / CPL;           // lanes per group: 16, 32 or 64
+  constexpr int NG = D / G;
+  constexpr int KPU = 16 / BITS;         // codes per 16-bit unit
+  constexpr int LPU = KPU / CPL;         // lanes per unit
+  const int lane = threadIdx.x & 63;
+  const int64_t s = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (s >= p.n_streams) return;          // uniform per wave
+  if (lane < D / 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p.k_new + s * p.k_new_stride + lane * 8);
+    *reinterpret_cast<uint4*>(p.k_res + s * p.k_res_stride + int64_t(p.k_row) * D + lane * 8) = v;
+  } else if (lane < D / 4) {
+    const int c = lane - D / 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(p.v_new + s * p.v_new_stride + c * 8);
+    *reinterpret_cast<uint4*>(p.v_res + s * p.v_res_stride + int64_t(p.v_row) * D + c * 8) = v;
+  }
+  if (p.v_quant_row < 0) return;
+  // the row being quantized is read where it is complete: the new value
+  // itself if it is the row written in this launch
+  const uint16_t* row = p.v_quant_row == p.v_row
+                            ? p.v_new + s * p.v_new_stride
+                            : p.v_res + s * p.v_res_stride + int64_t(p.v_quant_row) * D;
+  float xv[CPL];
+  if constexpr (CPL == 2) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[lane];
+    xv[0] = h2f(w & 0xffffu);
+    xv[1] = h2f(w >> 16);
+  } else {
+    xv[0] = h2f(row[lane]);
+  }
+  float mn = xv[0], mx = xv[0];
+  if constexpr (CPL == 2) {
+    mn = fminf(mn, xv[1]);
+    mx = fmaxf(mx, xv[1]);
+  }
+  mn = span_min<LPG>(mn);
+  mx = span_max<LPG>(mx);
+  const GroupScale gs = group_scale<BITS>(mn, mx);
+  uint32_t unit = 0;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) unit |= encode<BITS>(xv[k], gs) << (((lane * CPL + k) % KPU) * BITS);
+  unit = group_or<LPU>(unit);
+  const int64_t te = p.v_dst_tok;
+  const int64_t pair = te >> 1;
+  const int par = int(te & 1);
+  constexpr int64_t rb = int64_t(D) * BITS / 8;
+  uint8_t* blk = p.v_codes + s * p.v_codes_stride + pair * 2 * rb;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(p.v_meta + s * p.v_meta_stride);
+  const int uidx = lane * CPL / KPU;     // unit of the row = word of the pair block
+  const int g = lane / LPG;
+  if (lane % LPU == 0) {
+    *reinterpret_cast<uint16_t*>(blk + 4 * uidx + 2 * par) = static_cast<uint16_t>(unit);
+    if (par == 0) *reinterpret_cast<uint16_t*>(blk + 4 * uidx + 2) = 0;   // unwritten partner
+  }
+  if (lane % LPG == 0) {
+    meta[(pair * NG + g) * 2 + par] = gs.s16 | (gs.z16 << 16);
+    if (par == 0) meta[(pair * NG + g) * 2 + 1] = 0u;
   }
 }
 
@@ -190,6 +266,29 @@ hipError_t launch_quantize_values(const QuantParams& p, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_append_dg(const AppendParams& p, hipStream_t s) {
+  const dim3 grid(unsigned((p.n_streams + 3) / 4)), block(256);
+  switch (p.bits) {
+    case 2: hipLaunchKernelGGL((decode_append_kernel<2, D, G>), grid, block, 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_append_kernel<4, D, G>), grid, block, 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_append_kernel<8, D, G>), grid, block, 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const AppendParams& p, hipStream_t s) {
+  switch (p.D * 1000 + p.G) {
+    case 64032: return launch_append_dg<64, 32>(p, s);
+    case 64064: return launch_append_dg<64, 64>(p, s);
+    case 128032: return launch_append_dg<128, 32>(p, s);
+    case 128064: return launch_append_dg<128, 64>(p, s);
+    case 128128: return launch_append_dg<128, 128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_copy_rows(const uint16_t* src, int64_t src_stream_stride,

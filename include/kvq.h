@@ -159,6 +159,36 @@ kvq_status kvq_residual_append(int32_t n_streams, int32_t d_h, int32_t n_rows,
                                void* stream);
 
 /*
+ * kvq_decode_append -- one decode step's cache append in one launch (KIVI
+ * Algorithm 1, Decoding): for every stream, the new key row goes to row
+ * k_row of the key residual, the new value row to row v_row of the value
+ * window, and, when v_quant_row >= 0, value-window row v_quant_row (the new
+ * value row itself if v_quant_row == v_row) is quantized per token and
+ * appended to the value run as token v_dst_tok -- the same bytes as
+ * kvq_quantize_append(KVQ_VALUES, bits, group, ..., n_tok = 1, dst_tok =
+ * v_dst_tok) of that row, including the zeroed pair partner at an even index.
+ * Key-residual flushes (every R steps) stay kvq_quantize_append(KVQ_KEYS).
+ *   bits 2, 4 or 8; group in {32, 64, 128}, group <= d_h; d_h 64 or 128.
+ *   k_new, v_new   fp16 [n_streams] rows, stream s at element s*new_stride.
+ *   k_res, v_res   fp16 residual / window; row i of stream s at element
+ *                  s*res_stride + i*d_h.
+ *   v_codes, v_meta   the value run's first byte (arena + offset) of stream 0;
+ *                  stream s at + s*stride bytes (ignored if v_quant_row < 0).
+ * Strides in fp16 elements are multiples of 8, byte strides and pointers
+ * multiples of 16.  Rows and tokens are not range-checked on the device: they
+ * must address rows inside the caller's buffers.
+ */
+kvq_status kvq_decode_append(int32_t bits, int32_t group, int32_t n_streams, int32_t d_h,
+                             const void* k_new, int64_t k_new_stride,
+                             const void* v_new, int64_t v_new_stride,
+                             void* k_res, int64_t k_res_stride, int32_t k_row,
+                             void* v_res, int64_t v_res_stride, int32_t v_row,
+                             int32_t v_quant_row,
+                             void* v_codes, int64_t v_codes_stride,
+                             void* v_meta, int64_t v_meta_stride, int32_t v_dst_tok,
+                             void* stream);
+
+/*
  * kvq_reorder_windows -- WindowQuant window reorder (Sec. 3.3.1-3.3.2): a
  * stable sort of the windows by bit width, widest first (16, 8, 4, 2; equal
  * widths keep their original order), and the run table of the reordered cache.

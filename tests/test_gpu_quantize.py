@@ -105,3 +105,61 @@ def test_fp16_run_is_a_copy(kvq):
                             64, torch.from_numpy(rows).to(dev), out, out.stride(0), None, 0, 16)
     got = out.cpu().numpy().view(np.float16).reshape(2, 48, 64)
     assert np.array_equal(got[:, 16:], x[:, rows]) and not got[:, :16].view(np.uint16).any()
+
+
+# -- kvq_decode_append: one step's residual/window rows plus one value token ---------
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("d,G", [(64, 32), (128, 32), (128, 64)])
+@pytest.mark.parametrize("dst_tok,quant", [(6, "old"), (7, "old"), (7, "new"), (5, "none")])
+def test_decode_append_bit_exact(kvq, bits, d, G, dst_tok, quant):
+    import torch
+    rng = np.random.default_rng([7, bits, d, G, dst_tok, len(quant)])
+    S, R_rows, K_rows = 3, 6, 4
+    dev = torch.device("cuda")
+    k_new = _data(rng, S, 1, d)[:, 0]
+    v_new = _data(rng, S, 1, d)[:, 0]
+    v_win = _data(rng, S, R_rows, d)
+    k_res0 = _data(rng, S, K_rows, d)
+    # a value run that already holds dst_tok tokens (oracle bytes)
+    old = _data(rng, S, dst_tok, d)
+    k_row, v_row = 2, 4
+    v_quant_row = {"old": 1, "new": v_row, "none": -1}[quant]
+    total = dst_tok + 1
+    cb = ((total + 1) // 2 * d * bits // 4 + 15) // 16 * 16
+    mb = ((total + 1) // 2 * (d // G) * 8 + 15) // 16 * 16
+    codes0 = np.zeros((S, cb), np.uint8)
+    meta0 = np.zeros((S, mb), np.uint8)
+    for s in range(S):
+        c, sc, z = quantize_values(old[s], bits, G)
+        e = pack.pack_values(c, bits).reshape(-1)
+        codes0[s, :e.size] = e
+        m = pack.pack_value_meta(sc, z).view(np.uint8)
+        meta0[s, :m.size] = m
+    kn, vn = torch.from_numpy(k_new).to(dev), torch.from_numpy(v_new).to(dev)
+    kr, vr = torch.from_numpy(k_res0.copy()).to(dev), torch.from_numpy(v_win.copy()).to(dev)
+    codes, meta = torch.from_numpy(codes0).to(dev), torch.from_numpy(meta0).to(dev)
+    print(f"decode_append bits={bits} d={d} G={G} dst={dst_tok} quant={quant}", flush=True)
+    kvq.kvq_decode_append(bits, G, S, d, kn, d, vn, d, kr, K_rows * d, k_row, vr, R_rows * d, v_row,
+                          v_quant_row, codes, cb, meta, mb, dst_tok)
+    torch.cuda.synchronize()
+    exp_k = k_res0.copy()
+    exp_k[:, k_row] = k_new
+    exp_v = v_win.copy()
+    exp_v[:, v_row] = v_new
+    assert np.array_equal(kr.cpu().numpy().view(np.uint16), exp_k.view(np.uint16))
+    assert np.array_equal(vr.cpu().numpy().view(np.uint16), exp_v.view(np.uint16))
+    got_c, got_m = codes.cpu().numpy(), meta.cpu().numpy()
+    for s in range(S):
+        if quant == "none":
+            exp_c, exp_m = codes0[s], meta0[s]
+        else:
+            toks = np.concatenate([old[s], exp_v[s, v_quant_row][None]], axis=0)
+            c, sc, z = quantize_values(toks, bits, G)
+            exp_c = np.zeros(cb, np.uint8)
+            e = pack.pack_values(c, bits).reshape(-1)
+            exp_c[:e.size] = e
+            exp_m = np.zeros(mb, np.uint8)
+            m = pack.pack_value_meta(sc, z).view(np.uint8)
+            exp_m[:m.size] = m
+        assert np.array_equal(got_c[s], exp_c), f"value codes differ (stream {s})"
+        assert np.array_equal(got_m[s], exp_m), f"value scale/zero differ (stream {s})"
