@@ -89,25 +89,70 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   while (GQ < gq) GQ *= 2;
   if (kvq::decode_lds_bytes(D, GQ, 4) < 0) return KVQ_EUNSUPPORTED;
   const int64_t streams = int64_t(a->batch) * a->n_kv_heads;
+  // Cost pieces: maximal token ranges with one key source and one value
+  // source, priced in HBM bytes per token.
+  std::vector<kvq::CostPiece> pieces;
+  {
+    std::vector<int64_t> cuts = {0, N, nk, nv};
+    for (int i = 0; i < a->n_k_segs; ++i) cuts.push_back(a->k_segs[i].tok_begin);
+    for (int i = 0; i < a->n_v_segs; ++i) cuts.push_back(a->v_segs[i].tok_begin);
+    std::sort(cuts.begin(), cuts.end());
+    cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+    auto row_cost = [&](int bits, bool keys) -> int64_t {
+      if (bits == 16) return int64_t(D) * 2;
+      return int64_t(D) * bits / 8 + (keys ? int64_t(D) * 4 / G : int64_t(D / G) * 4);
+    };
+    int64_t c = 0;
+    for (size_t i = 0; i + 1 < cuts.size(); ++i) {
+      const int64_t t0 = cuts[i], t1 = cuts[i + 1];
+      if (t1 <= t0) continue;
+      int kb = 16, vb = 16;
+      for (int k = 0; k < a->n_k_segs; ++k)
+        if (t0 >= a->k_segs[k].tok_begin && t0 < a->k_segs[k].tok_begin + a->k_segs[k].n_tok) kb = a->k_segs[k].bits;
+      for (int k = 0; k < a->n_v_segs; ++k)
+        if (t0 >= a->v_segs[k].tok_begin && t0 < a->v_segs[k].tok_begin + a->v_segs[k].n_tok) vb = a->v_segs[k].bits;
+      const int64_t cost = row_cost(kb, true) + row_cost(vb, false);
+      pieces.push_back(kvq::CostPiece{int32_t(t0), int32_t(cost), c});
+      c += (t1 - t0) * cost;
+    }
+    if (pieces.empty() || pieces.size() > size_t(kvq::kMaxPieces)) return KVQ_EUNSUPPORTED;
+  }
+  const int64_t cost_total = pieces.back().c0 + (N - pieces.back().t0) * pieces.back().cost;
+
   // Each stream's N tokens are cut into kWaves * n_wg wave ranges of about
-  // equal length, kWaves waves per workgroup.  The automatic choice aims at
+  // equal cost, kWaves waves per workgroup.  The automatic choice aims at
   // wave_tokens(GQ) tokens per wave (one workgroup per stream when that
   // covers it: no partial states, no merge kernel) and shortens the ranges
   // while the grid has fewer than two workgroups per CU; split_tokens > 0
-  // asks for workgroups of that many tokens.
+  // asks for workgroups of that many tokens.  A plan whose longest wave range
+  // exceeds wave_cap(GQ) is refused (split_tokens) or refined (automatic).
   const int64_t wg_tok = int64_t(kvq::kWaves) * kvq::wave_tokens(GQ);
+  auto longest = [&](int64_t nws) {
+    int64_t worst = 0;
+    int prev = 0;
+    for (int64_t w = 1; w <= nws; ++w) {
+      const int b = kvq::wave_bound(pieces.data(), int(pieces.size()), cost_total, int(N), int(w), int(nws));
+      worst = std::max<int64_t>(worst, b - prev);
+      prev = b;
+    }
+    return worst;
+  };
   int64_t n_wg;
   if (a->split_tokens > 0) {
     n_wg = (N + a->split_tokens - 1) / a->split_tokens;
+    if (n_wg > (int64_t(1) << 20)) return KVQ_EUNSUPPORTED;
+    if (longest(kvq::kWaves * n_wg) > kvq::wave_cap(GQ)) return KVQ_EUNSUPPORTED;
   } else {
     n_wg = std::max<int64_t>(1, (N + wg_tok / 2) / wg_tok);
     while (streams * n_wg < 512 && (N + 2 * kvq::kWaves * n_wg - 1) / (2 * kvq::kWaves * n_wg) >= 64)
       n_wg *= 2;
+    while (longest(kvq::kWaves * n_wg) > kvq::wave_cap(GQ)) {
+      if (n_wg >= (int64_t(1) << 20)) return KVQ_EUNSUPPORTED;
+      n_wg *= 2;
+    }
   }
   const int nw = kvq::kWaves;
   const int64_t nws = nw * n_wg;
-  if (n_wg > (int64_t(1) << 28)) return KVQ_EUNSUPPORTED;
-  if ((N + nws - 1) / nws + kvq::kWaveAlign - 1 > kvq::wave_cap(GQ)) return KVQ_EUNSUPPORTED;
   if (kvq::decode_lds_bytes(D, GQ, nw) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
 
   Plan& pl = *out;
@@ -142,6 +187,9 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   p.waves_per_wg = nw;
   p.wg_per_stream = int32_t(n_wg);
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  p.n_pieces = int32_t(pieces.size());
+  p.cost_total = cost_total;
+  for (size_t i = 0; i < pieces.size(); ++i) p.pieces[i] = pieces[i];
   p.n_k_runs = a->n_k_segs;
   p.n_v_runs = a->n_v_segs;
   for (int i = 0; i < a->n_k_segs; ++i)

@@ -3,7 +3,7 @@
 // describes) with a cross-split softmax merge.
 //
 // The N tokens of a cache stream (batch b, kv head h) are cut into
-// waves_per_stream ranges of about equal length (starts at multiples of 32);
+// waves_per_stream ranges of about equal HBM bytes (starts at multiples of 32);
 // a workgroup holds eight consecutive ranges of one stream and the GQ query
 // heads that share it.  A wave's range may cross run boundaries: it walks the
 // key pieces (quantized runs, fp16 runs, the fp16 residual) and then the value
@@ -47,6 +47,21 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ __forceinline__ uint32_t as_u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Issue priority from the wave's progress through its range (keys, then
+// values; four levels, a wave that is behind gets a higher one).  The waves
+// of two workgroups share each CU; the issue arbiter otherwise favours the
+// older workgroup, which then finishes far earlier and leaves the younger one
+// to run the tail at half occupancy.
+__device__ __forceinline__ void progress_prio(int phase, int done, int total) {
+  const int level = 3 - 2 * phase - (2 * done >= total ? 1 : 0);
+  switch (level) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
 
 template <int W> struct LoadType;
 template <> struct LoadType<1> { typedef uint32_t T; };
@@ -122,7 +137,7 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 template <int D, int GQ, int BITS>
 __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
                                int64_t stream, const Run& run, int r0, int r1, int slot0,
-                               int lane) {
+                               int lane, int n_wave) {
   using KG = KeyGeo<D, GQ, BITS>;
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = KG::RB, LB = KG::LB, LPR = KG::LPR, TPI = KG::TPI, WPL = KG::WPL;
@@ -149,7 +164,8 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
   const int clo = (pi / NP) * CPW + kq, chi = clo + NP;
   const int qpos = (pi / PPL) * QSTR + pi % PPL;       // LDS dword of the pair's hi in its chunk
   const uint32_t meta_off = uint32_t((gsub * D + clo) * 4);
-  const _Float16 off = static_cast<_Float16>(Unpack<BITS>::offset(kq));
+  const Unpacker<BITS, false> unpack;                 // constants in registers, once
+  const _Float16 off = static_cast<_Float16>(Unpacker<BITS, false>::offset(kq));
   const half2_t nego = {-off, -off};
 
   half2_t qk[GQ];
@@ -229,7 +245,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
 #pragma unroll
       for (int w = 0; w < WPL; ++w) {
         uint32_t v[NP];
-        Unpack<BITS>::run(word<WPL>(B.buf[u], w), v);
+        unpack.run(word<WPL>(B.buf[u], w), v);
 #pragma unroll
         for (int h = 0; h < GQ; ++h)
 #pragma unroll
@@ -255,6 +271,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
     qk[h] = as_h2(q2) * as_h2(0x1C001C00u);                       // * 2^-8, exact
   }
   for (int i0 = 0; i0 < n_items; i0 += 2 * NB) {
+    progress_prio(0, slot0 + i0 * TPI, n_wave);
     issue(Bb, i0 + NB);
     consume(A, i0);
     issue(A, i0 + 2 * NB);
@@ -342,13 +359,15 @@ __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], in
 template <int D, int GQ, int BITS, class Softmax>
 __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_t stream,
                                  const Run& run, int r0, int r1, int ps0, int lane,
-                                 Softmax& softmax, bool softmax_done, int ph) {
+                                 Softmax& softmax, bool softmax_done, int ph, int n_wave) {
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = D * BITS / 8;
   constexpr int CPP = 2 * RB / 16;        // 16-byte chunks per pair block
   constexpr int PPI = 64 / CPP;           // pair blocks per wave instruction
   constexpr int CPCV = 64 / BITS;         // channels per chunk
-  constexpr int NP = Unpack<BITS>::NP;    // channels per 16-bit unit
+  using UP = Unpacker<BITS, true>;        // offsets up to 1024, fewer shifts
+  constexpr int NP = UP::NP;              // channels per 16-bit unit
+  const UP unpack;                        // constants in registers, once
   constexpr int HPP = (GQ * CPCV <= 64) ? GQ : ((64 / CPCV) > 0 ? (64 / CPCV) : 1);
   constexpr int NX = CPCV + 2;
   const int NG = D >> P.lg_g;
@@ -408,7 +427,7 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           uint32_t v[NP];
-          Unpack<BITS>::run(words[w], v);
+          unpack.run(words[w], v);
 #pragma unroll
           for (int hh = 0; hh < HPP; ++hh)
 #pragma unroll
@@ -433,6 +452,7 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
       }
     }
     for (int i0 = 0; i0 < n_inst; i0 += 2 * NBV) {
+      progress_prio(1, 2 * (ps0 + i0 * PPI), n_wave);
       issue(Bb, i0 + NBV);
       consume(A, i0);
       issue(A, i0 + 2 * NBV);
@@ -454,7 +474,7 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
           s += e[CPCV];
           z += e[CPCV + 1];
         }
-        W.ow[(hp + hh) * (D + 2) + 2 + ch] += a - Unpack<BITS>::offset(j % NP) * s + z;
+        W.ow[(hp + hh) * (D + 2) + 2 + ch] += a - UP::offset(j % NP) * s + z;
       }
       wave_lds_sync();
     }
@@ -526,12 +546,6 @@ __device__ void values_fp16(const DecodeParams& P, const WaveLds& W, const uint1
   }
 }
 
-// First token of wave range w of a stream of N tokens cut into NW ranges.
-__device__ __forceinline__ int wave_bound(int w, int N, int NW) {
-  if (w >= NW) return N;
-  return int((int64_t(w) * N / NW) & ~int64_t(kWaveAlign - 1));
-}
-
 // ---------------------------------------------------------------------------
 // Four waves per SIMD (<= 128 VGPRs) for one query head per kv head: 16
 // resident waves per CU (two workgroups) keep enough loads in flight to
@@ -552,8 +566,8 @@ decode_kernel(const DecodeParams P) {
   const int b = int(stream / P.Hkv), hkv = int(stream % P.Hkv);
   const int N = P.n_tok;
   const int gw = wg * NW + wave;
-  const int a = wave_bound(gw, N, P.waves_per_stream);
-  const int e = wave_bound(gw + 1, N, P.waves_per_stream);
+  const int a = wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw, P.waves_per_stream);
+  const int e = wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw + 1, P.waves_per_stream);
   const int n = e - a;
 
   const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;   // [gq][D]
@@ -569,9 +583,9 @@ decode_kernel(const DecodeParams P) {
       if (t0 >= t1) continue;
       const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
       switch (run.bits) {
-        case 2: keys_quantized<D, GQ, 2>(P, W, qg, stream, run, r0, r1, t0 - a, lane); break;
-        case 4: keys_quantized<D, GQ, 4>(P, W, qg, stream, run, r0, r1, t0 - a, lane); break;
-        case 8: keys_quantized<D, GQ, 8>(P, W, qg, stream, run, r0, r1, t0 - a, lane); break;
+        case 2: keys_quantized<D, GQ, 2>(P, W, qg, stream, run, r0, r1, t0 - a, lane, n); break;
+        case 4: keys_quantized<D, GQ, 4>(P, W, qg, stream, run, r0, r1, t0 - a, lane, n); break;
+        case 8: keys_quantized<D, GQ, 8>(P, W, qg, stream, run, r0, r1, t0 - a, lane, n); break;
         default:
           keys_fp16<D, GQ>(P, W, qg,
                            reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off) +
@@ -646,9 +660,9 @@ decode_kernel(const DecodeParams P) {
       // piece: its probability is zero while this run is read
       const int ph = ((r1 & 1) && t1 < e) ? t1 - a : -1;
       switch (run.bits) {
-        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph); break;
-        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph); break;
-        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph); break;
+        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
         default:
           if (!softmax_done) softmax();
           values_fp16<D, GQ>(P, W,

@@ -23,12 +23,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                 __builtin_bit_cast(half2_t, b), c, false);
 }
 
-// (x & mask) | magic in one VALU op (v_and_or_b32).  The gfx9-family VOP3
-// encoding takes no literal constant, so with literal masks the compiler
-// splits this into and + or.  Routing the constants through a trivial
-// (non-volatile, so hoistable) register move makes them opaque register
-// operands, and instruction selection then forms v_and_or_b32 while the
-// scheduler stays free to move the operation.
+// A constant in a scalar / vector register that the compiler cannot fold
+// (non-volatile, so it can still be hoisted and shared).
 __device__ __forceinline__ uint32_t opaque_sgpr(uint32_t c) {
   uint32_t r;
   asm("s_mov_b32 %0, %1" : "=s"(r) : "i"(c));
@@ -39,53 +35,110 @@ __device__ __forceinline__ uint32_t opaque_vgpr(uint32_t c) {
   asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
   return r;
 }
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
-  return (x & opaque_sgpr(mask)) | opaque_vgpr(magic);
-}
 
 // Unpacking one 32-bit word of codes into fp16 pairs without conversions:
 // a b-bit code moved into the fp16 mantissa under a fixed exponent reads as
 // (offset + code).  Pair k of a word combines the code at bit b*k of the low
-// half with the code at bit 16 + b*k of the high half.  The offsets are chosen
-// small (at most 64 for 2- and 4-bit codes) so that the fp32 accumulation of
-// (offset + code) * weight loses little against the later subtraction of
-// offset * sum(weight).
-template <int BITS> struct Unpack;
+// half with the code at bit 16 + b*k of the high half.  Each pair costs one
+// v_and_or_b32 (mask, exponent constant) plus the shifts that bring the codes
+// into the 10 mantissa bits.
+//
+// NARROW layouts keep every offset <= 64 (keys: their fp32 sums include large
+// outlier-channel weights, and offset * sum|weight| must stay small next to
+// the logit); WIDE layouts use offsets up to 1024 and save shifts (values:
+// the rounding of offset * sum(p*s) in fp32 stays far below the tolerance).
+//
+// The masks and exponent constants are materialized once per loop (an
+// Unpacker object built outside it): routed through opaque register moves,
+// they stay in registers, and instruction selection forms v_and_or_b32 (the
+// gfx9-family VOP3 encoding takes no literal constant).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+  return (x & mask) | magic;
+}
 
-template <> struct Unpack<2> {
+template <int BITS, bool WIDE> struct Unpacker;
+
+template <> struct Unpacker<2, false> {
   static constexpr int NP = 8;   // pairs per word
-  __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
+  uint32_t m45, m67, m89, e64, e16, e4;
+  __device__ __forceinline__ Unpacker()
+      : m45(opaque_sgpr(0x00300030u)), m67(opaque_sgpr(0x00C000C0u)), m89(opaque_sgpr(0x03000300u)),
+        e64(opaque_vgpr(0x54005400u)), e16(opaque_vgpr(0x4C004C00u)), e4(opaque_vgpr(0x44004400u)) {}
+  __device__ __forceinline__ void run(uint32_t w, uint32_t* v) const {
     const uint32_t a = w << 4, c = w >> 6;
-    v[0] = and_or(a, 0x00300030u, 0x54005400u);  // mantissa bits 4-5: 64 + code
-    v[1] = and_or(a, 0x00C000C0u, 0x4C004C00u);  // bits 6-7: 16 + code
-    v[2] = and_or(a, 0x03000300u, 0x44004400u);  // bits 8-9: 4 + code
-    v[3] = and_or(w, 0x00C000C0u, 0x4C004C00u);
-    v[4] = and_or(w, 0x03000300u, 0x44004400u);
-    v[5] = and_or(c, 0x00300030u, 0x54005400u);
-    v[6] = and_or(c, 0x00C000C0u, 0x4C004C00u);
-    v[7] = and_or(c, 0x03000300u, 0x44004400u);
+    v[0] = and_or(a, m45, e64);  // mantissa bits 4-5: 64 + code
+    v[1] = and_or(a, m67, e16);  // bits 6-7: 16 + code
+    v[2] = and_or(a, m89, e4);   // bits 8-9: 4 + code
+    v[3] = and_or(w, m67, e16);
+    v[4] = and_or(w, m89, e4);
+    v[5] = and_or(c, m45, e64);
+    v[6] = and_or(c, m67, e16);
+    v[7] = and_or(c, m89, e4);
   }
   __device__ static __forceinline__ float offset(int k) {
     return (k == 0 || k == 5) ? 64.f : ((k == 1 || k == 3 || k == 6) ? 16.f : 4.f);
   }
 };
 
-template <> struct Unpack<4> {
+template <> struct Unpacker<2, true> {
+  static constexpr int NP = 8;
+  uint32_t m01, m23, m45, m67, m89, e1024, e256, e64, e16, e4;
+  __device__ __forceinline__ Unpacker()
+      : m01(opaque_sgpr(0x00030003u)), m23(opaque_sgpr(0x000C000Cu)), m45(opaque_sgpr(0x00300030u)),
+        m67(opaque_sgpr(0x00C000C0u)), m89(opaque_sgpr(0x03000300u)),
+        e1024(opaque_vgpr(0x64006400u)), e256(opaque_vgpr(0x5C005C00u)), e64(opaque_vgpr(0x54005400u)),
+        e16(opaque_vgpr(0x4C004C00u)), e4(opaque_vgpr(0x44004400u)) {}
+  __device__ __forceinline__ void run(uint32_t w, uint32_t* v) const {
+    const uint32_t c = w >> 6;
+    v[0] = and_or(w, m01, e1024);  // mantissa bits 0-1: 1024 + code
+    v[1] = and_or(w, m23, e256);   // bits 2-3: 256 + code
+    v[2] = and_or(w, m45, e64);
+    v[3] = and_or(w, m67, e16);
+    v[4] = and_or(w, m89, e4);
+    v[5] = and_or(c, m45, e64);
+    v[6] = and_or(c, m67, e16);
+    v[7] = and_or(c, m89, e4);
+  }
+  __device__ static __forceinline__ float offset(int k) {
+    return k == 0 ? 1024.f : k == 1 ? 256.f : (k == 2 || k == 5) ? 64.f : (k == 3 || k == 6) ? 16.f : 4.f;
+  }
+};
+
+template <> struct Unpacker<4, false> {
   static constexpr int NP = 4;
-  __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
-    v[0] = and_or(w << 4, 0x00F000F0u, 0x54005400u);  // mantissa bits 4-7: 64 + code
-    v[1] = and_or(w, 0x00F000F0u, 0x54005400u);
-    v[2] = and_or(w >> 4, 0x00F000F0u, 0x54005400u);
-    v[3] = and_or(w >> 8, 0x00F000F0u, 0x54005400u);
+  uint32_t m, e64;
+  __device__ __forceinline__ Unpacker() : m(opaque_sgpr(0x00F000F0u)), e64(opaque_vgpr(0x54005400u)) {}
+  __device__ __forceinline__ void run(uint32_t w, uint32_t* v) const {
+    v[0] = and_or(w << 4, m, e64);   // mantissa bits 4-7: 64 + code
+    v[1] = and_or(w, m, e64);
+    v[2] = and_or(w >> 4, m, e64);
+    v[3] = and_or(w >> 8, m, e64);
   }
   __device__ static __forceinline__ float offset(int) { return 64.f; }
 };
 
-template <> struct Unpack<8> {
+template <> struct Unpacker<4, true> {
+  static constexpr int NP = 4;
+  uint32_t m03, m47, e1024, e64;
+  __device__ __forceinline__ Unpacker()
+      : m03(opaque_sgpr(0x000F000Fu)), m47(opaque_sgpr(0x00F000F0u)),
+        e1024(opaque_vgpr(0x64006400u)), e64(opaque_vgpr(0x54005400u)) {}
+  __device__ __forceinline__ void run(uint32_t w, uint32_t* v) const {
+    v[0] = and_or(w, m03, e1024);        // mantissa bits 0-3: 1024 + code
+    v[1] = and_or(w, m47, e64);          // bits 4-7: 64 + code
+    v[2] = and_or(w >> 4, m47, e64);
+    v[3] = and_or(w >> 12, m03, e1024);
+  }
+  __device__ static __forceinline__ float offset(int k) { return (k == 0 || k == 3) ? 1024.f : 64.f; }
+};
+
+template <bool WIDE> struct Unpacker<8, WIDE> {
   static constexpr int NP = 2;
-  __device__ static __forceinline__ void run(uint32_t w, uint32_t* v) {
-    v[0] = and_or(w, 0x00FF00FFu, 0x64006400u);       // mantissa bits 0-7: 1024 + code
-    v[1] = and_or(w >> 8, 0x00FF00FFu, 0x64006400u);
+  uint32_t m, e1024;
+  __device__ __forceinline__ Unpacker() : m(opaque_sgpr(0x00FF00FFu)), e1024(opaque_vgpr(0x64006400u)) {}
+  __device__ __forceinline__ void run(uint32_t w, uint32_t* v) const {
+    v[0] = and_or(w, m, e1024);          // mantissa bits 0-7: 1024 + code
+    v[1] = and_or(w >> 8, m, e1024);
   }
   __device__ static __forceinline__ float offset(int) { return 1024.f; }
 };

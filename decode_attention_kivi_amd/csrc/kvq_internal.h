@@ -99,6 +99,33 @@ struct Run {            // device copy of kvq_segment
   int64_t code_off, meta_off;
 };
 
+// Token ranges of uniform HBM cost (bytes per token of keys + values, meta
+// included): the cuts of the key and value runs and of the residuals.  Wave
+// ranges are cut at equal shares of a stream's cost, so a wave holding fp16
+// residual rows (256 bytes per token at d = 128) gets fewer tokens than one
+// holding 2-bit codes (about 48).
+constexpr int kMaxPieces = 2 * kMaxRuns + 2;
+struct CostPiece {
+  int32_t t0, cost;        // first token, bytes per token
+  int64_t c0;              // cost of the tokens before t0
+};
+
+// First token of wave range w of nw ranges: the token where the cumulative
+// cost reaches w/nw of the total, rounded down to a multiple of kWaveAlign
+// (0 for w <= 0, N for w >= nw).  Monotone in w.  nw <= 2^23, so the
+// products below stay within 64 bits.
+__host__ __device__ inline int wave_bound(const CostPiece* pc, int n_pieces, int64_t total, int N,
+                                          int w, int nw) {
+  if (w <= 0) return 0;
+  if (w >= nw) return N;
+  const int64_t target = (total / nw) * w + ((total % nw) * w) / nw;
+  int i = 0;
+  while (i + 1 < n_pieces && pc[i + 1].c0 <= target) ++i;
+  const int64_t t = pc[i].t0 + (target - pc[i].c0) / pc[i].cost;
+  const int64_t ta = t & ~int64_t(kWaveAlign - 1);
+  return int(ta < N ? ta : N);
+}
+
 struct DecodeParams {
   const uint16_t* q;
   float* out;
@@ -122,6 +149,9 @@ struct DecodeParams {
   int32_t n_k_runs, n_v_runs;
   Run k_runs[kMaxRuns];
   Run v_runs[kMaxRuns];
+  int32_t n_pieces;
+  int64_t cost_total;
+  CostPiece pieces[kMaxPieces];
 };
 
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s);
