@@ -55,6 +55,31 @@ def step_bytes(w: workloads.Workload, state):
     return attn, attn + extra
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_llama2_7b_int2_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kivi_amd", "csrc", f)
+                  for f in ("decode.hip", "kvq_device.h", "kvq_internal.h")]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed FETCH_SIZE/WRITE_SIZE
+    summary, or None when it does not cover this workload or the kernel
+    sources have changed since the counters were taken."""
+    import hashlib
+    if workload != "llama2_7b" or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch", "kernel_sources_sha256"):
+            k, v = line.strip().split(":", 1)
+            fields[k] = v.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    if fields.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, reps: int = 12, wall_s: float = 120.0):
     """Oracle decode step (append + float64 attention) on a sample of streams.
 
@@ -245,7 +270,11 @@ def main():
                    "cache_state_nKq_rK_nVq_rV": list(attn_probe),
                    "algorithmic_bytes_step": int(total_b), "algorithmic_bytes_attention": int(attn_b)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name),
+                     "traffic_note": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated), "
+                                     "null if the kernel changed since the counters were taken",
+                     "algorithmic_bytes_per_launch": int(attn_b),
                      "kernel": "decode_kernel: one kvq_decode_attn call (one workgroup per stream here, so no merge kernel)",
                      "us_per_launch": round(attn_ms * 1e3, 2)},
     }
