@@ -45,6 +45,9 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ half2_t as_h2(uint32_t x) { return __builtin_bit_cast(half2_t, x); }
 __device__ __forceinline__ uint32_t as_u32(half2_t x) { return __builtin_bit_cast(uint32_t, x); }
 
@@ -67,6 +70,8 @@ template <int W> struct LoadType;
 template <> struct LoadType<1> { typedef uint32_t T; };
 template <> struct LoadType<2> { typedef uint2 T; };
 template <> struct LoadType<4> { typedef uint4 T; };
+struct Words8 { uint4 a, b; };
+template <> struct LoadType<8> { typedef Words8 T; };
 
 template <int W>
 __device__ __forceinline__ uint32_t word(const typename LoadType<W>::T& x, int i) {
@@ -74,8 +79,12 @@ __device__ __forceinline__ uint32_t word(const typename LoadType<W>::T& x, int i
     return x;
   } else if constexpr (W == 2) {
     return i == 0 ? x.x : x.y;
-  } else {
+  } else if constexpr (W == 4) {
     return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
+  } else {
+    const uint4& y = i < 4 ? x.a : x.b;
+    const int k = i & 3;
+    return k == 0 ? y.x : k == 1 ? y.y : k == 2 ? y.z : y.w;
   }
 }
 
@@ -93,17 +102,21 @@ __device__ __forceinline__ typename LoadType<W>::T bload(Rsrc r, uint32_t off) {
   } else if constexpr (W == 2) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
     return make_uint2(v[0], v[1]);
-  } else {
+  } else if constexpr (W == 4) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
     return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+    return Words8{make_uint4(v[0], v[1], v[2], v[3]), make_uint4(w[0], w[1], w[2], w[3])};
   }
 }
 
 struct WaveLds {
   float* logit;      // [GQ][LT] logits by token slot; later the value row sums
   uint16_t* p16;     // [GQ][LT] fp16 probabilities, zero outside the wave's tokens
-  uint32_t* qs;      // [NGB][GQ][QHEAD] q*s hi/lo chunks of one load batch
-  float* bias;       // [NGB][GQ][LPR] per-chunk biases (after the largest q*s block)
+  uint32_t* qs;      // [NGB][QBLK] A blocks (q*s hi/lo rows) of one load batch
+  float* bias;       // [NGB][GQ] key biases per (group, head), after the largest A blocks
   float* ow;         // [GQ][D+2] (m, l, o[D]) of the wave (aliases qs/bias)
 };
 
@@ -123,26 +136,32 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 
 // ---------------------------------------------------------------------------
 // Keys of run tokens [r0, r1) (bits 2/4/8) -> raw logits q'.k (q' = q * 2^-8)
-// at slots slot0 + (t - r0).  r0 is a multiple of 32, so every item
-// (TPI <= 32 tokens) lies in one key group.  Whole items are written: slots
-// past r1 get values that a later piece overwrites or the softmax ignores.
+// at slots slot0 + (t - r0).  r0 is a multiple of 32, so every item (16
+// tokens) lies in one key group.  Whole items are written: slots past r1 get
+// values that a later piece overwrites or the softmax ignores.
 //
-// Per key group: hi = fp16(q'*s), lo = fp16(q'*s - hi) with packed fp16 ops
-// (q' = q * 2^-8 exactly, so no product can overflow fp16); a single fp16
-// q*s is too coarse for outlier channels, whose large logits would carry its
-// 2^-11 relative error into the softmax, while hi + lo keeps ~22 bits.  The
-// bias sum_c q'_c z_c - sum_c (hi + lo)_c * offset_c of each lane chunk comes
-// from three dot2 and a DPP sum over the chunk; it seeds the accumulator of
-// the lane that owns the chunk, so the row sum adds the whole bias.
+// Per key group, every channel's hi = fp16(q'*s) and lo = fp16(q'*s - hi)
+// (packed fp16 ops; q' = q * 2^-8 exactly): a single fp16 q*s is too coarse
+// for outlier channels, whose large logits would carry its 2^-11 relative
+// error into the softmax.  hi and lo of head h are rows 2h and 2h+1 of the A
+// operand of v_mfma_f32_16x16x32_f16; B is the unpacked codes of 16 tokens,
+// (offset + code) per channel, so D[2h][t] + D[2h+1][t] plus the group's bias
+// sum_c q'_c z_c - sum_c (hi + lo)_c * offset_c is the logit of token t (the
+// bias is reduced over the row's channels once per group).
+//
+// Operand layout (16x16x32): lane l holds A[l % 16][8*(l/16) .. +8),
+// B[8*(l/16) .. +8][l % 16] and D[4*(l/16) .. +4][l % 16].  k-block l/16 of
+// instruction m is code pairs 4m .. 4m+3 of the lane's quarter row (pair P:
+// word P / NP, position P % NP, channels clo and clo + NP).
 template <int D, int GQ, int BITS>
 __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
                                int64_t stream, const Run& run, int r0, int r1, int slot0,
                                int lane, int n_wave) {
   using KG = KeyGeo<D, GQ, BITS>;
   constexpr int LT = wave_slots(GQ);
-  constexpr int RB = KG::RB, LB = KG::LB, LPR = KG::LPR, TPI = KG::TPI, WPL = KG::WPL;
+  constexpr int RB = KG::RB, LB = KG::LB, TPI = KG::TPI, WPL = KG::WPL, MF = KG::MF;
   constexpr int NP = KG::NP, CPW = KG::CPW, PPL = KG::PPL, HD = KG::HD;
-  constexpr int NB = KG::NB, NGB = KG::NGB, QSTR = KG::QSTR, QHEAD = KG::QHEAD;
+  constexpr int NB = KG::NB, NGB = KG::NGB, ROWS = KG::ROWS, QBLK = KG::QBLK;
   constexpr int GPI = 64 / HD;                         // key groups per meta iteration
   constexpr int MI = (NGB + GPI - 1) / GPI;
   const int lg = P.lg_g;
@@ -154,15 +173,20 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
                              uint32_t(n) * RB);
   const Rsrc mrs = make_rsrc(P.k_meta + stream * P.k_meta_stride + run.meta_off + int64_t(jp) * D * 4,
                              uint32_t(n_groups) * D * 4);
-  const int tt = lane / LPR, tq = lane % LPR;
-  const uint32_t lane_off = uint32_t(tt * RB + tq * LB);
+  // matrix role of the lane: B column (token) col, k-block kb; A row col
+  const int col = lane & 15, kb = lane >> 4;
+  const uint32_t lane_off = uint32_t(col * RB + kb * LB);
+  // LDS dword of the lane's A row in block (m = 0, kb) of a group.  Rows past
+  // 2*GQ repeat row col % (2*GQ): they only feed D rows that are never read.
+  const int a_pos = (kb * ROWS + (col & (ROWS - 1))) * 4;
 
-  // meta role of the lane: pair pi of a row (word pi/NP, position pi%NP, i.e.
-  // channels clo and clo + NP) of the iteration's group gsub
+  // meta role of the lane: pair pi of a row of group gsub (of the meta
+  // iteration): k-block pj, pair pp of it
   const int pi = lane % HD, gsub = lane / HD;
-  const int kq = pi % NP;
-  const int clo = (pi / NP) * CPW + kq, chi = clo + NP;
-  const int qpos = (pi / PPL) * QSTR + pi % PPL;       // LDS dword of the pair's hi in its chunk
+  const int pj = pi / PPL, pp = pi % PPL;
+  const int kq = pp % NP;
+  const int clo = pj * (D / 4) + (pp / NP) * CPW + kq, chi = clo + NP;
+  const int qpos = ((pp / 4) * 4 + pj) * ROWS * 4 + pp % 4;   // its hi dword in block [pp/4][pj]
   const uint32_t meta_off = uint32_t((gsub * D + clo) * 4);
   const Unpacker<BITS, false> unpack;                 // constants in registers, once
   const _Float16 off = static_cast<_Float16>(Unpacker<BITS, false>::offset(kq));
@@ -205,60 +229,51 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
         float bp = __builtin_amdgcn_fdot2(qk[h], z2, 0.f, false);
         bp = __builtin_amdgcn_fdot2(hi, nego, bp, false);
         bp = __builtin_amdgcn_fdot2(lo, nego, bp, false);
-        bp = group_sum<PPL>(bp);
+        bp = group_sum<16>(bp);
+        bp = xrow_sum<HD / 16>(bp);          // over the HD pairs of the row
         if (js < ng) {
-          uint32_t* qs = W.qs + (js * GQ + h) * QHEAD;
-          qs[qpos] = as_u32(hi);
-          qs[LPR * QSTR + qpos] = as_u32(lo);
-          if (pi % PPL == 0) W.bias[(js * GQ + h) * LPR + pi / PPL] = bp;
+          uint32_t* qs = W.qs + js * QBLK + qpos;
+          qs[(2 * h) * 4] = as_u32(hi);
+          qs[(2 * h + 1) * 4] = as_u32(lo);
+          if (pi == 0) W.bias[js * GQ + h] = bp;
         }
       }
     }
     wave_lds_sync();
 
-    uint32_t qhi[GQ][PPL], qlo[GQ][PPL];
-    float bias[GQ];
+    half8_t am[MF];
+    float b0 = 0.f, b1 = 0.f;
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
       const int i = i0 + u;
       if (i >= n_items) continue;            // uniform
       const int rt = r0 + i * TPI;           // first run token of the item
       if (u == 0 || (rt & (P.G - 1)) == 0) {
-        // (uniform) the item starts a group: fetch the lane's q*s pairs
+        // (uniform) the item starts a group: fetch the lane's A row and the
+        // biases of the heads whose rows its D registers hold
         const int js = min((rt >> lg) - jp - jb0, NGB - 1);
+        const uint32_t* qs = W.qs + js * QBLK + a_pos;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-          const uint32_t* qs = W.qs + (js * GQ + h) * QHEAD + tq * QSTR;
-#pragma unroll
-          for (int p = 0; p < PPL; p += 4) {
-            const uint4 x = *reinterpret_cast<const uint4*>(qs + p);
-            const uint4 y = *reinterpret_cast<const uint4*>(qs + LPR * QSTR + p);
-            qhi[h][p] = x.x; qhi[h][p + 1] = x.y; qhi[h][p + 2] = x.z; qhi[h][p + 3] = x.w;
-            qlo[h][p] = y.x; qlo[h][p + 1] = y.y; qlo[h][p + 2] = y.z; qlo[h][p + 3] = y.w;
-          }
-          bias[h] = W.bias[(js * GQ + h) * LPR + tq];
-        }
+        for (int m = 0; m < MF; ++m)
+          am[m] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(qs + m * 4 * ROWS * 4));
+        b0 = W.bias[js * GQ + (2 * kb < GQ ? 2 * kb : 0)];
+        if (GQ > 1) b1 = W.bias[js * GQ + (2 * kb + 1 < GQ ? 2 * kb + 1 : 0)];
       }
-      float acc[GQ];
+      uint32_t v[PPL];
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) acc[h] = bias[h];
+      for (int w = 0; w < WPL; ++w) unpack.run(word<WPL>(B.buf[u], w), v + w * NP);
+      float4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < WPL; ++w) {
-        uint32_t v[NP];
-        unpack.run(word<WPL>(B.buf[u], w), v);
-#pragma unroll
-        for (int h = 0; h < GQ; ++h)
-#pragma unroll
-          for (int k = 0; k < NP; ++k) {
-            acc[h] = dot2(qhi[h][w * NP + k], v[k], acc[h]);
-            acc[h] = dot2(qlo[h][w * NP + k], v[k], acc[h]);
-          }
+      for (int m = 0; m < MF; ++m) {
+        const uint4 bm = make_uint4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[m], __builtin_bit_cast(half8_t, bm), d, 0, 0, 0);
       }
-      // every lane of the row holds the row sum; all of them store it
-#pragma unroll
-      for (int h = 0; h < GQ; ++h) W.logit[h * LT + slot0 + i * TPI + tt] = group_sum<LPR>(acc[h]);
+      // lane (kb, col) holds rows 4kb .. 4kb+3: heads 2kb and 2kb + 1
+      const int slot = slot0 + i * TPI + col;
+      if (2 * kb < GQ) W.logit[(2 * kb) * LT + slot] = (d[0] + b0) + d[1];
+      if (2 * kb + 1 < GQ) W.logit[(2 * kb + 1) * LT + slot] = (d[2] + b1) + d[3];
     }
-    wave_lds_sync();                         // the next batch rewrites q*s
+    wave_lds_sync();                         // the next batch rewrites the A blocks
   };
 
   Batch A, Bb;

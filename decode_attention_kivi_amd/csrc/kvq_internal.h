@@ -22,49 +22,45 @@ __host__ __device__ constexpr int wave_cap(int GQ) { return wave_tokens(GQ) * 3 
 // read and write whole items (up to 32 tokens) past a range's last token
 __host__ __device__ constexpr int wave_slots(int GQ) { return wave_cap(GQ) + 32; }
 
-// Geometry of the quantized-key loop for (D, GQ, BITS).  Each lane takes LB
-// bytes (WPL words, PPL fp16 code pairs) of one token row; LPR lanes share a
-// row, so one wave instruction covers TPI tokens, all of one key group.  The
-// q*s hi/lo pairs of the lane's PPL pairs for the GQ heads stay in registers
-// for all items of a group: LB is the widest load that keeps 2*GQ*PPL within
-// the register budget.
+// Geometry of the quantized-key loop for (D, GQ, BITS).  Logits of 16
+// tokens come from D/32 matrix instructions (v_mfma_f32_16x16x32_f16):
+// A = the q*s hi and lo rows of the GQ heads (2*GQ of 16 rows), B = the
+// tokens' unpacked code pairs (16 columns), k = 32 channels per instruction.
+// Lane l holds B column l % 16 for k-block l / 16: it loads LB = RB/4 bytes
+// (WPL words, PPL = D/8 code pairs) of one token row, a quarter of it, and
+// feeds MF = PPL/4 instructions four pairs each.
 template <int D, int GQ, int BITS>
 struct KeyGeo {
   static constexpr int RB = D * BITS / 8;       // bytes per token row
   static constexpr int NP = 16 / BITS;          // fp16 code pairs per 32-bit word
   static constexpr int CPW = 32 / BITS;         // channels per 32-bit word
-  static constexpr int PPL_MAX = GQ >= 8 ? 8 : 16;
-  static constexpr int LB0 = 4 * PPL_MAX / NP;
-  static constexpr int LB = LB0 > 16 ? (RB < 16 ? RB : 16) : (LB0 > RB ? RB : LB0);
-  static constexpr int LPR = RB / LB;           // lanes per row
-  static constexpr int TPI = 64 / LPR;          // tokens per wave instruction (item)
+  static constexpr int LB = RB / 4;             // bytes per lane: one k-block of a row
   static constexpr int WPL = LB / 4;            // code words per lane
   static constexpr int PPL = WPL * NP;          // code pairs per lane
+  static constexpr int MF = PPL / 4;            // matrix instructions per item
+  static constexpr int TPI = 16;                // tokens per item (B columns)
   static constexpr int HD = D / 2;              // code pairs per row
-  static constexpr int NB = 4;                  // items per load batch (two batches in flight)
-  static constexpr int NGB = NB * TPI / 32 > 1 ? NB * TPI / 32 : 1;  // key groups per batch
-  static constexpr int QSTR = PPL + 4;          // LDS dwords per chunk (padded against bank conflicts)
-  static constexpr int QHEAD = 2 * LPR * QSTR;  // LDS dwords per (group, head): hi chunks, lo chunks
-  static_assert(LPR * PPL == HD, "lanes of a row cover its pairs");
-  static_assert(TPI <= 32 && (NB * TPI) % 32 == 0, "items never straddle a key group");
+  static constexpr int NB = WPL >= 8 ? 2 : 4;   // items per load batch (two batches in flight)
+  static constexpr int NGB = NB * TPI / 32;     // key groups per batch (G >= 32)
+  static constexpr int ROWS = 2 * GQ;           // A rows in use: hi and lo of each head
+  static constexpr int QBLK = MF * 4 * ROWS * 4;  // LDS dwords of one group's A blocks [m][kblock][row][4]
+  static_assert(PPL * 4 == HD && PPL % 4 == 0, "four k-blocks cover a row, four pairs per instruction");
+  static_assert(ROWS <= 16, "at most 8 query heads per kv head");
 };
 
 __host__ __device__ constexpr int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
 __host__ __device__ constexpr int64_t cmax(int64_t a, int64_t b) { return a > b ? a : b; }
 
-// LDS dwords of the q*s blocks and of the per-chunk key biases of one load
-// batch, over the three code widths.
+// LDS dwords of the A blocks of one load batch and of the per-(group, head)
+// key biases (A blocks are the same size for every code width: D/32
+// instructions per item).
 template <int D, int GQ>
 __host__ __device__ constexpr int64_t kQsMax() {
-  return cmax(cmax(KeyGeo<D, GQ, 2>::NGB * GQ * KeyGeo<D, GQ, 2>::QHEAD,
-                   KeyGeo<D, GQ, 4>::NGB * GQ * KeyGeo<D, GQ, 4>::QHEAD),
-              KeyGeo<D, GQ, 8>::NGB * GQ * KeyGeo<D, GQ, 8>::QHEAD);
+  return cmax(KeyGeo<D, GQ, 2>::NGB, KeyGeo<D, GQ, 8>::NGB) * KeyGeo<D, GQ, 2>::QBLK;
 }
 template <int D, int GQ>
 __host__ __device__ constexpr int64_t kBiasMax() {
-  return cmax(cmax(KeyGeo<D, GQ, 2>::NGB * GQ * KeyGeo<D, GQ, 2>::LPR,
-                   KeyGeo<D, GQ, 4>::NGB * GQ * KeyGeo<D, GQ, 4>::LPR),
-              KeyGeo<D, GQ, 8>::NGB * GQ * KeyGeo<D, GQ, 8>::LPR);
+  return cmax(KeyGeo<D, GQ, 2>::NGB, KeyGeo<D, GQ, 8>::NGB) * GQ;
 }
 
 // Per-wave LDS of a decode workgroup (the device uses the same numbers).
@@ -73,7 +69,7 @@ __host__ __device__ constexpr int64_t kBiasMax() {
 //   logit  fp32 [GQ][LT]  logits by token slot; reused afterwards for the
 //                          row sums of the value reduction (at most 640 floats)
 //   p16    fp16 [GQ][LT]  probabilities, zero outside the wave's tokens
-//   area   q*s hi/lo pairs and per-chunk biases of the key groups of one load batch;
+//   area   A blocks (q*s hi/lo rows) and biases of the key groups of one load batch;
 //          afterwards the wave's (m, l, o[D]) per head
 struct DecodeLds {
   int64_t block, logit, p16, area, wave, total;   // total: for kWaves waves
@@ -87,7 +83,7 @@ __host__ __device__ constexpr DecodeLds decode_lds() {
   const int64_t block = 0;
   const int64_t logit = round16(cmax(int64_t(GQ) * lt * 4, 640 * 4));
   const int64_t p16 = round16(int64_t(GQ) * lt * 2);
-  // q*s blocks of the widest layout, then the per-chunk biases (see carve_wave)
+  // A blocks and zero block, then the per-(group, head) biases (see carve_wave)
   const int64_t qs = (kQsMax<D, GQ>() + kBiasMax<D, GQ>()) * 4;
   const int64_t area = round16(cmax(qs, int64_t(GQ) * (D + 2) * 4));
   const int64_t wave = logit + p16 + area;
