@@ -190,6 +190,11 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   p.n_pieces = int32_t(pieces.size());
   p.cost_total = cost_total;
   for (size_t i = 0; i < pieces.size(); ++i) p.pieces[i] = pieces[i];
+  if (nws <= kvq::kMaxBounds) {
+    p.n_bounds = int32_t(nws + 1);
+    for (int64_t w = 0; w <= nws; ++w)
+      p.bounds[w] = kvq::wave_bound(pieces.data(), int(pieces.size()), cost_total, int(N), int(w), int(nws));
+  }
   p.n_k_runs = a->n_k_segs;
   p.n_v_runs = a->n_v_segs;
   for (int i = 0; i < a->n_k_segs; ++i)

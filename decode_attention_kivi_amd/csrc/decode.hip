@@ -216,8 +216,11 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
   auto consume = [&](const Batch& B, int i0) {
     const int jb0 = ((r0 + i0 * TPI) >> lg) - jp;      // batch groups, relative to the piece
     const int ng = min(((r0 + min((i0 + NB) * TPI, n) - 1) >> lg) - jp - jb0 + 1, NGB);
+    float bpv[MI][GQ];                       // the lane's bias terms
 #pragma unroll
     for (int it = 0; it < MI; ++it) {
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) bpv[it][h] = 0.f;
       if (it * GPI >= ng) continue;          // uniform; keeps the loop fully unrolled
       const int js = it * GPI + gsub;
       const half2_t s2 = as_h2(__builtin_amdgcn_perm(B.mhi[it], B.mlo[it], 0x05040100u));
@@ -228,14 +231,29 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
         const half2_t lo = __builtin_elementwise_fma(qk[h], s2, -hi);
         float bp = __builtin_amdgcn_fdot2(qk[h], z2, 0.f, false);
         bp = __builtin_amdgcn_fdot2(hi, nego, bp, false);
-        bp = __builtin_amdgcn_fdot2(lo, nego, bp, false);
-        bp = group_sum<16>(bp);
-        bp = xrow_sum<HD / 16>(bp);          // over the HD pairs of the row
+        bpv[it][h] = __builtin_amdgcn_fdot2(lo, nego, bp, false);
         if (js < ng) {
           uint32_t* qs = W.qs + js * QBLK + qpos;
           qs[(2 * h) * 4] = as_u32(hi);
           qs[(2 * h + 1) * 4] = as_u32(lo);
-          if (pi == 0) W.bias[js * GQ + h] = bp;
+        }
+      }
+    }
+    // biases: sums of the terms over the HD pairs of a row
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      if constexpr (MI == 2 && GPI == 1) {
+        // both groups at once: fold the wave halves so that lanes 0-31 hold
+        // group 0's terms and lanes 32-63 group 1's, then sum 32 lanes
+        const auto r = __builtin_amdgcn_permlane32_swap(fbits(bpv[0][h]), fbits(bpv[1][h]), false, false);
+        const float x = xrow_sum<2>(group_sum<16>(bitsf(r[0]) + bitsf(r[1])));
+        if ((lane & 31) == 0 && (lane >> 5) < ng) W.bias[(lane >> 5) * GQ + h] = x;
+      } else {
+#pragma unroll
+        for (int it = 0; it < MI; ++it) {
+          if (it * GPI >= ng) continue;
+          const float x = xrow_sum<HD / 16>(group_sum<16>(bpv[it][h]));
+          if (pi == 0 && it * GPI + gsub < ng) W.bias[(it * GPI + gsub) * GQ + h] = x;
         }
       }
     }
@@ -581,8 +599,9 @@ decode_kernel(const DecodeParams P) {
   const int b = int(stream / P.Hkv), hkv = int(stream % P.Hkv);
   const int N = P.n_tok;
   const int gw = wg * NW + wave;
-  const int a = wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw, P.waves_per_stream);
-  const int e = wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw + 1, P.waves_per_stream);
+  const bool tab = P.n_bounds > 0;
+  const int a = tab ? P.bounds[gw] : wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw, P.waves_per_stream);
+  const int e = tab ? P.bounds[gw + 1] : wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw + 1, P.waves_per_stream);
   const int n = e - a;
 
   const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;   // [gq][D]
@@ -636,16 +655,22 @@ decode_kernel(const DecodeParams P) {
       }
       mx = wave_max64(mx);
       const float nm = -mx;
+      // exp2 of arguments <= 0 with the bare v_exp_f32: results below the
+      // fp32 normal range round to fp16 zero anyway.  Slots past n get 0.
       float sum = 0.f;
 #pragma unroll
-      for (int s = lane * 4; s < LT; s += 256) {
-        const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
-        const float xs[4] = {x.x, x.y, x.z, x.w};
-        uint32_t p16[4];
+      for (int s0 = 0; s0 < LT; s0 += 256) {
+        const int s = s0 + lane * 4;
+        if (s >= LT) continue;
+        uint32_t p16[4] = {0u, 0u, 0u, 0u};
+        if (s0 < n) {                   // uniform
+          const float4 x = *reinterpret_cast<const float4*>(W.logit + h * LT + s);
+          const float xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          p16[k] = s + k < n ? f2h(exp2f(__builtin_fmaf(xs[k], sc, nm))) : 0u;
-          sum += h2f(p16[k]);           // the same rounded values the A.V uses
+          for (int k = 0; k < 4; ++k) {
+            if (s + k < n) p16[k] = f2h(__builtin_amdgcn_exp2f(__builtin_fmaf(xs[k], sc, nm)));
+            sum += h2f(p16[k]);         // the same rounded values the A.V uses
+          }
         }
         *reinterpret_cast<uint2*>(W.p16 + h * LT + s) =
             make_uint2(p16[0] | (p16[1] << 16), p16[2] | (p16[3] << 16));

@@ -101,6 +101,7 @@ struct Run {            // device copy of kvq_segment
 // residual rows (256 bytes per token at d = 128) gets fewer tokens than one
 // holding 2-bit codes (about 48).
 constexpr int kMaxPieces = 2 * kMaxRuns + 2;
+constexpr int kMaxBounds = 64;          // waves per stream with host-computed wave bounds
 struct CostPiece {
   int32_t t0, cost;        // first token, bytes per token
   int64_t c0;              // cost of the tokens before t0
@@ -148,6 +149,12 @@ struct DecodeParams {
   int32_t n_pieces;
   int64_t cost_total;
   CostPiece pieces[kMaxPieces];
+  // wave_bound(.., w, waves_per_stream) for w = 0 .. waves_per_stream when
+  // waves_per_stream <= kMaxBounds (every stream has the same runs, so the
+  // bounds are the same for all of them); otherwise n_bounds = 0 and each
+  // wave computes its own (64-bit divisions: ~1 us per launch)
+  int32_t n_bounds;
+  int32_t bounds[kMaxBounds + 1];
 };
 
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s);
