@@ -8,13 +8,13 @@
 // heads that share it.  A wave's range may cross run boundaries: it walks the
 // key pieces (quantized runs, fp16 runs, the fp16 residual) and then the value
 // pieces in token order.  Per wave:
-//   1. logits, one load batch at a time: 8- or 16-byte code loads, the batch's
+//   1. logits, one load batch at a time: quarter-row code loads, the batch's
 //      key groups' q*s (per-channel key scales, KIVI note "Method details") as
-//      fp16 hi + lo pairs and the group bias sum_c q_c z_c into LDS; each lane
-//      keeps its pairs' q*s in registers for all tokens of a group, unpacks
-//      code pairs into fp16 (offset + code) by mask-and-or with an exponent
-//      constant and accumulates with v_dot2_f32_f16; residual rows dot q
-//      directly (A = Concat([A_g, A_r]));
+//      fp16 hi + lo rows of a matrix-core A operand and the group biases
+//      sum_c q_c z_c into LDS; code pairs are unpacked into fp16 (offset +
+//      code) by mask-and-or with an exponent constant and form the B operand
+//      of v_mfma_f32_16x16x32_f16 (16 tokens per instruction group); residual
+//      rows dot q directly (A = Concat([A_g, A_r]));
 //   2. the range's max and sum of exp2(logit - max): one softmax over the
 //      concatenation (KIVI Algorithm 1; WindowQuant Sec. 3.3.1);
 //   3. A.V over token-pair value blocks: one fp16 pair holds the same channel
