@@ -21,6 +21,7 @@ __all__ = [
     "kvq_abi_version", "kvq_strerror", "kvq_quantize_append", "kvq_residual_append",
     "kvq_decode_append",
     "kvq_reorder_windows", "kvq_decode_attn_workspace", "kvq_decode_attn",
+    "KiviCacheDesc", "kvq_kivi_step_workspace", "kvq_kivi_step",
 ]
 
 KVQ_KEYS = 0
@@ -69,6 +70,23 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class KiviCacheDesc(ctypes.Structure):
+    """kvq_kivi_cache (field order and types of include/kvq.h)."""
+    _fields_ = [
+        ("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("residual", ctypes.c_int32),
+        ("n_streams", ctypes.c_int32), ("d_h", ctypes.c_int32), ("capacity", ctypes.c_int32),
+        ("win_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("k_codes_stride", ctypes.c_int64),
+        ("k_meta", ctypes.c_void_p), ("k_meta_stride", ctypes.c_int64),
+        ("v_codes", ctypes.c_void_p), ("v_codes_stride", ctypes.c_int64),
+        ("v_meta", ctypes.c_void_p), ("v_meta_stride", ctypes.c_int64),
+        ("k_res", ctypes.c_void_p), ("k_res_stride", ctypes.c_int64),
+        ("v_res", ctypes.c_void_p), ("v_res_stride", ctypes.c_int64),
+        ("n_kq", ctypes.c_int32), ("r_k", ctypes.c_int32), ("n_vq", ctypes.c_int32),
+        ("r_v", ctypes.c_int32), ("v_start", ctypes.c_int32),
+    ]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -100,6 +118,12 @@ def _load():
     lib.kvq_decode_attn_workspace.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.kvq_decode_attn.restype = i32
     lib.kvq_decode_attn.argtypes = [ctypes.POINTER(DecodeArgs), vp]
+    lib.kvq_kivi_step_workspace.restype = i32
+    lib.kvq_kivi_step_workspace.argtypes = [ctypes.POINTER(KiviCacheDesc), i32, i32,
+                                            ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_kivi_step.restype = i32
+    lib.kvq_kivi_step.argtypes = [ctypes.POINTER(KiviCacheDesc), i32, i32, ctypes.c_float,
+                                  vp, i64, vp, i64, vp, vp, vp, ctypes.c_size_t, vp]
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -212,3 +236,19 @@ def kvq_decode_attn_workspace(args: DecodeArgs) -> int:
 
 def kvq_decode_attn(args: DecodeArgs, stream=None):
     _check(_load().kvq_decode_attn(ctypes.byref(args), _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_kivi_step_workspace(cache: KiviCacheDesc, batch: int, n_q_heads: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().kvq_kivi_step_workspace(ctypes.byref(cache), batch, n_q_heads, ctypes.byref(n)),
+           "kvq_kivi_step_workspace")
+    return int(n.value)
+
+
+def kvq_kivi_step(cache: KiviCacheDesc, batch, n_q_heads, sm_scale, k_new, k_new_stride, v_new,
+                  v_new_stride, q, out, workspace=None, workspace_bytes=0, stream=None):
+    """One KIVI decode step; updates the lengths in ``cache`` (a KiviCacheDesc)."""
+    _check(_load().kvq_kivi_step(ctypes.byref(cache), batch, n_q_heads, float(sm_scale),
+                                 _dev(k_new), k_new_stride, _dev(v_new), v_new_stride, _dev(q),
+                                 _dev(out), _dev(workspace), int(workspace_bytes), _stream(stream)),
+           "kvq_kivi_step")

@@ -23,9 +23,9 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (KVQ_KEYS, KVQ_VALUES, Segment, kvq_decode_append, kvq_decode_attn,
-               kvq_decode_attn_workspace, kvq_quantize_append, kvq_reorder_windows,
-               kvq_residual_append, make_decode_args)
+from . import (KVQ_KEYS, KVQ_VALUES, KiviCacheDesc, Segment, kvq_decode_append, kvq_decode_attn,
+               kvq_decode_attn_workspace, kvq_kivi_step, kvq_kivi_step_workspace,
+               kvq_quantize_append, kvq_reorder_windows, kvq_residual_append, make_decode_args)
 
 __all__ = ["KiviCache", "WindowCache", "arena_bytes"]
 
@@ -182,6 +182,36 @@ class KiviCache:
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         kvq_decode_attn(self.decode_args(q, out, sm_scale, split_tokens), stream)
+        return out
+
+    def desc(self) -> KiviCacheDesc:
+        """The cache as the C ABI's kvq_kivi_cache (buffers and current lengths)."""
+        return KiviCacheDesc(
+            self.bits, self.G, self.R, self.n_streams, self.d, self.capacity, self.v_win_rows, 0,
+            self.k_codes.data_ptr(), self.k_codes.stride(0), self.k_meta.data_ptr(), self.k_meta.stride(0),
+            self.v_codes.data_ptr(), self.v_codes.stride(0), self.v_meta.data_ptr(), self.v_meta.stride(0),
+            self.k_res.data_ptr(), self.k_res.stride(0), self.v_res.data_ptr(), self.v_res.stride(0),
+            self.n_kq, self.r_k, self.n_vq, self.r_v, self.v_start)
+
+    def step(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, sm_scale: float,
+             out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """append() followed by attend(), as one kvq_kivi_step call."""
+        assert self.n_tokens + 1 <= self.capacity
+        n, ss, _ = _streams(k_new)
+        n2, ss2, _ = _streams(v_new)
+        B, Hq, d = q.shape
+        assert n == n2 == self.n_streams and B == self.B and d == self.d
+        assert q.is_contiguous() and q.dtype == torch.float16
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        c = self.desc()
+        need = kvq_kivi_step_workspace(c, B, Hq)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws = self._ws if need else None
+        kvq_kivi_step(c, B, Hq, sm_scale, k_new, ss, v_new, ss2, q, out, ws,
+                      ws.numel() if ws is not None else 0, stream)
+        self.n_kq, self.r_k, self.n_vq, self.r_v, self.v_start = c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start
         return out
 
 

@@ -377,3 +377,157 @@ kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// One KIVI decode step (append, flushes, attention) from the cache state.
+namespace {
+
+struct KiviStep {
+  kvq_kivi_cache next;       // the state after the step
+  bool compact;              // move the window to row 0 first
+  int32_t v_row, v_quant_row, v_dst_tok, k_row;
+  bool flush_keys;           // quantize the R residual keys after the append
+  int32_t flush_dst_tok;
+  kvq_segment kseg, vseg;
+  kvq_decode_args args;      // attention over `next` (pointers to q/out filled by the caller)
+};
+
+kvq_status kivi_plan_step(const kvq_kivi_cache* c, int32_t batch, int32_t n_q_heads, float sm_scale,
+                          KiviStep* st) {
+  if (!c || !st) return KVQ_EINVAL;
+  const int64_t R = c->residual, G = c->group;
+  if (c->bits != 2 && c->bits != 4 && c->bits != 8) return KVQ_EINVAL;
+  if (G != 32 && G != 64 && G != 128) return KVQ_EINVAL;
+  if (c->d_h != 64 && c->d_h != 128) return KVQ_EUNSUPPORTED;
+  if (G > c->d_h || R < G || R % G != 0) return KVQ_EINVAL;
+  if (c->n_streams < 1 || batch < 1 || c->n_streams % batch != 0) return KVQ_EINVAL;
+  const int32_t hkv = c->n_streams / batch;
+  if (n_q_heads < hkv || n_q_heads % hkv != 0) return KVQ_EINVAL;
+  if (c->win_rows < 2 * R + 2 || c->reserved != 0) return KVQ_EINVAL;
+  if (c->n_kq < 0 || c->r_k < 0 || c->r_k >= R || c->n_kq % G != 0) return KVQ_EINVAL;
+  if (c->n_vq < 0 || c->r_v < 0 || c->r_v > R || c->v_start < 0 ||
+      int64_t(c->v_start) + c->r_v > c->win_rows)
+    return KVQ_EINVAL;
+  if (int64_t(c->n_kq) + c->r_k != int64_t(c->n_vq) + c->r_v) return KVQ_EINVAL;
+  if (int64_t(c->n_kq) + c->r_k + 1 > c->capacity) return KVQ_EINVAL;
+
+  KiviStep& s = *st;
+  s.next = *c;
+  kvq_kivi_cache& n = s.next;
+  // 1. window ring: with win_rows >= 2R + 2 the moved rows never overlap their source
+  s.compact = int64_t(n.v_start) + n.r_v + 1 > n.win_rows;
+  if (s.compact) n.v_start = 0;
+  // 2. append, and the value-window overflow
+  s.k_row = n.r_k;
+  s.v_row = n.v_start + n.r_v;
+  const bool quant = n.r_v + 1 > R;
+  s.v_quant_row = quant ? n.v_start : -1;
+  s.v_dst_tok = n.n_vq;
+  n.r_k += 1;
+  n.r_v += 1;
+  if (quant) {
+    n.n_vq += 1;
+    n.v_start += 1;
+    n.r_v -= 1;
+  }
+  // 3. key flush
+  s.flush_keys = n.r_k == R;
+  s.flush_dst_tok = n.n_kq;
+  if (s.flush_keys) {
+    n.n_kq += int32_t(R);
+    n.r_k = 0;
+  }
+  // 4. attention over the new state
+  s.kseg = kvq_segment{c->bits, 0, n.n_kq, 0, 0, 0};
+  s.vseg = kvq_segment{c->bits, 0, n.n_vq, 0, 0, 0};
+  kvq_decode_args& a = s.args;
+  std::memset(&a, 0, sizeof(a));
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = hkv;
+  a.d_h = c->d_h;
+  a.group = c->group;
+  a.sm_scale = sm_scale;
+  a.k_segs = &s.kseg;
+  a.n_k_segs = n.n_kq > 0 ? 1 : 0;
+  a.v_segs = &s.vseg;
+  a.n_v_segs = n.n_vq > 0 ? 1 : 0;
+  a.k_codes = c->k_codes; a.k_codes_stride = c->k_codes_stride;
+  a.k_meta = c->k_meta;   a.k_meta_stride = c->k_meta_stride;
+  a.v_codes = c->v_codes; a.v_codes_stride = c->v_codes_stride;
+  a.v_meta = c->v_meta;   a.v_meta_stride = c->v_meta_stride;
+  a.k_res = c->k_res; a.n_k_res = n.r_k; a.k_res_stride = c->k_res_stride;
+  a.v_res = static_cast<const uint16_t*>(c->v_res) + int64_t(n.v_start) * c->d_h;
+  a.n_v_res = n.r_v;
+  a.v_res_stride = c->v_res_stride;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_kivi_step_workspace(const kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads,
+                                   size_t* bytes) {
+  if (!bytes) return KVQ_EINVAL;
+  KiviStep st;
+  kvq_status r = kivi_plan_step(cache, batch, n_q_heads, 1.f, &st);
+  if (r != KVQ_OK) return r;
+  // the plan does not depend on q/out, but make_plan checks their alignment
+  st.args.q = cache->k_res;
+  st.args.out = static_cast<float*>(cache->v_res);
+  return kvq_decode_attn_workspace(&st.args, bytes);
+}
+
+kvq_status kvq_kivi_step(kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads, float sm_scale,
+                         const void* k_new, int64_t k_new_stride, const void* v_new,
+                         int64_t v_new_stride, const void* q, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  KiviStep st;
+  kvq_status r = kivi_plan_step(cache, batch, n_q_heads, sm_scale, &st);
+  if (r != KVQ_OK) return r;
+  const kvq_kivi_cache& c = *cache;
+  const kvq_kivi_cache& n = st.next;
+  if (!k_new || !v_new || !q || !out) return KVQ_EINVAL;
+  st.args.q = q;
+  st.args.out = out;
+  st.args.workspace = workspace;
+  st.args.workspace_bytes = workspace_bytes;
+  // every check before the first launch
+  Plan pl;
+  r = make_plan(&st.args, &pl);
+  if (r != KVQ_OK) return r;
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes)) return KVQ_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(k_new) & 15) || (reinterpret_cast<uintptr_t>(v_new) & 15) ||
+      (k_new_stride & 7) || (v_new_stride & 7))
+    return KVQ_EALIGN;
+  if (k_new_stride < c.d_h || v_new_stride < c.d_h) return KVQ_EINVAL;
+
+  if (st.compact) {
+    r = kvq_residual_append(c.n_streams, c.d_h, c.r_v,
+                            static_cast<const uint16_t*>(c.v_res) + int64_t(c.v_start) * c.d_h,
+                            c.v_res_stride, c.d_h, c.v_res, c.v_res_stride, 0, stream);
+    if (r != KVQ_OK) return r;
+  }
+  r = kvq_decode_append(c.bits, c.group, c.n_streams, c.d_h, k_new, k_new_stride, v_new, v_new_stride,
+                        c.k_res, c.k_res_stride, st.k_row, c.v_res, c.v_res_stride, st.v_row,
+                        st.v_quant_row, c.v_codes, c.v_codes_stride, c.v_meta, c.v_meta_stride,
+                        st.v_dst_tok, stream);
+  if (r != KVQ_OK) return r;
+  if (st.flush_keys) {
+    r = kvq_quantize_append(KVQ_KEYS, c.bits, c.group, c.n_streams, c.d_h, c.residual, c.k_res,
+                            c.k_res_stride, c.d_h, nullptr, c.k_codes, c.k_codes_stride, c.k_meta,
+                            c.k_meta_stride, st.flush_dst_tok, stream);
+    if (r != KVQ_OK) return r;
+  }
+  r = from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
+  if (r != KVQ_OK) return r;
+  cache->n_kq = n.n_kq;
+  cache->r_k = n.r_k;
+  cache->n_vq = n.n_vq;
+  cache->r_v = n.r_v;
+  cache->v_start = n.v_start;
+  return KVQ_OK;
+}
+
+}  // extern "C"

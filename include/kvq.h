@@ -278,6 +278,69 @@ kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes)
  */
 kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream);
 
+/*
+ * A KIVI cache of n_streams = B * Hkv streams in the state that KIVI's
+ * Algorithm 1 keeps between decode steps: one key run and one value run of
+ * b-bit codes (code and meta arenas with code_off = meta_off = 0, room for
+ * `capacity` tokens each), the fp16 key residual (R rows per stream) and the
+ * fp16 value window (a ring of win_rows rows per stream; the window's r_v
+ * rows start at row v_start).  The caller allocates every buffer; the five
+ * lengths are host integers that kvq_kivi_step reads and updates.
+ */
+typedef struct kvq_kivi_cache {
+  int32_t bits;           /* 2, 4 or 8                                         */
+  int32_t group;          /* G in {32, 64, 128}, G <= d_h                      */
+  int32_t residual;       /* R, a positive multiple of G                       */
+  int32_t n_streams;      /* B * Hkv >= 1                                      */
+  int32_t d_h;            /* 64 or 128                                         */
+  int32_t capacity;       /* tokens the key and value runs have room for       */
+  int32_t win_rows;       /* value-window rows per stream, >= 2R + 2           */
+  int32_t reserved;       /* must be 0                                         */
+  void* k_codes;  int64_t k_codes_stride;   /* arenas: base, bytes per stream */
+  void* k_meta;   int64_t k_meta_stride;
+  void* v_codes;  int64_t v_codes_stride;
+  void* v_meta;   int64_t v_meta_stride;
+  void* k_res;    int64_t k_res_stride;     /* fp16 elements per stream         */
+  void* v_res;    int64_t v_res_stride;
+  /* state: tokens in the key run, key residual, value run, value window,
+   * and the window's first row (n_kq + r_k == n_vq + r_v) */
+  int32_t n_kq, r_k, n_vq, r_v, v_start;
+} kvq_kivi_cache;
+
+/*
+ * Workspace bytes kvq_kivi_step needs for its attention call with the cache
+ * in the state the step leaves it in (see kvq_decode_attn_workspace).
+ */
+kvq_status kvq_kivi_step_workspace(const kvq_kivi_cache* cache, int32_t batch,
+                                   int32_t n_q_heads, size_t* bytes);
+
+/*
+ * kvq_kivi_step -- one whole KIVI decode step in one call (Algorithm 1,
+ * Decoding, followed by the attention of the new token's queries):
+ *   1. when the window ring has no free row after its last one, the r_v
+ *      window rows move to rows 0..r_v-1 (v_start = 0);
+ *   2. the new key row becomes key-residual row r_k and the new value row
+ *      window row v_start + r_v; if the window then holds more than R
+ *      values, its oldest one is quantized per token and appended to the
+ *      value run (kvq_decode_append);
+ *   3. if the key residual now holds R rows, they are quantized as R/G whole
+ *      groups and appended to the key run (kvq_quantize_append), r_k = 0;
+ *   4. kvq_decode_attn of q over the updated cache (split chosen by the
+ *      library) writes out.
+ *   k_new, v_new  fp16 rows, stream s at element s * new_stride.
+ *   q, out        fp16 [batch][n_q_heads][d_h] and fp32 [batch][n_q_heads][d_h];
+ *                 n_streams = batch * n_kv_heads with n_kv_heads dividing
+ *                 n_q_heads (Hq / Hkv <= 8).
+ * All checks (shapes, state consistency, capacity, workspace) run before
+ * anything is enqueued; on success the five lengths in *cache are updated.
+ * On KVQ_ELAUNCH the cache contents and lengths are undefined.
+ */
+kvq_status kvq_kivi_step(kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads,
+                         float sm_scale, const void* k_new, int64_t k_new_stride,
+                         const void* v_new, int64_t v_new_stride, const void* q,
+                         float* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

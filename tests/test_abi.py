@@ -147,3 +147,46 @@ def test_binding_refuses_host_tensors_as_device_buffers():
     import torch
     with pytest.raises(ValueError):
         _q(src=torch.zeros(16, dtype=torch.float16))
+
+
+def _kivi(**kw):
+    base = dict(bits=2, group=32, residual=64, n_streams=4, d_h=128, capacity=1024, win_rows=130,
+                reserved=0, k_codes=A, k_codes_stride=1 << 16, k_meta=A, k_meta_stride=1 << 16,
+                v_codes=A, v_codes_stride=1 << 16, v_meta=A, v_meta_stride=1 << 16,
+                k_res=A, k_res_stride=64 * 128, v_res=A, v_res_stride=130 * 128,
+                n_kq=256, r_k=5, n_vq=197, r_v=64, v_start=3)
+    base.update(kw)
+    return kvq.KiviCacheDesc(**base)
+
+
+def test_kivi_step_workspace_follows_the_state_after_the_step():
+    # 262 tokens after the step, one workgroup per stream: no workspace
+    assert kvq.kvq_kivi_step_workspace(_kivi(), 2, 8) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bits=3), EINVAL), (dict(group=16), EINVAL), (dict(d_h=96), EUNSUP),
+    (dict(residual=48), EINVAL), (dict(win_rows=129), EINVAL), (dict(reserved=1), EINVAL),
+    (dict(r_k=64), EINVAL), (dict(n_kq=250), EINVAL), (dict(r_v=65, n_vq=196), EINVAL),
+    (dict(n_vq=198), EINVAL),                    # token counts of keys and values differ
+    (dict(v_start=67), EINVAL),                  # window past the ring
+    (dict(capacity=261), EINVAL),                # no room for the new token
+    (dict(n_streams=5), EINVAL),                 # not batch * n_kv_heads
+])
+def test_kivi_step_rejects(kw, code):
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_kivi_step_workspace(_kivi(**kw), 2, 8)
+    assert e.value.status == code
+
+
+def test_kivi_step_rejects_before_any_launch_and_keeps_the_state():
+    c = _kivi()
+    for kw, code in [(dict(k_new=A + 2), EALIGN), (dict(q=None), EINVAL), (dict(n_q_heads=7), EINVAL),
+                     (dict(k_new_stride=64), EINVAL)]:
+        args = dict(batch=2, n_q_heads=8, sm_scale=0.088, k_new=A, k_new_stride=128, v_new=A,
+                    v_new_stride=128, q=A, out=A, workspace=None, workspace_bytes=0, stream=0)
+        args.update(kw)
+        with pytest.raises(KvqError) as e:
+            kvq.kvq_kivi_step(c, **args)
+        assert e.value.status == code
+        assert (c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start) == (256, 5, 197, 64, 3)

@@ -68,8 +68,10 @@ def _check_stream_bytes(cache, s, st, w):
     assert np.array_equal(vr.view(np.uint16), st.v_res.view(np.uint16)), "value residual"
 
 
-def run_kivi(kvq, w, units, steps=1, split_tokens=0, check_every_step=False, bytes_units=None):
-    """Prefill w.context tokens, then `steps` decode steps; compare with the oracle."""
+def run_kivi(kvq, w, units, steps=1, split_tokens=0, check_every_step=False, bytes_units=None,
+             one_call=False):
+    """Prefill w.context tokens, then `steps` decode steps; compare with the oracle.
+    one_call: every step is one kvq_kivi_step (append, flushes and attention)."""
     import torch
     from decode_attention_kivi_amd.cache import KiviCache
     dev = torch.device("cuda")
@@ -90,12 +92,16 @@ def run_kivi(kvq, w, units, steps=1, split_tokens=0, check_every_step=False, byt
     worst = 0.0
     for step in range(steps):
         t = L + step
-        cache.append(kt[:, :, t:t + 1], vt[:, :, t:t + 1])
+        if one_call:
+            out = cache.step(kt[:, :, t:t + 1], vt[:, :, t:t + 1], qt, w.sm_scale)
+        else:
+            cache.append(kt[:, :, t:t + 1], vt[:, :, t:t + 1])
         for (b, h), st in streams.items():
             st.decode_append(k[b, h, t], v[b, h, t])
         if not (check_every_step or step == steps - 1):
             continue
-        out = cache.attend(qt, w.sm_scale, split_tokens=split_tokens)
+        if not one_call:
+            out = cache.attend(qt, w.sm_scale, split_tokens=split_tokens)
         torch.cuda.synchronize()
         o = out.cpu().numpy()
         assert np.all(np.isfinite(o))
@@ -121,6 +127,21 @@ def test_ragged_lengths(kvq, L):
 def test_many_steps_flush_and_window(kvq, bits):
     w = SMALL.scaled(context=40, bits=bits, residual=32, n_kv_heads=2, n_q_heads=2)
     run_kivi(kvq, w, units=[(0, 0), (0, 1)], steps=3 * 32 + 5, check_every_step=True)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_one_call_steps(kvq, bits):
+    # kvq_kivi_step: append, value-window overflow, key flush every R steps,
+    # window compaction and attention in one call, checked after every step
+    w = SMALL.scaled(context=40, bits=bits, residual=32, n_kv_heads=2, n_q_heads=4)
+    run_kivi(kvq, w, units=[(0, 0), (0, 1)], steps=3 * 32 + 5, check_every_step=True, one_call=True)
+
+
+@pytest.mark.parametrize("context", [0, 1, 127, 128])
+def test_one_call_steps_d128_gqa(kvq, context):
+    w = SMALL.scaled(context=context, d_h=128, group=32, residual=128, n_kv_heads=2, n_q_heads=16,
+                     batch=2)
+    run_kivi(kvq, w, units=[(1, 0), (1, 1)], steps=140, check_every_step=False, one_call=True)
 
 
 @pytest.mark.parametrize("split", [2, 33, 64, 96, 1000])
