@@ -123,6 +123,76 @@ def cpu_baseline(w: workloads.Workload, budget_s: float = 12.0, reps: int = 12, 
                       f"{n_steps} steps in {times:.1f} s single-threaded"}
 
 
+def component_times(w, cache, k_new, v_new, q, out, stream, reps: int = 50):
+    """Mean microseconds of each library call of a decode step, one call at a
+    time between events (launch gaps included): the fused append, the key
+    flush of R tokens (every R steps), the attention, and the whole step as
+    one kvq_kivi_step call.  The cache state is restored after each call."""
+    import torch
+    from decode_attention_kivi_amd import KVQ_KEYS, kvq_quantize_append
+    saved = (cache.n_kq, cache.r_k, cache.n_vq, cache.r_v, cache.v_start)
+
+    def restore():
+        cache.n_kq, cache.r_k, cache.n_vq, cache.r_v, cache.v_start = saved
+
+    # the flush writes into scratch arenas of R tokens (the cache's own key run
+    # has no room past its current length)
+    kc = torch.empty(cache.n_streams, cache.R * cache.d * cache.bits // 8, dtype=torch.uint8,
+                     device=q.device)
+    km = torch.empty(cache.n_streams, cache.R // cache.G * cache.d * 4, dtype=torch.uint8, device=q.device)
+
+    def flush():
+        kvq_quantize_append(KVQ_KEYS, cache.bits, cache.G, cache.n_streams, cache.d, cache.R,
+                            cache.k_res, cache.k_res.stride(0), cache.d, None, kc, kc.stride(0),
+                            km, km.stride(0), 0, stream)
+
+    calls = {
+        "decode_append": lambda: cache.append(k_new, v_new, stream=stream),
+        "key_flush_R_tokens": flush,
+        "attention": lambda: cache.attend(q, w.sm_scale, out=out, stream=stream),
+        "kivi_step_one_call": lambda: cache.step(k_new, v_new, q, w.sm_scale, out=out, stream=stream),
+    }
+    res = {}
+    for name, fn in calls.items():
+        total = 0.0
+        for i in range(reps + 5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            restore()
+            torch.cuda.synchronize()
+            if i >= 5:
+                total += e0.elapsed_time(e1)
+        res[name] = round(total / reps * 1e3, 2)
+    return res
+
+
+def streaming_read_ceiling(dev, stream, gib: float = 1.0, reps: int = 20) -> float:
+    """GB/s of a plain streaming read on this GPU: torch's sum over a 1 GiB
+    buffer (well past the 256 MB Infinity Cache), the practical ceiling the
+    decode kernel is compared with (its roofline fraction stays against the
+    8 TB/s peak)."""
+    import torch
+    x = torch.ones(int(gib * (1 << 30)) // 8, dtype=torch.int64, device=dev)
+    for _ in range(3):
+        x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        x.sum()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del x
+    return round(x_bytes(gib) / (ms * 1e-3) / 1e9, 1)
+
+
+def x_bytes(gib: float) -> int:
+    return int(gib * (1 << 30)) // 8 * 8
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,18 +298,22 @@ def main():
     n_copies = len(caches) * args.rounds       # steps per graph replay
 
     def timed(graph, steps, warmup):
+        """Mean ms per step over the timed replays, the step count, and the
+        (p10, p50, p90) of the per-replay means (events between replays)."""
         reps_w = max(1, -(-warmup // n_copies))
         reps = max(1, -(-steps // n_copies))
         for _ in range(reps_w):
             graph.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for i in range(reps):
             graph.replay()
-        e1.record(stream)
+            ev[i + 1].record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * n_copies), reps * n_copies
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) / n_copies for i in range(reps))
+        pct = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+        return ev[0].elapsed_time(ev[reps]) / (reps * n_copies), reps * n_copies, (pct(.1), pct(.5), pct(.9))
 
     with torch.cuda.stream(stream):
         # let the clocks settle (both graphs, untimed) before either is timed
@@ -248,9 +322,10 @@ def main():
             step_graph.replay()
             attn_graph.replay()
             torch.cuda.synchronize()
-        attn_ms, _ = timed(attn_graph, args.steps, args.warmup)
-        step_ms, n_steps = timed(step_graph, args.steps, args.warmup)
-    t0 = time.perf_counter()
+        attn_ms, _, attn_pct = timed(attn_graph, args.steps, args.warmup)
+        step_ms, n_steps, step_pct = timed(step_graph, args.steps, args.warmup)
+        components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
+        ceiling = streaming_read_ceiling(dev, stream)
     torch.cuda.synchronize()
 
     achieved = attn_b / (attn_ms * 1e-3) / 1e9
@@ -276,7 +351,11 @@ def main():
                                      "null if the kernel changed since the counters were taken",
                      "algorithmic_bytes_per_launch": int(attn_b),
                      "kernel": "decode_kernel: one kvq_decode_attn call (one workgroup per stream here, so no merge kernel)",
-                     "us_per_launch": round(attn_ms * 1e3, 2)},
+                     "us_per_launch": round(attn_ms * 1e3, 2),
+                     "us_per_launch_p10_p50_p90": [round(x * 1e3, 2) for x in attn_pct],
+                     "streaming_read_ceiling_GBs": ceiling},
+        "us_per_step_p10_p50_p90": [round(x * 1e3, 2) for x in step_pct],
+        "components_us": components,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
