@@ -22,6 +22,7 @@ __all__ = [
     "kvq_decode_append",
     "kvq_reorder_windows", "kvq_decode_attn_workspace", "kvq_decode_attn",
     "KiviCacheDesc", "kvq_kivi_step_workspace", "kvq_kivi_step",
+    "kvq_window_thresholds", "kvq_window_search_workspace", "kvq_window_search",
 ]
 
 KVQ_KEYS = 0
@@ -121,6 +122,14 @@ def _load():
     lib.kvq_kivi_step_workspace.restype = i32
     lib.kvq_kivi_step_workspace.argtypes = [ctypes.POINTER(KiviCacheDesc), i32, i32,
                                             ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_window_thresholds.restype = i32
+    lib.kvq_window_thresholds.argtypes = [ctypes.c_float, ctypes.c_float, ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_float)]
+    lib.kvq_window_search_workspace.restype = i32
+    lib.kvq_window_search_workspace.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_window_search.restype = i32
+    lib.kvq_window_search.argtypes = [i32, i32, i32, i32, vp, i64, i64, vp, i64, i64, i32,
+                                      ctypes.c_float, ctypes.c_float, i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kvq_kivi_step.restype = i32
     lib.kvq_kivi_step.argtypes = [ctypes.POINTER(KiviCacheDesc), i32, i32, ctypes.c_float,
                                   vp, i64, vp, i64, vp, vp, vp, ctypes.c_size_t, vp]
@@ -252,3 +261,28 @@ def kvq_kivi_step(cache: KiviCacheDesc, batch, n_q_heads, sm_scale, k_new, k_new
                                  _dev(k_new), k_new_stride, _dev(v_new), v_new_stride, _dev(q),
                                  _dev(out), _dev(workspace), int(workspace_bytes), _stream(stream)),
            "kvq_kivi_step")
+
+
+def kvq_window_thresholds(layer_similarity: float, alpha: float):
+    """(t_low, t_high) of a layer, WindowQuant Eq. 10-11."""
+    lo, hi = ctypes.c_float(0), ctypes.c_float(0)
+    _check(_load().kvq_window_thresholds(float(layer_similarity), float(alpha), ctypes.byref(lo),
+                                         ctypes.byref(hi)), "kvq_window_thresholds")
+    return float(lo.value), float(hi.value)
+
+
+def kvq_window_search_workspace(batch, n_text, n_visual, dim, window_tokens) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().kvq_window_search_workspace(batch, n_text, n_visual, dim, window_tokens, ctypes.byref(n)),
+           "kvq_window_search_workspace")
+    return int(n.value)
+
+
+def kvq_window_search(batch, n_text, n_visual, dim, text, text_batch_stride, text_row_stride, visual,
+                      visual_batch_stride, visual_row_stride, window_tokens, t_low, t_high,
+                      first_window_fp16, scores, win_bits, workspace, workspace_bytes, stream=None):
+    _check(_load().kvq_window_search(batch, n_text, n_visual, dim, _dev(text), text_batch_stride,
+                                     text_row_stride, _dev(visual), visual_batch_stride, visual_row_stride,
+                                     window_tokens, float(t_low), float(t_high), int(first_window_fp16),
+                                     _dev(scores), _dev(win_bits), _dev(workspace), int(workspace_bytes),
+                                     _stream(stream)), "kvq_window_search")

@@ -531,3 +531,85 @@ kvq_status kvq_kivi_step(kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// WindowQuant window-level search.
+namespace {
+
+kvq_status search_shape(int32_t batch, int32_t n_text, int32_t n_visual, int32_t dim,
+                        int32_t window_tokens, int64_t* n_windows, int64_t* n_chunks) {
+  if (batch < 1 || n_text < 1 || window_tokens < 1 || n_visual < window_tokens) return KVQ_EINVAL;
+  if (dim < 8 || dim % 8 != 0) return KVQ_EINVAL;
+  if (dim > 4096 || batch > 65535) return KVQ_EUNSUPPORTED;
+  *n_windows = n_visual / window_tokens;
+  *n_chunks = kvq::search_chunks(n_text, int32_t(*n_windows), window_tokens);
+  if (*n_chunks > (int64_t(1) << 30)) return KVQ_EUNSUPPORTED;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_window_thresholds(float layer_similarity, float alpha, float* t_low, float* t_high) {
+  if (!t_low || !t_high || !std::isfinite(layer_similarity) || !std::isfinite(alpha) || alpha == 0.f)
+    return KVQ_EINVAL;
+  const double s = layer_similarity, a = alpha;
+  *t_low = float(std::expm1(a * s) / std::expm1(a));
+  *t_high = float(std::expm1(-a * s) / std::expm1(-a));
+  return KVQ_OK;
+}
+
+kvq_status kvq_window_search_workspace(int32_t batch, int32_t n_text, int32_t n_visual, int32_t dim,
+                                       int32_t window_tokens, size_t* bytes) {
+  if (!bytes) return KVQ_EINVAL;
+  int64_t w, c;
+  const kvq_status st = search_shape(batch, n_text, n_visual, dim, window_tokens, &w, &c);
+  if (st != KVQ_OK) return st;
+  *bytes = size_t(batch) * size_t(c) * size_t(dim) * sizeof(float);
+  return KVQ_OK;
+}
+
+kvq_status kvq_window_search(int32_t batch, int32_t n_text, int32_t n_visual, int32_t dim,
+                             const void* text, int64_t text_batch_stride, int64_t text_row_stride,
+                             const void* visual, int64_t visual_batch_stride, int64_t visual_row_stride,
+                             int32_t window_tokens, float t_low, float t_high, int32_t first_window_fp16,
+                             float* scores, uint8_t* win_bits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  int64_t n_windows, n_chunks;
+  kvq_status st = search_shape(batch, n_text, n_visual, dim, window_tokens, &n_windows, &n_chunks);
+  if (st != KVQ_OK) return st;
+  if (!text || !visual || !win_bits || !std::isfinite(t_low) || !std::isfinite(t_high)) return KVQ_EINVAL;
+  if (text_row_stride < dim || visual_row_stride < dim || text_batch_stride < 0 || visual_batch_stride < 0)
+    return KVQ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(text) & 15) || (reinterpret_cast<uintptr_t>(visual) & 15) ||
+      (reinterpret_cast<uintptr_t>(scores) & 3) || (reinterpret_cast<uintptr_t>(workspace) & 15) ||
+      (text_row_stride & 7) || (visual_row_stride & 7) || (text_batch_stride & 7) ||
+      (visual_batch_stride & 7))
+    return KVQ_EALIGN;
+  const size_t need = size_t(batch) * size_t(n_chunks) * size_t(dim) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return KVQ_EWORKSPACE;
+  kvq::SearchParams p{};
+  p.text = static_cast<const uint16_t*>(text);
+  p.visual = static_cast<const uint16_t*>(visual);
+  p.text_batch_stride = text_batch_stride;
+  p.text_row_stride = text_row_stride;
+  p.visual_batch_stride = visual_batch_stride;
+  p.visual_row_stride = visual_row_stride;
+  p.ws = static_cast<float*>(workspace);
+  p.scores = scores;
+  p.win_bits = win_bits;
+  p.B = batch;
+  p.N = n_text;
+  p.D = dim;
+  p.S = window_tokens;
+  p.n_windows = int32_t(n_windows);
+  p.chunks_per_window = (window_tokens + 63) / 64;
+  p.n_chunks = int32_t(n_chunks);
+  p.first_window_fp16 = first_window_fp16 ? 1 : 0;
+  p.t_low = t_low;
+  p.t_high = t_high;
+  return from_hip(kvq::launch_search(p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

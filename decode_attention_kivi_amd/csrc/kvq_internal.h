@@ -196,6 +196,20 @@ hipError_t launch_copy_rows(const uint16_t* src, int64_t src_stream_stride,
                             uint8_t* dst, int64_t dst_stream_bytes, int32_t dst_row0,
                             int32_t n_streams, int32_t D, int32_t n_rows, hipStream_t s);
 
+// WindowQuant window-level search (search.hip).
+struct SearchParams {
+  const uint16_t* text;      // fp16 [B][N][D] rows (strides in elements)
+  const uint16_t* visual;    // fp16 [B][M][D]
+  int64_t text_batch_stride, text_row_stride, visual_batch_stride, visual_row_stride;
+  float* ws;                 // [B][n_chunks][D] chunk sums of unit rows
+  float* scores;             // NULL or [B][n_windows]
+  uint8_t* win_bits;         // [n_windows]
+  int32_t B, N, D, S, n_windows, chunks_per_window, n_chunks, first_window_fp16;
+  float t_low, t_high;
+};
+int64_t search_chunks(int32_t n_text, int32_t n_windows, int32_t S);
+hipError_t launch_search(const SearchParams& p, hipStream_t s);
+
 hipError_t launch_reorder(const uint8_t* win_bits, int32_t n_windows, int32_t S,
                           int32_t G, int32_t D, int32_t* perm, void* segs,
                           int32_t* n_segs, int32_t* row_gather, hipStream_t s);

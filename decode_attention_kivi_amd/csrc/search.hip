@@ -1,0 +1,183 @@
+// WindowQuant window-level quantization search (ACM TACO, Sec. 3.2): each
+// visual window's score is the mean cosine similarity between the prompt's
+// text tokens and the window's visual tokens (Eq. 8); the score picks fp16,
+// int4 or int2 against the layer's two thresholds (Sec. 3.2.1, Eq. 10-11),
+// the first window stays fp16 (Sec. 3.2.2), and a batch shares one
+// configuration, each window taking the width most of its requests chose
+// (Sec. 3.2.3).
+//
+// The mean over all N*S pairs of unit vectors is the dot product of the two
+// sums of unit vectors divided by N*S, so the whole search is one streaming
+// pass over the tokens:
+//   search_sums_kernel   one workgroup per (chunk of <= 64 tokens of one
+//                        window or of the prompt, batch row): every token
+//                        row is normalized by one wave (a DPP sum of squares)
+//                        and added into the wave's fp32 sum; the four waves'
+//                        sums meet in LDS and the chunk sum goes to the
+//                        workspace;
+//   search_vote_kernel   one workgroup per window: the chunk sums of the
+//                        window and of the prompt, their dot product per
+//                        batch row, the choice per row and the vote.
+// Summation orders are fixed, so the results are deterministic.
+
+#include "kvq_internal.h"
+#include "kvq_device.h"
+#include "../../include/kvq.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kChunk = 64;          // tokens per workgroup of the sums kernel
+constexpr int kSearchThreads = 256;
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ uint4 load16(Rsrc r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// NSL: 16-byte slots (8 channels) per lane, D <= 512 * NSL.
+template <int NSL>
+__global__ void __launch_bounds__(kSearchThreads) search_sums_kernel(const SearchParams P) {
+  extern __shared__ __align__(16) float red[];     // [4][D]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int x = blockIdx.x, b = blockIdx.y;
+  const int D = P.D;
+  const int vis_chunks = P.n_windows * P.chunks_per_window;
+  // this chunk's token rows
+  const uint16_t* base;
+  int64_t row_stride;
+  int t0, t1;
+  if (x < vis_chunks) {
+    const int w = x / P.chunks_per_window, c = x % P.chunks_per_window;
+    base = P.visual + int64_t(b) * P.visual_batch_stride;
+    row_stride = P.visual_row_stride;
+    t0 = w * P.S + c * kChunk;
+    t1 = min(t0 + kChunk, (w + 1) * P.S);
+  } else {
+    base = P.text + int64_t(b) * P.text_batch_stride;
+    row_stride = P.text_row_stride;
+    t0 = (x - vis_chunks) * kChunk;
+    t1 = min(t0 + kChunk, P.N);
+  }
+  float acc[NSL][8];
+#pragma unroll
+  for (int i = 0; i < NSL; ++i)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[i][k] = 0.f;
+
+  const uint32_t row_bytes = uint32_t(D) * 2;
+  for (int t = t0 + wave; t < t1; t += 4) {
+    // the row through a range-checked resource: slots past D read as zero
+    const Rsrc r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + int64_t(t) * row_stride),
+                                                     short(0), int(row_bytes), 0x00020000);
+    uint4 v[NSL];
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) v[i] = load16(r, uint32_t(lane + 64 * i) * 16);
+    float f[NSL][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) {
+      const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f[i][2 * k] = h2f(w4[k] & 0xffffu);
+        f[i][2 * k + 1] = h2f(w4[k] >> 16);
+        ss = __builtin_fmaf(f[i][2 * k], f[i][2 * k], ss);
+        ss = __builtin_fmaf(f[i][2 * k + 1], f[i][2 * k + 1], ss);
+      }
+    }
+    ss = wave_sum64(ss);
+    // a zero row has no direction: it adds nothing
+    const float inv = ss > 0.f ? 1.f / __builtin_sqrtf(ss) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NSL; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[i][k] = __builtin_fmaf(f[i][k], inv, acc[i][k]);
+  }
+  // the four waves' sums, then the chunk sum in a fixed order
+#pragma unroll
+  for (int i = 0; i < NSL; ++i) {
+    const int c0 = (lane + 64 * i) * 8;
+    if (c0 < D) {
+      float4* dst = reinterpret_cast<float4*>(red + wave * D + c0);
+      dst[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+      dst[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+    }
+  }
+  __syncthreads();
+  float* out = P.ws + (int64_t(b) * P.n_chunks + x) * D;
+  for (int c = threadIdx.x; c < D; c += kSearchThreads)
+    out[c] = ((red[c] + red[D + c]) + red[2 * D + c]) + red[3 * D + c];
+}
+
+__device__ __forceinline__ float block_sum(float x, float* sh) {
+  x = wave_sum64(x);
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();                         // sh is reused across calls
+  if ((threadIdx.x & 63) == 0) sh[wave] = x;
+  __syncthreads();
+  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
+}
+
+__global__ void __launch_bounds__(kSearchThreads) search_vote_kernel(const SearchParams P) {
+  __shared__ float sh[4];
+  __shared__ int counts[3];                // fp16, int4, int2
+  const int w = blockIdx.x;
+  const int D = P.D;
+  const int vis_chunks = P.n_windows * P.chunks_per_window;
+  const int text_chunks = P.n_chunks - vis_chunks;
+  if (threadIdx.x < 3) counts[threadIdx.x] = 0;
+  const float inv_pairs = 1.f / (float(P.S) * float(P.N));
+  for (int b = 0; b < P.B; ++b) {
+    const float* part = P.ws + int64_t(b) * P.n_chunks * D;
+    float dot = 0.f;
+    for (int c = threadIdx.x; c < D; c += kSearchThreads) {
+      float ws = 0.f, ts = 0.f;
+      for (int k = 0; k < P.chunks_per_window; ++k) ws += part[int64_t(w * P.chunks_per_window + k) * D + c];
+      for (int k = 0; k < text_chunks; ++k) ts += part[int64_t(vis_chunks + k) * D + c];
+      dot = __builtin_fmaf(ws, ts, dot);
+    }
+    const float score = block_sum(dot, sh) * inv_pairs;
+    if (threadIdx.x == 0) {
+      if (P.scores) P.scores[int64_t(b) * P.n_windows + w] = score;
+      const int choice = score > P.t_high ? 0 : (score < P.t_low ? 2 : 1);
+      counts[choice] += 1;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    // the most frequent width; ties to the wider one
+    int best = 0;
+    for (int k = 1; k < 3; ++k)
+      if (counts[k] > counts[best]) best = k;
+    const uint8_t bits = (w == 0 && P.first_window_fp16) ? 16 : uint8_t(best == 0 ? 16 : best == 1 ? 4 : 2);
+    P.win_bits[w] = bits;
+  }
+}
+
+}  // namespace
+
+int64_t search_chunks(int32_t n_text, int32_t n_windows, int32_t S) {
+  return int64_t(n_windows) * ((S + kChunk - 1) / kChunk) + (n_text + kChunk - 1) / kChunk;
+}
+
+hipError_t launch_search(const SearchParams& p, hipStream_t s) {
+  const int nsl = (p.D + 511) / 512;
+  const size_t lds = size_t(4) * p.D * sizeof(float);
+  const dim3 grid(unsigned(p.n_chunks), unsigned(p.B));
+  switch (nsl <= 1 ? 1 : nsl <= 2 ? 2 : nsl <= 4 ? 4 : 8) {
+    case 1: hipLaunchKernelGGL(search_sums_kernel<1>, grid, dim3(kSearchThreads), lds, s, p); break;
+    case 2: hipLaunchKernelGGL(search_sums_kernel<2>, grid, dim3(kSearchThreads), lds, s, p); break;
+    case 4: hipLaunchKernelGGL(search_sums_kernel<4>, grid, dim3(kSearchThreads), lds, s, p); break;
+    default: hipLaunchKernelGGL(search_sums_kernel<8>, grid, dim3(kSearchThreads), lds, s, p); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(search_vote_kernel, dim3(unsigned(p.n_windows)), dim3(kSearchThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

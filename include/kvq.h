@@ -279,6 +279,53 @@ kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes)
 kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream);
 
 /*
+ * kvq_window_thresholds -- the two score thresholds of a layer (WindowQuant
+ * Sec. 3.2.3, Eq. 10 and 11): with s the layer's hidden-state similarity
+ * (Eq. 9) and alpha the hyper-parameter,
+ *   t_low  = (exp(alpha * s) - 1) / (exp(alpha) - 1),
+ *   t_high = (exp(-alpha * s) - 1) / (exp(-alpha) - 1).
+ * Host arithmetic in double, rounded to float.  alpha must be finite and
+ * non-zero, s finite; KVQ_EINVAL otherwise.
+ */
+kvq_status kvq_window_thresholds(float layer_similarity, float alpha, float* t_low,
+                                 float* t_high);
+
+/*
+ * kvq_window_search -- WindowQuant window-level quantization search (Sec.
+ * 3.2) on the device: for batch row b and visual window i (visual tokens
+ * i*S .. i*S+S-1; the floor(n_visual/S) full windows, trailing tokens are no
+ * window), the score is the mean cosine similarity over all pairs of a text
+ * token and a token of the window (Eq. 8); the row's choice is fp16 (16) for
+ * score > t_high, int2 (2) for score < t_low, int4 (4) otherwise (Sec.
+ * 3.2.1); the window's width is the choice most rows made, ties to the wider
+ * width (Sec. 3.2.3); with first_window_fp16, window 0 is 16 regardless
+ * (Sec. 3.2.2).  A token row of zero length counts as cosine 0 with every
+ * other token.  Scores are computed in fp32 (the mean of unit vectors' dot
+ * products as the dot product of their sums).
+ *   text     fp16 rows, row j of batch row b at element
+ *            b*text_batch_stride + j*text_row_stride; likewise visual.
+ *   dim      D, a multiple of 8, 8..4096.  n_text, window_tokens >= 1;
+ *            n_visual >= window_tokens.
+ *   scores   NULL or device float [batch][n_visual / window_tokens].
+ *   win_bits device uint8 [n_visual / window_tokens] (input of
+ *            kvq_reorder_windows).
+ *   workspace  device scratch of kvq_window_search_workspace bytes (chunk
+ *            sums; no initialization needed; calls sharing one must not
+ *            overlap).
+ * Pointers 16-byte aligned (scores 4), strides multiples of 8 elements and
+ * row strides >= dim.
+ */
+kvq_status kvq_window_search_workspace(int32_t batch, int32_t n_text, int32_t n_visual,
+                                       int32_t dim, int32_t window_tokens, size_t* bytes);
+kvq_status kvq_window_search(int32_t batch, int32_t n_text, int32_t n_visual, int32_t dim,
+                             const void* text, int64_t text_batch_stride,
+                             int64_t text_row_stride, const void* visual,
+                             int64_t visual_batch_stride, int64_t visual_row_stride,
+                             int32_t window_tokens, float t_low, float t_high,
+                             int32_t first_window_fp16, float* scores, uint8_t* win_bits,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * A KIVI cache of n_streams = B * Hkv streams in the state that KIVI's
  * Algorithm 1 keeps between decode steps: one key run and one value run of
  * b-bit codes (code and meta arenas with code_off = meta_off = 0, room for

@@ -190,3 +190,39 @@ def test_kivi_step_rejects_before_any_launch_and_keeps_the_state():
             kvq.kvq_kivi_step(c, **args)
         assert e.value.status == code
         assert (c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start) == (256, 5, 197, 64, 3)
+
+
+def test_window_thresholds_host_values():
+    lo, hi = kvq.kvq_window_thresholds(0.5, 2.0)
+    assert abs(lo - 0.2689414213699951) < 1e-7 and abs(hi - 0.7310585786300049) < 1e-7
+    for bad in [(0.5, 0.0), (float("nan"), 2.0), (0.5, float("inf"))]:
+        with pytest.raises(KvqError) as e:
+            kvq.kvq_window_thresholds(*bad)
+        assert e.value.status == EINVAL
+
+
+def test_window_search_workspace_is_chunk_sums():
+    # 4 windows of 100 tokens -> 2 chunks each; 70 text tokens -> 2 chunks
+    assert kvq.kvq_window_search_workspace(3, 70, 405, 64, 100) == 3 * (4 * 2 + 2) * 64 * 4
+
+
+def _search(**kw):
+    base = dict(batch=2, n_text=16, n_visual=512, dim=128, text=A, text_batch_stride=16 * 128,
+                text_row_stride=128, visual=A, visual_batch_stride=512 * 128, visual_row_stride=128,
+                window_tokens=64, t_low=0.3, t_high=0.7, first_window_fp16=1, scores=None,
+                win_bits=A, workspace=A, workspace_bytes=1 << 30, stream=0)
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dim=12), EINVAL), (dict(dim=8192), EUNSUP), (dict(n_visual=63), EINVAL),
+    (dict(n_text=0), EINVAL), (dict(batch=0), EINVAL), (dict(window_tokens=0), EINVAL),
+    (dict(text_row_stride=120), EINVAL), (dict(visual_row_stride=132), EALIGN),
+    (dict(text=A + 8), EALIGN), (dict(scores=A + 2), EALIGN), (dict(win_bits=None), EINVAL),
+    (dict(t_low=float("nan")), EINVAL), (dict(workspace_bytes=100), EWS), (dict(workspace=None), EWS),
+])
+def test_window_search_rejects(kw, code):
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_window_search(**_search(**kw))
+    assert e.value.status == code

@@ -47,7 +47,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "unit_kv", "queries", "outlier_channels",
-    "full_kv", "window_bits", "sample_units",
+    "full_kv", "window_bits", "sample_units", "search_tokens",
 ]
 
 
@@ -208,3 +208,29 @@ def sample_units(w: Workload, n: int, seed: int = 1234):
         idx.update(int(i) for i in rng.choice(total, size=min(n, total) - len(idx) + 2, replace=False))
     idx = sorted(idx)[:max(n, 2)]
     return [(i // w.n_kv_heads, i % w.n_kv_heads) for i in idx]
+
+
+def search_tokens(batch: int, n_text: int, n_visual: int, dim: int, window_tokens: int,
+                  seed: int = 0, prompt: float = 2.0, relevance_max: float = 3.0):
+    """Synthetic encoder outputs for the window-level search, fp16.
+
+    Stand-ins for the text-encoder tokens of a prompt and the vision-encoder
+    tokens of a video (the pages use LLaVA-OneVision / Qwen2-VL features of
+    real videos; none are available here).  A prompt direction u ~ N(0, I)
+    (shared by the batch) is drawn from ``default_rng([seed, 5])``; text token
+    = prompt * sqrt(D) * u/|u| + N(0, I); window i gets a relevance
+    c_i ~ U(0, relevance_max) (shared by the batch) and each of its tokens is
+    (c_i + N(0, 0.1)) * sqrt(D) * u/|u| + N(0, I), so the windows' scores
+    spread over (0, 1) and the batch rows mostly agree.  Rows past the last
+    full window get relevance 0.  Returns (text [B][N][D], visual [B][M][D]).
+    """
+    rng = np.random.default_rng([seed, 5])
+    u = rng.standard_normal(dim)
+    u = u / np.linalg.norm(u) * np.sqrt(dim)
+    n_win = n_visual // window_tokens
+    rel = np.zeros(n_visual)
+    rel[:n_win * window_tokens] = np.repeat(rng.uniform(0, relevance_max, n_win), window_tokens)
+    text = prompt * u + rng.standard_normal((batch, n_text, dim))
+    jitter = rng.normal(0.0, 0.1, size=(batch, n_visual, 1))
+    visual = (rel[None, :, None] + jitter) * u + rng.standard_normal((batch, n_visual, dim))
+    return text.astype(np.float16), visual.astype(np.float16)
