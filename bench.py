@@ -168,6 +168,42 @@ def component_times(w, cache, k_new, v_new, q, out, stream, reps: int = 50):
     return res
 
 
+def window_search_rate(dev, stream, reps: int = 20):
+    """The WindowQuant window-level search (kvq_window_search) at the size
+    of the pages' video workloads: one request, a 64-token prompt and 128
+    windows of 256 visual tokens, encoder dim 3584.  It reads every token
+    once: (64 + 32768) * 3584 * 2 bytes."""
+    import torch
+    import numpy as np
+    import decode_attention_kivi_amd as kvq
+    B, N, W, S, D = 1, 64, 128, 256, 3584
+    M = W * S
+    g = torch.Generator(device=dev).manual_seed(0)
+    text = torch.randn(B, N, D, generator=g, device=dev).half()
+    vis = torch.randn(B, M, D, generator=g, device=dev).half()
+    bits = torch.empty(W, dtype=torch.uint8, device=dev)
+    nbytes = kvq.kvq_window_search_workspace(B, N, M, D, S)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    t_low, t_high = kvq.kvq_window_thresholds(0.5, 2.0)
+
+    def call():
+        kvq.kvq_window_search(B, N, M, D, text, N * D, D, vis, M * D, D, S, t_low, t_high, 1, None,
+                              bits, ws, nbytes, stream)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    read = (N + M) * D * 2 * B
+    return {"config": "B1 prompt 64 tokens, 128 windows x 256 tokens, dim 3584", "us_per_call": round(us, 2),
+            "bytes_read": read, "GBs": round(read / (us * 1e-6) / 1e9, 1)}
+
+
 def streaming_read_ceiling(dev, stream, gib: float = 1.0, reps: int = 20) -> float:
     """GB/s of a plain streaming read on this GPU: torch's sum over a 1 GiB
     buffer (well past the 256 MB Infinity Cache), the practical ceiling the
@@ -326,6 +362,7 @@ def main():
         step_ms, n_steps, step_pct = timed(step_graph, args.steps, args.warmup)
         components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
         ceiling = streaming_read_ceiling(dev, stream)
+        search_rate = window_search_rate(dev, stream)
     torch.cuda.synchronize()
 
     achieved = attn_b / (attn_ms * 1e-3) / 1e9
@@ -356,6 +393,7 @@ def main():
                      "streaming_read_ceiling_GBs": ceiling},
         "us_per_step_p10_p50_p90": [round(x * 1e3, 2) for x in step_pct],
         "components_us": components,
+        "window_search": search_rate,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)

@@ -604,7 +604,7 @@ kvq_status kvq_window_search(int32_t batch, int32_t n_text, int32_t n_visual, in
   p.D = dim;
   p.S = window_tokens;
   p.n_windows = int32_t(n_windows);
-  p.chunks_per_window = (window_tokens + 63) / 64;
+  p.chunks_per_window = kvq::search_chunks_per_window(window_tokens);
   p.n_chunks = int32_t(n_chunks);
   p.first_window_fp16 = first_window_fp16 ? 1 : 0;
   p.t_low = t_low;

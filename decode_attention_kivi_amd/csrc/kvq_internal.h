@@ -207,6 +207,7 @@ struct SearchParams {
   int32_t B, N, D, S, n_windows, chunks_per_window, n_chunks, first_window_fp16;
   float t_low, t_high;
 };
+int32_t search_chunks_per_window(int32_t S);
 int64_t search_chunks(int32_t n_text, int32_t n_windows, int32_t S);
 hipError_t launch_search(const SearchParams& p, hipStream_t s);
 

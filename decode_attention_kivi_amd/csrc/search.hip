@@ -9,7 +9,7 @@
 // The mean over all N*S pairs of unit vectors is the dot product of the two
 // sums of unit vectors divided by N*S, so the whole search is one streaming
 // pass over the tokens:
-//   search_sums_kernel   one workgroup per (chunk of <= 64 tokens of one
+//   search_sums_kernel   one workgroup per (chunk of <= kChunk tokens of one
 //                        window or of the prompt, batch row): every token
 //                        row is normalized by one wave (a DPP sum of squares)
 //                        and added into the wave's fp32 sum; the four waves'
@@ -69,33 +69,45 @@ __global__ void __launch_bounds__(kSearchThreads) search_sums_kernel(const Searc
     for (int k = 0; k < 8; ++k) acc[i][k] = 0.f;
 
   const uint32_t row_bytes = uint32_t(D) * 2;
-  for (int t = t0 + wave; t < t1; t += 4) {
-    // the row through a range-checked resource: slots past D read as zero
-    const Rsrc r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + int64_t(t) * row_stride),
-                                                     short(0), int(row_bytes), 0x00020000);
-    uint4 v[NSL];
+  // one row per wave at a time, the next row's loads in flight while the
+  // current one is summed; rows go through range-checked resources (slots
+  // past D and rows past t1 read as zero and touch no memory)
+  auto load_row = [&](int t, uint4 (&v)[NSL]) {
+    const int tt = t < t1 ? t : t0;      // a row of the chunk; its loads are discarded
+    const Rsrc r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base + int64_t(tt) * row_stride),
+                                                     short(0), int(t < t1 ? row_bytes : 0u), 0x00020000);
 #pragma unroll
     for (int i = 0; i < NSL; ++i) v[i] = load16(r, uint32_t(lane + 64 * i) * 16);
-    float f[NSL][8];
+  };
+  uint4 cur[NSL], nxt[NSL];
+  load_row(t0 + wave, cur);
+  for (int t = t0 + wave; t < t1; t += 4) {
+    load_row(t + 4, nxt);
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NSL; ++i) {
-      const uint32_t w4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      const uint32_t w4[4] = {cur[i].x, cur[i].y, cur[i].z, cur[i].w};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        f[i][2 * k] = h2f(w4[k] & 0xffffu);
-        f[i][2 * k + 1] = h2f(w4[k] >> 16);
-        ss = __builtin_fmaf(f[i][2 * k], f[i][2 * k], ss);
-        ss = __builtin_fmaf(f[i][2 * k + 1], f[i][2 * k + 1], ss);
+        const float a = h2f(w4[k] & 0xffffu), c = h2f(w4[k] >> 16);
+        ss = __builtin_fmaf(a, a, ss);
+        ss = __builtin_fmaf(c, c, ss);
       }
     }
     ss = wave_sum64(ss);
     // a zero row has no direction: it adds nothing
     const float inv = ss > 0.f ? 1.f / __builtin_sqrtf(ss) : 0.f;
 #pragma unroll
-    for (int i = 0; i < NSL; ++i)
+    for (int i = 0; i < NSL; ++i) {
+      const uint32_t w4[4] = {cur[i].x, cur[i].y, cur[i].z, cur[i].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[i][k] = __builtin_fmaf(f[i][k], inv, acc[i][k]);
+      for (int k = 0; k < 4; ++k) {
+        acc[i][2 * k] = __builtin_fmaf(h2f(w4[k] & 0xffffu), inv, acc[i][2 * k]);
+        acc[i][2 * k + 1] = __builtin_fmaf(h2f(w4[k] >> 16), inv, acc[i][2 * k + 1]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NSL; ++i) cur[i] = nxt[i];
   }
   // the four waves' sums, then the chunk sum in a fixed order
 #pragma unroll
@@ -131,14 +143,30 @@ __global__ void __launch_bounds__(kSearchThreads) search_vote_kernel(const Searc
   const int text_chunks = P.n_chunks - vis_chunks;
   if (threadIdx.x < 3) counts[threadIdx.x] = 0;
   const float inv_pairs = 1.f / (float(P.S) * float(P.N));
+  const int D4 = D / 4;
   for (int b = 0; b < P.B; ++b) {
-    const float* part = P.ws + int64_t(b) * P.n_chunks * D;
+    const float4* part = reinterpret_cast<const float4*>(P.ws + int64_t(b) * P.n_chunks * D);
+    const float4* wrow = part + int64_t(w) * P.chunks_per_window * D4;
+    const float4* trow = part + int64_t(vis_chunks) * D4;
     float dot = 0.f;
-    for (int c = threadIdx.x; c < D; c += kSearchThreads) {
-      float ws = 0.f, ts = 0.f;
-      for (int k = 0; k < P.chunks_per_window; ++k) ws += part[int64_t(w * P.chunks_per_window + k) * D + c];
-      for (int k = 0; k < text_chunks; ++k) ts += part[int64_t(vis_chunks + k) * D + c];
-      dot = __builtin_fmaf(ws, ts, dot);
+    // up to four channel quads per thread (D <= 4096), all loads issued together
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = threadIdx.x + j * kSearchThreads;
+      if (c >= D4) continue;
+      float4 ws = make_float4(0.f, 0.f, 0.f, 0.f), ts = ws;
+      for (int k = 0; k < P.chunks_per_window; ++k) {
+        const float4 x = wrow[int64_t(k) * D4 + c];
+        ws.x += x.x; ws.y += x.y; ws.z += x.z; ws.w += x.w;
+      }
+      for (int k = 0; k < text_chunks; ++k) {
+        const float4 x = trow[int64_t(k) * D4 + c];
+        ts.x += x.x; ts.y += x.y; ts.z += x.z; ts.w += x.w;
+      }
+      dot = __builtin_fmaf(ws.x, ts.x, dot);
+      dot = __builtin_fmaf(ws.y, ts.y, dot);
+      dot = __builtin_fmaf(ws.z, ts.z, dot);
+      dot = __builtin_fmaf(ws.w, ts.w, dot);
     }
     const float score = block_sum(dot, sh) * inv_pairs;
     if (threadIdx.x == 0) {
@@ -160,8 +188,10 @@ __global__ void __launch_bounds__(kSearchThreads) search_vote_kernel(const Searc
 
 }  // namespace
 
+int32_t search_chunks_per_window(int32_t S) { return (S + kChunk - 1) / kChunk; }
+
 int64_t search_chunks(int32_t n_text, int32_t n_windows, int32_t S) {
-  return int64_t(n_windows) * ((S + kChunk - 1) / kChunk) + (n_text + kChunk - 1) / kChunk;
+  return int64_t(n_windows) * search_chunks_per_window(S) + (n_text + kChunk - 1) / kChunk;
 }
 
 hipError_t launch_search(const SearchParams& p, hipStream_t s) {
