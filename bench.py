@@ -4,7 +4,9 @@ Workload (the default): batch 16, 32 heads (MHA), d_h 128, 4096 cached tokens,
 G 32, R 128, int2; the step appends token 4096 and attends 4097 tokens.  A
 step is the whole path: the new key/value rows go into the fp16 residuals,
 the value that leaves the 128-token window is quantized and appended, and
-decode attention runs over [quantized | residual] keys and values.
+decode attention runs over [quantized | residual] keys and values -- one
+kvq_kivi_step call, which at this shape is one launch (the append runs in
+the attention kernel's last wave of each stream).
 
 Timing: the cache is built (prefill, on the GPU) in several independent
 copies whose total exceeds twice the 256 MB Infinity Cache, and each timed
@@ -304,10 +306,18 @@ def main():
         for c, s in zip(caches, saved):
             c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start = s
 
-    # prepare workspaces outside capture
+    # a decode step is one kvq_kivi_step call (append + attention; fused into
+    # one launch at this shape) unless a split size is forced, then the two
+    # separate calls; workspaces are prepared outside capture
+    def one_step(c, o):
+        if args.split_tokens:
+            c.append(k_new, v_new)
+            c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+        else:
+            c.step(k_new, v_new, q, w.sm_scale, out=o)
     for c, o in zip(caches, outs):
-        c.append(k_new, v_new)
-        c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+        one_step(c, o)
+    step_launches = caches[0].last_launches if not args.split_tokens else None
     restore()
     torch.cuda.synchronize()
 
@@ -319,8 +329,7 @@ def main():
             for _ in range(args.rounds):
                 restore()
                 for c, o in zip(caches, outs):
-                    c.append(k_new, v_new)
-                    c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+                    one_step(c, o)
         restore()
         for c in caches:           # attention-only graph on the post-step state
             c.append(k_new, v_new)
@@ -380,6 +389,7 @@ def main():
                    "attended_tokens": w.n_tokens, "group": w.group, "residual": w.residual,
                    "bits": w.bits, "cache_copies": len(caches), "steps_per_graph": n_copies,
                    "cache_state_nKq_rK_nVq_rV": list(attn_probe),
+                   "launches_per_step": step_launches,
                    "algorithmic_bytes_step": int(total_b), "algorithmic_bytes_attention": int(attn_b)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -84,7 +84,7 @@ class KiviCacheDesc(ctypes.Structure):
         ("k_res", ctypes.c_void_p), ("k_res_stride", ctypes.c_int64),
         ("v_res", ctypes.c_void_p), ("v_res_stride", ctypes.c_int64),
         ("n_kq", ctypes.c_int32), ("r_k", ctypes.c_int32), ("n_vq", ctypes.c_int32),
-        ("r_v", ctypes.c_int32), ("v_start", ctypes.c_int32),
+        ("r_v", ctypes.c_int32), ("v_start", ctypes.c_int32), ("last_launches", ctypes.c_int32),
     ]
 
 

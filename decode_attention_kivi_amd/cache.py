@@ -78,6 +78,7 @@ class KiviCache:
         self.v_win_rows = 2 * residual + 2
         self.v_res = torch.zeros(self.n_streams, self.v_win_rows, d_h, **f16)
         self.n_kq = self.r_k = self.n_vq = self.r_v = self.v_start = 0
+        self.last_launches = 0
         self._ws = None
 
     # -- state ---------------------------------------------------------------
@@ -191,7 +192,7 @@ class KiviCache:
             self.k_codes.data_ptr(), self.k_codes.stride(0), self.k_meta.data_ptr(), self.k_meta.stride(0),
             self.v_codes.data_ptr(), self.v_codes.stride(0), self.v_meta.data_ptr(), self.v_meta.stride(0),
             self.k_res.data_ptr(), self.k_res.stride(0), self.v_res.data_ptr(), self.v_res.stride(0),
-            self.n_kq, self.r_k, self.n_vq, self.r_v, self.v_start)
+            self.n_kq, self.r_k, self.n_vq, self.r_v, self.v_start, 0)
 
     def step(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, sm_scale: float,
              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -212,6 +213,7 @@ class KiviCache:
         kvq_kivi_step(c, B, Hq, sm_scale, k_new, ss, v_new, ss2, q, out, ws,
                       ws.numel() if ws is not None else 0, stream)
         self.n_kq, self.r_k, self.n_vq, self.r_v, self.v_start = c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start
+        self.last_launches = c.last_launches
         return out
 
 

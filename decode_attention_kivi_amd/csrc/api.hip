@@ -503,18 +503,57 @@ kvq_status kvq_kivi_step(kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads
     return KVQ_EALIGN;
   if (k_new_stride < c.d_h || v_new_stride < c.d_h) return KVQ_EINVAL;
 
+  // fused append + attention in one launch when the last wave of each
+  // stream's single workgroup holds every token the append writes
+  // (tokens the append writes: the new token N-1, key and value, and the
+  // quantized value token with its pair partner)
+  int32_t first_written = n.n_kq + st.k_row;
+  if (st.v_quant_row >= 0) first_written = std::min(first_written, st.v_dst_tok & ~1);
+  const bool fused = !st.compact && !st.flush_keys && pl.p.wg_per_stream == 1 && pl.p.n_bounds > 0 &&
+                     pl.p.bounds[pl.p.waves_per_stream - 1] <= first_written;
+  if (fused) {
+    kvq::AppendParams& ap = pl.p.app;
+    ap.k_new = static_cast<const uint16_t*>(k_new);
+    ap.v_new = static_cast<const uint16_t*>(v_new);
+    ap.k_res = static_cast<uint16_t*>(c.k_res);
+    ap.v_res = static_cast<uint16_t*>(c.v_res);
+    ap.v_codes = static_cast<uint8_t*>(c.v_codes);
+    ap.v_meta = static_cast<uint8_t*>(c.v_meta);
+    ap.k_new_stride = k_new_stride;
+    ap.v_new_stride = v_new_stride;
+    ap.k_res_stride = c.k_res_stride;
+    ap.v_res_stride = c.v_res_stride;
+    ap.v_codes_stride = c.v_codes_stride;
+    ap.v_meta_stride = c.v_meta_stride;
+    ap.bits = c.bits;
+    ap.G = c.group;
+    ap.D = c.d_h;
+    ap.n_streams = c.n_streams;
+    ap.k_row = st.k_row;
+    ap.v_row = st.v_row;
+    ap.v_quant_row = st.v_quant_row;
+    ap.v_dst_tok = st.v_dst_tok;
+    pl.p.fused_append = 1;
+    r = from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
+    if (r != KVQ_OK) return r;
+    cache->last_launches = 1;
+  } else {
+  int32_t launches = 0;
   if (st.compact) {
+    ++launches;
     r = kvq_residual_append(c.n_streams, c.d_h, c.r_v,
                             static_cast<const uint16_t*>(c.v_res) + int64_t(c.v_start) * c.d_h,
                             c.v_res_stride, c.d_h, c.v_res, c.v_res_stride, 0, stream);
     if (r != KVQ_OK) return r;
   }
+  ++launches;
   r = kvq_decode_append(c.bits, c.group, c.n_streams, c.d_h, k_new, k_new_stride, v_new, v_new_stride,
                         c.k_res, c.k_res_stride, st.k_row, c.v_res, c.v_res_stride, st.v_row,
                         st.v_quant_row, c.v_codes, c.v_codes_stride, c.v_meta, c.v_meta_stride,
                         st.v_dst_tok, stream);
   if (r != KVQ_OK) return r;
   if (st.flush_keys) {
+    ++launches;
     r = kvq_quantize_append(KVQ_KEYS, c.bits, c.group, c.n_streams, c.d_h, c.residual, c.k_res,
                             c.k_res_stride, c.d_h, nullptr, c.k_codes, c.k_codes_stride, c.k_meta,
                             c.k_meta_stride, st.flush_dst_tok, stream);
@@ -522,6 +561,8 @@ kvq_status kvq_kivi_step(kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads
   }
   r = from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
   if (r != KVQ_OK) return r;
+  cache->last_launches = launches + (pl.p.wg_per_stream > 1 ? 2 : 1);
+  }
   cache->n_kq = n.n_kq;
   cache->r_k = n.r_k;
   cache->n_vq = n.n_vq;

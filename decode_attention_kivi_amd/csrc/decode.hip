@@ -29,6 +29,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_device.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
@@ -605,6 +606,31 @@ decode_kernel(const DecodeParams P) {
   const int n = e - a;
 
   const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;   // [gq][D]
+
+  if (P.fused_append && wave == NW - 1) {
+    // this stream's decode-step append, by the wave whose range holds every
+    // token it writes; its stores complete before the wave reads them
+    const AppendParams& ap = P.app;
+    switch (ap.bits * 1000 + ap.G) {
+      case 2032: append_stream<2, D, 32>(ap, stream, lane); break;
+      case 2064: append_stream<2, D, 64>(ap, stream, lane); break;
+      case 4032: append_stream<4, D, 32>(ap, stream, lane); break;
+      case 4064: append_stream<4, D, 64>(ap, stream, lane); break;
+      case 8032: append_stream<8, D, 32>(ap, stream, lane); break;
+      case 8064: append_stream<8, D, 64>(ap, stream, lane); break;
+      default:
+        if constexpr (D >= 128) {
+          switch (ap.bits) {
+            case 2: append_stream<2, D, (D >= 128 ? 128 : 64)>(ap, stream, lane); break;
+            case 4: append_stream<4, D, (D >= 128 ? 128 : 64)>(ap, stream, lane); break;
+            default: append_stream<8, D, (D >= 128 ? 128 : 64)>(ap, stream, lane); break;
+          }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
 
   const WaveLds W = carve_wave<D, GQ>(smem, wave);
   // token t of the wave sits at slot t - a; a is even and quantized value

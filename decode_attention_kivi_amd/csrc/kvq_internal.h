@@ -123,6 +123,19 @@ __host__ __device__ inline int wave_bound(const CostPiece* pc, int n_pieces, int
   return int(ta < N ? ta : N);
 }
 
+struct AppendParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_res;
+  uint16_t* v_res;
+  uint8_t* v_codes;
+  uint8_t* v_meta;
+  int64_t k_new_stride, v_new_stride, k_res_stride, v_res_stride;   // fp16 elements
+  int64_t v_codes_stride, v_meta_stride;                            // bytes
+  int32_t bits, G, D, n_streams;
+  int32_t k_row, v_row, v_quant_row, v_dst_tok;
+};
+
 struct DecodeParams {
   const uint16_t* q;
   float* out;
@@ -155,6 +168,12 @@ struct DecodeParams {
   // wave computes its own (64-bit divisions: ~1 us per launch)
   int32_t n_bounds;
   int32_t bounds[kMaxBounds + 1];
+  // fused decode-step append: when set, the last wave of each stream's (only)
+  // workgroup first performs that stream's append (app) and then attends over
+  // the appended state; the host sets it only when every token the append
+  // writes lies in that wave's range
+  int32_t fused_append;
+  AppendParams app;
 };
 
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s);
@@ -172,18 +191,6 @@ struct QuantParams {
   int32_t bits, G, D, n_streams, n_tok, dst_tok;
 };
 
-struct AppendParams {
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  uint16_t* k_res;
-  uint16_t* v_res;
-  uint8_t* v_codes;
-  uint8_t* v_meta;
-  int64_t k_new_stride, v_new_stride, k_res_stride, v_res_stride;   // fp16 elements
-  int64_t v_codes_stride, v_meta_stride;                            // bytes
-  int32_t bits, G, D, n_streams;
-  int32_t k_row, v_row, v_quant_row, v_dst_tok;
-};
 
 hipError_t launch_quantize_keys(const QuantParams& p, hipStream_t s);
 hipError_t launch_quantize_values(const QuantParams& p, hipStream_t s);

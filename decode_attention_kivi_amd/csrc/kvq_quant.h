@@ -1,0 +1,116 @@
+// Quantizer pieces shared by the quantize kernels and the decode kernel's
+// fused append: one group's fp16 scale / zero point and the codes, and one
+// stream's decode-step append.
+//
+// Bit-exact contract (include/kvq.h): every step is one IEEE fp32 operation
+// on fp16-exact inputs -- subtract, correctly rounded divide, round half to
+// even -- with no FMA contraction, in every file that includes this one.
+#pragma once
+
+#include "kvq_internal.h"
+#include "kvq_device.h"
+
+namespace kvq {
+
+// One group's scale and zero point.  Zero extrema are canonicalized to +0
+// (min/max of {-0, +0} are not ordered), so z and s have single encodings.
+struct GroupScale {
+  uint32_t s16, z16;
+  float s, z;
+};
+
+template <int BITS>
+__device__ __forceinline__ GroupScale group_scale(float mn, float mx) {
+#pragma clang fp contract(off)
+  constexpr float kQmax = float((1 << BITS) - 1);
+  GroupScale g;
+  mn = mn + 0.0f;
+  mx = mx + 0.0f;
+  g.s16 = f2h(__fdiv_rn(mx - mn, kQmax));
+  g.z16 = f2h(mn);
+  g.s = h2f(g.s16);
+  g.z = h2f(g.z16);
+  return g;
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t encode(float x, const GroupScale& g) {
+#pragma clang fp contract(off)
+  constexpr float kQmax = float((1 << BITS) - 1);
+  if (g.s == 0.0f) return 0u;
+  float t = rintf(__fdiv_rn(x - g.z, g.s));
+  t = fminf(fmaxf(t, 0.0f), kQmax);
+  return static_cast<uint32_t>(t);
+}
+
+// One decode step's append for stream s, by one wave (KIVI note, Algorithm 1,
+// Decoding): lanes 0..D/8-1 copy the new key row into key-residual row
+// k_row, lanes D/8..D/4-1 the new value row into value-window row v_row (16
+// bytes per lane); then, when v_quant_row >= 0, the window row v_quant_row
+// (the new row itself when it is v_row) is quantized per token with each
+// lane holding D/64 channels: group min/max by cross-lane reductions, codes
+// from group_scale / encode, 16-bit units assembled by OR across the lanes of
+// a unit, written as token v_dst_tok of the value run with its (scale, zero)
+// pairs (at an even token the pair partner's halves and pairs are zeroed).
+template <int BITS, int D, int G>
+__device__ __forceinline__ void append_stream(const AppendParams& p, int64_t s, int lane) {
+#pragma clang fp contract(off)
+
+  constexpr int CPL = D / 64;            // channels per lane
+  constexpr int LPG = G / CPL;           // lanes per group: 16, 32 or 64
+  constexpr int NG = D / G;
+  constexpr int KPU = 16 / BITS;         // codes per 16-bit unit
+  constexpr int LPU = KPU / CPL;         // lanes per unit
+  if (lane < D / 8) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p.k_new + s * p.k_new_stride + lane * 8);
+    *reinterpret_cast<uint4*>(p.k_res + s * p.k_res_stride + int64_t(p.k_row) * D + lane * 8) = v;
+  } else if (lane < D / 4) {
+    const int c = lane - D / 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(p.v_new + s * p.v_new_stride + c * 8);
+    *reinterpret_cast<uint4*>(p.v_res + s * p.v_res_stride + int64_t(p.v_row) * D + c * 8) = v;
+  }
+  if (p.v_quant_row < 0) return;
+  // the row being quantized is read where it is complete: the new value
+  // itself if it is the row written in this launch
+  const uint16_t* row = p.v_quant_row == p.v_row
+                            ? p.v_new + s * p.v_new_stride
+                            : p.v_res + s * p.v_res_stride + int64_t(p.v_quant_row) * D;
+  float xv[CPL];
+  if constexpr (CPL == 2) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(row)[lane];
+    xv[0] = h2f(w & 0xffffu);
+    xv[1] = h2f(w >> 16);
+  } else {
+    xv[0] = h2f(row[lane]);
+  }
+  float mn = xv[0], mx = xv[0];
+  if constexpr (CPL == 2) {
+    mn = fminf(mn, xv[1]);
+    mx = fmaxf(mx, xv[1]);
+  }
+  mn = span_min<LPG>(mn);
+  mx = span_max<LPG>(mx);
+  const GroupScale gs = group_scale<BITS>(mn, mx);
+  uint32_t unit = 0;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) unit |= encode<BITS>(xv[k], gs) << (((lane * CPL + k) % KPU) * BITS);
+  unit = group_or<LPU>(unit);
+  const int64_t te = p.v_dst_tok;
+  const int64_t pair = te >> 1;
+  const int par = int(te & 1);
+  constexpr int64_t rb = int64_t(D) * BITS / 8;
+  uint8_t* blk = p.v_codes + s * p.v_codes_stride + pair * 2 * rb;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(p.v_meta + s * p.v_meta_stride);
+  const int uidx = lane * CPL / KPU;     // unit of the row = word of the pair block
+  const int g = lane / LPG;
+  if (lane % LPU == 0) {
+    *reinterpret_cast<uint16_t*>(blk + 4 * uidx + 2 * par) = static_cast<uint16_t>(unit);
+    if (par == 0) *reinterpret_cast<uint16_t*>(blk + 4 * uidx + 2) = 0;   // unwritten partner
+  }
+  if (lane % LPG == 0) {
+    meta[(pair * NG + g) * 2 + par] = gs.s16 | (gs.z16 << 16);
+    if (par == 0) meta[(pair * NG + g) * 2 + 1] = 0u;
+  }
+}
+
+}  // namespace kvq

@@ -352,6 +352,9 @@ typedef struct kvq_kivi_cache {
   /* state: tokens in the key run, key residual, value run, value window,
    * and the window's first row (n_kq + r_k == n_vq + r_v) */
   int32_t n_kq, r_k, n_vq, r_v, v_start;
+  /* out: kernel launches the last kvq_kivi_step enqueued (1 when the append
+   * ran fused into the attention kernel) */
+  int32_t last_launches;
 } kvq_kivi_cache;
 
 /*
@@ -374,6 +377,11 @@ kvq_status kvq_kivi_step_workspace(const kvq_kivi_cache* cache, int32_t batch,
  *      groups and appended to the key run (kvq_quantize_append), r_k = 0;
  *   4. kvq_decode_attn of q over the updated cache (split chosen by the
  *      library) writes out.
+ * When no compaction and no key flush is due, each stream fits one
+ * workgroup and every token the append writes falls in the range of that
+ * workgroup's last wave, steps 2 and 4 run as one launch: that wave performs
+ * the stream's append first, with the same arithmetic, so the result is the
+ * same as the separate calls.
  *   k_new, v_new  fp16 rows, stream s at element s * new_stride.
  *   q, out        fp16 [batch][n_q_heads][d_h] and fp32 [batch][n_q_heads][d_h];
  *                 n_streams = batch * n_kv_heads with n_kv_heads dividing

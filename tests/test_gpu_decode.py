@@ -69,9 +69,10 @@ def _check_stream_bytes(cache, s, st, w):
 
 
 def run_kivi(kvq, w, units, steps=1, split_tokens=0, check_every_step=False, bytes_units=None,
-             one_call=False):
+             one_call=False, launches=None):
     """Prefill w.context tokens, then `steps` decode steps; compare with the oracle.
-    one_call: every step is one kvq_kivi_step (append, flushes and attention)."""
+    one_call: every step is one kvq_kivi_step (append, flushes and attention);
+    `launches` (a list) then collects the kernel launches of every step."""
     import torch
     from decode_attention_kivi_amd.cache import KiviCache
     dev = torch.device("cuda")
@@ -94,6 +95,8 @@ def run_kivi(kvq, w, units, steps=1, split_tokens=0, check_every_step=False, byt
         t = L + step
         if one_call:
             out = cache.step(kt[:, :, t:t + 1], vt[:, :, t:t + 1], qt, w.sm_scale)
+            if launches is not None:
+                launches.append(cache.last_launches)
         else:
             cache.append(kt[:, :, t:t + 1], vt[:, :, t:t + 1])
         for (b, h), st in streams.items():
@@ -134,14 +137,37 @@ def test_one_call_steps(kvq, bits):
     # kvq_kivi_step: append, value-window overflow, key flush every R steps,
     # window compaction and attention in one call, checked after every step
     w = SMALL.scaled(context=40, bits=bits, residual=32, n_kv_heads=2, n_q_heads=4)
-    run_kivi(kvq, w, units=[(0, 0), (0, 1)], steps=3 * 32 + 5, check_every_step=True, one_call=True)
+    launches = []
+    run_kivi(kvq, w, units=[(0, 0), (0, 1)], steps=3 * 32 + 5, check_every_step=True, one_call=True,
+             launches=launches)
+    assert max(launches) >= 3          # flush steps: append, flush, attention
 
 
 @pytest.mark.parametrize("context", [0, 1, 127, 128])
 def test_one_call_steps_d128_gqa(kvq, context):
     w = SMALL.scaled(context=context, d_h=128, group=32, residual=128, n_kv_heads=2, n_q_heads=16,
                      batch=2)
-    run_kivi(kvq, w, units=[(1, 0), (1, 1)], steps=140, check_every_step=False, one_call=True)
+    launches = []
+    run_kivi(kvq, w, units=[(1, 0), (1, 1)], steps=140, check_every_step=True, one_call=True,
+             launches=launches)
+    assert max(launches) >= 3                        # flush steps
+    if context < 64:
+        # until the value window overflows, the tokens an append writes lie in
+        # the last wave's range: those steps run fused
+        assert 1 in launches
+
+
+@pytest.mark.parametrize("bits,d", [(2, 128), (4, 128), (8, 128), (2, 64)])
+def test_one_call_fused_steps_long_context(kvq, bits, d):
+    # the value window overflows every step and the last wave's range holds
+    # the residual and the value being quantized: the fused launch quantizes
+    # the oldest window value and attends in one kernel
+    w = SMALL.scaled(context=3 * 256 + 100, d_h=d, bits=bits, group=32, residual=32, n_kv_heads=2,
+                     n_q_heads=4, batch=1)
+    launches = []
+    run_kivi(kvq, w, units=[(0, 0), (0, 1)], steps=40, check_every_step=True, one_call=True,
+             launches=launches)
+    assert launches.count(1) >= 30, launches
 
 
 @pytest.mark.parametrize("split", [2, 33, 64, 96, 1000])
