@@ -59,7 +59,7 @@ def step_bytes(w: workloads.Workload, state):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_llama2_7b_int2_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "decode_attention_kivi_amd", "csrc", f)
-                  for f in ("decode.hip", "kvq_device.h", "kvq_internal.h")]
+                  for f in ("decode.hip", "kvq_device.h", "kvq_internal.h", "kvq_quant.h")]
 
 
 def measured_traffic(workload: str):
@@ -243,6 +243,9 @@ def main():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--part", choices=("all", "attention", "step"), default="all",
+                    help="profiling runs: time only the attention graph or only the step graph "
+                         "(and skip the extra measurements)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -322,22 +325,24 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
-    step_graph = torch.cuda.CUDAGraph()
-    attn_graph = torch.cuda.CUDAGraph()
+    step_graph = torch.cuda.CUDAGraph() if args.part in ("all", "step") else None
+    attn_graph = torch.cuda.CUDAGraph() if args.part in ("all", "attention") else None
     with torch.cuda.stream(stream):
-        with torch.cuda.graph(step_graph, stream=stream):
-            for _ in range(args.rounds):
-                restore()
-                for c, o in zip(caches, outs):
-                    one_step(c, o)
+        if step_graph is not None:
+            with torch.cuda.graph(step_graph, stream=stream):
+                for _ in range(args.rounds):
+                    restore()
+                    for c, o in zip(caches, outs):
+                        one_step(c, o)
         restore()
         for c in caches:           # attention-only graph on the post-step state
             c.append(k_new, v_new)
         torch.cuda.synchronize()
-        with torch.cuda.graph(attn_graph, stream=stream):
-            for _ in range(args.rounds):
-                for c, o in zip(caches, outs):
-                    c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+        if attn_graph is not None:
+            with torch.cuda.graph(attn_graph, stream=stream):
+                for _ in range(args.rounds):
+                    for c, o in zip(caches, outs):
+                        c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
     restore()
     torch.cuda.synchronize()
     n_copies = len(caches) * args.rounds       # steps per graph replay
@@ -364,16 +369,30 @@ def main():
         # let the clocks settle (both graphs, untimed) before either is timed
         t_settle = time.perf_counter()
         while time.perf_counter() - t_settle < args.settle_s:
-            step_graph.replay()
-            attn_graph.replay()
+            for g in (step_graph, attn_graph):
+                if g is not None:
+                    g.replay()
             torch.cuda.synchronize()
-        attn_ms, _, attn_pct = timed(attn_graph, args.steps, args.warmup)
-        step_ms, n_steps, step_pct = timed(step_graph, args.steps, args.warmup)
-        components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
-        ceiling = streaming_read_ceiling(dev, stream)
-        search_rate = window_search_rate(dev, stream)
+        attn_ms = step_ms = None
+        attn_pct = step_pct = (float("nan"),) * 3
+        n_steps = 0
+        components = ceiling = search_rate = None
+        if attn_graph is not None:
+            attn_ms, n_steps, attn_pct = timed(attn_graph, args.steps, args.warmup)
+        if step_graph is not None:
+            step_ms, n_steps, step_pct = timed(step_graph, args.steps, args.warmup)
+        if args.part == "all":
+            components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
+            ceiling = streaming_read_ceiling(dev, stream)
+            search_rate = window_search_rate(dev, stream)
     torch.cuda.synchronize()
 
+    if args.part != "all":
+        print(json.dumps({"part": args.part, "workload": w.name, "steps": n_steps,
+                          "us_per_launch": round(attn_ms * 1e3, 2) if attn_ms else None,
+                          "us_per_step": round(step_ms * 1e3, 2) if step_ms else None,
+                          "launches_per_step": step_launches}), flush=True)
+        return
     achieved = attn_b / (attn_ms * 1e-3) / 1e9
     value = total_b / (step_ms * 1e-3) / 1e9
     result = {
