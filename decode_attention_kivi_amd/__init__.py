@@ -23,6 +23,7 @@ __all__ = [
     "kvq_reorder_windows", "kvq_decode_attn_workspace", "kvq_decode_attn",
     "KiviCacheDesc", "kvq_kivi_step_workspace", "kvq_kivi_step",
     "kvq_window_thresholds", "kvq_window_search_workspace", "kvq_window_search",
+    "PagedArgs", "kvq_page_layout", "kvq_decode_attn_paged_workspace", "kvq_decode_attn_paged",
 ]
 
 KVQ_KEYS = 0
@@ -88,6 +89,22 @@ class KiviCacheDesc(ctypes.Structure):
     ]
 
 
+class PagedArgs(ctypes.Structure):
+    """kvq_paged_args (field order and types of include/kvq.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("d_h", ctypes.c_int32), ("group", ctypes.c_int32), ("bits", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float), ("page_tokens", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("pages", ctypes.c_void_p), ("page_bytes", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32),
+        ("lengths", ctypes.c_void_p), ("lengths_dev", ctypes.c_void_p),
+        ("k_res", ctypes.c_void_p), ("k_res_stride", ctypes.c_int64),
+        ("v_res", ctypes.c_void_p), ("v_res_stride", ctypes.c_int64),
+        ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -133,6 +150,12 @@ def _load():
     lib.kvq_kivi_step.restype = i32
     lib.kvq_kivi_step.argtypes = [ctypes.POINTER(KiviCacheDesc), i32, i32, ctypes.c_float,
                                   vp, i64, vp, i64, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kvq_page_layout.restype = i32
+    lib.kvq_page_layout.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.kvq_decode_attn_paged_workspace.restype = i32
+    lib.kvq_decode_attn_paged_workspace.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_decode_attn_paged.restype = i32
+    lib.kvq_decode_attn_paged.argtypes = [ctypes.POINTER(PagedArgs), vp]
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -286,3 +309,22 @@ def kvq_window_search(batch, n_text, n_visual, dim, text, text_batch_stride, tex
                                      window_tokens, float(t_low), float(t_high), int(first_window_fp16),
                                      _dev(scores), _dev(win_bits), _dev(workspace), int(workspace_bytes),
                                      _stream(stream)), "kvq_window_search")
+
+
+def kvq_page_layout(n_kv_heads, d_h, group, bits, page_tokens) -> dict:
+    """Byte layout of one page of the paged cache (head_bytes, kmeta_off,
+    vcodes_off, vmeta_off, page_bytes)."""
+    out = (ctypes.c_int64 * 5)()
+    _check(_load().kvq_page_layout(n_kv_heads, d_h, group, bits, page_tokens, out), "kvq_page_layout")
+    return dict(zip(("head_bytes", "kmeta_off", "vcodes_off", "vmeta_off", "page_bytes"), (int(x) for x in out)))
+
+
+def kvq_decode_attn_paged_workspace(args: PagedArgs) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().kvq_decode_attn_paged_workspace(ctypes.byref(args), ctypes.byref(n)),
+           "kvq_decode_attn_paged_workspace")
+    return int(n.value)
+
+
+def kvq_decode_attn_paged(args: PagedArgs, stream=None):
+    _check(_load().kvq_decode_attn_paged(ctypes.byref(args), _stream(stream)), "kvq_decode_attn_paged")

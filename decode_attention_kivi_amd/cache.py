@@ -9,6 +9,11 @@ residuals, flushes the key residual as a whole when it reaches R tokens and
 quantizes the oldest values beyond R.  The attention call then reads
 [quantized keys | key residual] and [quantized values | value window].
 
+``PagedKiviCache`` keeps the same KIVI state per sequence with its own
+lengths (a ragged batch), the quantized tokens in fixed-size pages of a
+shared pool listed by a block table (the serving layout the KIVI note's
+outlook pairs with PagedAttention).
+
 ``WindowCache`` keeps a WindowQuant cache (Sec. 3.1, 3.3.1): the visual
 windows are reordered by bit width on the device, each run is quantized from
 the gathered rows, and the text/new tokens stay fp16.
@@ -21,13 +26,15 @@ from __future__ import annotations
 import math
 from typing import List, Optional, Sequence, Tuple
 
+import numpy as np
 import torch
 
-from . import (KVQ_KEYS, KVQ_VALUES, KiviCacheDesc, Segment, kvq_decode_append, kvq_decode_attn,
-               kvq_decode_attn_workspace, kvq_kivi_step, kvq_kivi_step_workspace,
+from . import (KVQ_KEYS, KVQ_VALUES, KiviCacheDesc, PagedArgs, Segment, kvq_decode_append,
+               kvq_decode_attn, kvq_decode_attn_paged, kvq_decode_attn_paged_workspace,
+               kvq_decode_attn_workspace, kvq_kivi_step, kvq_kivi_step_workspace, kvq_page_layout,
                kvq_quantize_append, kvq_reorder_windows, kvq_residual_append, make_decode_args)
 
-__all__ = ["KiviCache", "WindowCache", "arena_bytes"]
+__all__ = ["KiviCache", "WindowCache", "PagedKiviCache", "arena_bytes", "kivi_step_lengths"]
 
 
 def _round16(x: int) -> int:
@@ -298,4 +305,118 @@ class WindowCache:
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         kvq_decode_attn(self.decode_args(q, out, sm_scale, split_tokens), stream)
+        return out
+
+
+def kivi_step_lengths(context: int, residual: int) -> Tuple[int, int, int, int]:
+    """(n_kq, r_k, n_vq, r_v) after a prefill of ``context`` tokens and one
+    decode step (KIVI Algorithm 1): the prefill quantizes keys up to
+    l - l % R and values up to l - R; the step appends one key (a full key
+    residual of R is flushed) and one value (a window beyond R loses its
+    oldest value to the quantized part)."""
+    R = residual
+    n_kq, r_k = context - context % R, context % R + 1
+    if r_k == R:
+        n_kq, r_k = n_kq + R, 0
+    n_vq, r_v = max(context - R, 0), min(context, R) + 1
+    if r_v > R:
+        n_vq, r_v = n_vq + 1, R
+    return n_kq, r_k, n_vq, r_v
+
+
+class PagedKiviCache:
+    """Paged, ragged KIVI cache of ``batch`` sequences x ``n_kv_heads`` heads.
+
+    Sequence b's quantized keys and values live in pages of ``page_tokens``
+    tokens (kvq_page_layout) taken from one pool in a shuffled order (so the
+    block table is a real indirection); its fp16 key residual and value
+    window are rows of per-stream buffers.  ``fill`` writes a sequence's state
+    with the library's quantize and row-copy calls, one call per page.
+    """
+
+    def __init__(self, batch: int, n_kv_heads: int, d_h: int, bits: int, group: int, residual: int,
+                 page_tokens: int, max_tokens: int, n_pages: Optional[int] = None, device="cuda",
+                 seed: int = 0):
+        self.B, self.H, self.d, self.bits, self.G, self.R = batch, n_kv_heads, d_h, bits, group, residual
+        self.PT = page_tokens
+        self.layout = kvq_page_layout(n_kv_heads, d_h, group, bits, page_tokens)
+        self.max_pages = max(1, -(-max_tokens // page_tokens))
+        n_pages = n_pages or batch * self.max_pages
+        assert n_pages >= batch * self.max_pages
+        self.page_bytes = self.layout["page_bytes"]
+        self.pool = torch.zeros(n_pages, self.page_bytes, dtype=torch.uint8, device=device)
+        order = torch.randperm(n_pages, generator=torch.Generator().manual_seed(seed))[:batch * self.max_pages]
+        self.block_table_host = order.to(torch.int32).reshape(batch, self.max_pages)
+        self.block_table = self.block_table_host.to(device)
+        f16 = dict(dtype=torch.float16, device=device)
+        self.n_streams = batch * n_kv_heads
+        self.k_res = torch.zeros(self.n_streams, residual, d_h, **f16)
+        self.v_res = torch.zeros(self.n_streams, residual + 1, d_h, **f16)
+        self.lens = np.zeros((batch, 4), dtype=np.int32)      # n_kq, n_vq, n_k_res, n_v_res
+        self.lens_dev = torch.zeros(batch, 4, dtype=torch.int32, device=device)
+        self._ws = None
+
+    def _page_ptr(self, b: int, j: int, part: str) -> int:
+        off = {"kcodes": 0, "kmeta": self.layout["kmeta_off"], "vcodes": self.layout["vcodes_off"],
+               "vmeta": self.layout["vmeta_off"]}[part]
+        return self.pool.data_ptr() + int(self.block_table_host[b, j]) * self.page_bytes + off
+
+    def fill(self, b: int, k: torch.Tensor, v: torch.Tensor, n_kq: int, n_vq: int, stream=None):
+        """Sequence b holds tokens k, v [Hkv][N][d] (fp16, on the device): keys
+        0..n_kq-1 and values 0..n_vq-1 quantized into its pages (one
+        kvq_quantize_append per page and half; a page is a key run and a
+        value run of its kv heads), the rest copied to the residual rows."""
+        H, d, PT, hb = self.H, self.d, self.PT, self.layout["head_bytes"]
+        assert k.shape == v.shape and k.shape[0] == H and k.shape[2] == d and k.dtype == torch.float16
+        N = k.shape[1]
+        assert n_kq % self.G == 0 and 0 <= n_vq <= n_kq <= N and N - n_kq <= self.R and N - n_vq <= self.R + 1
+        assert -(-n_kq // PT) <= self.max_pages
+        for which, src, n_q, codes, meta in ((KVQ_KEYS, k, n_kq, "kcodes", "kmeta"),
+                                             (KVQ_VALUES, v, n_vq, "vcodes", "vmeta")):
+            for j in range(-(-n_q // PT)):
+                t0, t1 = j * PT, min(n_q, (j + 1) * PT)
+                kvq_quantize_append(which, self.bits, self.G, H, d, t1 - t0, src[:, t0:], src.stride(0),
+                                    src.stride(1), None, self._page_ptr(b, j, codes), hb,
+                                    self._page_ptr(b, j, meta), hb, 0, stream)
+        s0 = b * H
+        if N > n_kq:
+            kvq_residual_append(H, d, N - n_kq, k[:, n_kq:], k.stride(0), k.stride(1), self.k_res[s0],
+                                self.k_res.stride(0), 0, stream)
+        if N > n_vq:
+            kvq_residual_append(H, d, N - n_vq, v[:, n_vq:], v.stride(0), v.stride(1), self.v_res[s0],
+                                self.v_res.stride(0), 0, stream)
+        self.lens[b] = (n_kq, n_vq, N - n_kq, N - n_vq)
+        self.lens_dev[b].copy_(torch.from_numpy(self.lens[b].copy()))
+
+    def fill_step(self, b: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+        """The state of sequence b after a prefill of N - 1 tokens and one
+        decode step (kivi_step_lengths) for k, v [Hkv][N][d]."""
+        n_kq, _, n_vq, _ = kivi_step_lengths(k.shape[1] - 1, self.R)
+        self.fill(b, k, v, n_kq, n_vq, stream)
+
+    def args(self, q: torch.Tensor, sm_scale: float, out: torch.Tensor) -> PagedArgs:
+        a = PagedArgs()
+        a.batch, a.n_q_heads, a.n_kv_heads = self.B, q.shape[1], self.H
+        a.d_h, a.group, a.bits, a.sm_scale, a.page_tokens = self.d, self.G, self.bits, float(sm_scale), self.PT
+        a.q, a.pages, a.page_bytes = q.data_ptr(), self.pool.data_ptr(), self.page_bytes
+        a.block_table, a.max_pages = self.block_table.data_ptr(), self.max_pages
+        a.lengths = self.lens.ctypes.data
+        a.lengths_dev = self.lens_dev.data_ptr()
+        a.k_res, a.k_res_stride = self.k_res.data_ptr(), self.k_res.stride(0)
+        a.v_res, a.v_res_stride = self.v_res.data_ptr(), self.v_res.stride(0)
+        a.out = out.data_ptr()
+        return a
+
+    def attend(self, q: torch.Tensor, sm_scale: float, out: Optional[torch.Tensor] = None, stream=None):
+        """kvq_decode_attn_paged of q [B][Hq][d] (fp16) over every sequence."""
+        assert q.dtype == torch.float16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        a = self.args(q, sm_scale, out)
+        need = kvq_decode_attn_paged_workspace(a)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if need:
+            a.workspace, a.workspace_bytes = self._ws.data_ptr(), self._ws.numel()
+        kvq_decode_attn_paged(a, stream)
         return out

@@ -211,6 +211,107 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   return KVQ_OK;
 }
 
+// Page layout (kvq_page_layout): a key run and a value run of PT tokens per
+// kv head, head blocks back to back.
+struct PageLayout {
+  int64_t head_bytes, kmeta_off, vcodes_off, vmeta_off, page_bytes;
+};
+kvq_status page_layout(int n_kv_heads, int d_h, int group, int bits, int page_tokens, PageLayout* out) {
+  if (n_kv_heads < 1 || page_tokens < 1) return KVQ_EINVAL;
+  if (bits != 2 && bits != 4 && bits != 8) return KVQ_EINVAL;
+  if (!valid_d(d_h) || !valid_group(group) || group > d_h) return KVQ_EUNSUPPORTED;
+  if (page_tokens % 64 != 0 || page_tokens % group != 0 || page_tokens > 65536) return KVQ_EUNSUPPORTED;
+  const int64_t PT = page_tokens, rb = int64_t(d_h) * bits / 8;
+  PageLayout L;
+  L.kmeta_off = PT * rb;
+  L.vcodes_off = L.kmeta_off + PT / group * d_h * 4;
+  L.vmeta_off = L.vcodes_off + PT * rb;
+  L.head_bytes = kvq::round16(L.vmeta_off + PT * (d_h / group) * 4);
+  L.page_bytes = L.head_bytes * n_kv_heads;
+  *out = L;
+  return KVQ_OK;
+}
+
+kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
+  if (!a) return KVQ_EINVAL;
+  if (a->batch < 1 || a->n_kv_heads < 1 || a->n_q_heads < 1) return KVQ_EINVAL;
+  if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_EINVAL;
+  const int gq = a->n_q_heads / a->n_kv_heads;
+  if (gq > 8) return KVQ_EUNSUPPORTED;
+  if (int64_t(a->batch) * a->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  PageLayout L;
+  kvq_status st = page_layout(a->n_kv_heads, a->d_h, a->group, a->bits, a->page_tokens, &L);
+  if (st != KVQ_OK) return st;
+  if (!std::isfinite(a->sm_scale)) return KVQ_EINVAL;
+  if (!a->q || !a->out || !a->pages || !a->block_table || !a->lengths || !a->lengths_dev) return KVQ_EINVAL;
+  if (a->max_pages < 1 || a->page_bytes < L.page_bytes) return KVQ_EINVAL;
+  if (a->page_bytes & 15) return KVQ_EALIGN;
+  for (const void* ptr : {a->q, static_cast<const void*>(a->out), a->pages, a->k_res, a->v_res,
+                          static_cast<const void*>(a->workspace)})
+    if (ptr && !aligned16(ptr)) return KVQ_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(a->block_table) & 3) || (reinterpret_cast<uintptr_t>(a->lengths_dev) & 3))
+    return KVQ_EALIGN;
+  for (int64_t s : {a->k_res_stride, a->v_res_stride})
+    if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
+  const int D = a->d_h, G = a->group;
+  int GQ = 1;
+  while (GQ < gq) GQ *= 2;
+  if (kvq::decode_lds_bytes(D, GQ, kvq::kWaves) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
+  const kvq::PagedCost pc = kvq::paged_cost(D, G, a->bits);
+  int wg_max = 1;
+  bool any_kres = false, any_vres = false;
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t nk = a->lengths[4 * b], nv = a->lengths[4 * b + 1];
+    const int64_t rk = a->lengths[4 * b + 2], rv = a->lengths[4 * b + 3];
+    if (nk < 0 || nv < 0 || rk < 0 || rv < 0 || nv > nk || nk % G != 0) return KVQ_EINVAL;
+    const int64_t N = nk + rk;
+    if (N != nv + rv || N < 1 || N > (int64_t(1) << 22)) return KVQ_EINVAL;
+    if ((nk + a->page_tokens - 1) / a->page_tokens > a->max_pages) return KVQ_EINVAL;
+    any_kres |= rk > 0;
+    any_vres |= rv > 0;
+    wg_max = std::max(wg_max, kvq::paged_wgs(pc, int(nk), int(nv), int(N), GQ, kvq::kWaves));
+  }
+  if ((any_kres && !a->k_res) || (any_vres && !a->v_res)) return KVQ_EINVAL;
+  if (wg_max > (1 << 16)) return KVQ_EUNSUPPORTED;
+
+  Plan& pl = *out;
+  DecodeParams& p = pl.p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.out = a->out;
+  p.ws = static_cast<float*>(a->workspace);
+  p.k_res = static_cast<const uint16_t*>(a->k_res);
+  p.v_res = static_cast<const uint16_t*>(a->v_res);
+  p.k_res_stride = a->k_res_stride;
+  p.v_res_stride = a->v_res_stride;
+  p.B = a->batch;
+  p.Hq = a->n_q_heads;
+  p.Hkv = a->n_kv_heads;
+  p.D = D;
+  p.G = G;
+  p.lg_g = G == 32 ? 5 : G == 64 ? 6 : 7;
+  p.gq = gq;
+  p.waves_per_wg = kvq::kWaves;
+  p.wg_per_stream = wg_max;
+  p.scale_log2 = a->sm_scale * 1.4426950408889634f;
+  p.pages = static_cast<const uint8_t*>(a->pages);
+  p.block_table = a->block_table;
+  p.lens = a->lengths_dev;
+  p.page_bytes = a->page_bytes;
+  p.head_bytes = L.head_bytes;
+  p.page_tokens = a->page_tokens;
+  p.max_pages = a->max_pages;
+  p.pg_kmeta_off = int32_t(L.kmeta_off);
+  p.pg_vcodes_off = int32_t(L.vcodes_off);
+  p.pg_vmeta_off = int32_t(L.vmeta_off);
+  p.bits = a->bits;
+  pl.GQ = GQ;
+  pl.ws_bytes = wg_max == 1 ? 0
+                            : size_t(a->batch) * size_t(a->n_kv_heads) * size_t(wg_max) * size_t(gq) *
+                                  size_t(D + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -374,6 +475,38 @@ kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream) {
   if (pl.ws_bytes > 0 && (!args->workspace || args->workspace_bytes < pl.ws_bytes))
     return KVQ_EWORKSPACE;
   return from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_page_layout(int32_t n_kv_heads, int32_t d_h, int32_t group, int32_t bits,
+                           int32_t page_tokens, int64_t out[5]) {
+  if (!out) return KVQ_EINVAL;
+  PageLayout L;
+  const kvq_status st = page_layout(n_kv_heads, d_h, group, bits, page_tokens, &L);
+  if (st != KVQ_OK) return st;
+  out[0] = L.head_bytes;
+  out[1] = L.kmeta_off;
+  out[2] = L.vcodes_off;
+  out[3] = L.vmeta_off;
+  out[4] = L.page_bytes;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn_paged_workspace(const kvq_paged_args* args, size_t* bytes) {
+  if (!bytes) return KVQ_EINVAL;
+  Plan pl;
+  const kvq_status st = make_paged_plan(args, &pl);
+  if (st != KVQ_OK) return st;
+  *bytes = pl.ws_bytes;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn_paged(const kvq_paged_args* args, void* stream) {
+  Plan pl;
+  const kvq_status st = make_paged_plan(args, &pl);
+  if (st != KVQ_OK) return st;
+  if (pl.ws_bytes > 0 && (!args->workspace || args->workspace_bytes < pl.ws_bytes))
+    return KVQ_EWORKSPACE;
+  return from_hip(kvq::launch_decode_paged(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

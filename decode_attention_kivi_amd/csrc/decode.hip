@@ -143,8 +143,9 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 
 // ---------------------------------------------------------------------------
 // Keys of run tokens [r0, r1) (bits 2/4/8) -> raw logits q'.k (q' = q * 2^-8)
-// at slots slot0 + (t - r0).  r0 is a multiple of 32, so every item (16
-// tokens) lies in one key group.  Whole items are written: slots past r1 get
+// at slots slot0 + (t - r0); cbase / mbase address the run's token 0 (codes)
+// and key group 0 (meta) of this stream.  r0 is a multiple of 32, so every
+// item (16 tokens) lies in one key group.  Whole items are written: slots past r1 get
 // values that a later piece overwrites or the softmax ignores.
 //
 // Per key group, every channel's hi = fp16(q'*s) and lo = fp16(q'*s - hi)
@@ -162,7 +163,7 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 // word P / NP, position P % NP, channels clo and clo + NP).
 template <int D, int GQ, int BITS>
 __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
-                               int64_t stream, const Run& run, int r0, int r1, int slot0,
+                               const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int slot0,
                                int lane, int n_wave) {
   using KG = KeyGeo<D, GQ, BITS>;
   constexpr int LT = wave_slots(GQ);
@@ -176,10 +177,8 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
   const int n_items = (n + TPI - 1) / TPI;
   const int jp = r0 >> lg;                             // first key group of the piece
   const int n_groups = ((r1 - 1) >> lg) - jp + 1;
-  const Rsrc crs = make_rsrc(P.k_codes + stream * P.k_codes_stride + run.code_off + int64_t(r0) * RB,
-                             uint32_t(n) * RB);
-  const Rsrc mrs = make_rsrc(P.k_meta + stream * P.k_meta_stride + run.meta_off + int64_t(jp) * D * 4,
-                             uint32_t(n_groups) * D * 4);
+  const Rsrc crs = make_rsrc(cbase + int64_t(r0) * RB, uint32_t(n) * RB);
+  const Rsrc mrs = make_rsrc(mbase + int64_t(jp) * D * 4, uint32_t(n_groups) * D * 4);
   // matrix role of the lane: B column (token) col, k-block kb; A row col
   const int col = lane & 15, kb = lane >> 4;
   const uint32_t lane_off = uint32_t(col * RB + kb * LB);
@@ -389,7 +388,8 @@ __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], in
   wave_lds_sync();
 }
 
-// Values of run tokens [r0, r1) (bits 2/4/8).  Pair block p of the run holds
+// Values of run tokens [r0, r1) (bits 2/4/8); cbase / mbase address the run's
+// pair block 0 (codes and meta) of this stream.  Pair block p of the run holds
 // run tokens 2p and 2p+1, whose probabilities are fp16 pair p - r0/2 of W.p16
 // counted from dword ps0 (r0 is even).  Slot ph >= 0 (the partner after an
 // odd run's last token, a token of the next piece) reads as zero while the
@@ -397,8 +397,8 @@ __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], in
 // zero codes and zero meta, so they add 0.  Unless softmax_done, `softmax`
 // runs after the first loads are issued (it writes W.p16).
 template <int D, int GQ, int BITS, class Softmax>
-__device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_t stream,
-                                 const Run& run, int r0, int r1, int ps0, int lane,
+__device__ void values_quantized(const DecodeParams& P, const WaveLds& W,
+                                 const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int ps0, int lane,
                                  Softmax& softmax, bool softmax_done, int ph, int n_wave) {
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = D * BITS / 8;
@@ -416,10 +416,8 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W, int64_
   const int p0 = r0 >> 1;
   const int np = ((r1 - 1) >> 1) - p0 + 1;
   const int n_inst = (np + PPI - 1) / PPI;
-  const Rsrc crs = make_rsrc(P.v_codes + stream * P.v_codes_stride + run.code_off + int64_t(p0) * 2 * RB,
-                             uint32_t(np) * 2 * RB);
-  const Rsrc mrs = make_rsrc(P.v_meta + stream * P.v_meta_stride + run.meta_off + int64_t(p0) * NG * 8,
-                             uint32_t(np) * NG * 8);
+  const Rsrc crs = make_rsrc(cbase + int64_t(p0) * 2 * RB, uint32_t(np) * 2 * RB);
+  const Rsrc mrs = make_rsrc(mbase + int64_t(p0) * NG * 8, uint32_t(np) * NG * 8);
   const uint32_t c_off = uint32_t(my_p * 2 * RB + my_c * 16);
   const uint32_t m_off = uint32_t((my_p * NG + g) * 8);
   const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16) + ps0;
@@ -591,7 +589,7 @@ __device__ void values_fp16(const DecodeParams& P, const WaveLds& W, const uint1
 // resident waves per CU (two workgroups) keep enough loads in flight to
 // cover HBM latency.  Grouped heads do GQ times the arithmetic per byte and
 // get 256 VGPRs (one workgroup per CU).
-template <int D, int GQ, int NW>
+template <int D, int GQ, int NW, bool PAGED>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQ == 1 ? 4 : 2)))
 decode_kernel(const DecodeParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -604,16 +602,31 @@ decode_kernel(const DecodeParams P) {
   const int wg = blockIdx.x;
   const int64_t stream = blockIdx.y;
   const int b = int(stream / P.Hkv), hkv = int(stream % P.Hkv);
-  const int N = P.n_tok;
   const int gw = wg * NW + wave;
-  const bool tab = P.n_bounds > 0;
-  const int a = tab ? P.bounds[gw] : wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw, P.waves_per_stream);
-  const int e = tab ? P.bounds[gw + 1] : wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw + 1, P.waves_per_stream);
+  int N, n_kq, n_vq, a, e;
+  if constexpr (PAGED) {
+    // this sequence's lengths; workgroups past the stream's share leave at once
+    n_kq = P.lens[4 * b];
+    n_vq = P.lens[4 * b + 1];
+    N = n_kq + P.lens[4 * b + 2];
+    const PagedCost pc = paged_cost(D, P.G, P.bits);
+    const int nwg = paged_wgs(pc, n_kq, n_vq, N, GQ, NW);
+    if (wg >= nwg) return;                   // the whole workgroup, before any barrier
+    a = paged_bound(pc, n_kq, n_vq, N, gw, nwg * NW);
+    e = paged_bound(pc, n_kq, n_vq, N, gw + 1, nwg * NW);
+  } else {
+    N = P.n_tok;
+    n_kq = P.n_kq;
+    n_vq = P.n_vq;
+    const bool tab = P.n_bounds > 0;
+    a = tab ? P.bounds[gw] : wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw, P.waves_per_stream);
+    e = tab ? P.bounds[gw + 1] : wave_bound(P.pieces, P.n_pieces, P.cost_total, N, gw + 1, P.waves_per_stream);
+  }
   const int n = e - a;
 
   const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;   // [gq][D]
 
-  if (P.fused_append && wave == NW - 1) {
+  if (!PAGED && P.fused_append && wave == NW - 1) {
     // this stream's decode-step append, by the wave whose range holds every
     // token it writes; its stores complete before the wave reads them
     const AppendParams& ap = P.app;
@@ -643,15 +656,34 @@ decode_kernel(const DecodeParams P) {
   // runs start at even tokens, so every value pair block starts at an even slot
   if (n > 0) {
     // key pieces in token order
-    for (int k = 0; k < P.n_k_runs; ++k) {
+    if constexpr (PAGED) {
+      // quantized keys, one piece per page (pages start on key groups)
+      const int kend = min(e, n_kq);
+      for (int t0 = a; t0 < kend;) {
+        const int pg = t0 / P.page_tokens;
+        const int p0 = pg * P.page_tokens;
+        const int t1 = min(kend, p0 + P.page_tokens);
+        const uint8_t* hb = P.pages + int64_t(P.block_table[int64_t(b) * P.max_pages + pg]) * P.page_bytes +
+                            int64_t(hkv) * P.head_bytes;
+        switch (P.bits) {
+          case 2: keys_quantized<D, GQ, 2>(P, W, qg, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          case 4: keys_quantized<D, GQ, 4>(P, W, qg, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          default: keys_quantized<D, GQ, 8>(P, W, qg, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+        }
+        t0 = t1;
+      }
+    }
+    for (int k = 0; k < (PAGED ? 0 : P.n_k_runs); ++k) {
       const Run& run = P.k_runs[k];
       const int t0 = max(a, run.tok_begin), t1 = min(e, run.tok_begin + run.n_tok);
       if (t0 >= t1) continue;
       const int r0 = t0 - run.tok_begin, r1 = t1 - run.tok_begin;
+      const uint8_t* cb = P.k_codes + stream * P.k_codes_stride + run.code_off;
+      const uint8_t* mb = P.k_meta + stream * P.k_meta_stride + run.meta_off;
       switch (run.bits) {
-        case 2: keys_quantized<D, GQ, 2>(P, W, qg, stream, run, r0, r1, t0 - a, lane, n); break;
-        case 4: keys_quantized<D, GQ, 4>(P, W, qg, stream, run, r0, r1, t0 - a, lane, n); break;
-        case 8: keys_quantized<D, GQ, 8>(P, W, qg, stream, run, r0, r1, t0 - a, lane, n); break;
+        case 2: keys_quantized<D, GQ, 2>(P, W, qg, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 4: keys_quantized<D, GQ, 4>(P, W, qg, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 8: keys_quantized<D, GQ, 8>(P, W, qg, cb, mb, r0, r1, t0 - a, lane, n); break;
         default:
           keys_fp16<D, GQ>(P, W, qg,
                            reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off) +
@@ -659,9 +691,9 @@ decode_kernel(const DecodeParams P) {
                            r1 - r0, t0 - a, lane);
       }
     }
-    if (e > P.n_kq) {
-      const int t0 = max(a, P.n_kq);
-      keys_fp16<D, GQ>(P, W, qg, P.k_res + stream * P.k_res_stride + int64_t(t0 - P.n_kq) * D, e - t0,
+    if (e > n_kq) {
+      const int t0 = max(a, n_kq);
+      keys_fp16<D, GQ>(P, W, qg, P.k_res + stream * P.k_res_stride + int64_t(t0 - n_kq) * D, e - t0,
                        t0 - a, lane);
     }
     wave_lds_sync();
@@ -723,7 +755,28 @@ decode_kernel(const DecodeParams P) {
   wave_lds_sync();
   if (n > 0) {
     // value pieces in token order
-    for (int k = 0; k < P.n_v_runs; ++k) {
+    if constexpr (PAGED) {
+      const int vend = min(e, n_vq);
+      for (int t0 = a; t0 < vend;) {
+        const int pg = t0 / P.page_tokens;
+        const int p0 = pg * P.page_tokens;
+        const int t1 = min(vend, p0 + P.page_tokens);
+        const uint8_t* hb = P.pages + int64_t(P.block_table[int64_t(b) * P.max_pages + pg]) * P.page_bytes +
+                            int64_t(hkv) * P.head_bytes;
+        const int r0 = t0 - p0, r1 = t1 - p0;
+        // an odd end is the last quantized value (pages hold an even number of tokens)
+        const int ph = ((r1 & 1) && t1 < e) ? t1 - a : -1;
+        const uint8_t* cb = hb + P.pg_vcodes_off;
+        const uint8_t* mb = hb + P.pg_vmeta_off;
+        switch (P.bits) {
+          case 2: values_quantized<D, GQ, 2>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+          case 4: values_quantized<D, GQ, 4>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+          default: values_quantized<D, GQ, 8>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        }
+        t0 = t1;
+      }
+    }
+    for (int k = 0; k < (PAGED ? 0 : P.n_v_runs); ++k) {
       const Run& run = P.v_runs[k];
       const int t0 = max(a, run.tok_begin), t1 = min(e, run.tok_begin + run.n_tok);
       if (t0 >= t1) continue;
@@ -731,10 +784,12 @@ decode_kernel(const DecodeParams P) {
       // the pair partner after an odd run's last token belongs to the next
       // piece: its probability is zero while this run is read
       const int ph = ((r1 & 1) && t1 < e) ? t1 - a : -1;
+      const uint8_t* cb = P.v_codes + stream * P.v_codes_stride + run.code_off;
+      const uint8_t* mb = P.v_meta + stream * P.v_meta_stride + run.meta_off;
       switch (run.bits) {
-        case 2: values_quantized<D, GQ, 2>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
-        case 4: values_quantized<D, GQ, 4>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
-        case 8: values_quantized<D, GQ, 8>(P, W, stream, run, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 2: values_quantized<D, GQ, 2>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 4: values_quantized<D, GQ, 4>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 8: values_quantized<D, GQ, 8>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
         default:
           if (!softmax_done) softmax();
           values_fp16<D, GQ>(P, W,
@@ -743,10 +798,10 @@ decode_kernel(const DecodeParams P) {
                              r1 - r0, t0 - a, lane);
       }
     }
-    if (e > P.n_vq) {
+    if (e > n_vq) {
       if (!softmax_done) softmax();
-      const int t0 = max(a, P.n_vq);
-      values_fp16<D, GQ>(P, W, P.v_res + stream * P.v_res_stride + int64_t(t0 - P.n_vq) * D, e - t0,
+      const int t0 = max(a, n_vq);
+      values_fp16<D, GQ>(P, W, P.v_res + stream * P.v_res_stride + int64_t(t0 - n_vq) * D, e - t0,
                          t0 - a, lane);
     }
   }
@@ -792,7 +847,7 @@ decode_kernel(const DecodeParams P) {
 // Cross-split merge, one thread per output element:
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the stream's
 // workgroup partials, folded in one pass with a running maximum.
-template <int D>
+template <int D, bool PAGED>
 __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
   const int64_t idx = int64_t(blockIdx.x) * NT + threadIdx.x;
   if (idx >= int64_t(P.B) * P.Hq * D) return;
@@ -803,9 +858,17 @@ __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
   const int64_t stream = int64_t(b) * P.Hkv + hkv;
   const int64_t step = int64_t(P.gq) * (D + 2);
   const float* w0 = P.ws + stream * P.wg_per_stream * step + h * (D + 2);
+  int nwg = P.wg_per_stream;
+  if constexpr (PAGED) {
+    // the workgroups this stream used (the rest of its slots are not written)
+    const int n_kq = P.lens[4 * b], n_vq = P.lens[4 * b + 1];
+    int GQ = 1;                              // the decode kernel's head block (power of two)
+    while (GQ < P.gq) GQ *= 2;
+    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], GQ, kWaves);
+  }
   float M = -INFINITY, L = 0.f, O = 0.f;
 #pragma unroll 4
-  for (int s = 0; s < P.wg_per_stream; ++s) {
+  for (int s = 0; s < nwg; ++s) {
     const float* w = w0 + s * step;
     const float m = w[0], l = w[1], o = w[2 + c];
     const float Mn = fmaxf(M, m);
@@ -818,31 +881,31 @@ __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
   P.out[idx] = O / L;
 }
 
-template <int D, int GQ, int NW>
+template <int D, int GQ, int NW, bool PAGED>
 hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
   const size_t lds = size_t(lds_bytes(decode_lds<D, GQ>(), NW));
-  hipLaunchKernelGGL((decode_kernel<D, GQ, NW>), dim3(p.wg_per_stream, p.B * p.Hkv), dim3(NW * 64),
+  hipLaunchKernelGGL((decode_kernel<D, GQ, NW, PAGED>), dim3(p.wg_per_stream, p.B * p.Hkv), dim3(NW * 64),
                      lds, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_stream == 1) return e;
   const int64_t n = int64_t(p.B) * p.Hq * D;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(unsigned((n + NT - 1) / NT)), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((merge_kernel<D, PAGED>), dim3(unsigned((n + NT - 1) / NT)), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
-template <int D, int GQ>
+template <int D, int GQ, bool PAGED>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t s) {
   if (p.waves_per_wg != kWaves) return hipErrorInvalidValue;
-  return launch_dgw<D, GQ, kWaves>(p, s);
+  return launch_dgw<D, GQ, kWaves, PAGED>(p, s);
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const DecodeParams& p, int GQ, hipStream_t s) {
   switch (GQ) {
-    case 1: return launch_dg<D, 1>(p, s);
-    case 2: return launch_dg<D, 2>(p, s);
-    case 4: return launch_dg<D, 4>(p, s);
-    case 8: return launch_dg<D, 8>(p, s);
+    case 1: return launch_dg<D, 1, PAGED>(p, s);
+    case 2: return launch_dg<D, 2, PAGED>(p, s);
+    case 4: return launch_dg<D, 4, PAGED>(p, s);
+    case 8: return launch_dg<D, 8, PAGED>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -851,8 +914,16 @@ hipError_t launch_d(const DecodeParams& p, int GQ, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s) {
   switch (p.D) {
-    case 64: return launch_d<64>(p, GQ, s);
-    case 128: return launch_d<128>(p, GQ, s);
+    case 64: return launch_d<64, false>(p, GQ, s);
+    case 128: return launch_d<128, false>(p, GQ, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_paged(const DecodeParams& p, int GQ, hipStream_t s) {
+  switch (p.D) {
+    case 64: return launch_d<64, true>(p, GQ, s);
+    case 128: return launch_d<128, true>(p, GQ, s);
     default: return hipErrorInvalidValue;
   }
 }

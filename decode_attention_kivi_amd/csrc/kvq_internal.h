@@ -174,9 +174,63 @@ struct DecodeParams {
   // writes lies in that wave's range
   int32_t fused_append;
   AppendParams app;
+  // Paged cache (decode_kernel<..., true>; k_runs, v_runs, pieces and bounds
+  // unused).  Sequence b's quantized tokens live in pages of page_tokens
+  // tokens: its page j is pool page block_table[b * max_pages + j] at
+  // pages + page * page_bytes, kv head h's block at + h * head_bytes, with key
+  // codes at 0, key meta at pg_kmeta_off, value codes at pg_vcodes_off and
+  // value meta at pg_vmeta_off (the layout of kvq_page_layout).
+  // lens[4 b + 0..3] = n_kq, n_vq, n_k_res, n_v_res of sequence b; every
+  // stream of the sequence uses paged_wgs(...) of the grid's wg_per_stream
+  // workgroups.
+  const uint8_t* pages;
+  const int32_t* block_table;
+  const int32_t* lens;
+  int64_t page_bytes, head_bytes;
+  int32_t page_tokens, max_pages, pg_kmeta_off, pg_vcodes_off, pg_vmeta_off, bits;
 };
 
+// Byte costs per token of a paged stream (keys + values): both quantized,
+// quantized key + fp16 value, both fp16.
+struct PagedCost {
+  int32_t both_q, key_q, both_16;
+};
+__host__ __device__ inline PagedCost paged_cost(int D, int G, int bits) {
+  const int32_t rb = D * bits / 8;
+  const int32_t kq = rb + D * 4 / G, vq = rb + (D / G) * 4, h16 = 2 * D;
+  return PagedCost{kq + vq, kq + h16, 2 * h16};
+}
+__host__ __device__ inline int64_t paged_total(const PagedCost& c, int n_kq, int n_vq, int N) {
+  return int64_t(n_vq) * c.both_q + int64_t(n_kq - n_vq) * c.key_q + int64_t(N - n_kq) * c.both_16;
+}
+// Workgroups of a paged stream: enough that a wave's share of the stream's
+// bytes is at most wave_tokens(GQ) tokens of the cheapest kind, so no wave
+// range exceeds wave_cap(GQ) (the starts are rounded down by < 32).
+__host__ __device__ inline int paged_wgs(const PagedCost& c, int n_kq, int n_vq, int N, int GQ, int NW) {
+  const int64_t per_wg = int64_t(NW) * wave_tokens(GQ) * c.both_q;
+  const int64_t t = paged_total(c, n_kq, n_vq, N);
+  const int64_t w = (t + per_wg - 1) / per_wg;
+  return int(w < 1 ? 1 : w);
+}
+// First token of wave range w of nw over a paged stream (same rounding as
+// wave_bound): token where the cost reaches w/nw of the total, rounded down
+// to a multiple of kWaveAlign.  Monotone in w.
+__host__ __device__ inline int paged_bound(const PagedCost& c, int n_kq, int n_vq, int N, int w, int nw) {
+  if (w <= 0) return 0;
+  if (w >= nw) return N;
+  const int64_t total = paged_total(c, n_kq, n_vq, N);
+  const int64_t target = total / nw * w + (total % nw) * w / nw;
+  const int64_t c0 = int64_t(n_vq) * c.both_q, c1 = c0 + int64_t(n_kq - n_vq) * c.key_q;
+  int64_t t;
+  if (target < c0) t = target / c.both_q;
+  else if (target < c1) t = n_vq + (target - c0) / c.key_q;
+  else t = n_kq + (target - c1) / c.both_16;
+  const int64_t ta = t & ~int64_t(kWaveAlign - 1);
+  return int(ta < N ? ta : N);
+}
+
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s);
+hipError_t launch_decode_paged(const DecodeParams& p, int GQ, hipStream_t s);
 // LDS bytes of a decode workgroup of `waves` waves; -1 if (D, GQ) is unsupported
 // LDS bytes of a decode workgroup of `waves` waves; -1 if (D, GQ) is unsupported
 int64_t decode_lds_bytes(int D, int GQ, int waves);

@@ -279,6 +279,86 @@ kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes)
 kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream);
 
 /*
+ * Paged, ragged cache (the serving layout).  The KIVI note's outlook pairs
+ * the method with PagedAttention ("Conclusion and outlook"); the VQ-LLM note
+ * measures paged FlashDecoding baselines.  Every sequence b has its own
+ * lengths, and its quantized tokens live in fixed-size pages taken from one
+ * pool in any order, listed by a block table.
+ *
+ * kvq_page_layout -- the byte layout of one page: page_tokens (PT) tokens of
+ * one sequence for all n_kv_heads kv heads, keys and values at one bit width.
+ * Kv head h's block starts at h*head_bytes; inside it:
+ *   key codes   at 0:          PT rows in the key-run format (row t = the
+ *                              page's token t);
+ *   key meta    at kmeta_off:  the (scale, zero) pairs of the PT/group key
+ *                              groups, key-run meta format;
+ *   value codes at vcodes_off: PT/2 token-pair blocks, value-run format;
+ *   value meta  at vmeta_off:  value-run meta format.
+ * So a page block is exactly a key run and a value run of PT tokens:
+ * kvq_quantize_append with codes = page + h0*head_bytes (+ the offset),
+ * codes_stream_stride = meta_stream_stride = head_bytes and n_streams = the
+ * sequence's kv heads writes the tokens of one page (dst_tok = token - j*PT).
+ *   out[0] = head_bytes, out[1] = kmeta_off, out[2] = vcodes_off,
+ *   out[3] = vmeta_off, out[4] = page_bytes = n_kv_heads * head_bytes
+ *   (all multiples of 16).
+ * page_tokens: a positive multiple of 64 and of group, at most 65536.
+ * bits 2, 4 or 8; group in {32, 64, 128}, group <= d_h; d_h 64 or 128.
+ */
+kvq_status kvq_page_layout(int32_t n_kv_heads, int32_t d_h, int32_t group, int32_t bits,
+                           int32_t page_tokens, int64_t out[5]);
+
+typedef struct kvq_paged_args {
+  int32_t batch, n_q_heads, n_kv_heads, d_h, group, bits;
+  float sm_scale;             /* logit scale (1/sqrt(d_h) in the workloads)          */
+  int32_t page_tokens;        /* PT, as in kvq_page_layout                           */
+  const void* q;              /* fp16 [batch][n_q_heads][d_h]                        */
+  const void* pages;          /* device pool; page p starts at pages + p*page_bytes  */
+  int64_t page_bytes;         /* >= kvq_page_layout's page_bytes, multiple of 16     */
+  const int32_t* block_table; /* device int32 [batch][max_pages]: sequence b's page j
+                                 (its tokens j*PT .. j*PT+PT-1) is pool page
+                                 block_table[b*max_pages + j]; the first
+                                 ceil(n_kq/PT) entries of a row must address pages
+                                 inside the pool (not checked on the device)      */
+  int32_t max_pages;
+  const int32_t* lengths;     /* host int32 [batch][4]: n_kq, n_vq, n_k_res, n_v_res */
+  const int32_t* lengths_dev; /* device int32 [batch][4] holding the same values     */
+  const void* k_res;          /* fp16 key residual: stream s = b*n_kv_heads + h has
+                                 rows at element s*k_res_stride, row i = token n_kq + i */
+  int64_t k_res_stride;
+  const void* v_res;          /* fp16 value residual, row i = token n_vq + i         */
+  int64_t v_res_stride;
+  float* out;                 /* fp32 [batch][n_q_heads][d_h]                         */
+  void* workspace;            /* device scratch, see kvq_decode_attn_paged_workspace  */
+  size_t workspace_bytes;
+} kvq_paged_args;
+
+/*
+ * Bytes of workspace kvq_decode_attn_paged needs (0 when every stream fits
+ * one workgroup; then workspace may be NULL).  It depends on the shapes and
+ * the host lengths only.  Partial softmax states; no initialization needed.
+ */
+kvq_status kvq_decode_attn_paged_workspace(const kvq_paged_args* args, size_t* bytes);
+
+/*
+ * kvq_decode_attn_paged -- decode attention over a paged, ragged cache: for
+ * every (b, hq), with kv = hq / (n_q_heads / n_kv_heads), one softmax over
+ * the sequence's N_b = n_kq + n_k_res logits (tokens 0..n_kq-1 dequantized
+ * from its pages, then its key residual rows) and
+ * out = sum_t p_t V'_t with tokens 0..n_vq-1 dequantized from the pages and
+ * the rest from its value residual rows -- the same result as
+ * kvq_decode_attn over one key run of n_kq and one value run of n_vq tokens.
+ * Checks (all before any launch), per sequence: n_kq % group == 0,
+ * 0 <= n_vq <= n_kq, n_k_res, n_v_res >= 0, n_kq + n_k_res == n_vq + n_v_res
+ * = N_b with 1 <= N_b <= 2^22, ceil(n_kq / PT) <= max_pages; a value count
+ * n_vq that is odd needs the missing pair partner's (scale, zero) finite
+ * (kvq_quantize_append leaves it zero); pointers 16-byte aligned, residual
+ * strides multiples of 8 elements, workspace large enough; n_q_heads /
+ * n_kv_heads <= 8.  Reads the pages, the residuals and q; writes out and the
+ * workspace only.
+ */
+kvq_status kvq_decode_attn_paged(const kvq_paged_args* args, void* stream);
+
+/*
  * kvq_window_thresholds -- the two score thresholds of a layer (WindowQuant
  * Sec. 3.2.3, Eq. 10 and 11): with s the layer's hidden-state similarity
  * (Eq. 9) and alpha the hyper-parameter,
