@@ -226,3 +226,85 @@ def test_window_search_rejects(kw, code):
     with pytest.raises(KvqError) as e:
         kvq.kvq_window_search(**_search(**kw))
     assert e.value.status == code
+
+
+# --- paged, ragged cache -----------------------------------------------------
+
+@pytest.mark.parametrize("H,d,G,bits,PT", [(32, 128, 32, 2, 256), (2, 64, 64, 4, 64), (8, 128, 128, 8, 128)])
+def test_page_layout_is_a_key_run_and_a_value_run(H, d, G, bits, PT):
+    # a head block = PT key rows, PT/G key groups of (scale, zero) pairs,
+    # PT/2 value pair blocks, PT * d/G value pairs (the run formats)
+    L = kvq.kvq_page_layout(H, d, G, bits, PT)
+    rb = d * bits // 8
+    assert L["kmeta_off"] == PT * rb
+    assert L["vcodes_off"] == PT * rb + (PT // G) * d * 4
+    assert L["vmeta_off"] == L["vcodes_off"] + (PT // 2) * 2 * rb
+    assert L["head_bytes"] == L["vmeta_off"] + PT * (d // G) * 4
+    assert L["page_bytes"] == H * L["head_bytes"] and L["page_bytes"] % 16 == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(PT=96), EUNSUP), (dict(PT=64, G=128), EUNSUP), (dict(bits=16), EINVAL),
+    (dict(G=128, d=64), EUNSUP), (dict(H=0), EINVAL),
+])
+def test_page_layout_rejects(kw, code):
+    a = dict(H=4, d=128, G=32, bits=2, PT=256)
+    a.update(kw)
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_page_layout(a["H"], a["d"], a["G"], a["bits"], a["PT"])
+    assert e.value.status == code
+
+
+def _paged(lengths, **kw):
+    """kvq_decode_attn_paged with fake device pointers (the host checks only)."""
+    import numpy as np
+    lens = np.asarray(lengths, dtype=np.int32).reshape(-1, 4)
+    a = kvq.PagedArgs()
+    a.batch, a.n_q_heads, a.n_kv_heads, a.d_h, a.group, a.bits = len(lens), 4, 2, 128, 32, 2
+    a.sm_scale, a.page_tokens = 0.088, 256
+    a.q = a.pages = a.block_table = a.lengths_dev = a.k_res = a.v_res = a.out = A
+    a.page_bytes = kvq.kvq_page_layout(2, 128, 32, 2, 256)["page_bytes"]
+    a.max_pages = 4
+    a.lengths = lens.ctypes.data
+    a.k_res_stride = a.v_res_stride = 129 * 128
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a, lens
+
+
+def test_paged_workspace_sizes():
+    # (n_kq, n_vq, n_k_res, n_v_res); one workgroup per stream -> no workspace
+    a, lens = _paged([[512, 385, 1, 128], [0, 0, 5, 5]])
+    assert kvq.kvq_decode_attn_paged_workspace(a) == 0
+    # an 8-wave workgroup covers 4096 tokens of 2-bit keys and values; 5120
+    # tokens need two: the workspace holds B * Hkv * 2 partial states of
+    # gq * (d + 2) floats
+    a, lens = _paged([[5120, 5000, 0, 120], [32, 0, 0, 32]], max_pages=20)
+    assert kvq.kvq_decode_attn_paged_workspace(a) == 2 * 2 * 2 * 2 * 130 * 4
+    a.workspace, a.workspace_bytes = A, 100
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_decode_attn_paged(a, 0)
+    assert e.value.status == EWS
+
+
+@pytest.mark.parametrize("lengths,kw,code", [
+    ([[33, 0, 0, 33]], {}, EINVAL),                 # n_kq not whole key groups
+    ([[64, 65, 0, -1]], {}, EINVAL),                # n_vq > n_kq
+    ([[64, 0, 1, 64]], {}, EINVAL),                 # key and value totals differ
+    ([[0, 0, 0, 0]], {}, EINVAL),                   # no token at all
+    ([[1280, 1280, 0, 0]], {}, EINVAL),             # 5 pages > max_pages
+    ([[64, 64, 0, 0]], dict(page_bytes=16), EINVAL),
+    ([[64, 64, 0, 0]], dict(page_bytes=24576 * 2 + 8), EALIGN),
+    ([[64, 64, 0, 0]], dict(pages=A + 4), EALIGN),
+    ([[64, 64, 0, 0]], dict(block_table=A + 2), EALIGN),
+    ([[64, 64, 0, 0]], dict(k_res_stride=12), EALIGN),
+    ([[64, 64, 0, 0]], dict(lengths_dev=None), EINVAL),
+    ([[64, 64, 0, 0]], dict(n_q_heads=36, n_kv_heads=2), EUNSUP),
+    ([[64, 64, 0, 0]], dict(page_tokens=100), EUNSUP),
+    ([[64, 32, 0, 32]], dict(v_res=None), EINVAL),  # value residual rows but no buffer
+])
+def test_paged_rejects(lengths, kw, code):
+    a, lens = _paged(lengths, **kw)
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_decode_attn_paged(a, 0)
+    assert e.value.status == code
