@@ -209,6 +209,67 @@ def window_search_rate(dev, stream, reps: int = 30, copies: int = 3):
             "us_per_call": round(us, 2), "bytes_read": read, "GBs": round(read / (us * 1e-6) / 1e9, 1)}
 
 
+def paged_ragged_rate(dev, stream, n_seq: int = 32, page_tokens: int = 256, copies: int = 2,
+                      reps: int = 40):
+    """kvq_decode_attn_paged on a ragged batch in pages: 32 sequences x 32
+    heads (Llama-2-7B attention), d128, G32, R128, int2, page 256 tokens,
+    contexts from workloads.ragged_contexts (log-uniform in [512, 8192]);
+    each sequence is in the state after its prefill and one decode step.
+    Consecutive calls use different cache copies (> 2 x 256 MB in total)."""
+    import torch
+    from decode_attention_kivi_amd.cache import PagedKiviCache, kivi_step_lengths
+    H, d, G, R, bits = 32, 128, 32, 128, 2
+    ctx = workloads.ragged_contexts(n_seq)
+    g = torch.Generator(device=dev).manual_seed(5)
+    caches = []
+    for c in range(copies):
+        cache = PagedKiviCache(n_seq, H, d, bits, G, R, page_tokens, max(ctx) + 1, device=dev, seed=c)
+        for b, L in enumerate(ctx):
+            k = torch.randn(H, L + 1, d, generator=g, device=dev).half()
+            v = torch.randn(H, L + 1, d, generator=g, device=dev).half()
+            cache.fill_step(b, k, v)
+            del k, v
+        caches.append(cache)
+    q = torch.randn(n_seq, H, d, generator=g, device=dev).half()
+    outs = [torch.empty(n_seq, H, d, dtype=torch.float32, device=dev) for _ in caches]
+    sm = 1.0 / d ** 0.5
+    for c, o in zip(caches, outs):
+        c.attend(q, sm, out=o)                      # workspace allocated outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(4):
+                for c, o in zip(caches, outs):
+                    c.attend(q, sm, out=o)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (reps * 4 * copies) * 1e3
+    rb = d * bits // 8
+    nbytes = 0
+    for L in ctx:
+        n_kq, r_k, n_vq, r_v = kivi_step_lengths(L, R)
+        nbytes += H * (n_kq * (rb + d * 4 // G) + n_vq * (rb + (d // G) * 4) + (r_k + r_v) * d * 2)
+    nbytes += n_seq * H * d * (2 + 4)
+    wg = caches[0].args(q, sm, outs[0])
+    import decode_attention_kivi_amd as kvq
+    ws = kvq.kvq_decode_attn_paged_workspace(wg)
+    del caches
+    return {"config": f"{n_seq} sequences, 32 heads, d128, G32, R128, int2, page {page_tokens} tokens, "
+                      f"contexts log-uniform in [512, 8192] (total {sum(ctx) + n_seq} tokens), "
+                      f"{copies} rotating cache copies",
+            "us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes),
+            "GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 8e12, 4),
+            "merge_kernel": ws > 0}
+
+
 def streaming_read_ceiling(dev, stream, gib: float = 1.0, reps: int = 20) -> float:
     """GB/s of a plain streaming read on this GPU: torch's sum over a 1 GiB
     buffer (well past the 256 MB Infinity Cache), the practical ceiling the
@@ -379,7 +440,7 @@ def main():
         attn_ms = step_ms = None
         attn_pct = step_pct = (float("nan"),) * 3
         n_steps = 0
-        components = ceiling = search_rate = None
+        components = ceiling = search_rate = paged_rate = None
         if attn_graph is not None:
             attn_ms, n_steps, attn_pct = timed(attn_graph, args.steps, args.warmup)
         if step_graph is not None:
@@ -388,6 +449,7 @@ def main():
             components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
             ceiling = streaming_read_ceiling(dev, stream)
             search_rate = window_search_rate(dev, stream)
+            paged_rate = paged_ragged_rate(dev, stream)
     torch.cuda.synchronize()
 
     if args.part != "all":
@@ -426,6 +488,7 @@ def main():
         "us_per_step_p10_p50_p90": [round(x * 1e3, 2) for x in step_pct],
         "components_us": components,
         "window_search": search_rate,
+        "paged_ragged": paged_rate,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)

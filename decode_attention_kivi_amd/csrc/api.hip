@@ -260,6 +260,8 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   const kvq::PagedCost pc = kvq::paged_cost(D, G, a->bits);
   int wg_max = 1;
   bool any_kres = false, any_vres = false;
+  std::vector<std::pair<double, int>> order;      // (-cost per workgroup, sequence)
+  std::vector<int> seq_wgs(a->batch);
   for (int b = 0; b < a->batch; ++b) {
     const int64_t nk = a->lengths[4 * b], nv = a->lengths[4 * b + 1];
     const int64_t rk = a->lengths[4 * b + 2], rv = a->lengths[4 * b + 3];
@@ -269,7 +271,10 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
     if ((nk + a->page_tokens - 1) / a->page_tokens > a->max_pages) return KVQ_EINVAL;
     any_kres |= rk > 0;
     any_vres |= rv > 0;
-    wg_max = std::max(wg_max, kvq::paged_wgs(pc, int(nk), int(nv), int(N), GQ, kvq::kWaves));
+    const int nwg = kvq::paged_wgs(pc, int(nk), int(nv), int(N), GQ, kvq::kWaves);
+    wg_max = std::max(wg_max, nwg);
+    seq_wgs[b] = nwg;
+    order.emplace_back(-double(kvq::paged_total(pc, int(nk), int(nv), int(N))) / nwg, b);
   }
   if ((any_kres && !a->k_res) || (any_vres && !a->v_res)) return KVQ_EINVAL;
   if (wg_max > (1 << 16)) return KVQ_EUNSUPPORTED;
@@ -305,6 +310,22 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   p.pg_vcodes_off = int32_t(L.vcodes_off);
   p.pg_vmeta_off = int32_t(L.vmeta_off);
   p.bits = a->bits;
+  if (a->batch <= kvq::kMaxSched) {
+    // heaviest workgroups first (longest-processing-time order), so the
+    // longest sequences do not start last; stable for equal costs
+    std::stable_sort(order.begin(), order.end(),
+                     [](const std::pair<double, int>& x, const std::pair<double, int>& y) { return x.first < y.first; });
+    int64_t acc = 0;
+    p.sched_n = a->batch;
+    for (int k = 0; k < a->batch; ++k) {
+      const int b = order[k].second;
+      p.sched_seq[k] = uint16_t(b);
+      p.sched_start[k] = int32_t(acc);
+      acc += int64_t(seq_wgs[b]) * a->n_kv_heads;
+    }
+    if (acc > INT32_MAX) return KVQ_EUNSUPPORTED;
+    p.sched_start[a->batch] = int32_t(acc);
+  }
   pl.GQ = GQ;
   pl.ws_bytes = wg_max == 1 ? 0
                             : size_t(a->batch) * size_t(a->n_kv_heads) * size_t(wg_max) * size_t(gq) *

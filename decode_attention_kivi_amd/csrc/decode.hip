@@ -599,8 +599,24 @@ decode_kernel(const DecodeParams P) {
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (scalar) so that every loop bound derived from it is scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = blockIdx.x;
-  const int64_t stream = blockIdx.y;
+  int wg = blockIdx.x;
+  int64_t stream = blockIdx.y;
+  if constexpr (PAGED) {
+    if (P.sched_n > 0) {
+      // 1-D grid in the host's order: find the sequence that owns this workgroup
+      const int i = int(blockIdx.x);
+      int lo = 0, hi = P.sched_n - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (P.sched_start[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      const int per = (P.sched_start[lo + 1] - P.sched_start[lo]) / P.Hkv;   // workgroups per stream
+      const int j = i - P.sched_start[lo];
+      stream = int64_t(P.sched_seq[lo]) * P.Hkv + j / per;
+      wg = j % per;
+    }
+  }
   const int b = int(stream / P.Hkv), hkv = int(stream % P.Hkv);
   const int gw = wg * NW + wave;
   int N, n_kq, n_vq, a, e;
@@ -884,8 +900,9 @@ __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
 template <int D, int GQ, int NW, bool PAGED>
 hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
   const size_t lds = size_t(lds_bytes(decode_lds<D, GQ>(), NW));
-  hipLaunchKernelGGL((decode_kernel<D, GQ, NW, PAGED>), dim3(p.wg_per_stream, p.B * p.Hkv), dim3(NW * 64),
-                     lds, s, p);
+  const dim3 grid = PAGED && p.sched_n > 0 ? dim3(unsigned(p.sched_start[p.sched_n]), 1)
+                                           : dim3(p.wg_per_stream, p.B * p.Hkv);
+  hipLaunchKernelGGL((decode_kernel<D, GQ, NW, PAGED>), grid, dim3(NW * 64), lds, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_stream == 1) return e;
   const int64_t n = int64_t(p.B) * p.Hq * D;

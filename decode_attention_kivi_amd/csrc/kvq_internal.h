@@ -102,6 +102,7 @@ struct Run {            // device copy of kvq_segment
 // holding 2-bit codes (about 48).
 constexpr int kMaxPieces = 2 * kMaxRuns + 2;
 constexpr int kMaxBounds = 64;          // waves per stream with host-computed wave bounds
+constexpr int kMaxSched = 256;          // sequences of a paged call with a sorted schedule
 struct CostPiece {
   int32_t t0, cost;        // first token, bytes per token
   int64_t c0;              // cost of the tokens before t0
@@ -188,6 +189,15 @@ struct DecodeParams {
   const int32_t* lens;
   int64_t page_bytes, head_bytes;
   int32_t page_tokens, max_pages, pg_kmeta_off, pg_vcodes_off, pg_vmeta_off, bits;
+  // Paged schedule (sched_n > 0, batch <= kMaxSched): a 1-D grid of exactly
+  // the workgroups the streams need, heaviest workgroups first.  Sequence
+  // sched_seq[k] owns grid workgroups sched_start[k] .. sched_start[k+1]-1:
+  // n_kv_heads streams of (sched_start[k+1] - sched_start[k]) / n_kv_heads
+  // workgroups each.  sched_n = 0: grid (wg_per_stream, streams), surplus
+  // workgroups leave at once.
+  int32_t sched_n;
+  int32_t sched_start[kMaxSched + 1];
+  uint16_t sched_seq[kMaxSched];
 };
 
 // Byte costs per token of a paged stream (keys + values): both quantized,

@@ -90,3 +90,10 @@ def test_ragged_d64(kvq, hq, hkv):
 def test_page_equals_group(kvq):
     # pages of 128 tokens with groups of 128 tokens: one key group per page
     run_paged([129, 384, 1000], 2, 2, 128, 128, 128, 4, 128)
+
+
+def test_more_sequences_than_the_schedule(kvq):
+    # above 256 sequences the grid is (workgroups per stream, streams) with
+    # surplus workgroups leaving at once, instead of the sorted 1-D schedule
+    rng = np.random.default_rng(3)
+    run_paged([int(x) for x in rng.integers(0, 300, size=260)], 1, 1, 64, 32, 32, 2, 64)

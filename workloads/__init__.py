@@ -47,7 +47,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "unit_kv", "queries", "outlier_channels",
-    "full_kv", "window_bits", "sample_units", "search_tokens",
+    "full_kv", "window_bits", "sample_units", "search_tokens", "ragged_contexts",
 ]
 
 
@@ -234,3 +234,13 @@ def search_tokens(batch: int, n_text: int, n_visual: int, dim: int, window_token
     jitter = rng.normal(0.0, 0.1, size=(batch, n_visual, 1))
     visual = (rel[None, :, None] + jitter) * u + rng.standard_normal((batch, n_visual, dim))
     return text.astype(np.float16), visual.astype(np.float16)
+
+
+def ragged_contexts(n: int, lo: int = 512, hi: int = 8192, seed: int = 0) -> list:
+    """Context lengths of a serving-shaped decode batch: ``n`` sequences whose
+    cached lengths are log-uniform in [lo, hi] (``default_rng([seed, 6])``).
+    The pages' serving runs (ShareGPT requests, long-document tasks) mix short
+    and long sequences in one batch; this mix stands in for them."""
+    rng = np.random.default_rng([seed, 6])
+    x = np.exp(rng.uniform(np.log(lo), np.log(hi), size=n))
+    return [int(v) for v in np.floor(x)]
