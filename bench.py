@@ -307,9 +307,10 @@ def main():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "attention", "step"), default="all",
-                    help="profiling runs: time only the attention graph or only the step graph "
-                         "(and skip the extra measurements)")
+    ap.add_argument("--part", choices=("all", "attention", "step", "paged"), default="all",
+                    help="profiling runs: time only the attention graph, only the step graph, "
+                         "or only the paged ragged batch (and skip the extra measurements)")
+    ap.add_argument("--page-tokens", type=int, default=256, help="page size of the paged ragged batch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -324,6 +325,10 @@ def main():
     if not os.path.exists(lib):
         import __graft_entry__
         __graft_entry__.build()
+    if args.part == "paged":
+        r = paged_ragged_rate(torch.device("cuda:0"), torch.cuda.Stream(), page_tokens=args.page_tokens)
+        print(json.dumps({"part": "paged", **r}), flush=True)
+        return
 
     w = workloads.get(args.workload)
     assert not w.mixed, "bench runs the uniform KIVI workloads"
@@ -449,7 +454,7 @@ def main():
             components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
             ceiling = streaming_read_ceiling(dev, stream)
             search_rate = window_search_rate(dev, stream)
-            paged_rate = paged_ragged_rate(dev, stream)
+            paged_rate = paged_ragged_rate(dev, stream, page_tokens=args.page_tokens)
     torch.cuda.synchronize()
 
     if args.part != "all":
