@@ -120,13 +120,12 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   const int64_t cost_total = pieces.back().c0 + (N - pieces.back().t0) * pieces.back().cost;
 
   // Each stream's N tokens are cut into kWaves * n_wg wave ranges of about
-  // equal cost, kWaves waves per workgroup.  The automatic choice aims at
-  // wave_tokens(GQ) tokens per wave (one workgroup per stream when that
-  // covers it: no partial states, no merge kernel) and shortens the ranges
-  // while the grid has fewer than two workgroups per CU; split_tokens > 0
-  // asks for workgroups of that many tokens.  A plan whose longest wave range
-  // exceeds wave_cap(GQ) is refused (split_tokens) or refined (automatic).
-  const int64_t wg_tok = int64_t(kvq::kWaves) * kvq::wave_tokens(GQ);
+  // equal cost, kWaves waves per workgroup.  The automatic choice takes the
+  // n_wg with the least (rounds of the grid over the chip) x (tokens per
+  // workgroup), ties to fewer workgroups (n_wg = 1: no partial states, no
+  // merge kernel), among the counts whose waves hold at least 64 tokens and
+  // at most wave_cap(GQ); split_tokens > 0 asks for workgroups of that many
+  // tokens (refused when a wave range would exceed wave_cap(GQ)).
   auto longest = [&](int64_t nws) {
     int64_t worst = 0;
     int prev = 0;
@@ -143,12 +142,24 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
     if (n_wg > (int64_t(1) << 20)) return KVQ_EUNSUPPORTED;
     if (longest(kvq::kWaves * n_wg) > kvq::wave_cap(GQ)) return KVQ_EUNSUPPORTED;
   } else {
-    n_wg = std::max<int64_t>(1, (N + wg_tok / 2) / wg_tok);
-    while (streams * n_wg < 512 && (N + 2 * kvq::kWaves * n_wg - 1) / (2 * kvq::kWaves * n_wg) >= 64)
-      n_wg *= 2;
-    while (longest(kvq::kWaves * n_wg) > kvq::wave_cap(GQ)) {
-      if (n_wg >= (int64_t(1) << 20)) return KVQ_EUNSUPPORTED;
-      n_wg *= 2;
+    const int64_t fill = 256 * kvq::decode_wgs_per_cu(GQ);   // workgroups resident at once
+    int64_t n_min = std::max<int64_t>(1, (N + int64_t(kvq::kWaves) * kvq::wave_tokens(GQ) * 3 / 2 - 1) /
+                                             (int64_t(kvq::kWaves) * kvq::wave_tokens(GQ) * 3 / 2));
+    while (longest(kvq::kWaves * n_min) > kvq::wave_cap(GQ)) {
+      if (n_min >= (int64_t(1) << 20)) return KVQ_EUNSUPPORTED;
+      n_min += std::max<int64_t>(1, n_min / 8);
+    }
+    n_wg = n_min;
+    double best = -1;
+    for (int64_t c = n_min; c <= std::min(8 * n_min, n_min + 256); ++c) {
+      if (c > n_min && (N + kvq::kWaves * c - 1) / (kvq::kWaves * c) < 64) break;
+      if (c > n_min && longest(kvq::kWaves * c) > kvq::wave_cap(GQ)) continue;
+      const double rounds = double((streams * c + fill - 1) / fill);
+      const double t = rounds * double(N) / double(c);
+      if (best < 0 || t < best * (1 - 1e-9)) {
+        best = t;
+        n_wg = c;
+      }
     }
   }
   const int nw = kvq::kWaves;

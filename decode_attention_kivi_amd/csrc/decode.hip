@@ -35,7 +35,10 @@ namespace kvq {
 namespace {
 
 constexpr int NT = kThreads;
-constexpr int NBV = 2;   // loads per batch in the value streaming loops (two batches in flight)
+// Loads per batch in the value streaming loops (two batches in flight): grouped
+// heads run at two waves per SIMD whatever their register count, so they
+// keep twice the loads in flight.
+template <int GQ> constexpr int value_batch() { return GQ == 1 ? 2 : 3; }
 
 // Make this wave's LDS writes visible to its own later LDS reads.  LDS
 // operations of one wave execute in order; this only keeps the compiler from
@@ -408,7 +411,11 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W,
   using UP = Unpacker<BITS, true>;        // offsets up to 1024, fewer shifts
   constexpr int NP = UP::NP;              // channels per 16-bit unit
   const UP unpack;                        // constants in registers, once
-  constexpr int HPP = (GQ * CPCV <= 64) ? GQ : ((64 / CPCV) > 0 ? (64 / CPCV) : 1);
+  // heads per pass over the values: every head at once up to 4 heads (their
+  // accumulators fit the two-waves-per-SIMD register budget), so the codes
+  // are read and unpacked once
+  constexpr int HPP = GQ <= 4 ? GQ : (64 / CPCV > 1 ? 64 / CPCV : 1);
+  constexpr int NBV = value_batch<GQ>();
   constexpr int NX = CPCV + 2;
   const int NG = D >> P.lg_g;
   const int my_p = lane / CPP, my_c = lane % CPP;

@@ -15,8 +15,15 @@ constexpr int kLdsLimit = 160 * 1024;  // LDS of one gfx950 CU: the most a workg
 constexpr int kWaveAlign = 32;         // wave token ranges start at multiples of this
 
 // Target tokens per wave; a wave may get up to wave_cap(GQ) tokens.  Larger
-// GQ needs more LDS per token (logits and probabilities of GQ heads).
-__host__ __device__ constexpr int wave_tokens(int GQ) { return 512 / GQ; }
+// GQ needs more LDS per token (logits and probabilities of GQ heads).  With
+// one query head per kv head two workgroups share a CU (48 KB of LDS each);
+// grouped heads run one 8-wave workgroup per CU (their registers), so its
+// waves take the longest ranges whose LDS still fits the CU's 160 KB
+// (96 / 156 / 155 KB at d128 for 2 / 4 / 8 heads): every range restart
+// drains a wave's load pipeline, and short waves are all restarts.
+__host__ __device__ constexpr int wave_tokens(int GQ) { return GQ <= 2 ? 512 : GQ == 4 ? 384 : 112; }
+// workgroups per CU of the decode kernel (its register budget)
+__host__ __device__ constexpr int decode_wgs_per_cu(int GQ) { return GQ == 1 ? 2 : 1; }
 __host__ __device__ constexpr int wave_cap(int GQ) { return wave_tokens(GQ) * 3 / 2 + kWaveAlign; }
 // token slots per wave in LDS: the cap plus 32, since the streaming loops
 // read and write whole items (up to 32 tokens) past a range's last token

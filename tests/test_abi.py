@@ -119,7 +119,8 @@ def test_workspace_size_follows_the_split_plan():
     (dict(v_segs=[(2, 5, 200, 0, 0)]), EINVAL), (dict(q=A + 2), EALIGN),
     (dict(k_codes_stride=100), EALIGN), (dict(k_res_stride=12), EALIGN),
     (dict(sm_scale=float("nan")), EINVAL), (dict(k_codes=None), EINVAL),
-    (dict(k_segs=[(2, 0, 2048, 0, 0)], v_segs=[(2, 0, 1992, 0, 0)], split_tokens=1 << 20), EUNSUP),
+    # one forced workgroup for 8195 tokens: waves of ~1024 tokens exceed the cap
+    (dict(k_segs=[(2, 0, 8192, 0, 0)], v_segs=[(2, 0, 8136, 0, 0)], split_tokens=1 << 20), EUNSUP),
     (dict(group=128, d_h=64), EUNSUP),
     # a quantized key run must start on a group boundary, a quantized value run on a pair
     (dict(k_segs=[(16, 0, 16, 0, 0), (2, 16, 256, 4096, 0)], v_segs=[(2, 0, 216, 0, 0)]), EUNSUP),
@@ -276,12 +277,12 @@ def test_paged_workspace_sizes():
     # (n_kq, n_vq, n_k_res, n_v_res); one workgroup per stream -> no workspace
     a, lens = _paged([[512, 385, 1, 128], [0, 0, 5, 5]])
     assert kvq.kvq_decode_attn_paged_workspace(a) == 0
-    # with 2 query heads per kv head an 8-wave workgroup covers 8 * 256 tokens
+    # with 2 query heads per kv head an 8-wave workgroup covers 8 * 512 tokens
     # of 2-bit keys and values (96 bytes each); 5000 such tokens plus 120
-    # residual-value tokens (304 bytes) need three: the workspace holds
-    # B * Hkv * 3 partial states of gq * (d + 2) floats
+    # residual-value tokens (304 bytes) need two: the workspace holds
+    # B * Hkv * 2 partial states of gq * (d + 2) floats
     a, lens = _paged([[5120, 5000, 0, 120], [32, 0, 0, 32]], max_pages=20)
-    assert kvq.kvq_decode_attn_paged_workspace(a) == 2 * 2 * 3 * 2 * 130 * 4
+    assert kvq.kvq_decode_attn_paged_workspace(a) == 2 * 2 * 2 * 2 * 130 * 4
     a.workspace, a.workspace_bytes = A, 100
     with pytest.raises(KvqError) as e:
         kvq.kvq_decode_attn_paged(a, 0)
