@@ -270,6 +270,54 @@ def paged_ragged_rate(dev, stream, n_seq: int = 32, page_tokens: int = 256, copi
             "merge_kernel": ws > 0}
 
 
+def windows_decode_rate(dev, stream, reps: int = 50):
+    """kvq_decode_attn on the mixed-precision window cache (qwen2_7b_windows:
+    28 q / 4 kv heads, 128 windows x 256 tokens at 8/4/2 bits after the
+    reorder + 65 fp16 tokens).  Its 17.7 MB fit the 256 MB Infinity Cache, so
+    this is the launch-latency-bound case (the rate is not an HBM rate)."""
+    import torch
+    from decode_attention_kivi_amd.cache import WindowCache
+    w = workloads.get("qwen2_7b_windows")
+    k, v = workloads.full_kv(w)
+    bits = workloads.window_bits(w, k)
+    q = torch.from_numpy(workloads.queries(w)).to(dev)
+    cache = WindowCache(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
+                        torch.from_numpy(bits).to(dev), w.window_tokens, w.group)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    cache.attend(q, w.sm_scale, out=out)            # workspace outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(16):
+                cache.attend(q, w.sm_scale, out=out)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (reps * 16) * 1e3
+    d, G, H = w.d_h, w.group, w.n_kv_heads
+    nbytes = 0
+    for sg in cache.segs:
+        b, n = sg[0], sg[2]
+        if b == 16:
+            nbytes += 2 * n * d * 2
+        else:
+            nbytes += n * d * b // 8 + n // G * d * 4 + n * d * b // 8 + n * (d // G) * 4
+    nbytes = H * (nbytes + 2 * cache.n_res * d * 2) + w.batch * w.n_q_heads * d * 6
+    return {"config": "qwen2_7b_windows: B1, 28 q / 4 kv heads, 128 windows x 256 tokens "
+                      f"({int((bits == 8).sum())} int8 / {int((bits == 4).sum())} int4 / "
+                      f"{int((bits == 2).sum())} int2, reordered) + {cache.n_res} fp16 tokens; "
+                      "cache-resident (17.7 MB), launch-latency-bound",
+            "us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes),
+            "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def streaming_read_ceiling(dev, stream, gib: float = 1.0, reps: int = 20) -> float:
     """GB/s of a plain streaming read on this GPU: torch's sum over a 1 GiB
     buffer (well past the 256 MB Infinity Cache), the practical ceiling the
@@ -445,7 +493,7 @@ def main():
         attn_ms = step_ms = None
         attn_pct = step_pct = (float("nan"),) * 3
         n_steps = 0
-        components = ceiling = search_rate = paged_rate = None
+        components = ceiling = search_rate = paged_rate = windows_rate = None
         if attn_graph is not None:
             attn_ms, n_steps, attn_pct = timed(attn_graph, args.steps, args.warmup)
         if step_graph is not None:
@@ -455,6 +503,7 @@ def main():
             ceiling = streaming_read_ceiling(dev, stream)
             search_rate = window_search_rate(dev, stream)
             paged_rate = paged_ragged_rate(dev, stream, page_tokens=args.page_tokens)
+            windows_rate = windows_decode_rate(dev, stream)
     torch.cuda.synchronize()
 
     if args.part != "all":
@@ -494,6 +543,7 @@ def main():
         "components_us": components,
         "window_search": search_rate,
         "paged_ragged": paged_rate,
+        "windows_decode": windows_rate,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
