@@ -47,7 +47,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "unit_kv", "queries", "outlier_channels",
-    "full_kv", "window_bits", "sample_units", "search_tokens", "ragged_contexts",
+    "full_kv", "window_bits", "sample_units", "search_tokens", "ragged_contexts", "pq_inputs",
 ]
 
 
@@ -244,3 +244,17 @@ def ragged_contexts(n: int, lo: int = 512, hi: int = 8192, seed: int = 0) -> lis
     rng = np.random.default_rng([seed, 6])
     x = np.exp(rng.uniform(np.log(lo), np.log(hi), size=n))
     return [int(v) for v in np.floor(x)]
+
+
+def pq_inputs(batch: int, n_kv_heads: int, n_tok: int, d_h: int, m: int, bits: int, seed: int = 0):
+    """PQ centroids and codes of a decode batch (PQCache note, "Method
+    details", Step 2 shapes): centroids fp16 [B][Hkv][m][2^bits][d_h/m] drawn
+    N(0, 1/m) (so a rebuilt key has about unit variance per channel), codes
+    uint8 [B][Hkv][n_tok][m] uniform in [0, 2^bits); ``default_rng([seed, 8])``.
+    K-means construction is not part of the path: these stand in for its
+    output."""
+    rng = np.random.default_rng([seed, 8])
+    dm = d_h // m
+    c = rng.standard_normal((batch, n_kv_heads, m, 1 << bits, dm), dtype=np.float32) / np.float32(np.sqrt(m))
+    codes = rng.integers(0, 1 << bits, size=(batch, n_kv_heads, n_tok, m), dtype=np.uint8)
+    return c.astype(np.float16), codes
