@@ -24,6 +24,7 @@ __all__ = [
     "KiviCacheDesc", "kvq_kivi_step_workspace", "kvq_kivi_step",
     "kvq_window_thresholds", "kvq_window_search_workspace", "kvq_window_search",
     "PagedArgs", "kvq_page_layout", "kvq_decode_attn_paged_workspace", "kvq_decode_attn_paged",
+    "kvq_pq_search",
 ]
 
 KVQ_KEYS = 0
@@ -156,6 +157,8 @@ def _load():
     lib.kvq_decode_attn_paged_workspace.argtypes = [ctypes.POINTER(PagedArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.kvq_decode_attn_paged.restype = i32
     lib.kvq_decode_attn_paged.argtypes = [ctypes.POINTER(PagedArgs), vp]
+    lib.kvq_pq_search.restype = i32
+    lib.kvq_pq_search.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp, vp]
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -328,3 +331,11 @@ def kvq_decode_attn_paged_workspace(args: PagedArgs) -> int:
 
 def kvq_decode_attn_paged(args: PagedArgs, stream=None):
     _check(_load().kvq_decode_attn_paged(ctypes.byref(args), _stream(stream)), "kvq_decode_attn_paged")
+
+
+def kvq_pq_search(batch, n_q_heads, n_kv_heads, d_h, m, bits, n_tok, top_k, q, centroids, codes,
+                  codes_stride, scores, top_idx, stream=None):
+    """PQCache decode-time PQ search: approximate scores and Top-k tokens."""
+    _check(_load().kvq_pq_search(batch, n_q_heads, n_kv_heads, d_h, m, bits, n_tok, top_k, _dev(q),
+                                 _dev(centroids), _dev(codes), int(codes_stride), _dev(scores),
+                                 _dev(top_idx), _stream(stream)), "kvq_pq_search")

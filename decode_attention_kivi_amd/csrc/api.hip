@@ -541,6 +541,47 @@ kvq_status kvq_decode_attn_paged(const kvq_paged_args* args, void* stream) {
   return from_hip(kvq::launch_decode_paged(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_h, int32_t m,
+                         int32_t bits, int32_t n_tok, int32_t top_k, const void* q, const void* centroids,
+                         const void* codes, int64_t codes_stride, float* scores, int32_t* top_idx,
+                         void* stream) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0) return KVQ_EINVAL;
+  const int gq = n_q_heads / n_kv_heads;
+  if (gq > 8 || int64_t(batch) * n_kv_heads > 65535 || int64_t(batch) * n_q_heads > (int64_t(1) << 31))
+    return KVQ_EUNSUPPORTED;
+  if (!valid_d(d_h)) return KVQ_EUNSUPPORTED;
+  if (m < 1 || d_h % m != 0 || (d_h / m) % 8 != 0 || 16 % m != 0) return KVQ_EUNSUPPORTED;
+  if (bits < 1 || bits > 8) return KVQ_EINVAL;
+  if (n_tok < 1 || n_tok > (1 << 24) || top_k < 1 || top_k > n_tok) return KVQ_EINVAL;
+  if (!q || !centroids || !codes || !scores || !top_idx) return KVQ_EINVAL;
+  if (codes_stride < int64_t(n_tok) * m) return KVQ_EINVAL;
+  if (codes_stride & 15) return KVQ_EALIGN;
+  for (const void* ptr : {q, centroids, codes, static_cast<const void*>(scores)})
+    if (!aligned16(ptr)) return KVQ_EALIGN;
+  if (reinterpret_cast<uintptr_t>(top_idx) & 3) return KVQ_EALIGN;
+  int GQ = 1;
+  while (GQ < gq) GQ *= 2;
+  if (kvq::pq_scores_lds_bytes(GQ, d_h, m, bits) > 64 * 1024) return KVQ_EUNSUPPORTED;
+  kvq::PqParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.centroids = static_cast<const uint16_t*>(centroids);
+  p.codes = static_cast<const uint8_t*>(codes);
+  p.scores = scores;
+  p.top_idx = top_idx;
+  p.codes_stride = codes_stride;
+  p.B = batch;
+  p.Hq = n_q_heads;
+  p.Hkv = n_kv_heads;
+  p.gq = gq;
+  p.D = d_h;
+  p.m = m;
+  p.bits = bits;
+  p.n_tok = n_tok;
+  p.top_k = top_k;
+  p.chunk_tokens = 2048;
+  return from_hip(kvq::launch_pq_search(p, GQ, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

@@ -359,6 +359,37 @@ kvq_status kvq_decode_attn_paged_workspace(const kvq_paged_args* args, size_t* b
 kvq_status kvq_decode_attn_paged(const kvq_paged_args* args, void* stream);
 
 /*
+ * kvq_pq_search -- PQCache's decode-time PQ search (PQCache note,
+ * "Background" on product quantization; "Method details", Steps 2 and 4):
+ * for every batch row b and query head hq, with kv = hq / (n_q_heads /
+ * n_kv_heads):
+ *   table[j][c] = q[b][hq][j*dm .. j*dm+dm) . centroids[b][kv][j][c][0..dm)
+ *                 for sub-space j < m, centroid c < 2^bits, dm = d_h / m
+ *                 (fp32 sums of fp16 products);
+ *   scores[b][hq][t] = sum_j table[j][codes[b][kv][t][j]]   (fp32, t < n_tok):
+ *                 the query's dot product with the key rebuilt from the
+ *                 centroids the token's codes name;
+ *   top_idx[b][hq][0..top_k) = the top_k tokens with the largest scores,
+ *                 ties to the lower token index, in ascending token order.
+ * Layouts: q fp16 [batch][n_q_heads][d_h]; centroids fp16
+ * [batch][n_kv_heads][m][2^bits][dm]; codes u8, stream s = b*n_kv_heads + kv
+ * at codes + s*codes_stride bytes, [n_tok][m]; scores fp32
+ * [batch][n_q_heads][n_tok] (written; the Top-k pass reads them back);
+ * top_idx int32 [batch][n_q_heads][top_k].
+ * Checks (before any launch): d_h 64 or 128; m divides 16 and d_h with dm a
+ * multiple of 8; 1 <= bits <= 8; 1 <= top_k <= n_tok <= 2^24; n_q_heads /
+ * n_kv_heads <= 8; codes_stride >= n_tok*m and a multiple of 16 (the kernel
+ * reads up to the next multiple of 16 past n_tok*m); the tables of a kv
+ * head's query heads fit 64 KB of LDS; q, centroids, codes, scores 16-byte
+ * aligned, top_idx 4-byte aligned.  Centroids and codes are inputs (the
+ * K-means construction of Step 2 runs elsewhere).
+ */
+kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_h,
+                         int32_t m, int32_t bits, int32_t n_tok, int32_t top_k,
+                         const void* q, const void* centroids, const void* codes,
+                         int64_t codes_stride, float* scores, int32_t* top_idx, void* stream);
+
+/*
  * kvq_window_thresholds -- the two score thresholds of a layer (WindowQuant
  * Sec. 3.2.3, Eq. 10 and 11): with s the layer's hidden-state similarity
  * (Eq. 9) and alpha the hyper-parameter,

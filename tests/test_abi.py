@@ -325,3 +325,21 @@ def test_split_plan_fills_the_chip_once():
     a = _decode(batch=16, n_q_heads=32, n_kv_heads=32, k_segs=[(2, 0, 4096, 0, 0)],
                 v_segs=[(2, 0, 3969, 0, 0)], n_k_res=1, n_v_res=128, split_tokens=0)
     assert kvq.kvq_decode_attn_workspace(a) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=3), EUNSUP), (dict(m=32), EUNSUP), (dict(d_h=96), EUNSUP), (dict(bits=9), EINVAL),
+    (dict(bits=0), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=101), EINVAL), (dict(n_tok=0), EINVAL),
+    (dict(codes_stride=192), EINVAL), (dict(codes_stride=204), EALIGN), (dict(q=A + 2), EALIGN),
+    (dict(top_idx=A + 2), EALIGN), (dict(scores=None), EINVAL), (dict(n_q_heads=7), EINVAL),
+    (dict(n_q_heads=4 * 16), EUNSUP),
+    # 8 query heads x 16 sub-spaces x 256 centroids of fp32 tables: 128 KB > 64 KB of LDS
+    (dict(n_q_heads=32, m=16, codes_stride=1600), EUNSUP),
+])
+def test_pq_search_rejects(kw, code):
+    a = dict(batch=2, n_q_heads=4, n_kv_heads=4, d_h=128, m=2, bits=8, n_tok=100, top_k=10,
+             q=A, centroids=A, codes=A, codes_stride=208, scores=A, top_idx=A, stream=0)
+    a.update(kw)
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_pq_search(**a)
+    assert e.value.status == code
