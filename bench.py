@@ -318,6 +318,47 @@ def windows_decode_rate(dev, stream, reps: int = 50):
             "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def pq_search_rate(dev, stream, reps: int = 50):
+    """kvq_pq_search (PQCache's decode-time PQ search) at the GQA long-context
+    shape: 4 sequences x 32 query heads over 8 kv heads, 32769 tokens, m = 2
+    sub-spaces of 256 centroids (8-bit codes), Top-k = 3277 (1/10 of the
+    tokens).  Per call: the scores kernel reads the codes and centroids and
+    writes fp32 scores; the Top-k kernel reads the scores back five times
+    (from L2) and writes the indices."""
+    import torch
+    import decode_attention_kivi_amd as kvq
+    B, Hq, Hkv, d, m, bits, n, k = 4, 32, 8, 128, 2, 8, 32769, 3277
+    w = workloads.Workload(name="pq", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, d_h=d, context=n,
+                           group=32, residual=32, bits=2)
+    c, codes = workloads.pq_inputs(B, Hkv, n, d, m, bits)
+    stride = (n * m + 15) // 16 * 16
+    padded = np.zeros((B * Hkv, stride), np.uint8)
+    padded[:, :n * m] = codes.reshape(B * Hkv, -1)
+    qt = torch.from_numpy(workloads.queries(w)).to(dev)
+    ct = torch.from_numpy(c).to(dev)
+    kt = torch.from_numpy(padded).to(dev)
+    sc = torch.empty(B, Hq, n, dtype=torch.float32, device=dev)
+    idx = torch.empty(B, Hq, k, dtype=torch.int32, device=dev)
+
+    def call():
+        kvq.kvq_pq_search(B, Hq, Hkv, d, m, bits, n, k, qt, ct, kt, stride, sc, idx, stream)
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = B * Hkv * (n * m + m * (1 << bits) * (d // m) * 2) + B * Hq * (d * 2 + n * 4 + k * 4)
+    return {"config": f"B{B}, {Hq} q / {Hkv} kv heads, d{d}, {n} tokens, m {m}, {1 << bits} centroids, "
+                      f"Top-k {k}", "us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes),
+            "tokens_scored_per_s": round(B * Hq * n / (us * 1e-6), 1)}
+
+
 def streaming_read_ceiling(dev, stream, gib: float = 1.0, reps: int = 20) -> float:
     """GB/s of a plain streaming read on this GPU: torch's sum over a 1 GiB
     buffer (well past the 256 MB Infinity Cache), the practical ceiling the
@@ -355,7 +396,7 @@ def main():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "attention", "step", "paged"), default="all",
+    ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq"), default="all",
                     help="profiling runs: time only the attention graph, only the step graph, "
                          "or only the paged ragged batch (and skip the extra measurements)")
     ap.add_argument("--page-tokens", type=int, default=256, help="page size of the paged ragged batch")
@@ -373,9 +414,10 @@ def main():
     if not os.path.exists(lib):
         import __graft_entry__
         __graft_entry__.build()
-    if args.part == "paged":
-        r = paged_ragged_rate(torch.device("cuda:0"), torch.cuda.Stream(), page_tokens=args.page_tokens)
-        print(json.dumps({"part": "paged", **r}), flush=True)
+    if args.part in ("paged", "pq"):
+        dev, st = torch.device("cuda:0"), torch.cuda.Stream()
+        r = paged_ragged_rate(dev, st, page_tokens=args.page_tokens) if args.part == "paged" else pq_search_rate(dev, st)
+        print(json.dumps({"part": args.part, **r}), flush=True)
         return
 
     w = workloads.get(args.workload)
@@ -493,7 +535,7 @@ def main():
         attn_ms = step_ms = None
         attn_pct = step_pct = (float("nan"),) * 3
         n_steps = 0
-        components = ceiling = search_rate = paged_rate = windows_rate = None
+        components = ceiling = search_rate = paged_rate = windows_rate = pq_rate = None
         if attn_graph is not None:
             attn_ms, n_steps, attn_pct = timed(attn_graph, args.steps, args.warmup)
         if step_graph is not None:
@@ -504,6 +546,7 @@ def main():
             search_rate = window_search_rate(dev, stream)
             paged_rate = paged_ragged_rate(dev, stream, page_tokens=args.page_tokens)
             windows_rate = windows_decode_rate(dev, stream)
+            pq_rate = pq_search_rate(dev, stream)
     torch.cuda.synchronize()
 
     if args.part != "all":
@@ -544,6 +587,7 @@ def main():
         "window_search": search_rate,
         "paged_ragged": paged_rate,
         "windows_decode": windows_rate,
+        "pq_search": pq_rate,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)

@@ -10,9 +10,13 @@
 //                     heads of one kv head in LDS (fp32 dot products of the
 //                     fp16 centroids and q), then 16-byte code loads (16/m
 //                     tokens per lane) and table lookups; scores fp32.
-//   pq_topk_kernel    one workgroup per (b, hq): radix select of the k-th
-//                     largest score over an order-preserving 32-bit key (four
-//                     passes of 8 bits, histograms in LDS), then a scanned
+//   pq_topk_kernel    one workgroup per (b, hq): the k-th largest score is
+//                     narrowed down by two levels of 2048 equal-width value
+//                     buckets (histograms in LDS: the scores spread over them,
+//                     where the leading bits of their float encodings would
+//                     pile into a few bins and serialize the atomics), then
+//                     found exactly by a radix select of the order-preserving
+//                     32-bit keys of the remaining candidates; a scanned
 //                     compaction writes the selected tokens in ascending
 //                     order, ties at the threshold to the lower token index.
 
@@ -136,38 +140,120 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* sh
   return r;
 }
 
+// Bucket of a score: 2^22 equal ranges of [lo, hi], taken as two levels of
+// 2048 (the high 11 bits of the id are the level-1 bin, the low 11 bits the
+// level-2 bin within it).  The id comes from one subtract-then-multiply, which
+// leaves no multiply-add for the compiler to fuse, so every pass that
+// recomputes a score's id gets the same id.  It is non-decreasing in the score
+// (fp32 subtraction of a constant and multiplication by a positive constant
+// preserve order), so equal scores share a bucket and a higher bucket holds
+// only higher scores.
+constexpr int kBins = 2048;
+__device__ __forceinline__ int bucket_id(float x, float lo, float s2) {
+  return min(kBins * kBins - 1, int(__fmul_rn(x - lo, s2)));
+}
+
+// The bin of hist[0..nbins) (counted from the top) that holds the k-th
+// largest element: returns the bin and, in *above, the count in higher bins.
+// One wave scans: lane L sums its 32 bins from the top, a wave scan finds
+// the crossing lane, which walks its bins.  Caller syncs before and after.
+__device__ __forceinline__ int find_bin(const uint32_t* hist, int nbins, uint32_t k, uint32_t* above,
+                                        uint32_t* sh) {
+  if (threadIdx.x < 64) {
+    if (threadIdx.x == 0) sh[0] = sh[1] = 0;
+    const int lane = threadIdx.x;
+    const int per = nbins / 64;
+    const int top = nbins - 1 - lane * per;             // this lane's bins: top, top-1, ..., top-per+1
+    uint32_t sum = 0;
+    for (int i = 0; i < per; ++i) sum += hist[top - i];
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const uint32_t excl = incl - sum;
+    if (excl < k && incl >= k) {                          // exactly one lane
+      uint32_t acc = excl;
+      int bin = top - per + 1;
+      for (int i = 0; i < per; ++i) {
+        const uint32_t c = hist[top - i];
+        if (acc + c >= k) { bin = top - i; break; }
+        acc += c;
+      }
+      sh[0] = uint32_t(bin);
+      sh[1] = acc;
+    }
+  }
+  __syncthreads();
+  *above = sh[1];
+  return int(sh[0]);
+}
+
 __global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P) {
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kBins];
   __shared__ uint32_t sh[72];
-  __shared__ uint32_t sel[2];
+  __shared__ float fsh[2 * kTopkThreads / 64];
   const int64_t head = blockIdx.x;                            // b * Hq + hq
   const float* sc = P.scores + head * P.n_tok;
-  const int n = P.n_tok, tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0, k_rem = uint32_t(P.top_k);
-  // four passes of 8 bits, most significant first: the digit of the k-th
-  // largest key among the keys that share the prefix found so far
+  const int n = P.n_tok, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // range of the scores
+  float lo = INFINITY, hi = -INFINITY;
+  for (int t = tid; t < n; t += kTopkThreads) {
+    const float x = sc[t] + 0.0f;
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  lo = span_min<64>(lo);
+  hi = span_max<64>(hi);
+  if (lane == 0) { fsh[wave] = lo; fsh[16 + wave] = hi; }
+  __syncthreads();
+  lo = fsh[0];
+  hi = fsh[16];
+  for (int w = 1; w < kTopkThreads / 64; ++w) { lo = fminf(lo, fsh[w]); hi = fmaxf(hi, fsh[16 + w]); }
+  // one bucket when the range is empty (or too narrow for a finite scale):
+  // the radix passes then resolve everything
+  float s2 = hi > lo ? float(kBins * kBins) / (hi - lo) : 0.f;
+  if (!(s2 < 1e30f)) s2 = 0.f;
+
+  // level 1 and level 2 buckets narrow the k-th largest score down
+  uint32_t k_rem = uint32_t(P.top_k), above;
+  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+  __syncthreads();
+  for (int t = tid; t < n; t += kTopkThreads) atomicAdd(&hist[bucket_id(sc[t] + 0.0f, lo, s2) >> 11], 1u);
+  __syncthreads();
+  const int b1 = find_bin(hist, kBins, k_rem, &above, sh);
+  k_rem -= above;
+  __syncthreads();
+  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+  __syncthreads();
+  for (int t = tid; t < n; t += kTopkThreads) {
+    const int id = bucket_id(sc[t] + 0.0f, lo, s2);
+    if ((id >> 11) == b1) atomicAdd(&hist[id & (kBins - 1)], 1u);
+  }
+  __syncthreads();
+  const int b2 = find_bin(hist, kBins, k_rem, &above, sh);
+  k_rem -= above;
+  __syncthreads();
+
+  // exact key among the candidates of bucket (b1, b2): four radix passes of
+  // 8 bits over their order-preserving keys
+  uint32_t prefix = 0, mask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     for (int t = tid; t < n; t += kTopkThreads) {
-      const uint32_t key = order_key(sc[t]);
+      const float x = sc[t] + 0.0f;
+      if (bucket_id(x, lo, s2) != b1 * kBins + b2) continue;
+      const uint32_t key = order_key(x);
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      uint32_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= k_rem) break;
-        above += hist[d];
-      }
-      sel[0] = uint32_t(d);
-      sel[1] = above;
-    }
-    __syncthreads();
-    prefix |= sel[0] << shift;
+    const int d = find_bin(hist, 256, k_rem, &above, sh);
+    k_rem -= above;
+    prefix |= uint32_t(d) << shift;
     mask |= 0xffu << shift;
-    k_rem -= sel[1];
     __syncthreads();
   }
   // prefix is the threshold key T: every key > T is selected and the first
