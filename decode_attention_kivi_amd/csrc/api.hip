@@ -561,7 +561,11 @@ kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
   if (reinterpret_cast<uintptr_t>(top_idx) & 3) return KVQ_EALIGN;
   int GQ = 1;
   while (GQ < gq) GQ *= 2;
-  if (kvq::pq_scores_lds_bytes(GQ, d_h, m, bits) > 64 * 1024) return KVQ_EUNSUPPORTED;
+  // one kernel when a head's scores fit in the 160 KB of LDS a gfx950
+  // workgroup can hold (up to about 38K tokens), else scores then Top-k
+  // through memory
+  const bool fused = kvq::pq_fused_lds_bytes(n_tok, d_h, m, bits) <= 160 * 1024;
+  if (!fused && kvq::pq_scores_lds_bytes(GQ, d_h, m, bits) > 64 * 1024) return KVQ_EUNSUPPORTED;
   kvq::PqParams p{};
   p.q = static_cast<const uint16_t*>(q);
   p.centroids = static_cast<const uint16_t*>(centroids);
@@ -579,7 +583,7 @@ kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
   p.n_tok = n_tok;
   p.top_k = top_k;
   p.chunk_tokens = 2048;
-  return from_hip(kvq::launch_pq_search(p, GQ, static_cast<hipStream_t>(stream)));
+  return from_hip(kvq::launch_pq_search(p, GQ, fused, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -300,7 +300,11 @@ struct PqParams {
   int32_t B, Hq, Hkv, gq, D, m, bits, n_tok, top_k, chunk_tokens;
 };
 int64_t pq_scores_lds_bytes(int gq_pow2, int D, int m, int bits);
-hipError_t launch_pq_search(const PqParams& p, int GQ, hipStream_t s);
+// LDS of the one-kernel search (a head's scores resident in LDS)
+int64_t pq_fused_lds_bytes(int n_tok, int D, int m, int bits);
+// fused: one workgroup per query head with its scores in LDS (the LDS must
+// hold pq_fused_lds_bytes); else the scores kernel, then the Top-k kernel
+hipError_t launch_pq_search(const PqParams& p, int GQ, bool fused, hipStream_t s);
 
 hipError_t launch_reorder(const uint8_t* win_bits, int32_t n_windows, int32_t S,
                           int32_t G, int32_t D, int32_t* perm, void* segs,

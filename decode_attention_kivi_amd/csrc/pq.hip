@@ -5,7 +5,7 @@
 // (the query's dot product with the key rebuilt from the centroids), then
 // the Top-k tokens by score.
 //
-// Two kernels:
+// Three kernels:
 //   pq_scores_kernel  grid (token chunks, B * Hkv): the tables of the GQ query
 //                     heads of one kv head in LDS (fp32 dot products of the
 //                     fp16 centroids and q), then 16-byte code loads (16/m
@@ -16,9 +16,11 @@
 //                     where the leading bits of their float encodings would
 //                     pile into a few bins and serialize the atomics), then
 //                     found exactly by a radix select of the order-preserving
-//                     32-bit keys of the remaining candidates; a scanned
+//                     32-bit keys of the remaining candidates; a ballot-based
 //                     compaction writes the selected tokens in ascending
 //                     order, ties at the threshold to the lower token index.
+//   pq_fused_kernel   one workgroup per (b, hq) doing both, the head's scores
+//                     resident in LDS (contexts up to about 38K tokens).
 
 #include "kvq_internal.h"
 #include "kvq_device.h"
@@ -110,36 +112,6 @@ __global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P)
   }
 }
 
-// Exclusive prefix sum over the block (1024 threads, 16 waves); returns this
-// thread's exclusive sum and the block total in *total.
-__device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t x, uint32_t* sh, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) sh[wave] = incl;
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    uint32_t wv = threadIdx.x < kTopkThreads / 64 ? sh[threadIdx.x] : 0u;
-    uint32_t wi = wv;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(wi, o, 64);
-      if (lane >= o) wi += y;
-    }
-    if (threadIdx.x < kTopkThreads / 64) sh[32 + threadIdx.x] = wi - wv;   // exclusive wave offsets
-    if (threadIdx.x == kTopkThreads / 64 - 1) sh[64] = wi;
-  }
-  __syncthreads();
-  const uint32_t r = sh[32 + wave] + incl - x;
-  *total = sh[64];
-  __syncthreads();
-  return r;
-}
-
 // Bucket of a score: 2^22 equal ranges of [lo, hi], taken as two levels of
 // 2048 (the high 11 bits of the id are the level-1 bin, the low 11 bits the
 // level-2 bin within it).  The id comes from one subtract-then-multiply, which
@@ -190,21 +162,9 @@ __device__ __forceinline__ int find_bin(const uint32_t* hist, int nbins, uint32_
   return int(sh[0]);
 }
 
-__global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t sh[72];
-  __shared__ float fsh[2 * kTopkThreads / 64];
-  const int64_t head = blockIdx.x;                            // b * Hq + hq
-  const float* sc = P.scores + head * P.n_tok;
-  const int n = P.n_tok, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // range of the scores
-  float lo = INFINITY, hi = -INFINITY;
-  for (int t = tid; t < n; t += kTopkThreads) {
-    const float x = sc[t] + 0.0f;
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
-  }
+// Range [lo, hi] of the n scores (+0 for -0), reduced over the block.
+__device__ __forceinline__ void block_range(float lo, float hi, float* fsh, float* lo_out, float* hi_out) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   lo = span_min<64>(lo);
   hi = span_max<64>(hi);
   if (lane == 0) { fsh[wave] = lo; fsh[16 + wave] = hi; }
@@ -212,42 +172,107 @@ __global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P)
   lo = fsh[0];
   hi = fsh[16];
   for (int w = 1; w < kTopkThreads / 64; ++w) { lo = fminf(lo, fsh[w]); hi = fmaxf(hi, fsh[16 + w]); }
+  __syncthreads();
+  *lo_out = lo;
+  *hi_out = hi;
+}
+
+// f(t, sc[t]) for every t < n, the block's threads striding over the
+// tokens with four reads in flight per thread.
+// Reads past the end take sc[n - 1] (n >= 1) and are not passed on:
+// unconditional reads issue back to back.
+template <typename F>
+__device__ __forceinline__ void for_scores(const float* sc, int n, F&& f) {
+  for (int t0 = threadIdx.x; t0 < n; t0 += 4 * kTopkThreads) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = sc[min(t0 + u * kTopkThreads, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (t0 + u * kTopkThreads < n) f(t0 + u * kTopkThreads, x[u] + 0.0f);
+  }
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+// Candidates of the threshold's bucket kept as a list of keys (in hist past
+// the 256 radix counters) when they are few; more (many equal scores) fall
+// back to radix passes over all n scores.
+constexpr int kCand = kBins - 256;
+
+// The k largest of sc[0..n) (LDS or global memory; lo/hi their range) into
+// out[0..k) in ascending token order, ties at the threshold to the lower
+// token index.  copy (may be null) receives sc[0..n) on the first pass.
+// hist holds kBins counters; every thread of the block calls.
+__device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k, float lo, float hi,
+                                             int32_t* out, float* copy, uint32_t* hist, uint32_t* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // one bucket when the range is empty (or too narrow for a finite scale):
   // the radix passes then resolve everything
   float s2 = hi > lo ? float(kBins * kBins) / (hi - lo) : 0.f;
   if (!(s2 < 1e30f)) s2 = 0.f;
 
   // level 1 and level 2 buckets narrow the k-th largest score down
-  uint32_t k_rem = uint32_t(P.top_k), above;
+  uint32_t k_rem = k, above;
   for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
   __syncthreads();
-  for (int t = tid; t < n; t += kTopkThreads) atomicAdd(&hist[bucket_id(sc[t] + 0.0f, lo, s2) >> 11], 1u);
+  for_scores(sc, n, [&](int t, float x) {
+    if (copy) copy[t] = x;
+    atomicAdd(&hist[bucket_id(x, lo, s2) >> 11], 1u);
+  });
   __syncthreads();
   const int b1 = find_bin(hist, kBins, k_rem, &above, sh);
+  const uint32_t in_b1 = hist[b1];
   k_rem -= above;
   __syncthreads();
-  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
-  __syncthreads();
-  for (int t = tid; t < n; t += kTopkThreads) {
-    const int id = bucket_id(sc[t] + 0.0f, lo, s2);
-    if ((id >> 11) == b1) atomicAdd(&hist[id & (kBins - 1)], 1u);
+  // candidates: the members of bucket b1 when they fit the list, else of the
+  // level-2 bucket (b1, b2) within it; a candidate has id >> cshift == target
+  int target = b1, cshift = 11;
+  if (in_b1 > uint32_t(kCand)) {
+    for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+    __syncthreads();
+    for_scores(sc, n, [&](int t, float x) {
+      const int id = bucket_id(x, lo, s2);
+      if ((id >> 11) == b1) atomicAdd(&hist[id & (kBins - 1)], 1u);
+    });
+    __syncthreads();
+    const int b2 = find_bin(hist, kBins, k_rem, &above, sh);
+    k_rem -= above;
+    target = b1 * kBins + b2;
+    cshift = 0;
   }
+  if (tid == 0) sh[70] = 0;
   __syncthreads();
-  const int b2 = find_bin(hist, kBins, k_rem, &above, sh);
-  k_rem -= above;
+  uint32_t* cand = hist + 256;
+  for_scores(sc, n, [&](int t, float x) {
+    if ((bucket_id(x, lo, s2) >> cshift) == target) {
+      const uint32_t slot = atomicAdd(&sh[70], 1u);
+      if (slot < uint32_t(kCand)) cand[slot] = order_key(x);
+    }
+  });
+  __syncthreads();
+  const uint32_t n_cand = sh[70];
   __syncthreads();
 
-  // exact key among the candidates of bucket (b1, b2): four radix passes of
-  // 8 bits over their order-preserving keys
+  // exact key among the candidates: four radix passes of 8 bits over their
+  // order-preserving keys
   uint32_t prefix = 0, mask = 0;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int t = tid; t < n; t += kTopkThreads) {
-      const float x = sc[t] + 0.0f;
-      if (bucket_id(x, lo, s2) != b1 * kBins + b2) continue;
-      const uint32_t key = order_key(x);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+    if (n_cand <= uint32_t(kCand)) {
+      for (int i = tid; i < int(n_cand); i += kTopkThreads) {
+        const uint32_t key = cand[i];
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+      }
+    } else {
+      for_scores(sc, n, [&](int t, float x) {
+        if ((bucket_id(x, lo, s2) >> cshift) != target) return;
+        const uint32_t key = order_key(x);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
+      });
     }
     __syncthreads();
     const int d = find_bin(hist, 256, k_rem, &above, sh);
@@ -256,41 +281,201 @@ __global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P)
     mask |= 0xffu << shift;
     __syncthreads();
   }
-  // prefix is the threshold key T: every key > T is selected and the first
-  // k_rem keys == T by token index
-  const uint32_t T = prefix;
-  const int seg = (n + kTopkThreads - 1) / kTopkThreads;
-  const int t0 = min(n, tid * seg), t1 = min(n, t0 + seg);
-  uint32_t gt = 0, eq = 0;
-  for (int t = t0; t < t1; ++t) {
-    const uint32_t key = order_key(sc[t]);
-    gt += key > T;
-    eq += key == T;
+
+  // prefix is the threshold key T of score Tf: every score > Tf is selected
+  // and the first k_rem scores == Tf by token index (float comparisons agree
+  // with the key order, -0 == +0 included).  Compaction: wave w owns a
+  // contiguous segment of tokens; a first pass counts its greater and equal
+  // scores (ballots), the wave totals are scanned, and a second pass writes
+  // each selected token to the greater tokens before it plus the selected
+  // equal tokens before it.
+  const float Tf = __builtin_bit_cast(float, (prefix & 0x80000000u) ? (prefix & 0x7fffffffu) : ~prefix);
+  constexpr int NW = kTopkThreads / 64;
+  const int seg = ((n + NW - 1) / NW + 63) / 64 * 64;
+  const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
+  uint32_t gt_w = 0, eq_w = 0;
+  for (int t0 = w0; t0 < w1; t0 += 256) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool in = t0 + u * 64 + lane < w1;
+      gt_w += uint32_t(__popcll(__ballot(in && x[u] > Tf)));
+      eq_w += uint32_t(__popcll(__ballot(in && x[u] == Tf)));
+    }
   }
-  uint32_t tot;
-  const uint32_t gt_before = block_exclusive_sum(gt, sh, &tot);
-  const uint32_t eq_before = block_exclusive_sum(eq, sh, &tot);
-  uint32_t pos = gt_before + min(eq_before, k_rem);
-  uint32_t eq_seen = eq_before;
-  int32_t* out = P.top_idx + head * P.top_k;
-  for (int t = t0; t < t1; ++t) {
-    const uint32_t key = order_key(sc[t]);
-    if (key > T) {
-      out[pos++] = t;
-    } else if (key == T) {
-      if (eq_seen < k_rem) out[pos++] = t;
-      ++eq_seen;
+  if (lane == 0) { sh[wave] = gt_w; sh[NW + wave] = eq_w; }
+  __syncthreads();
+  uint32_t gb = 0, eb = 0;
+  for (int w = 0; w < wave; ++w) { gb += sh[w]; eb += sh[NW + w]; }
+  for (int t0 = w0; t0 < w1; t0 += 256) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * 64 + lane;
+      const bool gt = t < w1 && x[u] > Tf, eq = t < w1 && x[u] == Tf;
+      const uint64_t mg = __ballot(gt), me = __ballot(eq);
+      const uint32_t g_before = gb + lanes_below(mg), e_before = eb + lanes_below(me);
+      if (gt) out[g_before + min(e_before, k_rem)] = t;
+      else if (eq && e_before < k_rem) out[g_before + e_before] = t;
+      gb += uint32_t(__popcll(mg));
+      eb += uint32_t(__popcll(me));
     }
   }
 }
 
+// Top-k of the scores pq_scores_kernel wrote: one workgroup per (b, hq).
+__global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sh[72];
+  __shared__ float fsh[2 * kTopkThreads / 64];
+  const int64_t head = blockIdx.x;                            // b * Hq + hq
+  const float* sc = P.scores + head * P.n_tok;
+  const int n = P.n_tok;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int t = threadIdx.x; t < n; t += kTopkThreads) {
+    const float x = sc[t] + 0.0f;
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  block_range(lo, hi, fsh, &lo, &hi);
+  select_top_k(sc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh);
+}
+
+// Whole search of one (b, hq) with its scores resident in LDS: the head's
+// table, the scores of all n_tok tokens from the codes, then the Top-k from
+// LDS; the scores are also written out.  D = head dim, M = sub-spaces (1,
+// 2, 4, 8, 16).  Dynamic LDS: scores [round16(n_tok)] | table [M][2^bits] |
+// q [D], fp32.
+template <int D, int M>
+__global__ void __launch_bounds__(kTopkThreads) pq_fused_kernel(const PqParams P) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sh[72];
+  __shared__ float fsh[2 * kTopkThreads / 64];
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int TPL = 16 / M;                                  // tokens per 16-byte code load
+  constexpr int U = 4;                                          // code loads in flight per lane
+  constexpr int dm = D / M;
+  const int nc = 1 << P.bits, n = P.n_tok, tid = threadIdx.x;
+  const int64_t head = blockIdx.x;                              // b * Hq + hq
+  const int b = int(head / P.Hq), hq = int(head % P.Hq);
+  const int64_t stream = int64_t(b) * P.Hkv + hq / P.gq;
+  float* ssc = reinterpret_cast<float*>(smem);
+  float* tab = ssc + (n + 15) / 16 * 16;
+  float* qf = tab + M * nc;
+  for (int i = tid; i < D; i += kTopkThreads) qf[i] = h2f(P.q[head * D + i]);
+  __syncthreads();
+  // table: q_j . centroid[j][c], one (j, c) per thread pass
+  const uint16_t* cen = P.centroids + stream * int64_t(M) * nc * dm;
+  for (int e = tid; e < M * nc; e += kTopkThreads) {
+    const int j = e / nc;
+    const uint4* row = reinterpret_cast<const uint4*>(cen + int64_t(e) * dm);
+    const float* qj = qf + j * dm;
+    uint4 rv[dm / 8];
+#pragma unroll
+    for (int kk = 0; kk < dm / 8; ++kk) rv[kk] = row[kk];
+    float acc = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < dm / 8; ++kk) {
+      const uint4 u = rv[kk];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = __builtin_fmaf(qj[kk * 8 + 2 * i], h2f(w[i] & 0xffffu), acc);
+        acc = __builtin_fmaf(qj[kk * 8 + 2 * i + 1], h2f(w[i] >> 16), acc);
+      }
+    }
+    tab[e] = acc;
+  }
+  __syncthreads();
+  // scores: U 16-byte code loads per lane in flight; loads past the codes'
+  // range (round16(n_tok * M) bytes) return zeros and their tokens are not
+  // stored; only the low `bits` bits of a code byte index the table
+  const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(P.codes + stream * P.codes_stride),
+                                                    short(0), int((int64_t(n) * M + 15) / 16 * 16), 0x00020000);
+  const uint32_t cmask = uint32_t(nc - 1);
+  float lo = INFINITY, hi = -INFINITY;
+  for (int base = tid * TPL; base < n; base += U * kTopkThreads * TPL) {
+    uint32_t w[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, uint32_t(base + u * kTopkThreads * TPL) * M, 0, 2);
+      w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t0 = base + u * kTopkThreads * TPL;
+      if (t0 >= n) break;
+      float s[TPL];
+#pragma unroll
+      for (int i = 0; i < TPL; ++i) {
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < M; ++j) {
+          const int byte = i * M + j;
+          acc += tab[j * nc + ((w[u][byte >> 2] >> ((byte & 3) * 8)) & cmask)];
+        }
+        s[i] = acc;
+        if (t0 + i < n) { lo = fminf(lo, acc + 0.0f); hi = fmaxf(hi, acc + 0.0f); }
+      }
+      if constexpr (TPL >= 4) {
+#pragma unroll
+        for (int i = 0; i < TPL; i += 4)
+          *reinterpret_cast<float4*>(ssc + t0 + i) = make_float4(s[i], s[i + 1], s[i + 2], s[i + 3]);
+      } else if constexpr (TPL == 2) {
+        *reinterpret_cast<float2*>(ssc + t0) = make_float2(s[0], s[1]);
+      } else {
+        ssc[t0] = s[0];
+      }
+    }
+  }
+  block_range(lo, hi, fsh, &lo, &hi);                           // syncs: the scores are in LDS
+  select_top_k(ssc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, P.scores + head * n, hist, sh);
+}
+
 }  // namespace
+
+int64_t pq_fused_lds_bytes(int n_tok, int D, int m, int bits) {
+  // dynamic part plus the kernel's static arrays (hist, sh, fsh)
+  return (int64_t(n_tok + 15) / 16 * 16 + int64_t(m) * (int64_t(1) << bits) + D) * 4 +
+         (kBins + 72 + 2 * kTopkThreads / 64) * 4;
+}
 
 int64_t pq_scores_lds_bytes(int gq_pow2, int D, int m, int bits) {
   return int64_t(gq_pow2) * m * (int64_t(1) << bits) * 4 + int64_t(gq_pow2) * D * 4;
 }
 
-hipError_t launch_pq_search(const PqParams& p, int GQ, hipStream_t s) {
+hipError_t launch_pq_search(const PqParams& p, int GQ, bool fused, hipStream_t s) {
+  if (fused) {
+    const dim3 grid(unsigned(int64_t(p.B) * p.Hq));
+    const size_t lds = size_t(pq_fused_lds_bytes(p.n_tok, p.D, p.m, p.bits)) - (kBins + 72 + 2 * kTopkThreads / 64) * 4;
+#define PQ_FUSED(D_, M_) hipLaunchKernelGGL((pq_fused_kernel<D_, M_>), grid, dim3(kTopkThreads), lds, s, p)
+    if (p.D == 64) {
+      switch (p.m) {
+        case 1: PQ_FUSED(64, 1); break;
+        case 2: PQ_FUSED(64, 2); break;
+        case 4: PQ_FUSED(64, 4); break;
+        case 8: PQ_FUSED(64, 8); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else if (p.D == 128) {
+      switch (p.m) {
+        case 1: PQ_FUSED(128, 1); break;
+        case 2: PQ_FUSED(128, 2); break;
+        case 4: PQ_FUSED(128, 4); break;
+        case 8: PQ_FUSED(128, 8); break;
+        case 16: PQ_FUSED(128, 16); break;
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      return hipErrorInvalidValue;
+    }
+#undef PQ_FUSED
+    return hipGetLastError();
+  }
   const int64_t chunks = (int64_t(p.n_tok) + p.chunk_tokens - 1) / p.chunk_tokens;
   const dim3 grid(unsigned(chunks), unsigned(int64_t(p.B) * p.Hkv));
   const size_t lds = size_t(pq_scores_lds_bytes(GQ, p.D, p.m, p.bits));

@@ -373,16 +373,22 @@ kvq_status kvq_decode_attn_paged(const kvq_paged_args* args, void* stream);
  *                 ties to the lower token index, in ascending token order.
  * Layouts: q fp16 [batch][n_q_heads][d_h]; centroids fp16
  * [batch][n_kv_heads][m][2^bits][dm]; codes u8, stream s = b*n_kv_heads + kv
- * at codes + s*codes_stride bytes, [n_tok][m]; scores fp32
- * [batch][n_q_heads][n_tok] (written; the Top-k pass reads them back);
+ * at codes + s*codes_stride bytes, [n_tok][m], each code < 2^bits (only its
+ * low `bits` bits are read); scores fp32 [batch][n_q_heads][n_tok] (written);
  * top_idx int32 [batch][n_q_heads][top_k].
+ * Two paths, one result: when a head's n_tok scores fit in a workgroup's LDS
+ * (up to about 38K tokens) one kernel does all three steps per query head
+ * with the scores resident in LDS; longer contexts run a scores kernel per
+ * kv head (its query heads' tables in LDS) and a Top-k kernel that reads the
+ * scores back.
  * Checks (before any launch): d_h 64 or 128; m divides 16 and d_h with dm a
  * multiple of 8; 1 <= bits <= 8; 1 <= top_k <= n_tok <= 2^24; n_q_heads /
  * n_kv_heads <= 8; codes_stride >= n_tok*m and a multiple of 16 (the kernel
- * reads up to the next multiple of 16 past n_tok*m); the tables of a kv
- * head's query heads fit 64 KB of LDS; q, centroids, codes, scores 16-byte
- * aligned, top_idx 4-byte aligned.  Centroids and codes are inputs (the
- * K-means construction of Step 2 runs elsewhere).
+ * reads up to the next multiple of 16 past n_tok*m); on the two-kernel path
+ * the tables of a kv head's query heads fit 64 KB of LDS (KVQ_EUNSUPPORTED
+ * otherwise); q, centroids, codes, scores 16-byte aligned, top_idx 4-byte
+ * aligned.  Centroids and codes are inputs (the K-means construction of
+ * Step 2 runs elsewhere).
  */
 kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_h,
                          int32_t m, int32_t bits, int32_t n_tok, int32_t top_k,

@@ -333,8 +333,9 @@ def test_split_plan_fills_the_chip_once():
     (dict(codes_stride=192), EINVAL), (dict(codes_stride=204), EALIGN), (dict(q=A + 2), EALIGN),
     (dict(top_idx=A + 2), EALIGN), (dict(scores=None), EINVAL), (dict(n_q_heads=7), EINVAL),
     (dict(n_q_heads=4 * 16), EUNSUP),
-    # 8 query heads x 16 sub-spaces x 256 centroids of fp32 tables: 128 KB > 64 KB of LDS
-    (dict(n_q_heads=32, m=16, codes_stride=1600), EUNSUP),
+    # too many tokens for a head's scores in LDS, and the scores kernel's 8
+    # query heads x 16 sub-spaces x 256 centroids of fp32 tables: 128 KB > 64 KB
+    (dict(n_q_heads=32, m=16, n_tok=100000, codes_stride=1600000), EUNSUP),
 ])
 def test_pq_search_rejects(kw, code):
     a = dict(batch=2, n_q_heads=4, n_kv_heads=4, d_h=128, m=2, bits=8, n_tok=100, top_k=10,

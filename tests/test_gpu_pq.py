@@ -11,8 +11,9 @@ the oracle (oracle/pq.py).
   tolerance above a chosen one.
 Shapes cover 1-8 query heads per kv head (7 included), m = 1..16, 3..8-bit
 codes, k = 1 and k = n_tok, token counts that are not multiples of the
-16-byte code loads, and the GQA long-context shape at full size (sampled
-heads checked).
+16-byte code loads, both paths (a head's scores resident in LDS up to about
+38K tokens, scores then Top-k through memory past that), and the GQA
+long-context shape at full size (sampled heads checked).
 """
 import numpy as np
 import pytest
@@ -31,14 +32,20 @@ def kvq():
     return m
 
 
-def run_pq(kvq, B, Hq, Hkv, d, m, bits, n_tok, k, heads=None, seed=0):
-    import torch
-    dev = torch.device("cuda:0")
+def run_pq(kvq, B, Hq, Hkv, d, m, bits, n_tok, k, heads=None, seed=0, prepare=None):
     print(f"pq: B{B} Hq{Hq} Hkv{Hkv} d{d} m{m} bits{bits} n{n_tok} k{k}", flush=True)
     w = workloads.Workload(name="pq", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, d_h=d, context=n_tok,
                            group=32, residual=32, bits=2, seed=seed)
     q = workloads.queries(w)
     c, codes = workloads.pq_inputs(B, Hkv, n_tok, d, m, bits, seed=seed)
+    if prepare:
+        prepare(q, c, codes)
+    check_pq(kvq, q, c, codes, B, Hq, Hkv, d, m, bits, n_tok, k, heads)
+
+
+def check_pq(kvq, q, c, codes, B, Hq, Hkv, d, m, bits, n_tok, k, heads=None):
+    import torch
+    dev = torch.device("cuda:0")
     stride = (n_tok * m + 15) // 16 * 16
     padded = np.full((B * Hkv, stride), 0xAB, np.uint8)          # padding bytes are read and ignored
     padded[:, :n_tok * m] = codes.reshape(B * Hkv, n_tok * m)
@@ -77,6 +84,14 @@ def run_pq(kvq, B, Hq, Hkv, d, m, bits, n_tok, k, heads=None, seed=0):
     (1, 28, 4, 128, 2, 8, 2049, 205),
     (2, 16, 2, 64, 1, 8, 300, 17),
     (1, 2, 1, 128, 16, 5, 4099, 64),
+    # past the LDS-resident one-kernel path (about 38K tokens): scores
+    # kernel, then the Top-k kernel through memory
+    (1, 4, 2, 128, 2, 8, 40001, 999),
+    (1, 2, 1, 64, 4, 4, 50000, 50000),
+    # 1-bit codes, one sub-space: two score values, so thousands of tokens
+    # tie at the threshold (more than the candidate list holds), both paths
+    (1, 2, 1, 64, 1, 1, 20000, 5000),
+    (1, 2, 1, 64, 1, 1, 60000, 7000),
 ])
 def test_pq_search(kvq, B, Hq, Hkv, d, m, bits, n_tok, k):
     run_pq(kvq, B, Hq, Hkv, d, m, bits, n_tok, k)
@@ -114,3 +129,16 @@ def test_pq_search_ties(kvq):
                       torch.from_numpy(padded).to(dev), stride, sc, idx2)
     torch.cuda.synchronize()
     assert idx2.cpu().numpy()[0, 0].tolist() == sorted(list(range(0, 50, 3)) + [1, 2, 4])
+
+
+def test_pq_search_outlier_score(kvq):
+    # one token far above the rest stretches the score range, so the others
+    # crowd into one or two of the 2048 equal-width level-1 buckets and the
+    # threshold is found through the level-2 buckets
+    def prepare(q, c, codes):
+        g, dm = q.shape[1] // c.shape[1], c.shape[-1]
+        c[:, :, 0, 0, :] = np.float16(1000.0) * np.sign(q[:, ::g, :dm].astype(np.float32)).astype(np.float16)
+        codes[:, :, :, 0] = np.maximum(codes[:, :, :, 0], 1)         # centroid 0 of sub-space 0 ...
+        codes[:, :, 777, 0] = 0                                       # ... for token 777 only
+    run_pq(kvq, 1, 4, 2, 64, 1, 8, 30000, 2500, prepare=prepare)
+    run_pq(kvq, 1, 2, 1, 128, 2, 8, 45000, 3000, prepare=prepare)
