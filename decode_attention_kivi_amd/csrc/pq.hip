@@ -122,7 +122,15 @@ __global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P)
 // only higher scores.
 constexpr int kBins = 2048;
 __device__ __forceinline__ int bucket_id(float x, float lo, float s2) {
-  return min(kBins * kBins - 1, int(__fmul_rn(x - lo, s2)));
+  return min(kBins * kBins - 1, max(0, int(__fmul_rn(x - lo, s2))));
+}
+
+// Scale of bucket_id for the range [lo, hi]: one bucket when the range is
+// empty (or too narrow for a finite scale); the radix passes then resolve
+// everything.
+__device__ __forceinline__ float bucket_scale(float lo, float hi) {
+  const float s2 = hi > lo ? float(kBins * kBins) / (hi - lo) : 0.f;
+  return s2 < 1e30f ? s2 : 0.f;
 }
 
 // The bin of hist[0..nbins) (counted from the top) that holds the k-th
@@ -202,27 +210,26 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // back to radix passes over all n scores.
 constexpr int kCand = kBins - 256;
 
-// The k largest of sc[0..n) (LDS or global memory; lo/hi their range) into
-// out[0..k) in ascending token order, ties at the threshold to the lower
-// token index.  copy (may be null) receives sc[0..n) on the first pass.
-// hist holds kBins counters; every thread of the block calls.
+// The k largest of sc[0..n) (LDS or global memory, every score within
+// [lo, hi]) into out[0..k) in ascending token order, ties at the threshold to
+// the lower token index.  copy (may be null) receives sc[0..n).  hist holds
+// kBins counters: with l1_ready the caller has filled it with the level-1
+// histogram (bucket_id(x, lo, bucket_scale(lo, hi)) >> 11 of every score)
+// and synced.  Every thread of the block calls.
 __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k, float lo, float hi,
-                                             int32_t* out, float* copy, uint32_t* hist, uint32_t* sh) {
+                                             int32_t* out, float* copy, uint32_t* hist, uint32_t* sh,
+                                             bool l1_ready) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // one bucket when the range is empty (or too narrow for a finite scale):
-  // the radix passes then resolve everything
-  float s2 = hi > lo ? float(kBins * kBins) / (hi - lo) : 0.f;
-  if (!(s2 < 1e30f)) s2 = 0.f;
+  const float s2 = bucket_scale(lo, hi);
 
   // level 1 and level 2 buckets narrow the k-th largest score down
   uint32_t k_rem = k, above;
-  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
-  __syncthreads();
-  for_scores(sc, n, [&](int t, float x) {
-    if (copy) copy[t] = x;
-    atomicAdd(&hist[bucket_id(x, lo, s2) >> 11], 1u);
-  });
-  __syncthreads();
+  if (!l1_ready) {
+    for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+    __syncthreads();
+    for_scores(sc, n, [&](int t, float x) { atomicAdd(&hist[bucket_id(x, lo, s2) >> 11], 1u); });
+    __syncthreads();
+  }
   const int b1 = find_bin(hist, kBins, k_rem, &above, sh);
   const uint32_t in_b1 = hist[b1];
   k_rem -= above;
@@ -247,6 +254,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   __syncthreads();
   uint32_t* cand = hist + 256;
   for_scores(sc, n, [&](int t, float x) {
+    if (copy) copy[t] = x;
     if ((bucket_id(x, lo, s2) >> cshift) == target) {
       const uint32_t slot = atomicAdd(&sh[70], 1u);
       if (slot < uint32_t(kCand)) cand[slot] = order_key(x);
@@ -342,14 +350,15 @@ __global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P)
     hi = fmaxf(hi, x);
   }
   block_range(lo, hi, fsh, &lo, &hi);
-  select_top_k(sc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh);
+  select_top_k(sc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh, false);
 }
 
 // Whole search of one (b, hq) with its scores resident in LDS: the head's
-// table, the scores of all n_tok tokens from the codes, then the Top-k from
-// LDS; the scores are also written out.  D = head dim, M = sub-spaces (1,
-// 2, 4, 8, 16).  Dynamic LDS: scores [round16(n_tok)] | table [M][2^bits] |
-// q [D], fp32.
+// table, a bound on the score range from it, the scores of all n_tok tokens
+// from the codes with their level-1 histogram, then the rest of the Top-k
+// from LDS; the scores are also written out.  D = head dim, M = sub-spaces
+// (1, 2, 4, 8, 16).  Dynamic LDS: scores [round16(n_tok)] | table
+// [M][2^bits] | q [D], fp32.
 template <int D, int M>
 __global__ void __launch_bounds__(kTopkThreads) pq_fused_kernel(const PqParams P) {
   __shared__ uint32_t hist[kBins];
@@ -391,13 +400,36 @@ __global__ void __launch_bounds__(kTopkThreads) pq_fused_kernel(const PqParams P
     tab[e] = acc;
   }
   __syncthreads();
-  // scores: U 16-byte code loads per lane in flight; loads past the codes'
-  // range (round16(n_tok * M) bytes) return zeros and their tokens are not
-  // stored; only the low `bits` bits of a code byte index the table
+  // range of the scores before any is computed: per sub-space the least and
+  // greatest table entry, summed in the order the scores are (rounded fp32
+  // addition is monotone, so every score lies within it)
+  const int lane = tid & 63, wave = tid >> 6;
+  if (wave < M) {
+    float a = INFINITY, z = -INFINITY;
+    for (int c = lane; c < nc; c += 64) {
+      a = fminf(a, tab[wave * nc + c]);
+      z = fmaxf(z, tab[wave * nc + c]);
+    }
+    a = span_min<64>(a);
+    z = span_max<64>(z);
+    if (lane == 0) { fsh[wave] = a; fsh[16 + wave] = z; }
+  }
+  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+  __syncthreads();
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    lo += fsh[j];
+    hi += fsh[16 + j];
+  }
+  const float s2 = bucket_scale(lo, hi);
+  // scores and their level-1 histogram: U 16-byte code loads per lane in
+  // flight; loads past the codes' range (round16(n_tok * M) bytes) return
+  // zeros and their tokens are neither stored nor counted; only the low
+  // `bits` bits of a code byte index the table
   const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(P.codes + stream * P.codes_stride),
                                                     short(0), int((int64_t(n) * M + 15) / 16 * 16), 0x00020000);
   const uint32_t cmask = uint32_t(nc - 1);
-  float lo = INFINITY, hi = -INFINITY;
   for (int base = tid * TPL; base < n; base += U * kTopkThreads * TPL) {
     uint32_t w[U][4];
 #pragma unroll
@@ -419,7 +451,7 @@ __global__ void __launch_bounds__(kTopkThreads) pq_fused_kernel(const PqParams P
           acc += tab[j * nc + ((w[u][byte >> 2] >> ((byte & 3) * 8)) & cmask)];
         }
         s[i] = acc;
-        if (t0 + i < n) { lo = fminf(lo, acc + 0.0f); hi = fmaxf(hi, acc + 0.0f); }
+        if (t0 + i < n) atomicAdd(&hist[bucket_id(acc + 0.0f, lo, s2) >> 11], 1u);
       }
       if constexpr (TPL >= 4) {
 #pragma unroll
@@ -432,8 +464,9 @@ __global__ void __launch_bounds__(kTopkThreads) pq_fused_kernel(const PqParams P
       }
     }
   }
-  block_range(lo, hi, fsh, &lo, &hi);                           // syncs: the scores are in LDS
-  select_top_k(ssc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, P.scores + head * n, hist, sh);
+  __syncthreads();
+  select_top_k(ssc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, P.scores + head * n, hist, sh,
+               true);
 }
 
 }  // namespace
