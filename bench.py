@@ -322,9 +322,10 @@ def pq_search_rate(dev, stream, reps: int = 50):
     """kvq_pq_search (PQCache's decode-time PQ search) at the GQA long-context
     shape: 4 sequences x 32 query heads over 8 kv heads, 32769 tokens, m = 2
     sub-spaces of 256 centroids (8-bit codes), Top-k = 3277 (1/10 of the
-    tokens).  Per call: the scores kernel reads the codes and centroids and
-    writes fp32 scores; the Top-k kernel reads the scores back five times
-    (from L2) and writes the indices."""
+    tokens).  One kernel per call (a head's 32769 scores fit in LDS): each
+    query head's workgroup reads its kv head's codes and centroids and q,
+    writes the fp32 scores and the Top-k indices.  Algorithmic bytes count
+    the codes and centroids once per kv head."""
     import torch
     import decode_attention_kivi_amd as kvq
     B, Hq, Hkv, d, m, bits, n, k = 4, 32, 8, 128, 2, 8, 32769, 3277
