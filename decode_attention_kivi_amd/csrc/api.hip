@@ -8,6 +8,7 @@
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
+#include "pq.h"
 
 namespace {
 

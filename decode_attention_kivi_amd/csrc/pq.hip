@@ -23,6 +23,7 @@
 //                     resident in LDS (contexts up to about 38K tokens).
 
 #include "kvq_internal.h"
+#include "pq.h"
 #include "kvq_device.h"
 
 namespace kvq {
