@@ -13,8 +13,8 @@
 //                        window or of the prompt, batch row): every token
 //                        row is normalized by one wave (a DPP sum of squares)
 //                        and added into the wave's fp32 sum; the four waves'
-//                        sums meet in LDS and the chunk sum goes to the
-//                        workspace;
+//                        sums are added in LDS in wave order and the chunk
+//                        sum goes to the workspace;
 //   search_vote_kernel   one workgroup per window: the chunk sums of the
 //                        window and of the prompt, their dot product per
 //                        batch row, the choice per row and the vote.
@@ -42,7 +42,7 @@ __device__ __forceinline__ uint4 load16(Rsrc r, uint32_t off) {
 // NSL: 16-byte slots (8 channels) per lane, D <= 512 * NSL.
 template <int NSL>
 __global__ void __launch_bounds__(kSearchThreads) search_sums_kernel(const SearchParams P) {
-  extern __shared__ __align__(16) float red[];     // [4][D]
+  extern __shared__ __align__(16) float red[];     // [D]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int x = blockIdx.x, b = blockIdx.y;
@@ -111,20 +111,38 @@ __global__ void __launch_bounds__(kSearchThreads) search_sums_kernel(const Searc
 #pragma unroll
     for (int i = 0; i < NSL; ++i) cur[i] = nxt[i];
   }
-  // the four waves' sums, then the chunk sum in a fixed order
-#pragma unroll
-  for (int i = 0; i < NSL; ++i) {
-    const int c0 = (lane + 64 * i) * 8;
-    if (c0 < D) {
-      float4* dst = reinterpret_cast<float4*>(red + wave * D + c0);
-      dst[0] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
-      dst[1] = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
-    }
-  }
-  __syncthreads();
+  // the chunk sum ((w0 + w1) + w2) + w3 of the four waves' sums: wave 0
+  // stores its sum in LDS, waves 1 and 2 add theirs in turn, wave 3 adds its
+  // own and writes the result (one D-float slot keeps the LDS small enough
+  // for three workgroups per CU)
   float* out = P.ws + (int64_t(b) * P.n_chunks + x) * D;
-  for (int c = threadIdx.x; c < D; c += kSearchThreads)
-    out[c] = ((red[c] + red[D + c]) + red[2 * D + c]) + red[3 * D + c];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int i = 0; i < NSL; ++i) {
+        const int c0 = (lane + 64 * i) * 8;
+        if (c0 >= D) continue;
+        float4* slot = reinterpret_cast<float4*>(red + c0);
+        float4 lo4 = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        float4 hi4 = make_float4(acc[i][4], acc[i][5], acc[i][6], acc[i][7]);
+        if (w > 0) {
+          const float4 a = slot[0], c = slot[1];
+          lo4 = make_float4(a.x + lo4.x, a.y + lo4.y, a.z + lo4.z, a.w + lo4.w);
+          hi4 = make_float4(c.x + hi4.x, c.y + hi4.y, c.z + hi4.z, c.w + hi4.w);
+        }
+        if (w < 3) {
+          slot[0] = lo4;
+          slot[1] = hi4;
+        } else {
+          float4* dst = reinterpret_cast<float4*>(out + c0);
+          dst[0] = lo4;
+          dst[1] = hi4;
+        }
+      }
+    }
+    if (w < 3) __syncthreads();
+  }
 }
 
 __device__ __forceinline__ float block_sum(float x, float* sh) {
@@ -157,10 +175,12 @@ __global__ void __launch_bounds__(kSearchThreads) search_vote_kernel(const Searc
       const int c = threadIdx.x + j * kSearchThreads;
       if (c >= D4) continue;
       float4 ws = make_float4(0.f, 0.f, 0.f, 0.f), ts = ws;
+#pragma unroll 4
       for (int k = 0; k < P.chunks_per_window; ++k) {
         const float4 x = wrow[int64_t(k) * D4 + c];
         ws.x += x.x; ws.y += x.y; ws.z += x.z; ws.w += x.w;
       }
+#pragma unroll 4
       for (int k = 0; k < text_chunks; ++k) {
         const float4 x = trow[int64_t(k) * D4 + c];
         ts.x += x.x; ts.y += x.y; ts.z += x.z; ts.w += x.w;
@@ -198,13 +218,15 @@ int64_t search_chunks(int32_t n_text, int32_t n_windows, int32_t S) {
 
 hipError_t launch_search(const SearchParams& p, hipStream_t s) {
   const int nsl = (p.D + 511) / 512;
-  const size_t lds = size_t(4) * p.D * sizeof(float);
+  const size_t lds = size_t(p.D) * sizeof(float);
   const dim3 grid(unsigned(p.n_chunks), unsigned(p.B));
-  switch (nsl <= 1 ? 1 : nsl <= 2 ? 2 : nsl <= 4 ? 4 : 8) {
-    case 1: hipLaunchKernelGGL(search_sums_kernel<1>, grid, dim3(kSearchThreads), lds, s, p); break;
-    case 2: hipLaunchKernelGGL(search_sums_kernel<2>, grid, dim3(kSearchThreads), lds, s, p); break;
-    case 4: hipLaunchKernelGGL(search_sums_kernel<4>, grid, dim3(kSearchThreads), lds, s, p); break;
-    default: hipLaunchKernelGGL(search_sums_kernel<8>, grid, dim3(kSearchThreads), lds, s, p); break;
+  switch (nsl) {
+#define SEARCH_SUMS(N) \
+    case N: hipLaunchKernelGGL(search_sums_kernel<N>, grid, dim3(kSearchThreads), lds, s, p); break;
+    SEARCH_SUMS(1) SEARCH_SUMS(2) SEARCH_SUMS(3) SEARCH_SUMS(4)
+    SEARCH_SUMS(5) SEARCH_SUMS(6) SEARCH_SUMS(7) SEARCH_SUMS(8)
+#undef SEARCH_SUMS
+    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
