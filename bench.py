@@ -397,9 +397,11 @@ def main():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq", "search"), default="all",
+    ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq", "search", "windows"),
+                    default="all",
                     help="profiling runs: time only the attention graph, only the step graph, the paged "
-                         "ragged batch, the PQ search or the window search (and skip the rest)")
+                         "ragged batch, the PQ search, the window search or the mixed-precision "
+                         "window cache (and skip the rest)")
     ap.add_argument("--page-tokens", type=int, default=256, help="page size of the paged ragged batch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
@@ -415,14 +417,16 @@ def main():
     if not os.path.exists(lib):
         import __graft_entry__
         __graft_entry__.build()
-    if args.part in ("paged", "pq", "search"):
+    if args.part in ("paged", "pq", "search", "windows"):
         dev, st = torch.device("cuda:0"), torch.cuda.Stream()
         if args.part == "paged":
             r = paged_ragged_rate(dev, st, page_tokens=args.page_tokens)
         elif args.part == "pq":
             r = pq_search_rate(dev, st)
-        else:
+        elif args.part == "search":
             r = window_search_rate(dev, st)
+        else:
+            r = windows_decode_rate(dev, st)
         print(json.dumps({"part": args.part, **r}), flush=True)
         return
 

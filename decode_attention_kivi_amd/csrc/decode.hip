@@ -872,10 +872,15 @@ decode_kernel(const DecodeParams P) {
 // workgroup partials, folded in one pass with a running maximum.
 template <int D, bool PAGED>
 __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
-  const int64_t idx = int64_t(blockIdx.x) * NT + threadIdx.x;
-  if (idx >= int64_t(P.B) * P.Hq * D) return;
-  const int c = int(idx % D);
-  const int64_t bhq = idx / D;
+  // one workgroup per (b, hq): M = the largest partial max; partial s then
+  // weighs f_s = 2^(m_s - M); L = sum_s l_s f_s and o[c] = sum_s o_s[c] f_s,
+  // the partials split over the threads (NT / D threads per channel, every
+  // load independent) in chunks of NT partials whose weights sit in LDS
+  constexpr int R = NT / D;                  // threads per output channel
+  __shared__ float f[NT];
+  __shared__ float red[NT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t bhq = blockIdx.x;
   const int b = int(bhq / P.Hq), hq = int(bhq % P.Hq);
   const int hkv = hq / P.gq, h = hq % P.gq;
   const int64_t stream = int64_t(b) * P.Hkv + hkv;
@@ -889,19 +894,44 @@ __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
     while (GQ < P.gq) GQ *= 2;
     nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], GQ, kWaves);
   }
-  float M = -INFINITY, L = 0.f, O = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < nwg; ++s) {
-    const float* w = w0 + s * step;
-    const float m = w[0], l = w[1], o = w[2 + c];
-    const float Mn = fmaxf(M, m);
-    const float fa = M == Mn ? 1.f : exp2f(M - Mn);   // also -inf == -inf
-    const float fb = m == Mn ? 1.f : exp2f(m - Mn);
-    L = L * fa + l * fb;
-    O = O * fa + o * fb;
-    M = Mn;
+  float mx = -INFINITY;
+  for (int s = tid; s < nwg; s += NT) mx = fmaxf(mx, w0[s * step]);
+  mx = wave_max64(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  float M = red[0];
+  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
+  const int c = tid % D, r = tid / D;
+  float O = 0.f, Lp = 0.f;
+  for (int s0 = 0; s0 < nwg; s0 += NT) {
+    __syncthreads();                         // red and f are free again
+    float fs = 0.f;
+    if (s0 + tid < nwg) {
+      const float* w = w0 + (s0 + tid) * step;
+      const float m = w[0];
+      fs = m == M ? 1.f : exp2f(m - M);      // also -inf == -inf
+      Lp = __builtin_fmaf(w[1], fs, Lp);
+    }
+    f[tid] = fs;
+    __syncthreads();
+    const int n = min(NT, nwg - s0);
+#pragma unroll 8
+    for (int j = r; j < n; j += R) O = __builtin_fmaf(w0[(s0 + j) * step + 2 + c], f[j], O);
   }
-  P.out[idx] = O / L;
+  Lp = wave_sum64(Lp);
+  __syncthreads();
+  if (lane == 0) red[wave] = Lp;
+  __syncthreads();
+  float L = 0.f;
+  for (int w = 0; w < NT / 64; ++w) L += red[w];
+  __syncthreads();
+  red[tid] = O;
+  __syncthreads();
+  if (r == 0) {
+    float o = red[c];
+    for (int k = 1; k < R; ++k) o += red[k * D + c];
+    P.out[bhq * D + c] = o / L;
+  }
 }
 
 template <int D, int GQ, int NW, bool PAGED>
@@ -912,8 +942,7 @@ hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<D, GQ, NW, PAGED>), grid, dim3(NW * 64), lds, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_stream == 1) return e;
-  const int64_t n = int64_t(p.B) * p.Hq * D;
-  hipLaunchKernelGGL((merge_kernel<D, PAGED>), dim3(unsigned((n + NT - 1) / NT)), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((merge_kernel<D, PAGED>), dim3(unsigned(int64_t(p.B) * p.Hq)), dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 
