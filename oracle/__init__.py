@@ -20,6 +20,7 @@ windows    WindowQuant window reorder and per-window quantization (Sec. 3.3)
 search     WindowQuant window-level quantization search (Sec. 3.2), float64
 attention  single-query softmax attention over the cache, float64
 pq         PQCache decode-time PQ search: approximate scores and Top-k, float64
+vq         decode attention over a vector-quantized (codebook) cache, float64
 
 Parity pins: every function is checked by ``tests/test_oracle_*.py`` against
 closed forms, hand-derived fixtures in ``tests/golden/``, brute force on tiny
@@ -27,4 +28,4 @@ inputs and a library routine (torch scaled_dot_product_attention, CPU fp64).
 The byte layout in ``pack`` is pinned by the header's written definition and
 hand-derived bytes, not by the pages (the pages define no layout).
 """
-from . import quant, pack, kivi, windows, search, attention, pq  # noqa: F401
+from . import quant, pack, kivi, windows, search, attention, pq, vq  # noqa: F401

@@ -258,3 +258,21 @@ def pq_inputs(batch: int, n_kv_heads: int, n_tok: int, d_h: int, m: int, bits: i
     c = rng.standard_normal((batch, n_kv_heads, m, 1 << bits, dm), dtype=np.float32) / np.float32(np.sqrt(m))
     codes = rng.integers(0, 1 << bits, size=(batch, n_kv_heads, n_tok, m), dtype=np.uint8)
     return c.astype(np.float16), codes
+
+
+def vq_inputs(batch: int, n_kv_heads: int, n_tok: int, d_h: int, rounds: int, seed: int = 0):
+    """Codebooks and codes of a vector-quantized KV cache (VQ-LLM note, the
+    CQ configurations: 4-channel sub-vectors, 256 entries each, ``rounds``
+    residual rounds).  Codebooks fp16 [Hkv][rounds][d_h/4][256][4] for keys
+    and for values, round r drawn N(0, 4^-r) (a residual round codes a
+    smaller remainder); codes uint8 [B][Hkv][n_tok][rounds][d_h/4] uniform;
+    ``default_rng([seed, 9])``.  Trained codebooks are not part of the path:
+    these stand in for them."""
+    rng = np.random.default_rng([seed, 9])
+    G = d_h // 4
+    scale = (0.5 ** np.arange(rounds, dtype=np.float32))[:, None, None, None]
+    kb = rng.standard_normal((n_kv_heads, rounds, G, 256, 4), dtype=np.float32) * scale
+    vb = rng.standard_normal((n_kv_heads, rounds, G, 256, 4), dtype=np.float32) * scale
+    kc = rng.integers(0, 256, size=(batch, n_kv_heads, n_tok, rounds, G), dtype=np.uint8)
+    vc = rng.integers(0, 256, size=(batch, n_kv_heads, n_tok, rounds, G), dtype=np.uint8)
+    return kb.astype(np.float16), vb.astype(np.float16), kc, vc
