@@ -360,6 +360,50 @@ def pq_search_rate(dev, stream, reps: int = 50):
             "tokens_scored_per_s": round(B * Hq * n / (us * 1e-6), 1)}
 
 
+def vq_decode_rate(dev, stream, rounds: int, reps: int = 30, copies: int = 2):
+    """kvq_vq_decode_attn (decode attention over a vector-quantized cache,
+    4-channel codebooks of 256 entries; rounds = 1 is CQ-2, 2 is CQ-4) at the
+    Llama-2-7B decode shape: 16 sequences x 32 heads, d128, 4097 tokens.
+    Consecutive calls read different copies of the codes (2 x 134 MB for
+    CQ-2), so they come from HBM.  Algorithmic bytes: the key and value codes
+    once, both codebooks of every kv head once, q and out."""
+    import torch
+    import decode_attention_kivi_amd as kvq
+    B, H, d, n = 16, 32, 128, 4097
+    tb = rounds * d // 4
+    stride = (n * tb + 15) // 16 * 16
+    g = torch.Generator(device=dev).manual_seed(0)
+    codes = [(torch.randint(0, 256, (B * H, stride), generator=g, device=dev, dtype=torch.uint8),
+              torch.randint(0, 256, (B * H, stride), generator=g, device=dev, dtype=torch.uint8))
+             for _ in range(copies)]
+    kb = torch.randn(H, rounds, d // 4, 256, 4, generator=g, device=dev).half()
+    vb = torch.randn(H, rounds, d // 4, 256, 4, generator=g, device=dev).half()
+    q = torch.randn(B, H, d, generator=g, device=dev).half()
+    out = torch.empty(B, H, d, dtype=torch.float32, device=dev)
+    ws_bytes = kvq.kvq_vq_decode_attn_workspace(B, H, H, d, rounds, n)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+
+    def call(i):
+        kc, vc = codes[i % copies]
+        kvq.kvq_vq_decode_attn(B, H, H, d, rounds, n, 1.0 / d ** 0.5, q, kc, vc, stride, kb, vb, out,
+                               ws if ws_bytes else None, ws_bytes, stream)
+    with torch.cuda.stream(stream):
+        for i in range(4):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = 2 * B * H * n * tb + 2 * H * rounds * (d // 4) * 256 * 4 * 2 + B * H * d * 6
+    return {"config": f"CQ-{2 * rounds}: 16 x 32 heads, d128, 4097 tokens, 4-channel codebooks of 256 entries, "
+                      f"{rounds} round(s)", "us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes),
+            "GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 8e12, 4)}
+
+
 def streaming_read_ceiling(dev, stream, gib: float = 1.0, reps: int = 20) -> float:
     """GB/s of a plain streaming read on this GPU: torch's sum over a 1 GiB
     buffer (well past the 256 MB Infinity Cache), the practical ceiling the
@@ -397,11 +441,11 @@ def main():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq", "search", "windows"),
+    ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq", "search", "windows", "vq"),
                     default="all",
                     help="profiling runs: time only the attention graph, only the step graph, the paged "
-                         "ragged batch, the PQ search, the window search or the mixed-precision "
-                         "window cache (and skip the rest)")
+                         "ragged batch, the PQ search, the window search, the mixed-precision "
+                         "window cache or the VQ-cache decode (and skip the rest)")
     ap.add_argument("--page-tokens", type=int, default=256, help="page size of the paged ragged batch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
@@ -417,6 +461,11 @@ def main():
     if not os.path.exists(lib):
         import __graft_entry__
         __graft_entry__.build()
+    if args.part == "vq":
+        dev, st = torch.device("cuda:0"), torch.cuda.Stream()
+        for rounds in (1, 2):
+            print(json.dumps({"part": "vq", **vq_decode_rate(dev, st, rounds)}), flush=True)
+        return
     if args.part in ("paged", "pq", "search", "windows"):
         dev, st = torch.device("cuda:0"), torch.cuda.Stream()
         if args.part == "paged":
@@ -545,7 +594,7 @@ def main():
         attn_ms = step_ms = None
         attn_pct = step_pct = (float("nan"),) * 3
         n_steps = 0
-        components = ceiling = search_rate = paged_rate = windows_rate = pq_rate = None
+        components = ceiling = search_rate = paged_rate = windows_rate = pq_rate = vq_rates = None
         if attn_graph is not None:
             attn_ms, n_steps, attn_pct = timed(attn_graph, args.steps, args.warmup)
         if step_graph is not None:
@@ -557,6 +606,7 @@ def main():
             paged_rate = paged_ragged_rate(dev, stream, page_tokens=args.page_tokens)
             windows_rate = windows_decode_rate(dev, stream)
             pq_rate = pq_search_rate(dev, stream)
+            vq_rates = {f"cq{2 * r}": vq_decode_rate(dev, stream, r) for r in (1, 2)}
     torch.cuda.synchronize()
 
     if args.part != "all":
@@ -598,6 +648,7 @@ def main():
         "paged_ragged": paged_rate,
         "windows_decode": windows_rate,
         "pq_search": pq_rate,
+        "vq_decode": vq_rates,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)

@@ -24,7 +24,7 @@ __all__ = [
     "KiviCacheDesc", "kvq_kivi_step_workspace", "kvq_kivi_step",
     "kvq_window_thresholds", "kvq_window_search_workspace", "kvq_window_search",
     "PagedArgs", "kvq_page_layout", "kvq_decode_attn_paged_workspace", "kvq_decode_attn_paged",
-    "kvq_pq_search",
+    "kvq_pq_search", "kvq_vq_decode_attn_workspace", "kvq_vq_decode_attn",
 ]
 
 KVQ_KEYS = 0
@@ -159,6 +159,11 @@ def _load():
     lib.kvq_decode_attn_paged.argtypes = [ctypes.POINTER(PagedArgs), vp]
     lib.kvq_pq_search.restype = i32
     lib.kvq_pq_search.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp, vp]
+    lib.kvq_vq_decode_attn_workspace.restype = i32
+    lib.kvq_vq_decode_attn_workspace.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.kvq_vq_decode_attn.restype = i32
+    lib.kvq_vq_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, vp, i64,
+                                       vp, vp, vp, vp, ctypes.c_size_t, vp]
     if lib.kvq_abi_version() != ABI_VERSION:
         raise ImportError(f"libkvq ABI {lib.kvq_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -339,3 +344,19 @@ def kvq_pq_search(batch, n_q_heads, n_kv_heads, d_h, m, bits, n_tok, top_k, q, c
     _check(_load().kvq_pq_search(batch, n_q_heads, n_kv_heads, d_h, m, bits, n_tok, top_k, _dev(q),
                                  _dev(centroids), _dev(codes), int(codes_stride), _dev(scores),
                                  _dev(top_idx), _stream(stream)), "kvq_pq_search")
+
+
+def kvq_vq_decode_attn_workspace(batch, n_q_heads, n_kv_heads, d_h, rounds, n_tok) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_load().kvq_vq_decode_attn_workspace(batch, n_q_heads, n_kv_heads, d_h, rounds, n_tok, ctypes.byref(n)),
+           "kvq_vq_decode_attn_workspace")
+    return int(n.value)
+
+
+def kvq_vq_decode_attn(batch, n_q_heads, n_kv_heads, d_h, rounds, n_tok, sm_scale, q, k_codes, v_codes,
+                       codes_stride, k_books, v_books, out, workspace=None, workspace_bytes=0, stream=None):
+    """Decode attention over a vector-quantized (codebook) KV cache."""
+    _check(_load().kvq_vq_decode_attn(batch, n_q_heads, n_kv_heads, d_h, rounds, n_tok, float(sm_scale), _dev(q),
+                                      _dev(k_codes), _dev(v_codes), int(codes_stride), _dev(k_books),
+                                      _dev(v_books), _dev(out), _dev(workspace), int(workspace_bytes),
+                                      _stream(stream)), "kvq_vq_decode_attn")

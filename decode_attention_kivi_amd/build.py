@@ -30,7 +30,7 @@ COMMON = [
 PER_FILE = {
     "quantize.hip": ["-ffp-contract=off"],
 }
-SOURCES = ["api.hip", "quantize.hip", "reorder.hip", "decode.hip", "search.hip", "pq.hip"]
+SOURCES = ["api.hip", "quantize.hip", "reorder.hip", "decode.hip", "search.hip", "pq.hip", "vq.hip"]
 
 
 def hipcc() -> str:

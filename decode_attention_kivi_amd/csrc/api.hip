@@ -9,6 +9,7 @@
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
 #include "pq.h"
+#include "vq.h"
 
 namespace {
 
@@ -585,6 +586,79 @@ kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
   p.top_k = top_k;
   p.chunk_tokens = 2048;
   return from_hip(kvq::launch_pq_search(p, GQ, fused, static_cast<hipStream_t>(stream)));
+}
+
+// Decode attention over a vector-quantized (codebook) cache: the token
+// chunks and the workspace of a call.
+static kvq_status vq_plan(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_h, int32_t rounds,
+                          int32_t n_tok, kvq::VqParams* p, size_t* ws_bytes) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0) return KVQ_EINVAL;
+  if (int64_t(batch) * n_kv_heads > 65535 || int64_t(batch) * n_q_heads > (int64_t(1) << 31))
+    return KVQ_EUNSUPPORTED;
+  if (!valid_d(d_h) || (rounds != 1 && rounds != 2)) return KVQ_EUNSUPPORTED;
+  if (n_tok < 1 || n_tok > (1 << 24)) return KVQ_EINVAL;
+  // chunks of at most kVqMaxChunk tokens; more (down to 256 tokens) when the
+  // streams alone give fewer than 512 workgroups (two per CU)
+  const int64_t streams = int64_t(batch) * n_kv_heads;
+  int64_t nc = (int64_t(n_tok) + kvq::kVqMaxChunk - 1) / kvq::kVqMaxChunk;
+  const int64_t want = std::min<int64_t>((512 + streams - 1) / streams, (int64_t(n_tok) + 255) / 256);
+  nc = std::max(nc, want);
+  int64_t chunk = (int64_t(n_tok) + nc - 1) / nc;
+  chunk = std::min<int64_t>(kvq::kVqMaxChunk, (chunk + 63) / 64 * 64);
+  nc = (int64_t(n_tok) + chunk - 1) / chunk;
+  if (nc > kvq::kVqMaxChunks) return KVQ_EUNSUPPORTED;
+  if (kvq::vq_lds_bytes(d_h, rounds, int(chunk)) + 4096 > 160 * 1024) return KVQ_EUNSUPPORTED;
+  std::memset(p, 0, sizeof(*p));
+  p->B = batch;
+  p->Hq = n_q_heads;
+  p->Hkv = n_kv_heads;
+  p->gq = n_q_heads / n_kv_heads;
+  p->D = d_h;
+  p->R = rounds;
+  p->n_tok = n_tok;
+  p->chunk_tokens = int32_t(chunk);
+  p->n_chunks = int32_t(nc);
+  *ws_bytes = nc == 1 ? 0 : size_t(streams) * size_t(nc) * size_t(p->gq) * size_t(d_h + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
+kvq_status kvq_vq_decode_attn_workspace(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_h,
+                                        int32_t rounds, int32_t n_tok, size_t* bytes) {
+  if (!bytes) return KVQ_EINVAL;
+  kvq::VqParams p;
+  return vq_plan(batch, n_q_heads, n_kv_heads, d_h, rounds, n_tok, &p, bytes);
+}
+
+kvq_status kvq_vq_decode_attn(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_h, int32_t rounds,
+                              int32_t n_tok, float sm_scale, const void* q, const void* k_codes,
+                              const void* v_codes, int64_t codes_stride, const void* k_books,
+                              const void* v_books, float* out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  kvq::VqParams p;
+  size_t need = 0;
+  const kvq_status st = vq_plan(batch, n_q_heads, n_kv_heads, d_h, rounds, n_tok, &p, &need);
+  if (st != KVQ_OK) return st;
+  if (!std::isfinite(sm_scale)) return KVQ_EINVAL;
+  if (!q || !k_codes || !v_codes || !k_books || !v_books || !out) return KVQ_EINVAL;
+  if (codes_stride < int64_t(n_tok) * rounds * (d_h / 4)) return KVQ_EINVAL;
+  if (codes_stride & 15) return KVQ_EALIGN;
+  for (const void* ptr : {q, k_codes, v_codes, k_books, v_books})
+    if (!aligned16(ptr)) return KVQ_EALIGN;
+  if (reinterpret_cast<uintptr_t>(out) & 3) return KVQ_EALIGN;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return KVQ_EWORKSPACE;
+    if (!aligned16(workspace)) return KVQ_EALIGN;
+  }
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_codes = static_cast<const uint8_t*>(k_codes);
+  p.v_codes = static_cast<const uint8_t*>(v_codes);
+  p.k_books = static_cast<const uint16_t*>(k_books);
+  p.v_books = static_cast<const uint16_t*>(v_books);
+  p.out = out;
+  p.ws = static_cast<float*>(workspace);
+  p.codes_stride = codes_stride;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  return from_hip(kvq::launch_vq_decode(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -396,6 +396,41 @@ kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
                          int64_t codes_stride, float* scores, int32_t* top_idx, void* stream);
 
 /*
+ * kvq_vq_decode_attn -- decode attention over a vector-quantized (codebook)
+ * KV cache (VQ-LLM note, "Background" on vector quantization and its CQ-2 /
+ * CQ-4 KV-cache configurations): the key (value) of token t in kv head kv is,
+ * in channels 4g .. 4g+3, the sum over rounds r < rounds of the codebook
+ * entry k_books[kv][r][g][code] with code = k_codes[t][r][g] (likewise for
+ * values); rounds = 1 is CQ-2 (2 bits per channel), rounds = 2 is CQ-4 (the
+ * second round codes the residual of the first, 4 bits per channel).  For
+ * every batch row b and query head hq, with kv = hq / (n_q_heads /
+ * n_kv_heads):
+ *   out[b][hq] = sum_t softmax_t(sm_scale * q[b][hq] . key_t) * value_t
+ * over the n_tok cached tokens (fp32 accumulation).
+ * Layouts: q fp16 [batch][n_q_heads][d_h]; k_codes, v_codes u8, stream
+ * s = b*n_kv_heads + kv at codes + s*codes_stride bytes, [n_tok][rounds][d_h/4];
+ * k_books, v_books fp16 [n_kv_heads][rounds][d_h/4][256][4] (shared by every
+ * batch row); out fp32 [batch][n_q_heads][d_h].
+ * workspace: device scratch of kvq_vq_decode_attn_workspace bytes (partial
+ * softmax states of token chunks; 0 bytes, and NULL allowed, when each
+ * stream is one chunk); calls sharing one must not overlap.
+ * Checks (before any launch): d_h 64 or 128 (KVQ_EUNSUPPORTED); rounds 1 or
+ * 2 (KVQ_EUNSUPPORTED); 1 <= n_tok <= 2^24 (at most 1024 chunks of up to
+ * 8192 tokens); n_q_heads a multiple of n_kv_heads; codes_stride >=
+ * n_tok*rounds*d_h/4 and a multiple of 16; q, codes and codebooks 16-byte
+ * aligned, out 4-byte aligned; sm_scale finite.  Codebooks and codes are
+ * inputs (their training runs elsewhere).  The value weights are summed with
+ * LDS atomics, so the last bits of out may differ between runs.
+ */
+kvq_status kvq_vq_decode_attn_workspace(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t d_h, int32_t rounds, int32_t n_tok, size_t* bytes);
+kvq_status kvq_vq_decode_attn(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_h,
+                              int32_t rounds, int32_t n_tok, float sm_scale, const void* q,
+                              const void* k_codes, const void* v_codes, int64_t codes_stride,
+                              const void* k_books, const void* v_books, float* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kvq_window_thresholds -- the two score thresholds of a layer (WindowQuant
  * Sec. 3.2.3, Eq. 10 and 11): with s the layer's hidden-state similarity
  * (Eq. 9) and alpha the hyper-parameter,

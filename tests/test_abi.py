@@ -344,3 +344,35 @@ def test_pq_search_rejects(kw, code):
     with pytest.raises(KvqError) as e:
         kvq.kvq_pq_search(**a)
     assert e.value.status == code
+
+
+def test_vq_workspace_plan():
+    # 512 streams (Llama-2-7B MHA shape, 4096 tokens): one chunk per stream,
+    # no partial states
+    assert kvq.kvq_vq_decode_attn_workspace(16, 32, 32, 128, 1, 4096) == 0
+    # 32 streams of 32768 tokens (GQA long context): 16 chunks of 2048 tokens
+    # fill 512 workgroups; partial states of 4 query heads per chunk
+    assert kvq.kvq_vq_decode_attn_workspace(4, 32, 8, 128, 2, 32768) == 32 * 16 * 4 * 130 * 4
+    # a short context is never cut below 256 tokens per chunk
+    assert kvq.kvq_vq_decode_attn_workspace(1, 1, 1, 64, 1, 300) == 2 * 1 * 66 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_h=96, codes_stride=2400), EUNSUP), (dict(rounds=3), EUNSUP), (dict(n_tok=0), EINVAL),
+    (dict(n_q_heads=5), EINVAL), (dict(codes_stride=3184), EINVAL), (dict(codes_stride=3208), EALIGN),
+    (dict(q=A + 2), EALIGN), (dict(k_books=A + 8), EALIGN), (dict(out=A + 2), EALIGN),
+    (dict(v_codes=None), EINVAL), (dict(sm_scale=float("nan")), EINVAL),
+    (dict(n_tok=1 << 25, codes_stride=1 << 30), EINVAL),
+    (dict(batch=1, n_q_heads=1, n_kv_heads=1, workspace=None), EWS),   # 2 chunks need partial states
+])
+def test_vq_decode_rejects(kw, code):
+    a = dict(batch=2, n_q_heads=4, n_kv_heads=2, d_h=128, rounds=1, n_tok=100, sm_scale=0.1, q=A, k_codes=A,
+             v_codes=A, codes_stride=3200, k_books=A, v_books=A, out=A, workspace=A, workspace_bytes=1 << 20,
+             stream=0)
+    a.update(kw)
+    if "n_tok" not in kw and a["batch"] == 1:
+        a["n_tok"] = 300                 # one stream of 300 tokens: two chunks
+        a["codes_stride"] = 300 * 32 // 16 * 16 + 16
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_vq_decode_attn(**a)
+    assert e.value.status == code

@@ -47,7 +47,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "get", "unit_kv", "queries", "outlier_channels",
-    "full_kv", "window_bits", "sample_units", "search_tokens", "ragged_contexts", "pq_inputs",
+    "full_kv", "window_bits", "sample_units", "search_tokens", "ragged_contexts", "pq_inputs", "vq_inputs",
 ]
 
 
