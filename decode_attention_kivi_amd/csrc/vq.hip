@@ -83,23 +83,33 @@ __global__ void __launch_bounds__(kVqThreads) vq_partial_kernel(const VqParams P
     }
     __syncthreads();
 
-    // base-2 logits of the chunk's tokens, one token per thread at a time
+    // base-2 logits of the chunk's tokens, a token per thread, the codes of
+    // UK tokens loaded together (past the end: token nt - 1, not stored)
+    constexpr int UK = 4;
     float mx = -INFINITY;
-    for (int t = tid; t < nt; t += kVqThreads) {
-      const uint4* c = reinterpret_cast<const uint4*>(kc + int64_t(t) * TB);
-      uint4 u[TB / 16];
+    for (int tb = tid; tb < nt; tb += UK * kVqThreads) {
+      uint4 u[UK][TB / 16];
 #pragma unroll
-      for (int w = 0; w < TB / 16; ++w) u[w] = c[w];
-      float acc = 0.f;
+      for (int k = 0; k < UK; ++k) {
+        const uint4* c = reinterpret_cast<const uint4*>(kc + int64_t(min(tb + k * kVqThreads, nt - 1)) * TB);
 #pragma unroll
-      for (int w = 0; w < TB / 16; ++w) {
-        const uint32_t wd[4] = {u[w].x, u[w].y, u[w].z, u[w].w};
-#pragma unroll
-        for (int k = 0; k < 16; ++k) acc += tab[(w * 16 + k) * 256 + ((wd[k >> 2] >> ((k & 3) * 8)) & 0xffu)];
+        for (int w = 0; w < TB / 16; ++w) u[k][w] = c[w];
       }
-      const float x = acc * P.scale_log2;
-      xs[t] = x;
-      mx = fmaxf(mx, x);
+#pragma unroll
+      for (int k = 0; k < UK; ++k) {
+        const int t = tb + k * kVqThreads;
+        if (t >= nt) break;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < TB / 16; ++w) {
+          const uint32_t wd[4] = {u[k][w].x, u[k][w].y, u[k][w].z, u[k][w].w};
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc += tab[(w * 16 + j) * 256 + ((wd[j >> 2] >> ((j & 3) * 8)) & 0xffu)];
+        }
+        const float x = acc * P.scale_log2;
+        xs[t] = x;
+        mx = fmaxf(mx, x);
+      }
     }
     mx = wave_max64(mx);
     if (lane == 0) red[wave] = mx;
@@ -137,22 +147,34 @@ __global__ void __launch_bounds__(kVqThreads) vq_partial_kernel(const VqParams P
     for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[gi][j] = 0.f;
-    for (int t = wave * TPW + ts; t < nt; t += kVqWaves * TPW) {
-      const float p = h2f(p16[t]);
-      uint32_t c4[R];
+    // the codes of UV steps loaded together (past the end: token nt - 1 with
+    // probability 0)
+    constexpr int UV = 8;
+    constexpr int STEP = kVqWaves * TPW;
+    for (int tb = wave * TPW + ts; tb < nt; tb += UV * STEP) {
+      uint32_t c4[UV][R];
+      float p[UV];
 #pragma unroll
-      for (int r = 0; r < R; ++r) c4[r] = *reinterpret_cast<const uint32_t*>(vc + int64_t(t) * TB + r * G + quad * 4);
+      for (int u = 0; u < UV; ++u) {
+        const int t = tb + u * STEP;
+        const uint8_t* c = vc + int64_t(min(t, nt - 1)) * TB + quad * 4;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+        for (int r = 0; r < R; ++r) c4[u][r] = *reinterpret_cast<const uint32_t*>(c + r * G);
+        p[u] = t < nt ? h2f(p16[t]) : 0.f;
+      }
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-          const int e = ((r * G + quad * 4 + gi) << 8) + int((c4[r] >> (8 * gi)) & 0xffu);
-          const uint2 v = *reinterpret_cast<const uint2*>(book + e * 4);
-          acc[gi][0] = __builtin_fmaf(p, h2f(v.x & 0xffffu), acc[gi][0]);
-          acc[gi][1] = __builtin_fmaf(p, h2f(v.x >> 16), acc[gi][1]);
-          acc[gi][2] = __builtin_fmaf(p, h2f(v.y & 0xffffu), acc[gi][2]);
-          acc[gi][3] = __builtin_fmaf(p, h2f(v.y >> 16), acc[gi][3]);
-        }
+      for (int u = 0; u < UV; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int gi = 0; gi < 4; ++gi) {
+            const int e = ((r * G + quad * 4 + gi) << 8) + int((c4[u][r] >> (8 * gi)) & 0xffu);
+            const uint2 v = *reinterpret_cast<const uint2*>(book + e * 4);
+            acc[gi][0] = __builtin_fmaf(p[u], h2f(v.x & 0xffffu), acc[gi][0]);
+            acc[gi][1] = __builtin_fmaf(p[u], h2f(v.x >> 16), acc[gi][1]);
+            acc[gi][2] = __builtin_fmaf(p[u], h2f(v.y & 0xffffu), acc[gi][2]);
+            acc[gi][3] = __builtin_fmaf(p[u], h2f(v.y >> 16), acc[gi][3]);
+          }
     }
     // sum over the lanes of a quad (lanes quad, quad + QPT, ...), then over
     // the waves in order
