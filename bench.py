@@ -451,8 +451,8 @@ def main():
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 "
+                                   "(sharding the streams or the context across GPUs is not built)"}))
         sys.exit(2)
 
     import torch
