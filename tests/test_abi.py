@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from tests.helpers import ROOT, ensure_built
@@ -376,3 +377,28 @@ def test_vq_decode_rejects(kw, code):
     with pytest.raises(KvqError) as e:
         kvq.kvq_vq_decode_attn(**a)
     assert e.value.status == code
+
+
+def test_vq_chunk_plan_properties():
+    # chunks cover the context, hold at most 8192 tokens, are not cut below
+    # 256 tokens (unless the context is shorter), and a split happens only
+    # when the streams alone give fewer than 512 workgroups or the context
+    # exceeds one chunk; the chunk count is read back from the workspace
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        B = int(rng.integers(1, 40))
+        hkv = int(rng.choice([1, 2, 4, 8, 32]))
+        gq = int(rng.integers(1, 9))
+        d = int(rng.choice([64, 128]))
+        R = int(rng.integers(1, 3))
+        n = int(rng.integers(1, 200000))
+        ws = kvq.kvq_vq_decode_attn_workspace(B, hkv * gq, hkv, d, R, n)
+        streams = B * hkv
+        nc = 1 if ws == 0 else ws // (streams * gq * (d + 2) * 4)
+        assert ws == 0 or ws == streams * nc * gq * (d + 2) * 4
+        assert 1 <= nc <= 1024
+        assert nc >= -(-n // 8192)
+        if nc > 1:
+            assert -(-n // nc) >= 64 and (n > 8192 or streams * nc <= 2 * 512)
+        if n <= 256 and streams >= 1:
+            assert nc == 1

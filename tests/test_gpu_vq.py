@@ -1,7 +1,7 @@
 """GPU parity of decode attention over a vector-quantized (codebook) KV cache
 (kvq_vq_decode_attn) against the oracle (oracle/vq.py): every output within
 2e-3 abs + 1e-3 rel of the float64 oracle (tests/helpers.py).  Shapes cover
-both head dims, one and two rounds (CQ-2 / CQ-4), MHA and 2-7 query heads
+both head dims, one and two rounds (CQ-2 / CQ-4), MHA and 2-16 query heads
 per kv head, one chunk per stream (output written directly) and many
 chunks (partial states and the merge kernel), ragged chunk tails, a single
 token, and the Llama-2-7B decode shape at full size (sampled heads)."""
@@ -62,6 +62,9 @@ def run_vq(kvq, B, Hq, Hkv, d, R, n, heads=None, seed=0):
     (1, 2, 1, 128, 2, 40000),
     (2, 4, 4, 128, 1, 1),
     (1, 8, 1, 64, 1, 4097),
+    # many query heads per kv head (the kernel loops over them) and chunks
+    (1, 16, 1, 128, 1, 9000),
+    (2, 16, 2, 64, 2, 17000),
 ])
 def test_vq_decode(kvq, B, Hq, Hkv, d, R, n):
     run_vq(kvq, B, Hq, Hkv, d, R, n)
