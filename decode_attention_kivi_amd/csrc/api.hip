@@ -607,7 +607,7 @@ static kvq_status vq_plan(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, 
   chunk = std::min<int64_t>(kvq::kVqMaxChunk, (chunk + 63) / 64 * 64);
   nc = (int64_t(n_tok) + chunk - 1) / chunk;
   if (nc > kvq::kVqMaxChunks) return KVQ_EUNSUPPORTED;
-  if (kvq::vq_lds_bytes(d_h, rounds, int(chunk)) + 4096 > 160 * 1024) return KVQ_EUNSUPPORTED;
+  if (kvq::vq_lds_bytes(d_h, int(chunk)) + 4096 > 160 * 1024) return KVQ_EUNSUPPORTED;
   std::memset(p, 0, sizeof(*p));
   p->B = batch;
   p->Hq = n_q_heads;

@@ -24,16 +24,16 @@ struct VqParams {
 constexpr int kVqMaxChunk = 8192;       // tokens per workgroup at most
 constexpr int kVqMaxChunks = 1024;      // chunks per stream at most
 
-// LDS region of the partial kernel: the key table (R * D/4 * 256 fp32) and
-// the chunk's logits (fp32) first, the value codebook (R * D/4 * 256 * 4
-// fp16) after them
-__host__ __device__ inline int64_t vq_region_bytes(int D, int R, int chunk_tokens) {
-  const int64_t ne = int64_t(R) * (D / 4) * 256;
+// LDS region of the partial kernel, one codebook round at a time: a round's
+// key table (D/4 * 256 fp32) and the chunk's logits (fp32) first, the
+// round's value codebook (D/4 * 256 * 4 fp16) after them
+__host__ __device__ inline int64_t vq_region_bytes(int D, int chunk_tokens) {
+  const int64_t ne = int64_t(D / 4) * 256;
   const int64_t a = ne * 8, b = (ne + chunk_tokens) * 4;
   return ((a > b ? a : b) + 15) / 16 * 16;
 }
 // LDS bytes of the partial kernel (region, fp16 probabilities, q)
-int64_t vq_lds_bytes(int D, int R, int chunk_tokens);
+int64_t vq_lds_bytes(int D, int chunk_tokens);
 hipError_t launch_vq_decode(const VqParams& p, hipStream_t s);
 
 }  // namespace kvq
