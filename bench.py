@@ -318,17 +318,18 @@ def windows_decode_rate(dev, stream, reps: int = 50):
             "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
-def pq_search_rate(dev, stream, reps: int = 50):
+def pq_search_rate(dev, stream, reps: int = 50, B: int = 4, n: int = 32769):
     """kvq_pq_search (PQCache's decode-time PQ search) at the GQA long-context
-    shape: 4 sequences x 32 query heads over 8 kv heads, 32769 tokens, m = 2
-    sub-spaces of 256 centroids (8-bit codes), Top-k = 3277 (1/10 of the
-    tokens).  One kernel per call (a head's 32769 scores fit in LDS): each
+    shape: B sequences x 32 query heads over 8 kv heads, n tokens (32769, or
+    the page's 128K context), m = 2 sub-spaces of 256 centroids (8-bit
+    codes), Top-k = 1/10 of the tokens.  One kernel per call (a head's 32769 scores fit in LDS): each
     query head's workgroup reads its kv head's codes and centroids and q,
     writes the fp32 scores and the Top-k indices.  Algorithmic bytes count
     the codes and centroids once per kv head."""
     import torch
     import decode_attention_kivi_amd as kvq
-    B, Hq, Hkv, d, m, bits, n, k = 4, 32, 8, 128, 2, 8, 32769, 3277
+    Hq, Hkv, d, m, bits = 32, 8, 128, 2, 8
+    k = (n + 9) // 10
     w = workloads.Workload(name="pq", batch=B, n_q_heads=Hq, n_kv_heads=Hkv, d_h=d, context=n,
                            group=32, residual=32, bits=2)
     c, codes = workloads.pq_inputs(B, Hkv, n, d, m, bits)
@@ -472,6 +473,7 @@ def main():
             r = paged_ragged_rate(dev, st, page_tokens=args.page_tokens)
         elif args.part == "pq":
             r = pq_search_rate(dev, st)
+            r["context_128k"] = pq_search_rate(dev, st, reps=20, B=1, n=131072)
         elif args.part == "search":
             r = window_search_rate(dev, st)
         else:
@@ -606,6 +608,7 @@ def main():
             paged_rate = paged_ragged_rate(dev, stream, page_tokens=args.page_tokens)
             windows_rate = windows_decode_rate(dev, stream)
             pq_rate = pq_search_rate(dev, stream)
+            pq_rate["context_128k"] = pq_search_rate(dev, stream, reps=20, B=1, n=131072)
             vq_rates = {f"cq{2 * r}": vq_decode_rate(dev, stream, r) for r in (1, 2)}
     torch.cuda.synchronize()
 

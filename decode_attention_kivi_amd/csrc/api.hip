@@ -584,7 +584,7 @@ kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
   p.bits = bits;
   p.n_tok = n_tok;
   p.top_k = top_k;
-  p.chunk_tokens = 2048;
+  p.chunk_tokens = 4096;
   return from_hip(kvq::launch_pq_search(p, GQ, fused, static_cast<hipStream_t>(stream)));
 }
 

@@ -187,17 +187,17 @@ __device__ __forceinline__ void block_range(float lo, float hi, float* fsh, floa
 }
 
 // f(t, sc[t]) for every t < n, the block's threads striding over the
-// tokens with four reads in flight per thread.
-// Reads past the end take sc[n - 1] (n >= 1) and are not passed on:
-// unconditional reads issue back to back.
-template <typename F>
+// tokens with U reads in flight per thread (4 from LDS, 16 from memory,
+// where the latency is longer).  Reads past the end take sc[n - 1]
+// (n >= 1) and are not passed on: unconditional reads issue back to back.
+template <int U = 4, typename F>
 __device__ __forceinline__ void for_scores(const float* sc, int n, F&& f) {
-  for (int t0 = threadIdx.x; t0 < n; t0 += 4 * kTopkThreads) {
-    float x[4];
+  for (int t0 = threadIdx.x; t0 < n; t0 += U * kTopkThreads) {
+    float x[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = sc[min(t0 + u * kTopkThreads, n - 1)];
+    for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * kTopkThreads, n - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
       if (t0 + u * kTopkThreads < n) f(t0 + u * kTopkThreads, x[u] + 0.0f);
   }
 }
@@ -217,6 +217,7 @@ constexpr int kCand = kBins - 256;
 // kBins counters: with l1_ready the caller has filled it with the level-1
 // histogram (bucket_id(x, lo, bucket_scale(lo, hi)) >> 11 of every score)
 // and synced.  Every thread of the block calls.
+template <int U>
 __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k, float lo, float hi,
                                              int32_t* out, float* copy, uint32_t* hist, uint32_t* sh,
                                              bool l1_ready) {
@@ -228,7 +229,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   if (!l1_ready) {
     for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for_scores(sc, n, [&](int t, float x) { atomicAdd(&hist[bucket_id(x, lo, s2) >> 11], 1u); });
+    for_scores<U>(sc, n, [&](int t, float x) { atomicAdd(&hist[bucket_id(x, lo, s2) >> 11], 1u); });
     __syncthreads();
   }
   const int b1 = find_bin(hist, kBins, k_rem, &above, sh);
@@ -241,7 +242,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   if (in_b1 > uint32_t(kCand)) {
     for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for_scores(sc, n, [&](int t, float x) {
+    for_scores<U>(sc, n, [&](int t, float x) {
       const int id = bucket_id(x, lo, s2);
       if ((id >> 11) == b1) atomicAdd(&hist[id & (kBins - 1)], 1u);
     });
@@ -254,7 +255,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   if (tid == 0) sh[70] = 0;
   __syncthreads();
   uint32_t* cand = hist + 256;
-  for_scores(sc, n, [&](int t, float x) {
+  for_scores<U>(sc, n, [&](int t, float x) {
     if (copy) copy[t] = x;
     if ((bucket_id(x, lo, s2) >> cshift) == target) {
       const uint32_t slot = atomicAdd(&sh[70], 1u);
@@ -277,7 +278,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
       }
     } else {
-      for_scores(sc, n, [&](int t, float x) {
+      for_scores<U>(sc, n, [&](int t, float x) {
         if ((bucket_id(x, lo, s2) >> cshift) != target) return;
         const uint32_t key = order_key(x);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
@@ -303,12 +304,12 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   const int seg = ((n + NW - 1) / NW + 63) / 64 * 64;
   const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
   uint32_t gt_w = 0, eq_w = 0;
-  for (int t0 = w0; t0 < w1; t0 += 256) {
-    float x[4];
+  for (int t0 = w0; t0 < w1; t0 += 64 * U) {
+    float x[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+    for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const bool in = t0 + u * 64 + lane < w1;
       gt_w += uint32_t(__popcll(__ballot(in && x[u] > Tf)));
       eq_w += uint32_t(__popcll(__ballot(in && x[u] == Tf)));
@@ -318,12 +319,12 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   __syncthreads();
   uint32_t gb = 0, eb = 0;
   for (int w = 0; w < wave; ++w) { gb += sh[w]; eb += sh[NW + w]; }
-  for (int t0 = w0; t0 < w1; t0 += 256) {
-    float x[4];
+  for (int t0 = w0; t0 < w1; t0 += 64 * U) {
+    float x[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+    for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int t = t0 + u * 64 + lane;
       const bool gt = t < w1 && x[u] > Tf, eq = t < w1 && x[u] == Tf;
       const uint64_t mg = __ballot(gt), me = __ballot(eq);
@@ -345,13 +346,12 @@ __global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P)
   const float* sc = P.scores + head * P.n_tok;
   const int n = P.n_tok;
   float lo = INFINITY, hi = -INFINITY;
-  for (int t = threadIdx.x; t < n; t += kTopkThreads) {
-    const float x = sc[t] + 0.0f;
+  for_scores<16>(sc, n, [&](int, float x) {
     lo = fminf(lo, x);
     hi = fmaxf(hi, x);
-  }
+  });
   block_range(lo, hi, fsh, &lo, &hi);
-  select_top_k(sc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh, false);
+  select_top_k<16>(sc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh, false);
 }
 
 // Whole search of one (b, hq) with its scores resident in LDS: the head's
@@ -466,8 +466,8 @@ __global__ void __launch_bounds__(kTopkThreads) pq_fused_kernel(const PqParams P
     }
   }
   __syncthreads();
-  select_top_k(ssc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, P.scores + head * n, hist, sh,
-               true);
+  select_top_k<4>(ssc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, P.scores + head * n, hist, sh,
+                  true);
 }
 
 }  // namespace
