@@ -8,8 +8,9 @@
 // Three kernels:
 //   pq_scores_kernel  grid (token chunks, B * Hkv): the tables of the GQ query
 //                     heads of one kv head in LDS (fp32 dot products of the
-//                     fp16 centroids and q), then 16-byte code loads (16/m
-//                     tokens per lane) and table lookups; scores fp32.
+//                     fp16 centroids and q), then a token per lane (its m
+//                     code bytes in one load) and table lookups; scores fp32,
+//                     stored by consecutive lanes to consecutive tokens.
 //   pq_topk_kernel    one workgroup per (b, hq): the k-th largest score is
 //                     narrowed down by two levels of 2048 equal-width value
 //                     buckets (histograms in LDS: the scores spread over them,
@@ -40,10 +41,11 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-template <int GQ>
+template <int GQ, int M>
 __global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int D = P.D, m = P.m, dm = D / m, nc = 1 << P.bits;
+  constexpr int m = M;
+  const int D = P.D, dm = D / m, nc = 1 << P.bits;
   const int64_t stream = blockIdx.y;
   const int b = int(stream / P.Hkv), kv = int(stream % P.Hkv);
   float* tab = reinterpret_cast<float*>(smem);                        // [GQ][m][nc]
@@ -81,34 +83,56 @@ __global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P)
     for (int h = 0; h < GQ; ++h) tab[(h * m + j) * nc + (e - j * nc)] = acc[h];
   }
   __syncthreads();
-  // codes: lane loads 16 bytes = 16/m tokens; chunk = blockDim * U loads
-  const int tpl = 16 / m;                                   // tokens per 16-byte load
+  // one token per lane (its m code bytes), UT tokens in flight, so that
+  // consecutive lanes store consecutive scores; past the end: token
+  // t_end - 1, not stored; only the low `bits` bits of a code byte index
+  // the table
+  constexpr int UT = 4;
+  constexpr int NW = (M + 3) / 4;                           // code words per token
   const int64_t t_base = int64_t(blockIdx.x) * P.chunk_tokens;
   const int64_t t_end = min(int64_t(P.n_tok), t_base + P.chunk_tokens);
   const uint8_t* cb = P.codes + stream * P.codes_stride;
-  // the range check works per dword: the range is the codes rounded up to
-  // 16 bytes (within the stride the caller allocated), so the last tokens'
-  // codes are never cut off; bytes past n_tok * m are read and ignored
-  const Rsrc rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cb), short(0),
-                                                    int((int64_t(P.n_tok) * m + 15) / 16 * 16), 0x00020000);
-  for (int64_t t0 = t_base + int64_t(tid) * tpl; t0 < t_end; t0 += int64_t(kPqThreads) * tpl) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, uint32_t(t0 * m), 0, 2);
-    const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
-    for (int i = 0; i < tpl; ++i) {
-      const int64_t t = t0 + i;
+  const uint32_t cmask = uint32_t(nc - 1);
+  float* out0 = P.scores + (int64_t(b) * P.Hq + int64_t(kv) * P.gq) * P.n_tok;
+  for (int64_t tb = t_base + tid; tb < t_end; tb += UT * kPqThreads) {
+    uint32_t w[UT][NW];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const int64_t t = min(tb + u * kPqThreads, t_end - 1);
+      if constexpr (M == 1) {
+        w[u][0] = cb[t];
+      } else if constexpr (M == 2) {
+        w[u][0] = reinterpret_cast<const uint16_t*>(cb)[t];
+      } else if constexpr (M == 4) {
+        w[u][0] = reinterpret_cast<const uint32_t*>(cb)[t];
+      } else if constexpr (M == 8) {
+        const uint2 x = reinterpret_cast<const uint2*>(cb)[t];
+        w[u][0] = x.x;
+        w[u][1] = x.y;
+      } else {
+        const uint4 x = reinterpret_cast<const uint4*>(cb)[t];
+        w[u][0] = x.x;
+        w[u][1] = x.y;
+        w[u][2] = x.z;
+        w[u][3] = x.w;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+      const int64_t t = tb + u * kPqThreads;
       if (t >= t_end) break;
-      float s[GQ];
+      float sc[GQ];
 #pragma unroll
-      for (int h = 0; h < GQ; ++h) s[h] = 0.f;
-      for (int j = 0; j < m; ++j) {
-        const int byte = i * m + j;
-        const int code = int((w[byte >> 2] >> ((byte & 3) * 8)) & 0xffu);
+      for (int h = 0; h < GQ; ++h) sc[h] = 0.f;
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) s[h] += tab[(h * m + j) * nc + code];
+      for (int j = 0; j < M; ++j) {
+        const int code = int((w[u][j >> 2] >> ((j & 3) * 8)) & cmask);
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) sc[h] += tab[(h * M + j) * nc + code];
       }
 #pragma unroll
       for (int h = 0; h < GQ; ++h)
-        if (h < P.gq) P.scores[((int64_t(b) * P.Hq + int64_t(kv) * P.gq + h) * P.n_tok) + t] = s[h];
+        if (h < P.gq) out0[int64_t(h) * P.n_tok + t] = sc[h];
     }
   }
 }
@@ -513,13 +537,25 @@ hipError_t launch_pq_search(const PqParams& p, int GQ, bool fused, hipStream_t s
   const int64_t chunks = (int64_t(p.n_tok) + p.chunk_tokens - 1) / p.chunk_tokens;
   const dim3 grid(unsigned(chunks), unsigned(int64_t(p.B) * p.Hkv));
   const size_t lds = size_t(pq_scores_lds_bytes(GQ, p.D, p.m, p.bits));
+#define PQ_SCORES(G_, M_) hipLaunchKernelGGL((pq_scores_kernel<G_, M_>), grid, dim3(kPqThreads), lds, s, p)
+#define PQ_SCORES_M(G_)                      \
+  switch (p.m) {                             \
+    case 1: PQ_SCORES(G_, 1); break;         \
+    case 2: PQ_SCORES(G_, 2); break;         \
+    case 4: PQ_SCORES(G_, 4); break;         \
+    case 8: PQ_SCORES(G_, 8); break;         \
+    case 16: PQ_SCORES(G_, 16); break;       \
+    default: return hipErrorInvalidValue;    \
+  }
   switch (GQ) {
-    case 1: hipLaunchKernelGGL((pq_scores_kernel<1>), grid, dim3(kPqThreads), lds, s, p); break;
-    case 2: hipLaunchKernelGGL((pq_scores_kernel<2>), grid, dim3(kPqThreads), lds, s, p); break;
-    case 4: hipLaunchKernelGGL((pq_scores_kernel<4>), grid, dim3(kPqThreads), lds, s, p); break;
-    case 8: hipLaunchKernelGGL((pq_scores_kernel<8>), grid, dim3(kPqThreads), lds, s, p); break;
+    case 1: PQ_SCORES_M(1); break;
+    case 2: PQ_SCORES_M(2); break;
+    case 4: PQ_SCORES_M(4); break;
+    case 8: PQ_SCORES_M(8); break;
     default: return hipErrorInvalidValue;
   }
+#undef PQ_SCORES_M
+#undef PQ_SCORES
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pq_topk_kernel, dim3(unsigned(int64_t(p.B) * p.Hq)), dim3(kTopkThreads), 0, s, p);
