@@ -195,21 +195,6 @@ __device__ __forceinline__ int find_bin(const uint32_t* hist, int nbins, uint32_
   return int(sh[0]);
 }
 
-// Range [lo, hi] of the n scores (+0 for -0), reduced over the block.
-__device__ __forceinline__ void block_range(float lo, float hi, float* fsh, float* lo_out, float* hi_out) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  lo = span_min<64>(lo);
-  hi = span_max<64>(hi);
-  if (lane == 0) { fsh[wave] = lo; fsh[16 + wave] = hi; }
-  __syncthreads();
-  lo = fsh[0];
-  hi = fsh[16];
-  for (int w = 1; w < kTopkThreads / 64; ++w) { lo = fminf(lo, fsh[w]); hi = fmaxf(hi, fsh[16 + w]); }
-  __syncthreads();
-  *lo_out = lo;
-  *hi_out = hi;
-}
-
 // f(t, sc[t]) for every t < n, the block's threads striding over the
 // tokens with U reads in flight per thread (4 from LDS, 16 from memory,
 // where the latency is longer).  Reads past the end take sc[n - 1]
@@ -362,20 +347,55 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
 }
 
 // Top-k of the scores pq_scores_kernel wrote: one workgroup per (b, hq).
+// The score range comes from the head's tables (per sub-space the least and
+// greatest q_j . centroid, summed) instead of a pass over the scores: bucket
+// ids are clamped and non-decreasing, so a bound that a rounding difference
+// leaves a score just outside only widens the end buckets.
 __global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t sh[72];
   __shared__ float fsh[2 * kTopkThreads / 64];
+  __shared__ float tabr[16 * 256];                           // [m][2^bits] table entries
   const int64_t head = blockIdx.x;                            // b * Hq + hq
-  const float* sc = P.scores + head * P.n_tok;
-  const int n = P.n_tok;
-  float lo = INFINITY, hi = -INFINITY;
-  for_scores<16>(sc, n, [&](int, float x) {
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
-  });
-  block_range(lo, hi, fsh, &lo, &hi);
-  select_top_k<16>(sc, n, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh, false);
+  const int b = int(head / P.Hq), hq = int(head % P.Hq);
+  const int D = P.D, m = P.m, dm = D / m, nc = 1 << P.bits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint16_t* qh = P.q + head * D;
+  const uint16_t* cen = P.centroids + (int64_t(b) * P.Hkv + hq / P.gq) * int64_t(m) * nc * dm;
+  for (int e = tid; e < m * nc; e += kTopkThreads) {
+    const int j = e / nc;
+    const uint4* row = reinterpret_cast<const uint4*>(cen + int64_t(e) * dm);
+    float acc = 0.f;
+    for (int kk = 0; kk < dm / 8; ++kk) {
+      const uint4 u = row[kk];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = __builtin_fmaf(h2f(qh[j * dm + kk * 8 + 2 * i]), h2f(w[i] & 0xffffu), acc);
+        acc = __builtin_fmaf(h2f(qh[j * dm + kk * 8 + 2 * i + 1]), h2f(w[i] >> 16), acc);
+      }
+    }
+    tabr[e] = acc;
+  }
+  __syncthreads();
+  if (wave < m) {
+    float a = INFINITY, z = -INFINITY;
+    for (int c = lane; c < nc; c += 64) {
+      a = fminf(a, tabr[wave * nc + c]);
+      z = fmaxf(z, tabr[wave * nc + c]);
+    }
+    a = span_min<64>(a);
+    z = span_max<64>(z);
+    if (lane == 0) { fsh[wave] = a; fsh[16 + wave] = z; }
+  }
+  __syncthreads();
+  float lo = 0.f, hi = 0.f;
+  for (int j = 0; j < m; ++j) {
+    lo += fsh[j];
+    hi += fsh[16 + j];
+  }
+  select_top_k<16>(P.scores + head * P.n_tok, P.n_tok, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k,
+                   nullptr, hist, sh, false);
 }
 
 // Whole search of one (b, hq) with its scores resident in LDS: the head's
