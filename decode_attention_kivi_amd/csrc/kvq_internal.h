@@ -249,7 +249,6 @@ __host__ __device__ inline int paged_bound(const PagedCost& c, int n_kq, int n_v
 hipError_t launch_decode(const DecodeParams& p, int GQ, hipStream_t s);
 hipError_t launch_decode_paged(const DecodeParams& p, int GQ, hipStream_t s);
 // LDS bytes of a decode workgroup of `waves` waves; -1 if (D, GQ) is unsupported
-// LDS bytes of a decode workgroup of `waves` waves; -1 if (D, GQ) is unsupported
 int64_t decode_lds_bytes(int D, int GQ, int waves);
 
 struct QuantParams {
