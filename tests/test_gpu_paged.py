@@ -97,3 +97,27 @@ def test_more_sequences_than_the_schedule(kvq):
     # surplus workgroups leaving at once, instead of the sorted 1-D schedule
     rng = np.random.default_rng(3)
     run_paged([int(x) for x in rng.integers(0, 300, size=260)], 1, 1, 64, 32, 32, 2, 64)
+
+
+def _random_case(seed: int):
+    # page sizes are multiples of 64 and of G; G <= d; R a multiple of G
+    rng = np.random.default_rng([seed, 78])
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([32, 64] if d == 64 else [32, 64, 128]))
+    R = G * int(rng.integers(1, 3))
+    pt = int(np.lcm(64, G) * rng.integers(1, 5))
+    hkv = int(rng.integers(1, 4))
+    hq = hkv * int(rng.choice([1, 2, 3, 4, 7, 8]))
+    n = int(rng.integers(1, 9))
+    contexts = [int(x) for x in rng.integers(0, 3000, size=n)]
+    if rng.integers(0, 2):
+        contexts[0] = int(rng.integers(5000, 12000))      # a sequence that needs several workgroups
+    return contexts, hq, hkv, d, G, R, int(rng.choice([2, 4, 8])), pt
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_paged_batches(kvq, seed):
+    # seeded random batches: lengths, heads, GQA ratio, head dim, group,
+    # residual, width and page size drawn together
+    contexts, hq, hkv, d, G, R, bits, pt = _random_case(seed)
+    run_paged(contexts, hq, hkv, d, G, R, bits, pt, n_out=2, factor=8.0, seed=seed)
