@@ -35,3 +35,28 @@ def test_random_shapes(kvq, seed):  # noqa: F811
     w, steps, one_call, split = _case(seed)
     units = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
     run_kivi(kvq, w, units, steps=steps, split_tokens=split, check_every_step=True, one_call=one_call)
+
+
+def _window_case(seed: int):
+    rng = np.random.default_rng([seed, 79])
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([32, 64]))
+    S = int(rng.choice([64, 128, 256]))
+    W = int(rng.integers(2, 21))
+    text = int(rng.integers(0, 71))
+    hkv = int(rng.integers(1, 4))
+    w = workloads.get("qwen2_7b_windows").scaled(
+        name=f"windows{seed}", batch=int(rng.integers(1, 3)), n_kv_heads=hkv,
+        n_q_heads=hkv * int(rng.choice([1, 2, 4, 7])), d_h=d, group=G, windows=W, window_tokens=S,
+        text_tokens=text, context=W * S + text - 1, seed=seed)
+    bits = [int(x) for x in rng.choice([2, 4, 8, 16], size=W, p=[0.4, 0.3, 0.2, 0.1])]
+    split = 0 if rng.integers(0, 2) == 0 else int(rng.integers(64, 500))
+    return w, bits, split
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_windows(kvq, seed):  # noqa: F811
+    from tests.test_gpu_decode import run_windows
+    w, bits, split = _window_case(seed)
+    run_windows(kvq, w, bits, units=[(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)],
+                split_tokens=split)
