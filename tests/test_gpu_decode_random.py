@@ -3,8 +3,11 @@ kv heads, query heads per kv head (1-8, including ones that are not powers of
 two), head dim, group size, residual length, bit width, context length
 (including 0 and lengths that are not multiples of anything), several decode
 steps, forced split sizes and the one-call step, drawn together so that
-combinations the hand-picked cases do not cover are exercised.  Cache bytes
-bit for bit and attention within 2e-3 abs + 1e-3 rel, as in test_gpu_decode."""
+combinations the hand-picked cases do not cover are exercised; and random
+mixed-width window caches (window count and size, group, head dim, GQA
+ratio, trailing fp16 tokens, a width of 2/4/8/16 bits per window, forced
+splits).  Cache bytes bit for bit and attention within 2e-3 abs + 1e-3 rel,
+as in test_gpu_decode."""
 import numpy as np
 import pytest
 
