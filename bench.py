@@ -647,6 +647,8 @@ def main():
                      "streaming_read_ceiling_GBs": ceiling},
         "us_per_step_p10_p50_p90": [round(x * 1e3, 2) for x in step_pct],
         "components_us": components,
+        "components_note": "each library call timed alone between events with a synchronize after it "
+                           "(launch latency included); us_per_step is the graph-replayed step",
         "window_search": search_rate,
         "paged_ragged": paged_rate,
         "windows_decode": windows_rate,
