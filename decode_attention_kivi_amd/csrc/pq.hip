@@ -199,15 +199,36 @@ __device__ __forceinline__ int find_bin(const uint32_t* hist, int nbins, uint32_
 // tokens with U reads in flight per thread (4 from LDS, 16 from memory,
 // where the latency is longer).  Reads past the end take sc[n - 1]
 // (n >= 1) and are not passed on: unconditional reads issue back to back.
-template <int U = 4, typename F>
+// With V4 (n a multiple of 4, sc 16-byte aligned) a read is 4 consecutive
+// tokens, so four times the bytes are in flight.
+template <int U = 4, bool V4 = false, typename F>
 __device__ __forceinline__ void for_scores(const float* sc, int n, F&& f) {
-  for (int t0 = threadIdx.x; t0 < n; t0 += U * kTopkThreads) {
-    float x[U];
+  if constexpr (V4) {
+    const float4* s4 = reinterpret_cast<const float4*>(sc);
+    for (int t0 = 4 * int(threadIdx.x); t0 < n; t0 += 4 * U * kTopkThreads) {
+      float4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * kTopkThreads, n - 1)];
+      for (int u = 0; u < U; ++u) x[u] = s4[min(t0 + 4 * u * kTopkThreads, n - 4) >> 2];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (t0 + u * kTopkThreads < n) f(t0 + u * kTopkThreads, x[u] + 0.0f);
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + 4 * u * kTopkThreads;
+        if (t < n) {
+          f(t, x[u].x + 0.0f);
+          f(t + 1, x[u].y + 0.0f);
+          f(t + 2, x[u].z + 0.0f);
+          f(t + 3, x[u].w + 0.0f);
+        }
+      }
+    }
+  } else {
+    for (int t0 = threadIdx.x; t0 < n; t0 += U * kTopkThreads) {
+      float x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * kTopkThreads, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t0 + u * kTopkThreads < n) f(t0 + u * kTopkThreads, x[u] + 0.0f);
+    }
   }
 }
 
@@ -226,7 +247,7 @@ constexpr int kCand = kBins - 256;
 // kBins counters: with l1_ready the caller has filled it with the level-1
 // histogram (bucket_id(x, lo, bucket_scale(lo, hi)) >> 11 of every score)
 // and synced.  Every thread of the block calls.
-template <int U>
+template <int U, bool V4 = false>
 __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k, float lo, float hi,
                                              int32_t* out, float* copy, uint32_t* hist, uint32_t* sh,
                                              bool l1_ready) {
@@ -238,7 +259,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   if (!l1_ready) {
     for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for_scores<U>(sc, n, [&](int t, float x) { atomicAdd(&hist[bucket_id(x, lo, s2) >> 11], 1u); });
+    for_scores<U, V4>(sc, n, [&](int t, float x) { atomicAdd(&hist[bucket_id(x, lo, s2) >> 11], 1u); });
     __syncthreads();
   }
   const int b1 = find_bin(hist, kBins, k_rem, &above, sh);
@@ -251,7 +272,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   if (in_b1 > uint32_t(kCand)) {
     for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for_scores<U>(sc, n, [&](int t, float x) {
+    for_scores<U, V4>(sc, n, [&](int t, float x) {
       const int id = bucket_id(x, lo, s2);
       if ((id >> 11) == b1) atomicAdd(&hist[id & (kBins - 1)], 1u);
     });
@@ -264,7 +285,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   if (tid == 0) sh[70] = 0;
   __syncthreads();
   uint32_t* cand = hist + 256;
-  for_scores<U>(sc, n, [&](int t, float x) {
+  for_scores<U, V4>(sc, n, [&](int t, float x) {
     if (copy) copy[t] = x;
     if ((bucket_id(x, lo, s2) >> cshift) == target) {
       const uint32_t slot = atomicAdd(&sh[70], 1u);
@@ -287,7 +308,7 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
       }
     } else {
-      for_scores<U>(sc, n, [&](int t, float x) {
+      for_scores<U, V4>(sc, n, [&](int t, float x) {
         if ((bucket_id(x, lo, s2) >> cshift) != target) return;
         const uint32_t key = order_key(x);
         if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 0xffu], 1u);
@@ -309,39 +330,105 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   // each selected token to the greater tokens before it plus the selected
   // equal tokens before it.
   const float Tf = __builtin_bit_cast(float, (prefix & 0x80000000u) ? (prefix & 0x7fffffffu) : ~prefix);
-  constexpr int NW = kTopkThreads / 64;
-  const int seg = ((n + NW - 1) / NW + 63) / 64 * 64;
-  const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
-  uint32_t gt_w = 0, eq_w = 0;
-  for (int t0 = w0; t0 < w1; t0 += 64 * U) {
-    float x[U];
+  if constexpr (V4) {
+    // 4 consecutive tokens per lane per read: lane L's token j of a step
+    // follows every token of the lower lanes and its own tokens before j
+    const float4* s4 = reinterpret_cast<const float4*>(sc);
+    constexpr int NW = kTopkThreads / 64;
+    const int seg = ((n + NW - 1) / NW + 255) / 256 * 256;
+    const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
+    uint32_t gt_w = 0, eq_w = 0;
+    for (int t0 = w0; t0 < w1; t0 += 256 * U) {
+      float4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+      for (int u = 0; u < U; ++u) x[u] = s4[min(t0 + u * 256 + 4 * lane, n - 4) >> 2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool in = t0 + u * 64 + lane < w1;
-      gt_w += uint32_t(__popcll(__ballot(in && x[u] > Tf)));
-      eq_w += uint32_t(__popcll(__ballot(in && x[u] == Tf)));
+      for (int u = 0; u < U; ++u) {
+        const int tb = t0 + u * 256 + 4 * lane;
+        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool in = tb + j < w1;
+          gt_w += uint32_t(__popcll(__ballot(in && xs[j] > Tf)));
+          eq_w += uint32_t(__popcll(__ballot(in && xs[j] == Tf)));
+        }
+      }
     }
-  }
-  if (lane == 0) { sh[wave] = gt_w; sh[NW + wave] = eq_w; }
-  __syncthreads();
-  uint32_t gb = 0, eb = 0;
-  for (int w = 0; w < wave; ++w) { gb += sh[w]; eb += sh[NW + w]; }
-  for (int t0 = w0; t0 < w1; t0 += 64 * U) {
-    float x[U];
+    if (lane == 0) { sh[wave] = gt_w; sh[NW + wave] = eq_w; }
+    __syncthreads();
+    uint32_t gb = 0, eb = 0;
+    for (int w = 0; w < wave; ++w) { gb += sh[w]; eb += sh[NW + w]; }
+    for (int t0 = w0; t0 < w1; t0 += 256 * U) {
+      float4 x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+      for (int u = 0; u < U; ++u) x[u] = s4[min(t0 + u * 256 + 4 * lane, n - 4) >> 2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * 64 + lane;
-      const bool gt = t < w1 && x[u] > Tf, eq = t < w1 && x[u] == Tf;
-      const uint64_t mg = __ballot(gt), me = __ballot(eq);
-      const uint32_t g_before = gb + lanes_below(mg), e_before = eb + lanes_below(me);
-      if (gt) out[g_before + min(e_before, k_rem)] = t;
-      else if (eq && e_before < k_rem) out[g_before + e_before] = t;
-      gb += uint32_t(__popcll(mg));
-      eb += uint32_t(__popcll(me));
+      for (int u = 0; u < U; ++u) {
+        const int tb = t0 + u * 256 + 4 * lane;
+        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+        bool g[4], e[4];
+        uint64_t mg[4], me[4];
+        uint32_t g_low = 0, e_low = 0;            // selected tokens of the lower lanes
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          g[j] = tb + j < w1 && xs[j] > Tf;
+          e[j] = tb + j < w1 && xs[j] == Tf;
+          mg[j] = __ballot(g[j]);
+          me[j] = __ballot(e[j]);
+          g_low += lanes_below(mg[j]);
+          e_low += lanes_below(me[j]);
+        }
+        uint32_t g_own = 0, e_own = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t g_before = gb + g_low + g_own, e_before = eb + e_low + e_own;
+          if (g[j]) out[g_before + min(e_before, k_rem)] = tb + j;
+          else if (e[j] && e_before < k_rem) out[g_before + e_before] = tb + j;
+          g_own += g[j];
+          e_own += e[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          gb += uint32_t(__popcll(mg[j]));
+          eb += uint32_t(__popcll(me[j]));
+        }
+      }
+    }
+  } else {
+    constexpr int NW = kTopkThreads / 64;
+    const int seg = ((n + NW - 1) / NW + 63) / 64 * 64;
+    const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
+    uint32_t gt_w = 0, eq_w = 0;
+    for (int t0 = w0; t0 < w1; t0 += 64 * U) {
+      float x[U];
+  #pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+  #pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool in = t0 + u * 64 + lane < w1;
+        gt_w += uint32_t(__popcll(__ballot(in && x[u] > Tf)));
+        eq_w += uint32_t(__popcll(__ballot(in && x[u] == Tf)));
+      }
+    }
+    if (lane == 0) { sh[wave] = gt_w; sh[NW + wave] = eq_w; }
+    __syncthreads();
+    uint32_t gb = 0, eb = 0;
+    for (int w = 0; w < wave; ++w) { gb += sh[w]; eb += sh[NW + w]; }
+    for (int t0 = w0; t0 < w1; t0 += 64 * U) {
+      float x[U];
+  #pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+  #pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * 64 + lane;
+        const bool gt = t < w1 && x[u] > Tf, eq = t < w1 && x[u] == Tf;
+        const uint64_t mg = __ballot(gt), me = __ballot(eq);
+        const uint32_t g_before = gb + lanes_below(mg), e_before = eb + lanes_below(me);
+        if (gt) out[g_before + min(e_before, k_rem)] = t;
+        else if (eq && e_before < k_rem) out[g_before + e_before] = t;
+        gb += uint32_t(__popcll(mg));
+        eb += uint32_t(__popcll(me));
+      }
     }
   }
 }
@@ -394,8 +481,14 @@ __global__ void __launch_bounds__(kTopkThreads) pq_topk_kernel(const PqParams P)
     lo += fsh[j];
     hi += fsh[16 + j];
   }
-  select_top_k<16>(P.scores + head * P.n_tok, P.n_tok, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k,
-                   nullptr, hist, sh, false);
+  // 16-byte reads when every head's scores start 16-byte aligned
+  const float* sc = P.scores + head * P.n_tok;
+  if ((P.n_tok & 3) == 0)
+    select_top_k<16, true>(sc, P.n_tok, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh,
+                           false);
+  else
+    select_top_k<16, false>(sc, P.n_tok, uint32_t(P.top_k), lo, hi, P.top_idx + head * P.top_k, nullptr, hist, sh,
+                            false);
 }
 
 // Whole search of one (b, hq) with its scores resident in LDS: the head's
