@@ -3,15 +3,22 @@ against the oracle (WindowQuant Sec. 3.2).
 
 * scores within 2e-5 of the float64 oracle (the kernel sums fp32 unit
   vectors; the oracle averages the full matrix of pairwise cosines);
-* window widths equal to the oracle's wherever no batch row's score lies
-  within 1e-4 of a threshold: there the fp32 and float64 decisions may both
-  be right, and the test only checks the width is one of the three;
+* window widths in the set the oracle's rule admits: per batch row, every
+  width the decision rule gives for a score within 1e-4 of the oracle's
+  (one width unless a threshold is that close: then the two widths on
+  either side of it, and only those), and per window the vote over every
+  combination of the rows' admissible widths; so a window far from both
+  thresholds must get exactly the oracle's width, and one near T_low can
+  never get 16 (nor one near T_high 2);
+* scores placed just below T_low and just above T_high on purpose;
 * shapes with partial 64-token chunks, trailing tokens that are no window,
   one text token, zero-length rows, dims 8 .. 4096 and batches of 1 .. 5;
 * the first-window rule both ways, repeated calls bit-identical, and the
   full-size case (128 windows of 256 tokens, dim 3584) at the batch size the
   pages' VLM workloads use.
 """
+import itertools
+
 import numpy as np
 import pytest
 
@@ -62,13 +69,32 @@ def check(kvq, text, visual, S, t_low, t_high, first=True, **pad):
     assert got_s.shape == ref_s.shape
     err = np.abs(got_s - ref_s).max()
     assert err <= SCORE_TOL, f"score error {err}"
-    near = (np.abs(ref_s - t_low) < MARGIN) | (np.abs(ref_s - t_high) < MARGIN)
     for i in range(ref_b.size):
-        if near[:, i].any() and not (first and i == 0):
-            assert got_b[i] in (16, 4, 2)
-        else:
-            assert got_b[i] == ref_b[i], (i, got_b[i], ref_b[i], ref_s[:, i])
+        ok = admissible(ref_s[:, i], t_low, t_high, first and i == 0)
+        assert ref_b[i] in ok
+        assert got_b[i] in ok, (i, got_b[i], sorted(ok), ref_b[i], ref_s[:, i])
     return got_s, got_b
+
+
+def row_widths(score, t_low, t_high):
+    """Widths the decision rule (Sec. 3.2.1) gives for scores within MARGIN
+    of `score`: the rule is monotone in the score (2, then 4, then 16), so
+    these are the widths between its choices at score - MARGIN and
+    score + MARGIN."""
+    order = (2, 4, 16)
+    lo = order.index(search.choose_bits(score - MARGIN, t_low, t_high))
+    hi = order.index(search.choose_bits(score + MARGIN, t_low, t_high))
+    return order[lo:hi + 1]
+
+
+def admissible(scores, t_low, t_high, first_fp16):
+    """Widths a window may get (Sec. 3.2.3): the batch vote over every
+    combination of the rows' admissible widths; 16 only for a forced-fp16
+    first window (Sec. 3.2.2)."""
+    if first_fp16:
+        return {16}
+    per_row = [row_widths(float(s), t_low, t_high) for s in scores]
+    return {search.batch_vote(c) for c in itertools.product(*per_row)}
 
 
 @pytest.mark.parametrize("B,N,M,D,S", [
@@ -124,3 +150,21 @@ def test_full_size(kvq):
     text, vis = workloads.search_tokens(1, 64, 128 * 256, 3584, 256, seed=0)
     _, bits = check(kvq, text, vis, 256, t_low, t_high)
     assert set(bits.tolist()) <= {16, 4, 2} and bits[0] == 16
+
+
+@pytest.mark.parametrize("side", ["below_low", "above_low", "below_high", "above_high"])
+def test_scores_at_thresholds(kvq, side):
+    """Thresholds placed a third of the margin from a window's oracle score,
+    so that window's admissible set is exactly the two widths next to that
+    threshold: a kernel writing the third width fails."""
+    text, vis = workloads.search_tokens(1, 16, 9 * 64, 256, 64, seed=21)
+    ref, _ = search.search(text.astype(np.float64), vis.astype(np.float64), 64, 0.0, 1.0, False)
+    j = int(np.argsort(ref[0])[4])                     # a window in the middle of the range
+    s = float(ref[0, j])
+    d = MARGIN / 3
+    t_low, t_high = {"below_low": (s + d, s + 0.5), "above_low": (s - d, s + 0.5),
+                     "below_high": (s - 0.5, s + d), "above_high": (s - 0.5, s - d)}[side]
+    _, bits = check(kvq, text, vis, 64, t_low, t_high, first=False)
+    near_low = side.endswith("low")
+    assert admissible(ref[:, j], t_low, t_high, False) == ({2, 4} if near_low else {4, 16})
+    assert bits[j] != (16 if near_low else 2)

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 
 from oracle import search
+from tests.test_gpu_search import MARGIN, admissible
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "search_examples.json")))
 
@@ -98,3 +99,19 @@ def test_decision_rule_and_first_window():
     assert bits.tolist() == [2] * 5
     _, bits = search.search(text, vis, 4, -10.0, -5.0)            # every score above T_high
     assert bits.tolist() == [16] * 5
+
+
+def test_admissible_set_rule():
+    """The GPU window-search test's admissible sets (CPU arithmetic): one width far
+    from the thresholds, the two neighbours of a near threshold only, and the
+    vote over the rows' combinations."""
+    lo, hi = 0.3, 0.6
+    assert admissible([0.1], lo, hi, False) == {2}
+    assert admissible([0.45], lo, hi, False) == {4}
+    assert admissible([0.9], lo, hi, False) == {16}
+    assert admissible([lo - MARGIN / 2], lo, hi, False) == {2, 4}
+    assert admissible([hi + MARGIN / 2], lo, hi, False) == {4, 16}
+    assert admissible([0.1, 0.9, lo + MARGIN / 2], lo, hi, False) == {2, 16}   # 2/16/{2,4}: 2 wins 2-1, or a 3-way tie -> 16
+    assert admissible([0.1, 0.1, hi + MARGIN / 2], lo, hi, False) == {2}
+    assert admissible([0.1], lo, hi, True) == {16}
+
