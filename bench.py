@@ -82,56 +82,103 @@ def measured_traffic(workload: str):
     return int(fields["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(w: workloads.Workload, budget_s: float = 15.0, reps: int = 32, wall_s: float = 150.0):
-    """Oracle decode step (append + float64 attention) on a sample of streams.
-
-    Streams are taken in a seeded random order; each one's cache state is
-    built (untimed) and `reps` identical copies of it each run one timed
-    decode step, until about `budget_s` of timed CPU work has accumulated.
-    """
+def _cpu_worker(job):
+    """One CPU-baseline worker (its own process, single-threaded BLAS): for
+    each of its streams, the oracle's prefill (quantize + pack, timed apart)
+    and `reps` decode steps (append + float64 attention) on identical copies
+    of the state, until `budget_s` of timed work has accumulated."""
+    name, units, reps, budget_s = job
     import copy
     from threadpoolctl import threadpool_limits
     from oracle.kivi import KiviStream
+    w = workloads.get(name)
     q = workloads.queries(w)
-    L = w.context
-    g = w.gqa
-    units = workloads.sample_units(w, w.batch * w.n_kv_heads, seed=99)
-    times, n_steps, n_streams = 0.0, 0, 0
-    t_wall = time.perf_counter()
+    L, g = w.context, w.gqa
+    t_step = t_quant = 0.0
+    n_steps = n_streams = 0
+    last = None
     with threadpool_limits(limits=1):
         for i, (b, h) in enumerate(units):
             k, v = workloads.unit_kv(w, b, h)
             st = KiviStream(w.d_h, w.bits, w.group, w.residual)
-            st.prefill(k[:L], v[:L])                           # cache state, not timed
+            t0 = time.perf_counter()
+            st.prefill(k[:L], v[:L])
+            dt = time.perf_counter() - t0
+            if i > 0:                                          # the first call pays library set-up
+                t_quant += dt
             copies = [copy.deepcopy(st) for _ in range(reps)]
-            if i == 0:                                         # first call pays library set-up
+            if i == 0:
                 st.decode_append(k[L], v[L])
                 st.attend(q[b, h * g:(h + 1) * g], w.sm_scale)
             for c in copies:
                 t0 = time.perf_counter()
                 c.decode_append(k[L], v[L])
                 c.attend(q[b, h * g:(h + 1) * g], w.sm_scale)
-                times += time.perf_counter() - t0
+                t_step += time.perf_counter() - t0
                 n_steps += 1
+            last = copies[0].lengths
             n_streams += 1
-            if times > budget_s or time.perf_counter() - t_wall > wall_s:
+            if t_step + t_quant > budget_s:
                 break
-    attn_b, step_b = step_bytes(w, copies[0].lengths)
+    return {"t_step": t_step, "n_steps": n_steps, "t_quant": t_quant, "n_quant": max(n_streams - 1, 0),
+            "n_streams": n_streams, "lengths": last}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w: workloads.Workload, budget_s: float = 8.0, reps: int = 16, max_workers: int = 16):
+    """The oracle's decode step on this host's cores: one single-threaded
+    worker process per core this process may run on (at most 16, the CPU
+    share of one GPU), each taking its own streams of the workload in a
+    seeded random order until about `budget_s` of timed work.  The rate is
+    the sum of the workers' rates (they run at once).  The oracle's
+    quantizer (the prefill of a stream: keys and values quantized and
+    packed) is timed apart and reported beside it."""
+    import multiprocessing as mp
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_workers))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"                          # inherited by the workers
+    units = workloads.sample_units(w, w.batch * w.n_kv_heads, seed=99)
+    jobs = [(w.name, units[i::cores], reps, budget_s) for i in range(cores)]
+    t_wall = time.perf_counter()
+    with mp.get_context("spawn").Pool(cores) as pool:
+        res = pool.map(_cpu_worker, jobs)
+    t_wall = time.perf_counter() - t_wall
+    lengths = next(r["lengths"] for r in res if r["lengths"] is not None)
+    _, step_b = step_bytes(w, lengths)
     per_stream = step_b / (w.batch * w.n_kv_heads)
-    return {"value": round(per_stream * n_steps / times / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+    rate = sum(per_stream * r["n_steps"] / r["t_step"] for r in res if r["t_step"] > 0)
+    n_steps = sum(r["n_steps"] for r in res)
+    n_streams = sum(r["n_streams"] for r in res)
+    qb = 2 * w.context * w.d_h * 2                     # fp16 keys + values of one stream's prefill
+    q_rate = sum(qb * r["n_quant"] / r["t_quant"] for r in res if r["t_quant"] > 0)
+    return {"value": round(rate / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "us_per_step": round(w.batch * w.n_kv_heads * per_stream / rate * 1e6, 1),
+            "quantize_GBs": round(q_rate / 1e9, 4),
             "sample": f"{n_streams} of {w.batch * w.n_kv_heads} (batch, kv-head) streams of the same "
-                      f"workload, {reps} identical decode steps each (append + float64 attention), "
-                      f"{n_steps} steps in {times:.1f} s single-threaded"}
+                      f"workload over {cores} single-threaded worker processes, {reps} identical decode "
+                      f"steps each (append + float64 attention), {n_steps} steps, {t_wall:.1f} s wall; "
+                      f"quantize_GBs: the oracle's prefill quantizer (keys and values of a stream, "
+                      f"{w.context} tokens) in fp16 input bytes per second"}
 
 
 def component_times(w, cache, k_new, v_new, q, out, stream, reps: int = 50):
     """Mean microseconds of each library call of a decode step, one call at a
     time between events (launch gaps included): the fused append, the key
-    flush of R tokens (every R steps), the attention, and the whole step as
-    one kvq_kivi_step call.  The cache state is restored after each call."""
+    flush of R tokens (every R steps), the value-window compaction (R rows,
+    every R + 2 steps), the attention, and the whole step as one
+    kvq_kivi_step call.  The cache state is restored after each call."""
     import torch
-    from decode_attention_kivi_amd import KVQ_KEYS, kvq_quantize_append
+    from decode_attention_kivi_amd import KVQ_KEYS, kvq_quantize_append, kvq_residual_append
     saved = (cache.n_kq, cache.r_k, cache.n_vq, cache.r_v, cache.v_start)
 
     def restore():
@@ -148,9 +195,15 @@ def component_times(w, cache, k_new, v_new, q, out, stream, reps: int = 50):
                             cache.k_res, cache.k_res.stride(0), cache.d, None, kc, kc.stride(0),
                             km, km.stride(0), 0, stream)
 
+    def compaction():
+        # the value window's R rows move back to row 0 (every R + 2 steps)
+        kvq_residual_append(cache.n_streams, cache.d, cache.R, cache.v_res[:, cache.R + 2:], cache.v_res.stride(0),
+                            cache.d, cache.v_res, cache.v_res.stride(0), 0, stream)
+
     calls = {
         "decode_append": lambda: cache.append(k_new, v_new, stream=stream),
         "key_flush_R_tokens": flush,
+        "window_compaction_R_rows": compaction,
         "attention": lambda: cache.attend(q, w.sm_scale, out=out, stream=stream),
         "kivi_step_one_call": lambda: cache.step(k_new, v_new, q, w.sm_scale, out=out, stream=stream),
     }
@@ -168,6 +221,111 @@ def component_times(w, cache, k_new, v_new, q, out, stream, reps: int = 50):
                 total += e0.elapsed_time(e1)
         res[name] = round(total / reps * 1e3, 2)
     return res
+
+
+def host_call_us(cache, q, out, sm_scale, stream, calls: int = 200):
+    """Host microseconds per eager call (argument marshalling in the binding,
+    the library's checks and launch plan, the launch itself), for
+    kvq_decode_attn with the arguments built once and for the cache helper
+    that builds them per call (its workspace query plans a second time)."""
+    import torch
+    import decode_attention_kivi_amd as kvq
+    a = cache.decode_args(q, out, sm_scale)
+    res = {}
+    for name, fn in (("kvq_decode_attn", lambda: kvq.kvq_decode_attn(a, stream)),
+                     ("cache_attend", lambda: cache.attend(q, sm_scale, out=out, stream=stream))):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        res[name] = round((time.perf_counter() - t0) / calls * 1e6, 2)
+        torch.cuda.synchronize()
+    return res
+
+
+def device_kv(w: workloads.Workload, dev, seed: int = 0):
+    """Keys and values fp16 [B][Hkv][N][d] of a workload drawn on the device
+    with the workload's distribution (N(0, 1), the same outlier key channels
+    scaled in fp32 before the cast); only the timing uses these, so they come
+    from torch's device generator rather than the host streams."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(seed)
+    shape = (w.batch, w.n_kv_heads, w.n_tokens, w.d_h)
+    k = torch.randn(shape, generator=g, device=dev)
+    for h in range(w.n_kv_heads):
+        oc = workloads.outlier_channels(w, h)
+        if oc.size:
+            k[:, h, :, torch.from_numpy(oc).to(dev)] *= w.outlier_factor
+    k = k.half()
+    v = torch.randn(shape, generator=g, device=dev).half()
+    return k, v
+
+
+def graph_time_us(stream, calls_per_graph: int, record, reps: int = 40, warm: int = 3):
+    """Mean microseconds per call of `record()` (which enqueues
+    calls_per_graph calls) captured in one HIP graph and replayed `reps`
+    times between events on `stream`."""
+    import torch
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            record()
+        for _ in range(warm):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * calls_per_graph) * 1e3
+
+
+def config_rate(name: str, dev, stream, min_copies: int = 2):
+    """kvq_decode_attn at one of the uniform KIVI workloads' full sizes, in
+    the state after prefill and one decode step, over rotating cache copies
+    (at least two and more than twice the 256 MB Infinity Cache, so the
+    reads come from HBM; a cache smaller than that is simply repeated)."""
+    import torch
+    from decode_attention_kivi_amd.cache import KiviCache
+    w = workloads.get(name)
+    k, v = device_kv(w, dev)
+    q = torch.randn(w.batch, w.n_q_heads, w.d_h, generator=torch.Generator(device=dev).manual_seed(1),
+                    device=dev).half()
+    L = w.context
+    caches = []
+    while True:
+        c = KiviCache(w.batch, w.n_kv_heads, w.d_h, w.bits, w.group, w.residual, w.n_tokens, dev)
+        c.prefill(k[:, :, :L], v[:, :, :L])
+        c.append(k[:, :, L:L + 1], v[:, :, L:L + 1])
+        caches.append(c)
+        attn_b, _ = step_bytes(w, c.lengths)
+        if len(caches) >= min_copies and (len(caches) * attn_b > 2 * 256e6 or len(caches) >= 32):
+            break
+    del k, v
+    outs = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in caches]
+    for c, o in zip(caches, outs):
+        c.attend(q, w.sm_scale, out=o)              # workspaces outside capture
+    rounds = max(1, 16 // len(caches))
+
+    def record():
+        for _ in range(rounds):
+            for c, o in zip(caches, outs):
+                c.attend(q, w.sm_scale, out=o)
+    us = graph_time_us(stream, rounds * len(caches), record)
+    a = caches[0].decode_args(q, outs[0], w.sm_scale)
+    import decode_attention_kivi_amd as kvq
+    merge = kvq.kvq_decode_attn_workspace(a) > 0
+    n_copies = len(caches)
+    del caches, a
+    torch.cuda.synchronize()
+    return {"us_per_launch": round(us, 2), "algorithmic_bytes": int(attn_b),
+            "GBs": round(attn_b / (us * 1e-6) / 1e9, 1), "frac": round(attn_b / (us * 1e-6) / 8e12, 4),
+            "cache_copies": n_copies, "merge_kernel": merge,
+            "tokens_context_per_s": round(w.batch * w.n_tokens / (us * 1e-6), 1)}
 
 
 def window_search_rate(dev, stream, reps: int = 30, copies: int = 3):
@@ -270,37 +428,29 @@ def paged_ragged_rate(dev, stream, n_seq: int = 32, page_tokens: int = 256, copi
             "merge_kernel": ws > 0}
 
 
-def windows_decode_rate(dev, stream, reps: int = 50):
+def windows_decode_rate(dev, stream, copies: int = 32):
     """kvq_decode_attn on the mixed-precision window cache (qwen2_7b_windows:
     28 q / 4 kv heads, 128 windows x 256 tokens at 8/4/2 bits after the
-    reorder + 65 fp16 tokens).  Its 17.7 MB fit the 256 MB Infinity Cache, so
-    this is the launch-latency-bound case (the rate is not an HBM rate)."""
+    reorder + 65 fp16 tokens).  The cache is 17.7 MB, so `copies` copies
+    (566 MB, more than twice the 256 MB Infinity Cache) are read in turn and
+    every call reads HBM."""
     import torch
     from decode_attention_kivi_amd.cache import WindowCache
     w = workloads.get("qwen2_7b_windows")
     k, v = workloads.full_kv(w)
     bits = workloads.window_bits(w, k)
     q = torch.from_numpy(workloads.queries(w)).to(dev)
-    cache = WindowCache(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev),
-                        torch.from_numpy(bits).to(dev), w.window_tokens, w.group)
-    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    cache.attend(q, w.sm_scale, out=out)            # workspace outside capture
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            for _ in range(16):
-                cache.attend(q, w.sm_scale, out=out)
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            graph.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / (reps * 16) * 1e3
+    kt, vt, bt = torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), torch.from_numpy(bits).to(dev)
+    caches = [WindowCache(kt, vt, bt, w.window_tokens, w.group) for _ in range(copies)]
+    outs = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in caches]
+    for c, o in zip(caches, outs):
+        c.attend(q, w.sm_scale, out=o)              # workspace outside capture
+
+    def record():
+        for c, o in zip(caches, outs):
+            c.attend(q, w.sm_scale, out=o)
+    us = graph_time_us(stream, copies, record)
+    cache = caches[0]
     d, G, H = w.d_h, w.group, w.n_kv_heads
     nbytes = 0
     for sg in cache.segs:
@@ -310,12 +460,14 @@ def windows_decode_rate(dev, stream, reps: int = 50):
         else:
             nbytes += n * d * b // 8 + n // G * d * 4 + n * d * b // 8 + n * (d // G) * 4
     nbytes = H * (nbytes + 2 * cache.n_res * d * 2) + w.batch * w.n_q_heads * d * 6
+    n_res = cache.n_res
+    del caches, cache
     return {"config": "qwen2_7b_windows: B1, 28 q / 4 kv heads, 128 windows x 256 tokens "
                       f"({int((bits == 8).sum())} int8 / {int((bits == 4).sum())} int4 / "
-                      f"{int((bits == 2).sum())} int2, reordered) + {cache.n_res} fp16 tokens; "
-                      "cache-resident (17.7 MB), launch-latency-bound",
-            "us_per_call": round(us, 2), "algorithmic_bytes": int(nbytes),
-            "GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+                      f"{int((bits == 2).sum())} int2, reordered) + {n_res} fp16 tokens; "
+                      f"{copies} rotating cache copies",
+            "us_per_launch": round(us, 2), "algorithmic_bytes": int(nbytes),
+            "GBs": round(nbytes / (us * 1e-6) / 1e9, 1), "frac": round(nbytes / (us * 1e-6) / 8e12, 4)}
 
 
 def pq_search_rate(dev, stream, reps: int = 50, B: int = 4, n: int = 32769):
@@ -442,11 +594,13 @@ def main():
     ap.add_argument("--settle-s", type=float, default=1.0,
                     help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq", "search", "windows", "vq"),
+    ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq", "search", "windows", "vq",
+                                       "config"),
                     default="all",
                     help="profiling runs: time only the attention graph, only the step graph, the paged "
                          "ragged batch, the PQ search, the window search, the mixed-precision "
-                         "window cache or the VQ-cache decode (and skip the rest)")
+                         "window cache, the VQ-cache decode or one workload's attention (--workload; "
+                         "and skip the rest)")
     ap.add_argument("--page-tokens", type=int, default=256, help="page size of the paged ragged batch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
@@ -467,9 +621,11 @@ def main():
         for rounds in (1, 2):
             print(json.dumps({"part": "vq", **vq_decode_rate(dev, st, rounds)}), flush=True)
         return
-    if args.part in ("paged", "pq", "search", "windows"):
+    if args.part in ("paged", "pq", "search", "windows", "config"):
         dev, st = torch.device("cuda:0"), torch.cuda.Stream()
-        if args.part == "paged":
+        if args.part == "config":
+            r = {"workload": args.workload, **config_rate(args.workload, dev, st)}
+        elif args.part == "paged":
             r = paged_ragged_rate(dev, st, page_tokens=args.page_tokens)
         elif args.part == "pq":
             r = pq_search_rate(dev, st)
@@ -521,6 +677,7 @@ def main():
             break
     torch.cuda.synchronize()
     t_build = time.perf_counter() - t_build
+    n_caches = len(caches)
     saved = [(c.n_kq, c.r_k, c.n_vq, c.r_v, c.v_start) for c in caches]
     outs = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in caches]
     k_new, v_new = kt[:, :, L:L + 1], vt[:, :, L:L + 1]
@@ -566,24 +723,52 @@ def main():
     restore()
     torch.cuda.synchronize()
     n_copies = len(caches) * args.rounds       # steps per graph replay
+    # the steps a whole number of replays leaves over: one more graph of that
+    # many steps (the first copies of a pass), so exactly --steps are timed
+    tail_n = args.steps % n_copies
+    step_tail = attn_tail = None
+    if tail_n:
+        with torch.cuda.stream(stream):
+            if step_graph is not None:
+                step_tail = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(step_tail, stream=stream):
+                    restore()
+                    for c, o in list(zip(caches, outs))[:tail_n]:
+                        one_step(c, o)
+            restore()
+            for c in caches:
+                c.append(k_new, v_new)
+            torch.cuda.synchronize()
+            if attn_graph is not None:
+                attn_tail = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(attn_tail, stream=stream):
+                    for c, o in list(zip(caches, outs))[:tail_n]:
+                        c.attend(q, w.sm_scale, out=o, split_tokens=args.split_tokens)
+        restore()
+        torch.cuda.synchronize()
 
-    def timed(graph, steps, warmup):
-        """Mean ms per step over the timed replays, the step count, and the
-        (p10, p50, p90) of the per-replay means (events between replays)."""
+    def timed(graph, tail, steps, warmup):
+        """Mean ms per step over exactly `steps` timed steps (whole replays,
+        then the tail graph), the step count, and the (p10, p50, p90) of the
+        per-replay means of the whole replays (events between replays)."""
         reps_w = max(1, -(-warmup // n_copies))
-        reps = max(1, -(-steps // n_copies))
+        reps = steps // n_copies
         for _ in range(reps_w):
             graph.replay()
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 2)]
         ev[0].record(stream)
         for i in range(reps):
             graph.replay()
             ev[i + 1].record(stream)
+        if steps % n_copies:
+            tail.replay()
+        ev[reps + 1].record(stream)
         torch.cuda.synchronize()
-        per = sorted(ev[i].elapsed_time(ev[i + 1]) / n_copies for i in range(reps))
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) / n_copies for i in range(reps)) or \
+            [ev[0].elapsed_time(ev[1]) / max(steps, 1)]
         pct = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
-        return ev[0].elapsed_time(ev[reps]) / (reps * n_copies), reps * n_copies, (pct(.1), pct(.5), pct(.9))
+        return ev[0].elapsed_time(ev[reps + 1]) / steps, steps, (pct(.1), pct(.5), pct(.9))
 
     with torch.cuda.stream(stream):
         # let the clocks settle (both graphs, untimed) before either is timed
@@ -597,16 +782,24 @@ def main():
         attn_pct = step_pct = (float("nan"),) * 3
         n_steps = 0
         components = ceiling = search_rate = paged_rate = windows_rate = pq_rate = vq_rates = None
+        configs = host_us = None
         if attn_graph is not None:
-            attn_ms, n_steps, attn_pct = timed(attn_graph, args.steps, args.warmup)
+            attn_ms, n_steps, attn_pct = timed(attn_graph, attn_tail, args.steps, args.warmup)
         if step_graph is not None:
-            step_ms, n_steps, step_pct = timed(step_graph, args.steps, args.warmup)
+            step_ms, n_steps, step_pct = timed(step_graph, step_tail, args.steps, args.warmup)
         if args.part == "all":
             components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
+            host_us = host_call_us(caches[0], q, outs[0], w.sm_scale, stream)
+            restore()
             ceiling = streaming_read_ceiling(dev, stream)
             search_rate = window_search_rate(dev, stream)
             paged_rate = paged_ragged_rate(dev, stream, page_tokens=args.page_tokens)
             windows_rate = windows_decode_rate(dev, stream)
+            del caches, outs, kt, vt
+            configs = {"llama2_7b": None}
+            for name in ("tiny", "llama2_7b_b64_int2", "llama2_7b_b64_int4", "llama31_8b_gqa"):
+                configs[name] = config_rate(name, dev, stream)
+            configs["qwen2_7b_windows"] = windows_rate
             pq_rate = pq_search_rate(dev, stream)
             pq_rate["context_128k"] = pq_search_rate(dev, stream, reps=20, B=1, n=131072)
             vq_rates = {f"cq{2 * r}": vq_decode_rate(dev, stream, r) for r in (1, 2)}
@@ -620,6 +813,14 @@ def main():
         return
     achieved = attn_b / (attn_ms * 1e-3) / 1e9
     value = total_b / (step_ms * 1e-3) / 1e9
+    configs["llama2_7b"] = {"us_per_launch": round(attn_ms * 1e3, 2), "algorithmic_bytes": int(attn_b),
+                            "GBs": round(achieved, 1), "frac": round(achieved / HBM_PEAK_GBS, 4),
+                            "cache_copies": n_caches, "merge_kernel": False,
+                            "tokens_context_per_s": round(w.batch * w.n_tokens / (attn_ms * 1e-3), 1)}
+    # a step that also flushes the key residual (every R steps) or compacts
+    # the value window (every R + 2 steps) costs those calls on top
+    amortized = step_ms * 1e3 + components["key_flush_R_tokens"] / w.residual + \
+        components["window_compaction_R_rows"] / (w.residual + 2)
     result = {
         "metric": "decode-attn effective KV GB/s (% of HBM peak) + us/step, int2 Llama-2-7B shape",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
@@ -631,7 +832,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "d_h": w.d_h, "context": w.context,
                    "attended_tokens": w.n_tokens, "group": w.group, "residual": w.residual,
-                   "bits": w.bits, "cache_copies": len(caches), "steps_per_graph": n_copies,
+                   "bits": w.bits, "cache_copies": n_caches, "steps_per_graph": n_copies,
                    "cache_state_nKq_rK_nVq_rV": list(attn_probe),
                    "launches_per_step": step_launches,
                    "algorithmic_bytes_step": int(total_b), "algorithmic_bytes_attention": int(attn_b)},
@@ -644,14 +845,21 @@ def main():
                      "kernel": "decode_kernel: one kvq_decode_attn call (one workgroup per stream here, so no merge kernel)",
                      "us_per_launch": round(attn_ms * 1e3, 2),
                      "us_per_launch_p10_p50_p90": [round(x * 1e3, 2) for x in attn_pct],
-                     "streaming_read_ceiling_GBs": ceiling},
+                     "streaming_read_ceiling_GBs": ceiling,
+                     "frac_by_workload": {k: c["frac"] for k, c in configs.items()}},
+        "configs": configs,
+        "configs_note": "kvq_decode_attn per workload at full size, graph-replayed over rotating cache "
+                        "copies (HBM reads); algorithmic bytes / us per launch (split + merge kernels)",
         "us_per_step_p10_p50_p90": [round(x * 1e3, 2) for x in step_pct],
         "components_us": components,
         "components_note": "each library call timed alone between events with a synchronize after it "
                            "(launch latency included); us_per_step is the graph-replayed step",
+        "us_per_step_amortized": round(amortized, 2),
+        "us_per_step_amortized_note": "us_per_step + key flush / R + window compaction / (R + 2), the "
+                                      "last two from components_us (eager calls: an upper bound)",
+        "host_us_per_call": host_us,
         "window_search": search_rate,
         "paged_ragged": paged_rate,
-        "windows_decode": windows_rate,
         "pq_search": pq_rate,
         "vq_decode": vq_rates,
     }

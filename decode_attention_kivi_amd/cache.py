@@ -87,6 +87,7 @@ class KiviCache:
         self.n_kq = self.r_k = self.n_vq = self.r_v = self.v_start = 0
         self.last_launches = 0
         self._ws = None
+        self._need = {}
 
     # -- state ---------------------------------------------------------------
     @property
@@ -177,7 +178,12 @@ class KiviCache:
             k_res=self.k_res, n_k_res=self.r_k, k_res_stride=self.k_res.stride(0),
             v_res=self.v_res.data_ptr() + self.v_start * d * 2, n_v_res=self.r_v,
             v_res_stride=self.v_res.stride(0), out=out, split_tokens=split_tokens)
-        need = kvq_decode_attn_workspace(a)
+        # the workspace size depends on the shapes and lengths only: asked
+        # once per state instead of planning twice per call
+        key = (B, Hq, self.lengths, split_tokens)
+        need = self._need.get(key)
+        if need is None:
+            need = self._need[key] = kvq_decode_attn_workspace(a)
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
         a.workspace = self._ws.data_ptr()

@@ -58,7 +58,6 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_EINVAL;
   const int gq = a->n_q_heads / a->n_kv_heads;
   if (!valid_d(a->d_h) || !valid_group(a->group) || a->group > a->d_h) return KVQ_EUNSUPPORTED;
-  if (gq > 8) return KVQ_EUNSUPPORTED;
   if (int64_t(a->batch) * a->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
   if (!(std::isfinite(a->sm_scale))) return KVQ_EINVAL;
   if (!a->q || !a->out) return KVQ_EINVAL;
@@ -87,8 +86,9 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   for (int64_t s : {a->k_res_stride, a->v_res_stride})
     if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
 
-  int GQ = 1;
-  while (GQ < gq) GQ *= 2;
+  // head blocks of up to 8 query heads per workgroup (grid z)
+  const int GQ = kvq::head_block(gq);
+  const int64_t hblocks = (gq + GQ - 1) / GQ;
   if (kvq::decode_lds_bytes(D, GQ, 4) < 0) return KVQ_EUNSUPPORTED;
   const int64_t streams = int64_t(a->batch) * a->n_kv_heads;
   // Cost pieces: maximal token ranges with one key source and one value
@@ -155,13 +155,14 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
     double best = -1;
     for (int64_t c = n_min; c <= std::min(8 * n_min, n_min + 256); ++c) {
       if (c > n_min && (N + kvq::kWaves * c - 1) / (kvq::kWaves * c) < 64) break;
-      if (c > n_min && longest(kvq::kWaves * c) > kvq::wave_cap(GQ)) continue;
-      const double rounds = double((streams * c + fill - 1) / fill);
+      const double rounds = double((streams * hblocks * c + fill - 1) / fill);
       const double t = rounds * double(N) / double(c);
-      if (best < 0 || t < best * (1 - 1e-9)) {
-        best = t;
-        n_wg = c;
-      }
+      if (best >= 0 && t >= best * (1 - 1e-9)) continue;
+      // the wave-length check walks every wave bound: only for a candidate
+      // that would be taken
+      if (c > n_min && longest(kvq::kWaves * c) > kvq::wave_cap(GQ)) continue;
+      best = t;
+      n_wg = c;
     }
   }
   const int nw = kvq::kWaves;
@@ -250,7 +251,6 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   if (a->batch < 1 || a->n_kv_heads < 1 || a->n_q_heads < 1) return KVQ_EINVAL;
   if (a->n_q_heads % a->n_kv_heads != 0) return KVQ_EINVAL;
   const int gq = a->n_q_heads / a->n_kv_heads;
-  if (gq > 8) return KVQ_EUNSUPPORTED;
   if (int64_t(a->batch) * a->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
   PageLayout L;
   kvq_status st = page_layout(a->n_kv_heads, a->d_h, a->group, a->bits, a->page_tokens, &L);
@@ -267,8 +267,7 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   for (int64_t s : {a->k_res_stride, a->v_res_stride})
     if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
   const int D = a->d_h, G = a->group;
-  int GQ = 1;
-  while (GQ < gq) GQ *= 2;
+  const int GQ = kvq::head_block(gq);     // head blocks of up to 8 query heads (grid z)
   if (kvq::decode_lds_bytes(D, GQ, kvq::kWaves) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
   const kvq::PagedCost pc = kvq::paged_cost(D, G, a->bits);
   int wg_max = 1;
@@ -549,7 +548,7 @@ kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
                          void* stream) {
   if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0) return KVQ_EINVAL;
   const int gq = n_q_heads / n_kv_heads;
-  if (gq > 8 || int64_t(batch) * n_kv_heads > 65535 || int64_t(batch) * n_q_heads > (int64_t(1) << 31))
+  if (int64_t(batch) * n_kv_heads > 65535 || int64_t(batch) * n_q_heads > (int64_t(1) << 31))
     return KVQ_EUNSUPPORTED;
   if (!valid_d(d_h)) return KVQ_EUNSUPPORTED;
   if (m < 1 || d_h % m != 0 || (d_h / m) % 8 != 0 || 16 % m != 0) return KVQ_EUNSUPPORTED;
@@ -561,8 +560,7 @@ kvq_status kvq_pq_search(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
   for (const void* ptr : {q, centroids, codes, static_cast<const void*>(scores)})
     if (!aligned16(ptr)) return KVQ_EALIGN;
   if (reinterpret_cast<uintptr_t>(top_idx) & 3) return KVQ_EALIGN;
-  int GQ = 1;
-  while (GQ < gq) GQ *= 2;
+  const int GQ = kvq::head_block(gq);     // the scores kernel's head block (grid z)
   // one kernel when a head's scores fit in the 160 KB of LDS a gfx950
   // workgroup can hold (up to about 38K tokens), else scores then Top-k
   // through memory
@@ -795,6 +793,7 @@ kvq_status kvq_kivi_step(kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads
   int32_t first_written = n.n_kq + st.k_row;
   if (st.v_quant_row >= 0) first_written = std::min(first_written, st.v_dst_tok & ~1);
   const bool fused = !st.compact && !st.flush_keys && pl.p.wg_per_stream == 1 && pl.p.n_bounds > 0 &&
+                     pl.p.gq <= pl.GQ &&
                      pl.p.bounds[pl.p.waves_per_stream - 1] <= first_written;
   if (fused) {
     kvq::AppendParams& ap = pl.p.app;

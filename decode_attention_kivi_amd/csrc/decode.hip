@@ -165,7 +165,7 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 // instruction m is code pairs 4m .. 4m+3 of the lane's quarter row (pair P:
 // word P / NP, position P % NP, channels clo and clo + NP).
 template <int D, int GQ, int BITS>
-__device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
+__device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
                                const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int slot0,
                                int lane, int n_wave) {
   using KG = KeyGeo<D, GQ, BITS>;
@@ -309,7 +309,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
   // the first batch is in flight; padded heads are zero
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    const uint32_t q2 = h < P.gq ? uint32_t(qg[h * D + clo]) | (uint32_t(qg[h * D + chi]) << 16) : 0u;
+    const uint32_t q2 = h < nh ? uint32_t(qg[h * D + clo]) | (uint32_t(qg[h * D + chi]) << 16) : 0u;
     qk[h] = as_h2(q2) * as_h2(0x1C001C00u);                       // * 2^-8, exact
   }
   for (int i0 = 0; i0 < n_items; i0 += 2 * NB) {
@@ -324,7 +324,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
 // Keys from fp16 rows rows[0..n) -> raw logits q'.k at slots slot0 + i
 // (whole items are written, as above).
 template <int D, int GQ>
-__device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
+__device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
                           const uint16_t* rows, int n, int slot0, int lane) {
   constexpr int LT = wave_slots(GQ);
   constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -336,7 +336,7 @@ __device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_
   uint32_t qq[GQ][4];
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    const uint4 x = h < P.gq ? reinterpret_cast<const uint4*>(qg + h * D)[my_c] : make_uint4(0, 0, 0, 0);
+    const uint4 x = h < nh ? reinterpret_cast<const uint4*>(qg + h * D)[my_c] : make_uint4(0, 0, 0, 0);
     const half2_t s8 = as_h2(0x1C001C00u);                        // * 2^-8, exact
     qq[h][0] = as_u32(as_h2(x.x) * s8);
     qq[h][1] = as_u32(as_h2(x.y) * s8);
@@ -647,7 +647,11 @@ decode_kernel(const DecodeParams P) {
   }
   const int n = e - a;
 
-  const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(hkv) * P.gq) * D;   // [gq][D]
+  // query heads h0 .. h0 + nh - 1 of the kv head's gq (head block blockIdx.z
+  // of GQ heads; more than GQ heads per kv head take several blocks)
+  const int h0 = int(blockIdx.z) * GQ;
+  const int nh = min(GQ, P.gq - h0);
+  const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(hkv) * P.gq + h0) * D;   // [nh][D]
 
   if (!PAGED && P.fused_append && wave == NW - 1) {
     // this stream's decode-step append, by the wave whose range holds every
@@ -689,9 +693,9 @@ decode_kernel(const DecodeParams P) {
         const uint8_t* hb = P.pages + int64_t(P.block_table[int64_t(b) * P.max_pages + pg]) * P.page_bytes +
                             int64_t(hkv) * P.head_bytes;
         switch (P.bits) {
-          case 2: keys_quantized<D, GQ, 2>(P, W, qg, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
-          case 4: keys_quantized<D, GQ, 4>(P, W, qg, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
-          default: keys_quantized<D, GQ, 8>(P, W, qg, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          case 2: keys_quantized<D, GQ, 2>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          case 4: keys_quantized<D, GQ, 4>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          default: keys_quantized<D, GQ, 8>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
         }
         t0 = t1;
       }
@@ -704,11 +708,11 @@ decode_kernel(const DecodeParams P) {
       const uint8_t* cb = P.k_codes + stream * P.k_codes_stride + run.code_off;
       const uint8_t* mb = P.k_meta + stream * P.k_meta_stride + run.meta_off;
       switch (run.bits) {
-        case 2: keys_quantized<D, GQ, 2>(P, W, qg, cb, mb, r0, r1, t0 - a, lane, n); break;
-        case 4: keys_quantized<D, GQ, 4>(P, W, qg, cb, mb, r0, r1, t0 - a, lane, n); break;
-        case 8: keys_quantized<D, GQ, 8>(P, W, qg, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 2: keys_quantized<D, GQ, 2>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 4: keys_quantized<D, GQ, 4>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 8: keys_quantized<D, GQ, 8>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
         default:
-          keys_fp16<D, GQ>(P, W, qg,
+          keys_fp16<D, GQ>(P, W, qg, nh,
                            reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off) +
                                int64_t(r0) * D,
                            r1 - r0, t0 - a, lane);
@@ -716,7 +720,7 @@ decode_kernel(const DecodeParams P) {
     }
     if (e > n_kq) {
       const int t0 = max(a, n_kq);
-      keys_fp16<D, GQ>(P, W, qg, P.k_res + stream * P.k_res_stride + int64_t(t0 - n_kq) * D, e - t0,
+      keys_fp16<D, GQ>(P, W, qg, nh, P.k_res + stream * P.k_res_stride + int64_t(t0 - n_kq) * D, e - t0,
                        t0 - a, lane);
     }
     wave_lds_sync();
@@ -841,12 +845,11 @@ decode_kernel(const DecodeParams P) {
 
   // combine the waves; with one workgroup per stream that is the output
   // (and there is no merge kernel)
-  const int gq = P.gq;
-  const int64_t step = int64_t(gq) * (D + 2);
+  const int64_t step = int64_t(P.gq) * (D + 2);
   const bool single = P.wg_per_stream == 1;
   const float* ow0 = reinterpret_cast<const float*>(smem + lay.block + lay.logit + lay.p16);
   constexpr int WSTEP = int(lay.wave / 4);
-  for (int i = tid; i < gq * (D + 2); i += NW * 64) {
+  for (int i = tid; i < nh * (D + 2); i += NW * 64) {
     const int h = i / (D + 2), j = i % (D + 2);
     float M = -INFINITY;
 #pragma unroll
@@ -860,9 +863,9 @@ decode_kernel(const DecodeParams P) {
       l += f * ow[1];
     }
     if (single) {
-      if (j >= 2) P.out[(int64_t(b) * P.Hq + int64_t(hkv) * gq + h) * D + (j - 2)] = r / l;
+      if (j >= 2) P.out[(int64_t(b) * P.Hq + int64_t(hkv) * P.gq + h0 + h) * D + (j - 2)] = r / l;
     } else {
-      P.ws[(stream * P.wg_per_stream + wg) * step + i] = j == 0 ? M : r;
+      P.ws[(stream * P.wg_per_stream + wg) * step + int64_t(h0) * (D + 2) + i] = j == 0 ? M : r;
     }
   }
 }
@@ -890,9 +893,7 @@ __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
   if constexpr (PAGED) {
     // the workgroups this stream used (the rest of its slots are not written)
     const int n_kq = P.lens[4 * b], n_vq = P.lens[4 * b + 1];
-    int GQ = 1;                              // the decode kernel's head block (power of two)
-    while (GQ < P.gq) GQ *= 2;
-    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], GQ, kWaves);
+    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], head_block(P.gq), kWaves);
   }
   float mx = -INFINITY;
   for (int s = tid; s < nwg; s += NT) mx = fmaxf(mx, w0[s * step]);
@@ -937,8 +938,9 @@ __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
 template <int D, int GQ, int NW, bool PAGED>
 hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
   const size_t lds = size_t(lds_bytes(decode_lds<D, GQ>(), NW));
-  const dim3 grid = PAGED && p.sched_n > 0 ? dim3(unsigned(p.sched_start[p.sched_n]), 1)
-                                           : dim3(p.wg_per_stream, p.B * p.Hkv);
+  const unsigned hblocks = unsigned((p.gq + GQ - 1) / GQ);
+  const dim3 grid = PAGED && p.sched_n > 0 ? dim3(unsigned(p.sched_start[p.sched_n]), 1, hblocks)
+                                           : dim3(p.wg_per_stream, p.B * p.Hkv, hblocks);
   hipLaunchKernelGGL((decode_kernel<D, GQ, NW, PAGED>), grid, dim3(NW * 64), lds, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_stream == 1) return e;

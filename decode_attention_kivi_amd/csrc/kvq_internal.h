@@ -13,6 +13,13 @@ constexpr int kWaves = 8;              // waves per decode workgroup
 constexpr int kMaxRuns = 8;            // runs per half of the cache
 constexpr int kLdsLimit = 160 * 1024;  // LDS of one gfx950 CU: the most a workgroup can use
 constexpr int kWaveAlign = 32;         // wave token ranges start at multiples of this
+// Query heads per kv head that one decode workgroup serves (its head block);
+// a kv head with more query heads takes several head blocks (grid z).
+constexpr int kMaxHeadBlock = 8;
+// The head block of gq query heads per kv head: the next power of two, at most 8.
+__host__ __device__ constexpr int head_block(int gq) {
+  return gq <= 1 ? 1 : gq <= 2 ? 2 : gq <= 4 ? 4 : kMaxHeadBlock;
+}
 
 // Target tokens per wave; a wave may get up to wave_cap(GQ) tokens.  Larger
 // GQ needs more LDS per token (logits and probabilities of GQ heads).  With
@@ -52,7 +59,7 @@ struct KeyGeo {
   static constexpr int ROWS = 2 * GQ;           // A rows in use: hi and lo of each head
   static constexpr int QBLK = MF * 4 * ROWS * 4;  // LDS dwords of one group's A blocks [m][kblock][row][4]
   static_assert(PPL * 4 == HD && PPL % 4 == 0, "four k-blocks cover a row, four pairs per instruction");
-  static_assert(ROWS <= 16, "at most 8 query heads per kv head");
+  static_assert(ROWS <= 16, "at most 8 query heads per head block");
 };
 
 __host__ __device__ constexpr int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }

@@ -6,8 +6,8 @@
 // the Top-k tokens by score.
 //
 // Three kernels:
-//   pq_scores_kernel  grid (token chunks, B * Hkv): the tables of the GQ query
-//                     heads of one kv head in LDS (fp32 dot products of the
+//   pq_scores_kernel  grid (token chunks, B * Hkv, head blocks of up to 8
+//                     query heads): the tables of a head block of one kv head in LDS (fp32 dot products of the
 //                     fp16 centroids and q), then a token per lane (its m
 //                     code bytes in one load) and table lookups; scores fp32,
 //                     stored by consecutive lanes to consecutive tokens.
@@ -51,10 +51,13 @@ __global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P)
   float* tab = reinterpret_cast<float*>(smem);                        // [GQ][m][nc]
   float* qf = tab + GQ * m * nc;                                      // [GQ][D]
   const int tid = threadIdx.x;
-  const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(kv) * P.gq) * D;
+  // query heads h0 .. h0 + nh - 1 of the kv head (head block blockIdx.z)
+  const int h0 = int(blockIdx.z) * GQ;
+  const int nh = min(GQ, P.gq - h0);
+  const uint16_t* qg = P.q + (int64_t(b) * P.Hq + int64_t(kv) * P.gq + h0) * D;
   for (int i = tid; i < GQ * D; i += kPqThreads) {
     const int h = i / D;
-    qf[i] = h < P.gq ? h2f(qg[i]) : 0.f;
+    qf[i] = h < nh ? h2f(qg[i]) : 0.f;
   }
   __syncthreads();
   // tables: one (j, c) per thread pass, every head at once
@@ -93,7 +96,7 @@ __global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P)
   const int64_t t_end = min(int64_t(P.n_tok), t_base + P.chunk_tokens);
   const uint8_t* cb = P.codes + stream * P.codes_stride;
   const uint32_t cmask = uint32_t(nc - 1);
-  float* out0 = P.scores + (int64_t(b) * P.Hq + int64_t(kv) * P.gq) * P.n_tok;
+  float* out0 = P.scores + (int64_t(b) * P.Hq + int64_t(kv) * P.gq + h0) * P.n_tok;
   for (int64_t tb = t_base + tid; tb < t_end; tb += UT * kPqThreads) {
     uint32_t w[UT][NW];
 #pragma unroll
@@ -132,7 +135,7 @@ __global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P)
       }
 #pragma unroll
       for (int h = 0; h < GQ; ++h)
-        if (h < P.gq) out0[int64_t(h) * P.n_tok + t] = sc[h];
+        if (h < nh) out0[int64_t(h) * P.n_tok + t] = sc[h];
     }
   }
 }
@@ -648,7 +651,7 @@ hipError_t launch_pq_search(const PqParams& p, int GQ, bool fused, hipStream_t s
     return hipGetLastError();
   }
   const int64_t chunks = (int64_t(p.n_tok) + p.chunk_tokens - 1) / p.chunk_tokens;
-  const dim3 grid(unsigned(chunks), unsigned(int64_t(p.B) * p.Hkv));
+  const dim3 grid(unsigned(chunks), unsigned(int64_t(p.B) * p.Hkv), unsigned((p.gq + GQ - 1) / GQ));
   const size_t lds = size_t(pq_scores_lds_bytes(GQ, p.D, p.m, p.bits));
 #define PQ_SCORES(G_, M_) hipLaunchKernelGGL((pq_scores_kernel<G_, M_>), grid, dim3(kPqThreads), lds, s, p)
 #define PQ_SCORES_M(G_)                      \

@@ -233,7 +233,7 @@ kvq_status kvq_reorder_windows(const uint8_t* win_bits, int32_t n_windows,
  */
 typedef struct kvq_decode_args {
   int32_t batch;          /* B >= 1                                              */
-  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads, Hq/Hkv <= 8           */
+  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads (any ratio: MHA, GQA, MQA) */
   int32_t n_kv_heads;     /* Hkv >= 1                                            */
   int32_t d_h;            /* 64 or 128                                           */
   int32_t group;          /* G of the quantized runs (32, 64, 128; <= d_h)       */
@@ -352,8 +352,7 @@ kvq_status kvq_decode_attn_paged_workspace(const kvq_paged_args* args, size_t* b
  * = N_b with 1 <= N_b <= 2^22, ceil(n_kq / PT) <= max_pages; a value count
  * n_vq that is odd needs the missing pair partner's (scale, zero) finite
  * (kvq_quantize_append leaves it zero); pointers 16-byte aligned, residual
- * strides multiples of 8 elements, workspace large enough; n_q_heads /
- * n_kv_heads <= 8.  Reads the pages, the residuals and q; writes out and the
+ * strides multiples of 8 elements, workspace large enough.  Reads the pages, the residuals and q; writes out and the
  * workspace only.
  */
 kvq_status kvq_decode_attn_paged(const kvq_paged_args* args, void* stream);
@@ -382,10 +381,9 @@ kvq_status kvq_decode_attn_paged(const kvq_paged_args* args, void* stream);
  * kv head (its query heads' tables in LDS) and a Top-k kernel that reads the
  * scores back.
  * Checks (before any launch): d_h 64 or 128; m divides 16 and d_h with dm a
- * multiple of 8; 1 <= bits <= 8; 1 <= top_k <= n_tok <= 2^24; n_q_heads /
- * n_kv_heads <= 8; codes_stride >= n_tok*m and a multiple of 16 (the kernel
+ * multiple of 8; 1 <= bits <= 8; 1 <= top_k <= n_tok <= 2^24; codes_stride >= n_tok*m and a multiple of 16 (the kernel
  * reads up to the next multiple of 16 past n_tok*m); on the two-kernel path
- * the tables of a kv head's query heads fit 64 KB of LDS (KVQ_EUNSUPPORTED
+ * the tables of a kv head's query heads (up to 8 at a time) fit 64 KB of LDS (KVQ_EUNSUPPORTED
  * otherwise); q, centroids, codes, scores 16-byte aligned, top_idx 4-byte
  * aligned.  Centroids and codes are inputs (the K-means construction of
  * Step 2 runs elsewhere).
@@ -529,15 +527,16 @@ kvq_status kvq_kivi_step_workspace(const kvq_kivi_cache* cache, int32_t batch,
  *      groups and appended to the key run (kvq_quantize_append), r_k = 0;
  *   4. kvq_decode_attn of q over the updated cache (split chosen by the
  *      library) writes out.
- * When no compaction and no key flush is due, each stream fits one
- * workgroup and every token the append writes falls in the range of that
- * workgroup's last wave, steps 2 and 4 run as one launch: that wave performs
+ * When no compaction and no key flush is due, the kv heads have at most 8
+ * query heads each, each stream fits one workgroup and every token the
+ * append writes falls in the range of that workgroup's last wave, steps 2
+ * and 4 run as one launch: that wave performs
  * the stream's append first, with the same arithmetic, so the result is the
  * same as the separate calls.
  *   k_new, v_new  fp16 rows, stream s at element s * new_stride.
  *   q, out        fp16 [batch][n_q_heads][d_h] and fp32 [batch][n_q_heads][d_h];
  *                 n_streams = batch * n_kv_heads with n_kv_heads dividing
- *                 n_q_heads (Hq / Hkv <= 8).
+ *                 n_q_heads.
  * All checks (shapes, state consistency, capacity, workspace) run before
  * anything is enqueued; on success the five lengths in *cache are updated.
  * On KVQ_ELAUNCH the cache contents and lengths are undefined.

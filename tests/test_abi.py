@@ -114,7 +114,7 @@ def test_workspace_size_follows_the_split_plan():
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(n_q_heads=7), EINVAL), (dict(n_q_heads=2 * 16), EUNSUP), (dict(d_h=96), EUNSUP),
+    (dict(n_q_heads=7), EINVAL), (dict(n_q_heads=2 * 16 + 1), EINVAL), (dict(d_h=96), EUNSUP),
     (dict(n_k_res=4), EINVAL), (dict(k_segs=[(2, 0, 250, 0, 0)], n_k_res=9), EINVAL),
     (dict(k_segs=[(3, 0, 256, 0, 0)]), EINVAL), (dict(k_segs=[(2, 0, 256, 8, 0)]), EALIGN),
     (dict(v_segs=[(2, 5, 200, 0, 0)]), EINVAL), (dict(q=A + 2), EALIGN),
@@ -143,6 +143,15 @@ def test_decode_needs_workspace():
     with pytest.raises(KvqError) as e:
         kvq.kvq_decode_attn(a, 0)
     assert e.value.status == EWS
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (16, 2), (12, 1), (64, 4)])
+def test_any_head_ratio_plans(hq, hkv):
+    """More than 8 query heads per kv head run in head blocks of 8 (one more
+    grid dimension); the partial states still cover every query head."""
+    a = _decode(batch=2, n_q_heads=hq, n_kv_heads=hkv)
+    # N = 259, 64 tokens per workgroup: 5 workgroups per stream
+    assert kvq.kvq_decode_attn_workspace(a) == 2 * hkv * 5 * (hq // hkv) * 130 * 4
 
 
 def test_binding_refuses_host_tensors_as_device_buffers():
@@ -302,7 +311,7 @@ def test_paged_workspace_sizes():
     ([[64, 64, 0, 0]], dict(block_table=A + 2), EALIGN),
     ([[64, 64, 0, 0]], dict(k_res_stride=12), EALIGN),
     ([[64, 64, 0, 0]], dict(lengths_dev=None), EINVAL),
-    ([[64, 64, 0, 0]], dict(n_q_heads=36, n_kv_heads=2), EUNSUP),
+    ([[64, 64, 0, 0]], dict(n_q_heads=37, n_kv_heads=2), EINVAL),
     ([[64, 64, 0, 0]], dict(page_tokens=100), EUNSUP),
     ([[64, 32, 0, 32]], dict(v_res=None), EINVAL),  # value residual rows but no buffer
 ])
@@ -333,7 +342,7 @@ def test_split_plan_fills_the_chip_once():
     (dict(bits=0), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=101), EINVAL), (dict(n_tok=0), EINVAL),
     (dict(codes_stride=192), EINVAL), (dict(codes_stride=204), EALIGN), (dict(q=A + 2), EALIGN),
     (dict(top_idx=A + 2), EALIGN), (dict(scores=None), EINVAL), (dict(n_q_heads=7), EINVAL),
-    (dict(n_q_heads=4 * 16), EUNSUP),
+    (dict(n_q_heads=4 * 16 + 2), EINVAL),
     # too many tokens for a head's scores in LDS, and the scores kernel's 8
     # query heads x 16 sub-spaces x 256 centroids of fp32 tables: 128 KB > 64 KB
     (dict(n_q_heads=32, m=16, n_tok=100000, codes_stride=1600000), EUNSUP),

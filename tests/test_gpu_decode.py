@@ -274,3 +274,42 @@ def test_workload_windows_full(kvq):
     bits = workloads.window_bits(w, k)
     assert sorted(bits.tolist()).count(8) == 12 and sorted(bits.tolist()).count(4) == 39
     run_windows(kvq, w, bits, units=[(0, h) for h in range(w.n_kv_heads)])
+
+
+# -- more than 8 query heads per kv head (head blocks) -----------------------------
+@pytest.mark.parametrize("hq,hkv,d,bits,split", [
+    (32, 1, 128, 2, 0), (32, 1, 128, 4, 0), (32, 1, 128, 2, 128), (16, 2, 128, 2, 0),
+    (12, 1, 64, 8, 0), (71, 1, 64, 2, 0), (24, 2, 128, 4, 96),
+])
+def test_many_query_heads_per_kv_head(kvq, hq, hkv, d, bits, split):
+    # MQA (one kv head for 32 query heads; Falcon-7B's 71 heads of d64 over
+    # one kv head) and GQA above 8: head blocks of 8 query heads per
+    # workgroup, also through the partial-state merge (forced splits)
+    w = SMALL.scaled(n_q_heads=hq, n_kv_heads=hkv, d_h=d, bits=bits, group=32, residual=64,
+                     context=900, batch=2, n_outlier=3, outlier_factor=8.0)
+    run_kivi(kvq, w, units=[(b, h) for b in range(2) for h in range(hkv)], split_tokens=split)
+
+
+def test_one_call_steps_mqa(kvq):
+    # kvq_kivi_step with 32 query heads per kv head: never the fused launch
+    # (several head blocks read the residual the append writes)
+    w = SMALL.scaled(context=40, d_h=128, bits=2, group=32, residual=32, n_kv_heads=1, n_q_heads=32)
+    launches = []
+    run_kivi(kvq, w, units=[(0, 0)], steps=70, check_every_step=True, one_call=True, launches=launches)
+    assert min(launches) >= 2
+
+
+# -- value magnitudes: large scale and outlier channels ------------------------------
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_large_values_and_value_outliers(kvq, bits):
+    # values N(0, 16^2) with three channels x2 more: the value loop's fp16
+    # (offset + code) unpack, its fp16 weights p and p*s and the offset
+    # removal after fp32 accumulation stay within the tolerance at large
+    # magnitudes (a CPU emulation of the fp16 weights puts this case at about
+    # 0.7 of the tolerance; the error grows with |V|, see the value-path
+    # precision notes)
+    w = SMALL.scaled(d_h=128, bits=bits, group=32, residual=64, context=1500, n_kv_heads=2, n_q_heads=4,
+                     value_scale=16.0, n_value_outlier=3, value_outlier_factor=2.0, n_outlier=3,
+                     outlier_factor=8.0)
+    worst = run_kivi(kvq, w, units=[(0, 0), (0, 1)])
+    print(f"int{bits} large values: max |gpu - oracle| = {worst:.3e}", flush=True)

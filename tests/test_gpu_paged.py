@@ -87,6 +87,12 @@ def test_ragged_d64(kvq, hq, hkv):
     run_paged([3, 100, 333, 1200], hq, hkv, 64, 32, 32, 2, 64)
 
 
+@pytest.mark.parametrize("hq,hkv,d", [(32, 1, 128), (24, 2, 64)])
+def test_ragged_many_query_heads(kvq, hq, hkv, d):
+    # more than 8 query heads per kv head: head blocks of 8
+    run_paged([5, 300, 2000], hq, hkv, d, 32, 32, 2, 256, n_out=3, factor=8.0)
+
+
 def test_page_equals_group(kvq):
     # pages of 128 tokens with groups of 128 tokens: one key group per page
     run_paged([129, 384, 1000], 2, 2, 128, 128, 128, 4, 128)

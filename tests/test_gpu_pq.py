@@ -92,6 +92,11 @@ def check_pq(kvq, q, c, codes, B, Hq, Hkv, d, m, bits, n_tok, k, heads=None):
     # tie at the threshold (more than the candidate list holds), both paths
     (1, 2, 1, 64, 1, 1, 20000, 5000),
     (1, 2, 1, 64, 1, 1, 60000, 7000),
+    # more than 8 query heads per kv head: the fused path (one workgroup
+    # per query head) and the scores kernel's head blocks of 8
+    (1, 32, 1, 128, 2, 8, 3000, 300),
+    (1, 32, 1, 128, 2, 8, 40001, 500),
+    (2, 24, 2, 64, 4, 6, 40001, 100),
 ])
 def test_pq_search(kvq, B, Hq, Hkv, d, m, bits, n_tok, k):
     run_pq(kvq, B, Hq, Hkv, d, m, bits, n_tok, k)

@@ -25,6 +25,9 @@ Recipe (all configs):
 * the outlier channels of kv head h come from
   ``default_rng([seed, 2, h]).choice(d_h, n_out, replace=False)`` (sorted);
   those key channels are multiplied by the outlier factor in fp32;
+* values are N(0, 1) unless a case scales them (``value_scale``) or gives
+  them outlier channels of their own (``default_rng([seed, 3, h])``, same
+  draw as the keys'), again in fp32 before the cast;
 * queries of batch row b come from ``default_rng([seed, 1, b])``:
   ``standard_normal((Hq, d_h), float32)``;
 * everything is then rounded to fp16 (round-to-nearest-even).
@@ -75,6 +78,9 @@ class Workload:
     text_tokens: int = 0           # fp16 text tokens after the visual windows
     frac8: float = 0.0
     frac4: float = 0.0
+    value_scale: float = 1.0       # values drawn N(0, value_scale^2)
+    n_value_outlier: int = 0       # value channels per kv head scaled by value_outlier_factor
+    value_outlier_factor: float = 1.0
     seed: int = 0
     note: str = ""
 
@@ -157,6 +163,11 @@ def unit_kv(w: Workload, b: int, h: int, n_tokens: Optional[int] = None
     oc = outlier_channels(w, h)
     if oc.size:
         k[:, oc] *= np.float32(w.outlier_factor)
+    if w.value_scale != 1.0:
+        v *= np.float32(w.value_scale)
+    if w.n_value_outlier > 0:
+        vc = np.sort(np.random.default_rng([w.seed, 3, h]).choice(w.d_h, size=w.n_value_outlier, replace=False))
+        v[:, vc] *= np.float32(w.value_outlier_factor)
     return k.astype(np.float16), v.astype(np.float16)
 
 
