@@ -20,7 +20,8 @@ __all__ = [
     "KVQ_KEYS", "KVQ_VALUES", "KvqError", "Segment", "DecodeArgs", "library_path",
     "kvq_abi_version", "kvq_strerror", "kvq_quantize_append", "kvq_residual_append",
     "kvq_decode_append",
-    "kvq_reorder_windows", "kvq_decode_attn_workspace", "kvq_decode_attn",
+    "kvq_reorder_windows", "kvq_decode_attn_workspace", "kvq_decode_attn", "kvq_decode_attn_noalloc",
+    "KVQ_SCRATCH_BYTES",
     "KiviCacheDesc", "kvq_kivi_step_workspace", "kvq_kivi_step",
     "kvq_window_thresholds", "kvq_window_search_workspace", "kvq_window_search",
     "PagedArgs", "kvq_page_layout", "kvq_decode_attn_paged_workspace", "kvq_decode_attn_paged",
@@ -29,6 +30,7 @@ __all__ = [
 
 KVQ_KEYS = 0
 KVQ_VALUES = 1
+KVQ_SCRATCH_BYTES = 8 << 20     # the library's static scratch (kvq_decode_attn_noalloc)
 ABI_VERSION = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -137,6 +139,8 @@ def _load():
     lib.kvq_decode_attn_workspace.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ctypes.c_size_t)]
     lib.kvq_decode_attn.restype = i32
     lib.kvq_decode_attn.argtypes = [ctypes.POINTER(DecodeArgs), vp]
+    lib.kvq_decode_attn_noalloc.restype = i32
+    lib.kvq_decode_attn_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), vp]
     lib.kvq_kivi_step_workspace.restype = i32
     lib.kvq_kivi_step_workspace.argtypes = [ctypes.POINTER(KiviCacheDesc), i32, i32,
                                             ctypes.POINTER(ctypes.c_size_t)]
@@ -276,6 +280,12 @@ def kvq_decode_attn_workspace(args: DecodeArgs) -> int:
 
 def kvq_decode_attn(args: DecodeArgs, stream=None):
     _check(_load().kvq_decode_attn(ctypes.byref(args), _stream(stream)), "kvq_decode_attn")
+
+
+def kvq_decode_attn_noalloc(args: DecodeArgs, stream=None):
+    """kvq_decode_attn with the partial states in the library's static scratch
+    (``args.workspace`` is ignored); for callers that cannot allocate."""
+    _check(_load().kvq_decode_attn_noalloc(ctypes.byref(args), _stream(stream)), "kvq_decode_attn_noalloc")
 
 
 def kvq_kivi_step_workspace(cache: KiviCacheDesc, batch: int, n_q_heads: int) -> int:

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/kvq.h"
@@ -359,6 +360,7 @@ const char* kvq_strerror(int32_t status) {
     case KVQ_EUNSUPPORTED: return "unsupported shape";
     case KVQ_EWORKSPACE: return "workspace missing or too small";
     case KVQ_ELAUNCH: return "kernel launch failed";
+    case KVQ_ESCRATCH: return "partial states exceed the library's static scratch (KVQ_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -507,6 +509,58 @@ kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream) {
   if (st != KVQ_OK) return st;
   if (pl.ws_bytes > 0 && (!args->workspace || args->workspace_bytes < pl.ws_bytes))
     return KVQ_EWORKSPACE;
+  return from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode attention for callers that cannot allocate: the partial softmax
+// states go to a file-scope device array instead of a caller workspace.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(8) << 20;   // KVQ_SCRATCH_BYTES
+static_assert(kScratchBytes == KVQ_SCRATCH_BYTES, "header and library agree on the scratch size");
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU the library runs on, held until the process ends.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's `scratch` (the host-side name of the
+// array is not a device address), looked up once per device with that
+// device current.
+kvq_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KVQ_ELAUNCH;
+  if (dev >= kMaxDevices) return KVQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KVQ_ELAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attn_noalloc(const kvq_decode_args* args, void* stream) {
+  Plan pl;
+  const kvq_status st = make_plan(args, &pl);
+  if (st != KVQ_OK) return st;
+  if (pl.ws_bytes > kScratchBytes) return KVQ_ESCRATCH;
+  if (pl.ws_bytes > 0) {
+    void* ws = nullptr;
+    const kvq_status sa = scratch_address(&ws);
+    if (sa != KVQ_OK) return sa;
+    pl.p.ws = static_cast<float*>(ws);
+  }
   return from_hip(kvq::launch_decode(pl.p, pl.GQ, static_cast<hipStream_t>(stream)));
 }
 

@@ -80,7 +80,8 @@ typedef enum kvq_status {
   KVQ_EALIGN = 2,       /* pointer, offset or stride not aligned as required */
   KVQ_EUNSUPPORTED = 3, /* well-formed, but not a shape this library runs */
   KVQ_EWORKSPACE = 4,   /* workspace missing or smaller than required */
-  KVQ_ELAUNCH = 5       /* the HIP runtime refused a kernel launch */
+  KVQ_ELAUNCH = 5,      /* the HIP runtime refused a kernel launch */
+  KVQ_ESCRATCH = 6      /* kvq_decode_attn_noalloc: more than KVQ_SCRATCH_BYTES needed */
 } kvq_status;
 
 /* Which half of the cache a quantize call writes. */
@@ -277,6 +278,24 @@ kvq_status kvq_decode_attn_workspace(const kvq_decode_args* args, size_t* bytes)
  * Reads the cache, q and the residuals; writes out and the workspace only.
  */
 kvq_status kvq_decode_attn(const kvq_decode_args* args, void* stream);
+
+/*
+ * kvq_decode_attn_noalloc -- kvq_decode_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the same checks, kernels and result, but the
+ * partial softmax states go to the library's own device array of
+ * KVQ_SCRATCH_BYTES (one per GPU, held until the process ends) instead of
+ * args->workspace, which is ignored (workspace_bytes too).  Returns
+ * KVQ_ESCRATCH, touching nothing, when kvq_decode_attn_workspace would
+ * report more than KVQ_SCRATCH_BYTES.  Calls no allocating routine; the
+ * first call on a device looks up that device's array address (with the
+ * device current) and keeps it.  Every call on one GPU shares that array:
+ * calls that overlap on one GPU (other HIP streams, other threads) race and
+ * must be ordered by the caller; the array needs no initialization (each
+ * call writes every partial state it reads).
+ */
+#define KVQ_SCRATCH_BYTES (8u << 20)
+kvq_status kvq_decode_attn_noalloc(const kvq_decode_args* args, void* stream);
 
 /*
  * Paged, ragged cache (the serving layout).  The KIVI note's outlook pairs

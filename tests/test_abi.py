@@ -14,7 +14,7 @@ ensure_built()
 import decode_attention_kivi_amd as kvq  # noqa: E402
 from decode_attention_kivi_amd import KVQ_KEYS, KVQ_VALUES, KvqError  # noqa: E402
 
-EINVAL, EALIGN, EUNSUP, EWS = 1, 2, 3, 4
+EINVAL, EALIGN, EUNSUP, EWS, ESCRATCH = 1, 2, 3, 4, 6
 A = 1 << 20        # a fake, 16-byte aligned device address (never dereferenced)
 
 
@@ -152,6 +152,22 @@ def test_any_head_ratio_plans(hq, hkv):
     a = _decode(batch=2, n_q_heads=hq, n_kv_heads=hkv)
     # N = 259, 64 tokens per workgroup: 5 workgroups per stream
     assert kvq.kvq_decode_attn_workspace(a) == 2 * hkv * 5 * (hq // hkv) * 130 * 4
+
+
+def test_noalloc_checks_before_any_launch():
+    """kvq_decode_attn_noalloc applies kvq_decode_attn's checks and refuses a
+    plan whose partial states exceed the static scratch (KVQ_ESCRATCH),
+    all on the host: nothing here is launched."""
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_decode_attn_noalloc(_decode(n_q_heads=7), 0)
+    assert e.value.status == EINVAL
+    big = _decode(batch=64, n_q_heads=64, n_kv_heads=8, k_segs=[(2, 0, 8192, 0, 0)],
+                  v_segs=[(2, 0, 8136, 0, 0)], split_tokens=64)
+    assert kvq.kvq_decode_attn_workspace(big) > kvq.KVQ_SCRATCH_BYTES
+    with pytest.raises(KvqError) as e:
+        kvq.kvq_decode_attn_noalloc(big, 0)
+    assert e.value.status == ESCRATCH
+    assert "scratch" in kvq.kvq_strerror(ESCRATCH)
 
 
 def test_binding_refuses_host_tensors_as_device_buffers():
