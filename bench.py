@@ -616,6 +616,16 @@ def main():
     if not os.path.exists(lib):
         import __graft_entry__
         __graft_entry__.build()
+    if args.copy_probe_mib:
+        # a plain copy of known size through the library's row-copy kernel:
+        # its FETCH_SIZE / WRITE_SIZE per byte calibrate the traffic counters
+        import decode_attention_kivi_amd as kvq
+        rows = args.copy_probe_mib * (1 << 20) // 256
+        src = torch.ones(rows, 128, dtype=torch.float16, device="cuda:0")
+        dst = torch.empty_like(src)
+        kvq.kvq_residual_append(1, 128, rows, src, 0, 128, dst, 0, 0)
+        torch.cuda.synchronize()
+        del src, dst
     if args.part == "vq":
         dev, st = torch.device("cuda:0"), torch.cuda.Stream()
         for rounds in (1, 2):
@@ -640,16 +650,6 @@ def main():
     w = workloads.get(args.workload)
     assert not w.mixed, "bench runs the uniform KIVI workloads"
     dev = torch.device("cuda:0")
-    if args.copy_probe_mib:
-        # a plain copy of known size through the library's row-copy kernel:
-        # its FETCH_SIZE / WRITE_SIZE per byte calibrate the traffic counters
-        import decode_attention_kivi_amd as kvq
-        rows = args.copy_probe_mib * (1 << 20) // 256
-        src = torch.ones(rows, 128, dtype=torch.float16, device=dev)
-        dst = torch.empty_like(src)
-        kvq.kvq_residual_append(1, 128, rows, src, 0, 128, dst, 0, 0)
-        torch.cuda.synchronize()
-        del src, dst
     L = w.context
     k, v = workloads.full_kv(w)
     q = torch.from_numpy(workloads.queries(w)).to(dev)
