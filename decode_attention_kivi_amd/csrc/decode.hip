@@ -165,14 +165,14 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 // instruction m is code pairs 4m .. 4m+3 of the lane's quarter row (pair P:
 // word P / NP, position P % NP, channels clo and clo + NP).
 template <int D, int GQ, int BITS>
-__device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
+__device__ __forceinline__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
                                const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int slot0,
                                int lane, int n_wave) {
   using KG = KeyGeo<D, GQ, BITS>;
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = KG::RB, LB = KG::LB, TPI = KG::TPI, WPL = KG::WPL, MF = KG::MF;
   constexpr int NP = KG::NP, CPW = KG::CPW, PPL = KG::PPL, HD = KG::HD;
-  constexpr int NB = KG::NB, NGB = KG::NGB, ROWS = KG::ROWS, QBLK = KG::QBLK;
+  constexpr int NB = KG::NB, NGB = KG::NGB, ROWS = KG::ROWS, BS = KG::BS, QBLK = KG::QBLK;
   constexpr int GPI = 64 / HD;                         // key groups per meta iteration
   constexpr int MI = (NGB + GPI - 1) / GPI;
   const int lg = P.lg_g;
@@ -187,7 +187,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
   const uint32_t lane_off = uint32_t(col * RB + kb * LB);
   // LDS dword of the lane's A row in block (m = 0, kb) of a group.  Rows past
   // 2*GQ repeat row col % (2*GQ): they only feed D rows that are never read.
-  const int a_pos = (kb * ROWS + (col & (ROWS - 1))) * 4;
+  const int a_pos = kb * BS + (col & (ROWS - 1)) * 4;
 
   // meta role of the lane: pair pi of a row of group gsub (of the meta
   // iteration): k-block pj, pair pp of it
@@ -195,7 +195,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
   const int pj = pi / PPL, pp = pi % PPL;
   const int kq = pp % NP;
   const int clo = pj * (D / 4) + (pp / NP) * CPW + kq, chi = clo + NP;
-  const int qpos = ((pp / 4) * 4 + pj) * ROWS * 4 + pp % 4;   // its hi dword in block [pp/4][pj]
+  const int qpos = ((pp / 4) * 4 + pj) * BS + pp % 4;   // its hi dword in block [pp/4][pj]
   const uint32_t meta_off = uint32_t((gsub * D + clo) * 4);
   const Unpacker<BITS, false> unpack;                 // constants in registers, once
   const _Float16 off = static_cast<_Float16>(Unpacker<BITS, false>::offset(kq));
@@ -282,7 +282,7 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
         const uint32_t* qs = W.qs + js * QBLK + a_pos;
 #pragma unroll
         for (int m = 0; m < MF; ++m)
-          am[m] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(qs + m * 4 * ROWS * 4));
+          am[m] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4*>(qs + m * 4 * BS));
         b0 = W.bias[js * GQ + (2 * kb < GQ ? 2 * kb : 0)];
         if (GQ > 1) b1 = W.bias[js * GQ + (2 * kb + 1 < GQ ? 2 * kb + 1 : 0)];
       }
@@ -303,8 +303,9 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
     wave_lds_sync();                         // the next batch rewrites the A blocks
   };
 
-  Batch A, Bb;
+  Batch A, Bb, Cc;
   issue(A, 0);
+  if constexpr (GQ > 1) issue(Bb, NB);
   // q of the lane's meta pair for the GQ heads (global, cached), loaded while
   // the first batch is in flight; padded heads are zero
 #pragma unroll
@@ -312,19 +313,33 @@ __device__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const ui
     const uint32_t q2 = h < nh ? uint32_t(qg[h * D + clo]) | (uint32_t(qg[h * D + chi]) << 16) : 0u;
     qk[h] = as_h2(q2) * as_h2(0x1C001C00u);                       // * 2^-8, exact
   }
-  for (int i0 = 0; i0 < n_items; i0 += 2 * NB) {
-    progress_prio(0, slot0 + i0 * TPI, n_wave);
-    issue(Bb, i0 + NB);
-    consume(A, i0);
-    issue(A, i0 + 2 * NB);
-    if (i0 + NB < n_items) consume(Bb, i0 + NB);
+  if constexpr (GQ > 1) {
+    // grouped heads run two waves per SIMD with registers to spare: three
+    // batches in flight
+    for (int i0 = 0; i0 < n_items; i0 += 3 * NB) {
+      progress_prio(0, slot0 + i0 * TPI, n_wave);
+      issue(Cc, i0 + 2 * NB);
+      consume(A, i0);
+      issue(A, i0 + 3 * NB);
+      if (i0 + NB < n_items) consume(Bb, i0 + NB);
+      issue(Bb, i0 + 4 * NB);
+      if (i0 + 2 * NB < n_items) consume(Cc, i0 + 2 * NB);
+    }
+  } else {
+    for (int i0 = 0; i0 < n_items; i0 += 2 * NB) {
+      progress_prio(0, slot0 + i0 * TPI, n_wave);
+      issue(Bb, i0 + NB);
+      consume(A, i0);
+      issue(A, i0 + 2 * NB);
+      if (i0 + NB < n_items) consume(Bb, i0 + NB);
+    }
   }
 }
 
 // Keys from fp16 rows rows[0..n) -> raw logits q'.k at slots slot0 + i
 // (whole items are written, as above).
 template <int D, int GQ>
-__device__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
+__device__ __forceinline__ void keys_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
                           const uint16_t* rows, int n, int slot0, int lane) {
   constexpr int LT = wave_slots(GQ);
   constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -400,7 +415,7 @@ __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], in
 // zero codes and zero meta, so they add 0.  Unless softmax_done, `softmax`
 // runs after the first loads are issued (it writes W.p16).
 template <int D, int GQ, int BITS, class Softmax>
-__device__ void values_quantized(const DecodeParams& P, const WaveLds& W,
+__device__ __forceinline__ void values_quantized(const DecodeParams& P, const WaveLds& W,
                                  const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int ps0, int lane,
                                  Softmax& softmax, bool softmax_done, int ph, int n_wave) {
   constexpr int LT = wave_slots(GQ);
@@ -532,11 +547,213 @@ __device__ void values_quantized(const DecodeParams& P, const WaveLds& W,
   }
 }
 
+// The same values on matrix cores, for d_h = 128 and grouped query heads:
+// the A.V products of every head come from v_mfma_f32_16x16x32_f16, so the
+// code unpacking is the only per-element work and is shared by the heads.
+//
+// A step is 16 pair blocks (32 tokens).  Lane l is column n = l % 16 and
+// k-block kb = l / 16 of the operands: it reads bytes [n LW, (n+1) LW) of
+// pair blocks 4 kb .. 4 kb + 3 (LW = 2 RB / 16, one 4, 8 or 16-byte load
+// each: channels 8n .. 8n+7 of both tokens), so every k-block row of 16
+// lanes holds the same eight tokens.  B of instruction j is channel 8n + j
+// of those tokens, unpacked as (offset + code) pairs; A row m is (head
+// m >> lg(NG), channel group m & (NG - 1)) with NG = 128 / G groups per
+// token, and holds p * s of that head and group for the eight tokens (fp16,
+// as in the pair loop above), so D row (h, g) at column n is
+//   sum_t p_h(t) s_g(t) (offset_j + code_t,8n+j),
+// which is wanted where 8n + j lies in group g.  Up to 16 / NG heads share an
+// A block; more heads take a second block against the same B.  sum p * s and
+// sum p * z of each row are kept beside, summed over the four k-blocks at
+// the end and folded in: o = D - offset_j sum(p s) + sum(p z).
+template <int D, int GQ, int BITS, class Softmax>
+__device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W,
+                                      const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int ps0, int lane,
+                                      Softmax& softmax, bool softmax_done, int ph, int n_wave) {
+  static_assert(D == 128, "eight channels per lane and column");
+  constexpr int LT = wave_slots(GQ);
+  constexpr int RB = D * BITS / 8;
+  constexpr int LW = 2 * RB / 16;         // bytes per lane and pair block
+  constexpr int WPL = LW / 4;
+  using UP = Unpacker<BITS, true>;
+  constexpr int NP = UP::NP;              // channels per word
+  static_assert(WPL * NP == 8, "eight channels per lane");
+  constexpr int NAB = (GQ + 3) / 4;       // A blocks for 32-channel groups
+  constexpr int NBV = BITS == 2 ? 2 : 1;  // steps per load batch (three batches in flight)
+  const UP unpack;
+  const int lg_ng = 7 - lg_g;
+  const int NG = 1 << lg_ng;
+  const int hpb = 16 >> lg_ng;            // heads per A block
+  const int nab = (GQ + hpb - 1) / hpb;   // (uniform) A blocks in use
+  const int col = lane & 15, kb = lane >> 4;
+  const int ga = col & (NG - 1);          // the group of the lane's A row
+  const int p0 = r0 >> 1;
+  const int np = ((r1 - 1) >> 1) - p0 + 1;
+  const int n_steps = (np + 15) >> 4;
+  const Rsrc crs = make_rsrc(cbase + int64_t(p0) * 2 * RB, uint32_t(np) * 2 * RB);
+  const Rsrc mrs = make_rsrc(mbase + int64_t(p0) * NG * 8, uint32_t(np) * NG * 8);
+  const uint32_t c_off = uint32_t(4 * kb * 2 * RB + col * LW);
+  const uint32_t m_off = uint32_t((4 * kb * NG + ga) * 8);
+  const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16) + ps0;
+  const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  int prow[NAB];                          // p16 dword row of the lane's A-row head (padded rows repeat a head)
+#pragma unroll
+  for (int ab = 0; ab < NAB; ++ab) prow[ab] = min(ab * hpb + (col >> lg_ng), GQ - 1) * (LT / 2);
+
+  float4_t acc[NAB][8];
+  float srow[NAB], zrow[NAB];
+#pragma unroll
+  for (int ab = 0; ab < NAB; ++ab) {
+    srow[ab] = 0.f;
+    zrow[ab] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[ab][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // steps past the end read zeros and touch no memory
+  struct Batch {
+    typename LoadType<WPL>::T c[NBV][4];
+    uint2 m[NBV][4];
+  };
+  auto issue = [&](Batch& B, int s0) {
+#pragma unroll
+    for (int v = 0; v < NBV; ++v)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pr = 16 * (s0 + v) + u;
+        B.c[v][u] = bload<WPL>(crs, c_off + uint32_t(pr * 2 * RB));
+        B.m[v][u] = bload<2>(mrs, m_off + uint32_t(pr * NG * 8));
+      }
+  };
+  auto consume = [&](const Batch& B, int s0) {
+#pragma unroll
+    for (int v = 0; v < NBV; ++v) {
+      if (s0 + v >= n_steps) continue;    // uniform
+      const int pb = 16 * (s0 + v) + 4 * kb;
+      uint32_t s2[4], z2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        s2[u] = __builtin_amdgcn_perm(B.m[v][u].y, B.m[v][u].x, 0x05040100u);
+        z2[u] = __builtin_amdgcn_perm(B.m[v][u].y, B.m[v][u].x, 0x07060302u);
+      }
+      half8_t am[NAB];
+#pragma unroll
+      for (int ab = 0; ab < NAB; ++ab) {
+        if (ab >= nab) continue;          // uniform
+        uint32_t aw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // pair np (zero, or a probability whose meta here reads as zero)
+          // stands in for every pair past the range
+          const half2_t p2 = as_h2(pp[prow[ab] + min(pb + u, np)]);
+          const half2_t psh = p2 * as_h2(s2[u]);
+          aw[u] = as_u32(psh);
+          srow[ab] = __builtin_amdgcn_fdot2(psh, one2, srow[ab], false);
+          zrow[ab] = __builtin_amdgcn_fdot2(p2, as_h2(z2[u]), zrow[ab], false);
+        }
+        am[ab] = __builtin_bit_cast(half8_t, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+      }
+      uint32_t vv[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < WPL; ++w) unpack.run(word<WPL>(B.c[v][u], w), &vv[u][w * NP]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const half8_t bm = __builtin_bit_cast(half8_t, make_uint4(vv[0][j], vv[1][j], vv[2][j], vv[3][j]));
+#pragma unroll
+        for (int ab = 0; ab < NAB; ++ab)
+          if (ab < nab) acc[ab][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[ab], bm, acc[ab][j], 0, 0, 0);
+      }
+    }
+  };
+
+  Batch A, Bb, Cc;
+  issue(A, 0);
+  issue(Bb, NBV);
+  uint16_t keep[GQ];
+  // the probabilities are made while the first loads are in flight
+  if (!softmax_done) softmax();
+  if (ph >= 0) {
+    // (uniform) clear the partner slot after an odd run end for this run
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      keep[h] = W.p16[h * LT + ph];
+      wave_lds_sync();
+      if (lane == 0) W.p16[h * LT + ph] = 0;
+    }
+    wave_lds_sync();
+  }
+  for (int s0 = 0; s0 < n_steps; s0 += 3 * NBV) {
+    progress_prio(1, 2 * (ps0 + 16 * s0), n_wave);
+    issue(Cc, s0 + 2 * NBV);
+    consume(A, s0);
+    issue(A, s0 + 3 * NBV);
+    if (s0 + NBV < n_steps) consume(Bb, s0 + NBV);
+    issue(Bb, s0 + 4 * NBV);
+    if (s0 + 2 * NBV < n_steps) consume(Cc, s0 + 2 * NBV);
+  }
+
+  // row sums over the four k-blocks, then to LDS (W.logit is free by now)
+  float* red = W.logit;                   // [NAB][sum p*s of 16 rows | sum p*z of 16 rows]
+#pragma unroll
+  for (int ab = 0; ab < NAB; ++ab) {
+    float x = srow[ab], y = zrow[ab];
+    auto a1 = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
+    auto b1 = __builtin_amdgcn_permlane16_swap(fbits(y), fbits(y), false, false);
+    x = bitsf(a1[0]) + bitsf(a1[1]);
+    y = bitsf(b1[0]) + bitsf(b1[1]);
+    auto a2 = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
+    auto b2 = __builtin_amdgcn_permlane32_swap(fbits(y), fbits(y), false, false);
+    x = bitsf(a2[0]) + bitsf(a2[1]);
+    y = bitsf(b2[0]) + bitsf(b2[1]);
+    if (lane < 16) {
+      red[ab * 32 + col] = x;
+      red[ab * 32 + 16 + col] = y;
+    }
+  }
+  wave_lds_sync();
+  // lane (n, kb) holds D rows 4 kb .. 4 kb + 3 at column n for channels
+  // 8n .. 8n+7, all in group gc
+  const int gc = (8 * col) >> lg_g;
+#pragma unroll
+  for (int ab = 0; ab < NAB; ++ab) {
+    if (ab >= nab) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * kb + r;
+      const int h = ab * hpb + (row >> lg_ng);
+      if ((row & (NG - 1)) != gc || h >= GQ) continue;
+      const float sr = red[ab * 32 + row], zr = red[ab * 32 + 16 + row];
+      float* o = W.ow + h * (D + 2) + 2 + 8 * col;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] += acc[ab][j][r] - UP::offset(j % NP) * sr + zr;
+    }
+  }
+  wave_lds_sync();
+  if (ph >= 0) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h)
+      if (lane == 0) W.p16[h * LT + ph] = keep[h];
+    wave_lds_sync();
+  }
+}
+
+// Quantized values: matrix cores for grouped heads at d_h = 128, the pair
+// loop otherwise.
+template <int D, int GQ, int BITS, class Softmax>
+__device__ __forceinline__ void values_q(const DecodeParams& P, const WaveLds& W, const uint8_t* cbase,
+                                         const uint8_t* mbase, int r0, int r1, int ps0, int lane, Softmax& softmax,
+                                         bool softmax_done, int ph, int n_wave) {
+  if constexpr (D == 128 && GQ >= 2)
+    values_quantized_mfma<D, GQ, BITS>(P.lg_g, W, cbase, mbase, r0, r1, ps0, lane, softmax, softmax_done, ph, n_wave);
+  else
+    values_quantized<D, GQ, BITS>(P, W, cbase, mbase, r0, r1, ps0, lane, softmax, softmax_done, ph, n_wave);
+}
+
 // Values from fp16 rows rows[0..n), probabilities at slots slot0 + i
 // (slots past the range are zero or belong to other pieces; rows past the
 // range read as zero).
 template <int D, int GQ>
-__device__ void values_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* rows,
+__device__ __forceinline__ void values_fp16(const DecodeParams& P, const WaveLds& W, const uint16_t* rows,
                             int n, int slot0, int lane) {
   constexpr int LT = wave_slots(GQ);
   constexpr int CPR = D / 8;
@@ -796,9 +1013,9 @@ decode_kernel(const DecodeParams P) {
         const uint8_t* cb = hb + P.pg_vcodes_off;
         const uint8_t* mb = hb + P.pg_vmeta_off;
         switch (P.bits) {
-          case 2: values_quantized<D, GQ, 2>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
-          case 4: values_quantized<D, GQ, 4>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
-          default: values_quantized<D, GQ, 8>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+          case 2: values_q<D, GQ, 2>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+          case 4: values_q<D, GQ, 4>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+          default: values_q<D, GQ, 8>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
         }
         t0 = t1;
       }
@@ -814,9 +1031,9 @@ decode_kernel(const DecodeParams P) {
       const uint8_t* cb = P.v_codes + stream * P.v_codes_stride + run.code_off;
       const uint8_t* mb = P.v_meta + stream * P.v_meta_stride + run.meta_off;
       switch (run.bits) {
-        case 2: values_quantized<D, GQ, 2>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
-        case 4: values_quantized<D, GQ, 4>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
-        case 8: values_quantized<D, GQ, 8>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 2: values_q<D, GQ, 2>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 4: values_q<D, GQ, 4>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
+        case 8: values_q<D, GQ, 8>(P, W, cb, mb, r0, r1, (t0 - a) >> 1, lane, softmax, softmax_done, ph, n); break;
         default:
           if (!softmax_done) softmax();
           values_fp16<D, GQ>(P, W,

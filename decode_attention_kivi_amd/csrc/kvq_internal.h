@@ -57,7 +57,11 @@ struct KeyGeo {
   static constexpr int NB = WPL >= 8 ? 2 : 4;   // items per load batch (two batches in flight)
   static constexpr int NGB = NB * TPI / 32;     // key groups per batch (G >= 32)
   static constexpr int ROWS = 2 * GQ;           // A rows in use: hi and lo of each head
-  static constexpr int QBLK = MF * 4 * ROWS * 4;  // LDS dwords of one group's A blocks [m][kblock][row][4]
+  // LDS dwords per (m, kblock) A block: ROWS rows of 4 dwords plus 4 of
+  // padding, so that the 64 lanes' A-row stores of a group (each lane one
+  // dword of one block) fall in distinct banks
+  static constexpr int BS = ROWS * 4 + 4;
+  static constexpr int QBLK = MF * 4 * BS;      // LDS dwords of one group's A blocks [m][kblock][row][4]
   static_assert(PPL * 4 == HD && PPL % 4 == 0, "four k-blocks cover a row, four pairs per instruction");
   static_assert(ROWS <= 16, "at most 8 query heads per head block");
 };
