@@ -34,7 +34,9 @@ KVQ_SCRATCH_BYTES = 8 << 20     # the library's static scratch (kvq_decode_attn_
 ABI_VERSION = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIBRARY names another library file in this directory (a comparison
+# build of build.VARIANTS); by default libkvq.so
+_LIB_PATH = os.path.join(_HERE, os.path.basename(os.environ.get("KVQ_LIBRARY") or "libkvq.so"))
 _lib = None
 
 

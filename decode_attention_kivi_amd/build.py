@@ -30,6 +30,13 @@ COMMON = [
 PER_FILE = {
     "quantize.hip": ["-ffp-contract=off"],
 }
+# Comparison builds (made only on request, never by build()): extra flags per
+# source and the library name.  "keys-dot2" runs the decode kernel's
+# quantized-key loop on v_dot2 instead of matrix cores for one query head per
+# kv head; the binding loads it when KVQ_LIBRARY names it.
+VARIANTS = {
+    "keys-dot2": ({"decode.hip": ["-DKVQ_KEY_LOOP_DOT2"]}, "libkvq_keys_dot2.so"),
+}
 SOURCES = ["api.hip", "quantize.hip", "reorder.hip", "decode.hip", "search.hip", "pq.hip", "vq.hip"]
 
 
@@ -40,15 +47,17 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every kernel source for gfx950 and link libkvq.so; returns its path."""
+def build(verbose: bool = False, jobs: int = 4, variant: str | None = None) -> str:
+    """Compile every kernel source for gfx950 and link libkvq.so (or a
+    comparison library of VARIANTS); returns its path."""
     cc = hipcc()
+    extra, lib = ({}, LIB) if variant is None else (VARIANTS[variant][0], os.path.join(HERE, VARIANTS[variant][1]))
     with tempfile.TemporaryDirectory(prefix="kvq_build_") as tmp:
         procs = []
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
-            cmd = [cc, *COMMON, *PER_FILE.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *COMMON, *PER_FILE.get(src, []), *extra.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -66,16 +75,17 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
                 print("\n".join(lines))
         if failed:
             raise RuntimeError("hipcc failed:\n" + "\n\n".join(f"[{s}]\n{t}" for s, t in failed))
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = lib + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    v = sys.argv[sys.argv.index("--variant") + 1] if "--variant" in sys.argv else None
+    print(build(verbose="-v" in sys.argv, variant=v))

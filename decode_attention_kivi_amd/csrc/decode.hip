@@ -336,6 +336,172 @@ __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const Wave
   }
 }
 
+// The key loop on v_dot2 instead of matrix cores, for one query head per kv
+// head.  It is compiled only into the comparison library that the build
+// makes on request (KVQ_KEY_LOOP_DOT2 defined), to measure the matrix-core
+// loop against: the same code loads, meta loads and unpacking; per key group
+// hi = fp16(q'*s) and lo = fp16(q'*s - hi) of every channel pair go to LDS
+// in lane-chunk order, and per item each lane applies them to its unpacked
+// pairs with two v_dot2 per pair, its accumulator seeded with the chunk's
+// share of the bias sum_c q'_c z_c - sum_c (hi + lo)_c offset_c; a DPP sum
+// over the lanes of a token row gives the logit.
+#ifdef KVQ_KEY_LOOP_DOT2
+constexpr bool kKeyLoopDot2 = true;
+#else
+constexpr bool kKeyLoopDot2 = false;
+#endif
+
+template <int D, int BITS>
+struct KeyGeoDot2 {
+  static constexpr int RB = D * BITS / 8;       // bytes per token row
+  static constexpr int NP = 16 / BITS;          // fp16 code pairs per 32-bit word
+  static constexpr int CPW = 32 / BITS;         // channels per 32-bit word
+  static constexpr int LB0 = 4 * 16 / NP;
+  static constexpr int LB = LB0 > 16 ? (RB < 16 ? RB : 16) : (LB0 > RB ? RB : LB0);
+  static constexpr int LPR = RB / LB;           // lanes per token row
+  static constexpr int TPI = 64 / LPR;          // tokens per wave instruction (item)
+  static constexpr int WPL = LB / 4;            // code words per lane
+  static constexpr int PPL = WPL * NP;          // code pairs per lane
+  static constexpr int HD = D / 2;              // code pairs per row
+  static constexpr int NB = 4;                  // items per load batch
+  static constexpr int NGB = NB * TPI / 32 > 1 ? NB * TPI / 32 : 1;  // key groups per batch
+  static constexpr int QSTR = PPL + 4;          // LDS dwords per lane chunk (padded)
+  static constexpr int QGRP = 2 * LPR * QSTR;   // LDS dwords per group: hi chunks, then lo chunks
+  static_assert(LPR * PPL == HD, "lanes of a row cover its pairs");
+  static_assert(TPI <= 32 && (NB * TPI) % 32 == 0, "items never straddle a key group");
+  static_assert(NGB * (QGRP + LPR) <= kQsMax<D, 1>() + kBiasMax<D, 1>(), "fits the A-block area");
+};
+
+template <int D, int BITS>
+__device__ __forceinline__ void keys_quantized_dot2(const DecodeParams& P, const WaveLds& W, const uint16_t* qg,
+                                                    int nh, const uint8_t* cbase, const uint8_t* mbase, int r0,
+                                                    int r1, int slot0, int lane, int n_wave) {
+  using KG = KeyGeoDot2<D, BITS>;
+  constexpr int LT = wave_slots(1);
+  constexpr int RB = KG::RB, LB = KG::LB, LPR = KG::LPR, TPI = KG::TPI, WPL = KG::WPL;
+  constexpr int NP = KG::NP, CPW = KG::CPW, PPL = KG::PPL, HD = KG::HD;
+  constexpr int NB = KG::NB, NGB = KG::NGB, QSTR = KG::QSTR, QGRP = KG::QGRP;
+  constexpr int GPI = 64 / HD;                         // key groups per meta iteration
+  constexpr int MI = (NGB + GPI - 1) / GPI;
+  const int lg = P.lg_g;
+  const int n = r1 - r0;
+  const int n_items = (n + TPI - 1) / TPI;
+  const int jp = r0 >> lg;
+  const int n_groups = ((r1 - 1) >> lg) - jp + 1;
+  const Rsrc crs = make_rsrc(cbase + int64_t(r0) * RB, uint32_t(n) * RB);
+  const Rsrc mrs = make_rsrc(mbase + int64_t(jp) * D * 4, uint32_t(n_groups) * D * 4);
+  const int tt = lane / LPR, tq = lane % LPR;          // token of the item, chunk of its row
+  const uint32_t lane_off = uint32_t(tt * RB + tq * LB);
+  uint32_t* qsb = W.qs;                                // [NGB][QGRP] q*s chunks
+  float* bsb = reinterpret_cast<float*>(W.qs + NGB * QGRP);   // [NGB][LPR] chunk biases
+
+  // meta role: pair pi of a row (channels clo and clo + NP) of group gsub
+  const int pi = lane % HD, gsub = lane / HD;
+  const int kq = pi % NP;
+  const int clo = (pi / NP) * CPW + kq, chi = clo + NP;
+  const int qpos = (pi / PPL) * QSTR + pi % PPL;       // LDS dword of the pair's hi in its chunk
+  const uint32_t meta_off = uint32_t((gsub * D + clo) * 4);
+  const Unpacker<BITS, false> unpack;
+  const _Float16 off = static_cast<_Float16>(Unpacker<BITS, false>::offset(kq));
+  const half2_t nego = {-off, -off};
+  const uint32_t q2 = nh > 0 ? uint32_t(qg[clo]) | (uint32_t(qg[chi]) << 16) : 0u;
+  const half2_t qk = as_h2(q2) * as_h2(0x1C001C00u);   // * 2^-8, exact
+
+  struct Batch {
+    typename LoadType<WPL>::T buf[NB];
+    uint32_t mlo[MI], mhi[MI];
+  };
+  auto issue = [&](Batch& B, int i0) {
+    const uint32_t cb = lane_off + uint32_t(i0 * TPI * RB);
+#pragma unroll
+    for (int u = 0; u < NB; ++u) B.buf[u] = bload<WPL>(crs, cb + u * TPI * RB);
+    const uint32_t mb = meta_off + uint32_t((((r0 + i0 * TPI) >> lg) - jp) * D * 4);
+#pragma unroll
+    for (int it = 0; it < MI; ++it) {
+      B.mlo[it] = bload<1>(mrs, mb + it * GPI * D * 4);
+      B.mhi[it] = bload<1>(mrs, mb + it * GPI * D * 4 + NP * 4);
+    }
+  };
+  auto consume = [&](const Batch& B, int i0) {
+    const int jb0 = ((r0 + i0 * TPI) >> lg) - jp;
+    const int ng = min(((r0 + min((i0 + NB) * TPI, n) - 1) >> lg) - jp - jb0 + 1, NGB);
+#pragma unroll
+    for (int it = 0; it < MI; ++it) {
+      if (it * GPI >= ng) continue;                    // uniform
+      const int js = it * GPI + gsub;
+      const half2_t s2 = as_h2(__builtin_amdgcn_perm(B.mhi[it], B.mlo[it], 0x05040100u));
+      const half2_t z2 = as_h2(__builtin_amdgcn_perm(B.mhi[it], B.mlo[it], 0x07060302u));
+      const half2_t hi = qk * s2;
+      const half2_t lo = __builtin_elementwise_fma(qk, s2, -hi);
+      float bp = __builtin_amdgcn_fdot2(qk, z2, 0.f, false);
+      bp = __builtin_amdgcn_fdot2(hi, nego, bp, false);
+      bp = __builtin_amdgcn_fdot2(lo, nego, bp, false);
+      bp = group_sum<PPL>(bp);
+      if (js < ng) {
+        qsb[js * QGRP + qpos] = as_u32(hi);
+        qsb[js * QGRP + LPR * QSTR + qpos] = as_u32(lo);
+        if (pi % PPL == 0) bsb[js * LPR + pi / PPL] = bp;
+      }
+    }
+    wave_lds_sync();
+    uint32_t qhi[PPL], qlo[PPL];
+    float bias = 0.f;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      if (i >= n_items) continue;                      // uniform
+      const int rt = r0 + i * TPI;
+      if (u == 0 || (rt & (P.G - 1)) == 0) {
+        const int js = min((rt >> lg) - jp - jb0, NGB - 1);
+        const uint32_t* qs = qsb + js * QGRP + tq * QSTR;
+#pragma unroll
+        for (int p = 0; p < PPL; p += 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(qs + p);
+          const uint4 y = *reinterpret_cast<const uint4*>(qs + LPR * QSTR + p);
+          qhi[p] = x.x; qhi[p + 1] = x.y; qhi[p + 2] = x.z; qhi[p + 3] = x.w;
+          qlo[p] = y.x; qlo[p + 1] = y.y; qlo[p + 2] = y.z; qlo[p + 3] = y.w;
+        }
+        bias = bsb[js * LPR + tq];
+      }
+      float acc = bias;
+#pragma unroll
+      for (int w = 0; w < WPL; ++w) {
+        uint32_t v[NP];
+        unpack.run(word<WPL>(B.buf[u], w), v);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+          acc = dot2(qhi[w * NP + k], v[k], acc);
+          acc = dot2(qlo[w * NP + k], v[k], acc);
+        }
+      }
+      W.logit[slot0 + i * TPI + tt] = group_sum<LPR>(acc);
+    }
+    wave_lds_sync();
+  };
+
+  Batch A, Bb;
+  issue(A, 0);
+  for (int i0 = 0; i0 < n_items; i0 += 2 * NB) {
+    progress_prio(0, slot0 + i0 * TPI, n_wave);
+    issue(Bb, i0 + NB);
+    consume(A, i0);
+    issue(A, i0 + 2 * NB);
+    if (i0 + NB < n_items) consume(Bb, i0 + NB);
+  }
+}
+
+// Quantized keys: matrix cores (the comparison library: v_dot2 for one head
+// at d_h = 128).
+template <int D, int GQ, int BITS>
+__device__ __forceinline__ void keys_q(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
+                                       const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int slot0,
+                                       int lane, int n_wave) {
+  if constexpr (kKeyLoopDot2 && GQ == 1 && D == 128)
+    keys_quantized_dot2<D, BITS>(P, W, qg, nh, cbase, mbase, r0, r1, slot0, lane, n_wave);
+  else
+    keys_quantized<D, GQ, BITS>(P, W, qg, nh, cbase, mbase, r0, r1, slot0, lane, n_wave);
+}
+
 // Keys from fp16 rows rows[0..n) -> raw logits q'.k at slots slot0 + i
 // (whole items are written, as above).
 template <int D, int GQ>
@@ -910,9 +1076,9 @@ decode_kernel(const DecodeParams P) {
         const uint8_t* hb = P.pages + int64_t(P.block_table[int64_t(b) * P.max_pages + pg]) * P.page_bytes +
                             int64_t(hkv) * P.head_bytes;
         switch (P.bits) {
-          case 2: keys_quantized<D, GQ, 2>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
-          case 4: keys_quantized<D, GQ, 4>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
-          default: keys_quantized<D, GQ, 8>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          case 2: keys_q<D, GQ, 2>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          case 4: keys_q<D, GQ, 4>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
+          default: keys_q<D, GQ, 8>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, t0 - p0, t1 - p0, t0 - a, lane, n); break;
         }
         t0 = t1;
       }
@@ -925,9 +1091,9 @@ decode_kernel(const DecodeParams P) {
       const uint8_t* cb = P.k_codes + stream * P.k_codes_stride + run.code_off;
       const uint8_t* mb = P.k_meta + stream * P.k_meta_stride + run.meta_off;
       switch (run.bits) {
-        case 2: keys_quantized<D, GQ, 2>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
-        case 4: keys_quantized<D, GQ, 4>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
-        case 8: keys_quantized<D, GQ, 8>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 2: keys_q<D, GQ, 2>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 4: keys_q<D, GQ, 4>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
+        case 8: keys_q<D, GQ, 8>(P, W, qg, nh, cb, mb, r0, r1, t0 - a, lane, n); break;
         default:
           keys_fp16<D, GQ>(P, W, qg, nh,
                            reinterpret_cast<const uint16_t*>(P.k_codes + stream * P.k_codes_stride + run.code_off) +
