@@ -34,7 +34,6 @@
 namespace kvq {
 namespace {
 
-constexpr int NT = kThreads;
 // Loads per batch in the value streaming loops (two batches in flight): grouped
 // heads run at two waves per SIMD whatever their register count, so they
 // keep twice the loads in flight.
@@ -1253,19 +1252,20 @@ decode_kernel(const DecodeParams P) {
   }
 }
 
-// Cross-split merge, one thread per output element:
+// Cross-split merge, one workgroup per (b, hq):
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the stream's
-// workgroup partials, folded in one pass with a running maximum.
+// workgroup partials, M the largest m_s.  The MT threads split the partials
+// (MT / D threads per channel); each folds its share with a running maximum,
+// CH partials at a time with every load of the chunk issued before any is
+// used (one memory round trip per chunk, not a max pass and then a sum
+// pass), and the shares of a channel meet in LDS.
+constexpr int MT = 1024;                     // merge threads: 64 partials in one round trip at d_h 128
 template <int D, bool PAGED>
-__global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
-  // one workgroup per (b, hq): M = the largest partial max; partial s then
-  // weighs f_s = 2^(m_s - M); L = sum_s l_s f_s and o[c] = sum_s o_s[c] f_s,
-  // the partials split over the threads (NT / D threads per channel, every
-  // load independent) in chunks of NT partials whose weights sit in LDS
-  constexpr int R = NT / D;                  // threads per output channel
-  __shared__ float f[NT];
-  __shared__ float red[NT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__global__ void __launch_bounds__(MT) merge_kernel(const DecodeParams P) {
+  constexpr int R = MT / D;                  // threads per output channel
+  constexpr int CH = 8;                      // partials per chunk and thread
+  __shared__ float share[3][MT];
+  const int tid = threadIdx.x;
   const int64_t bhq = blockIdx.x;
   const int b = int(bhq / P.Hq), hq = int(bhq % P.Hq);
   const int hkv = hq / P.gq, h = hq % P.gq;
@@ -1278,43 +1278,50 @@ __global__ void __launch_bounds__(NT) merge_kernel(const DecodeParams P) {
     const int n_kq = P.lens[4 * b], n_vq = P.lens[4 * b + 1];
     nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], head_block(P.gq), kWaves);
   }
-  float mx = -INFINITY;
-  for (int s = tid; s < nwg; s += NT) mx = fmaxf(mx, w0[s * step]);
-  mx = wave_max64(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  float M = red[0];
-  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
   const int c = tid % D, r = tid / D;
-  float O = 0.f, Lp = 0.f;
-  for (int s0 = 0; s0 < nwg; s0 += NT) {
-    __syncthreads();                         // red and f are free again
-    float fs = 0.f;
-    if (s0 + tid < nwg) {
-      const float* w = w0 + (s0 + tid) * step;
-      const float m = w[0];
-      fs = m == M ? 1.f : exp2f(m - M);      // also -inf == -inf
-      Lp = __builtin_fmaf(w[1], fs, Lp);
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int s0 = r * CH; s0 < nwg; s0 += R * CH) {
+    float m[CH], l[CH], o[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float* w = w0 + min(s0 + k, nwg - 1) * step;   // past the end: a repeat, skipped below
+      m[k] = w[0];
+      l[k] = w[1];
+      o[k] = w[2 + c];
     }
-    f[tid] = fs;
-    __syncthreads();
-    const int n = min(NT, nwg - s0);
-#pragma unroll 8
-    for (int j = r; j < n; j += R) O = __builtin_fmaf(w0[(s0 + j) * step + 2 + c], f[j], O);
+    float cm = M;
+#pragma unroll
+    for (int k = 0; k < CH; ++k)
+      if (s0 + k < nwg) cm = fmaxf(cm, m[k]);
+    const float fr = M == cm ? 1.f : exp2f(M - cm);        // also -inf == -inf
+    L *= fr;
+    O *= fr;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      if (s0 + k >= nwg) continue;
+      const float f = m[k] == cm ? 1.f : exp2f(m[k] - cm);
+      L = __builtin_fmaf(l[k], f, L);
+      O = __builtin_fmaf(o[k], f, O);
+    }
+    M = cm;
   }
-  Lp = wave_sum64(Lp);
-  __syncthreads();
-  if (lane == 0) red[wave] = Lp;
-  __syncthreads();
-  float L = 0.f;
-  for (int w = 0; w < NT / 64; ++w) L += red[w];
-  __syncthreads();
-  red[tid] = O;
+  share[0][tid] = M;
+  share[1][tid] = L;
+  share[2][tid] = O;
   __syncthreads();
   if (r == 0) {
-    float o = red[c];
-    for (int k = 1; k < R; ++k) o += red[k * D + c];
-    P.out[bhq * D + c] = o / L;
+    float Mt = M;
+#pragma unroll
+    for (int k = 1; k < R; ++k) Mt = fmaxf(Mt, share[0][k * D + c]);
+    float Lt = 0.f, Ot = 0.f;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const float mk = share[0][k * D + c];
+      const float f = mk == Mt ? 1.f : exp2f(mk - Mt);
+      Lt = __builtin_fmaf(share[1][k * D + c], f, Lt);
+      Ot = __builtin_fmaf(share[2][k * D + c], f, Ot);
+    }
+    P.out[bhq * D + c] = Ot / Lt;
   }
 }
 
@@ -1327,7 +1334,7 @@ hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<D, GQ, NW, PAGED>), grid, dim3(NW * 64), lds, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_stream == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<D, PAGED>), dim3(unsigned(int64_t(p.B) * p.Hq)), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((merge_kernel<D, PAGED>), dim3(unsigned(int64_t(p.B) * p.Hq)), dim3(MT), 0, s, p);
   return hipGetLastError();
 }
 

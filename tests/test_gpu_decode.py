@@ -176,6 +176,38 @@ def test_forced_split_sizes(kvq, split):
     run_kivi(kvq, w, units=[(0, 0), (0, 1)], split_tokens=split)
 
 
+def test_workspace_reused_across_splits(kvq):
+    """One cache (one workspace) serves calls whose split changes (64, 128,
+    automatic, 96, 64 tokens per workgroup, each merged across its
+    workgroups) and then calls with another query-head count: every result
+    matches the oracle."""
+    import torch
+    from decode_attention_kivi_amd.cache import KiviCache
+    dev = torch.device("cuda")
+    w = SMALL.scaled(context=700, n_kv_heads=2, n_q_heads=4)
+    k, v = _kv(w)
+    L = w.context
+    cache = KiviCache(w.batch, w.n_kv_heads, w.d_h, w.bits, w.group, w.residual, L + 1, dev)
+    cache.prefill(torch.from_numpy(k[:, :, :L]).to(dev), torch.from_numpy(v[:, :, :L]).to(dev))
+    streams = {}
+    for h in range(w.n_kv_heads):
+        st = KiviStream(w.d_h, w.bits, w.group, w.residual)
+        st.prefill(k[0, h, :L], v[0, h, :L])
+        streams[h] = st
+    for hq, splits in [(4, [64, 128, 0, 96, 64]), (8, [64, 96])]:
+        wq = w.scaled(n_q_heads=hq)
+        q = workloads.queries(wq)
+        g = hq // w.n_kv_heads
+        for split in splits:
+            print(f"workspace reuse: Hq{hq} split={split}", flush=True)
+            out = cache.attend(torch.from_numpy(q).to(dev), w.sm_scale, split_tokens=split)
+            torch.cuda.synchronize()
+            o = out.cpu().numpy()
+            for h, st in streams.items():
+                assert_close(o[0, h * g:(h + 1) * g], st.attend(q[0, h * g:(h + 1) * g], w.sm_scale),
+                             f"Hq{hq} split {split} h{h}")
+
+
 @pytest.mark.parametrize("hq,hkv", [(2, 1), (4, 1), (8, 2), (7, 1), (6, 2), (16, 2)])
 @pytest.mark.parametrize("d,G", [(64, 32), (128, 64)])
 def test_gqa_and_head_dims(kvq, hq, hkv, d, G):
