@@ -5,6 +5,7 @@
 // Bit-exact contract (include/kvq.h): every step is one IEEE fp32 operation
 // on fp16-exact inputs -- subtract, correctly rounded divide, round half to
 // even -- with no FMA contraction, in every file that includes this one.
+// The divide is only needed where it can change the code: see encode().
 #pragma once
 
 #include "kvq_internal.h"
@@ -17,6 +18,7 @@ namespace kvq {
 struct GroupScale {
   uint32_t s16, z16;
   float s, z;
+  float inv;              // v_rcp_f32(s), within 1 ulp of 1/s; 0 when s == 0 (all codes 0)
 };
 
 template <int BITS>
@@ -30,9 +32,12 @@ __device__ __forceinline__ GroupScale group_scale(float mn, float mx) {
   g.z16 = f2h(mn);
   g.s = h2f(g.s16);
   g.z = h2f(g.z16);
+  g.inv = g.s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(g.s);
   return g;
 }
 
+// code = clamp(rint(fl(d / s))), d = fl(x - z), with fl(d / s) the correctly
+// rounded quotient (the definition).
 template <int BITS>
 __device__ __forceinline__ uint32_t encode(float x, const GroupScale& g) {
 #pragma clang fp contract(off)
@@ -42,6 +47,30 @@ __device__ __forceinline__ uint32_t encode(float x, const GroupScale& g) {
   t = fminf(fmaxf(t, 0.0f), kQmax);
   return static_cast<uint32_t>(t);
 }
+
+// The same code without the division where it cannot matter: q = fl(d * inv)
+// lies within |d/s| * 2^-22 of the correctly rounded quotient (inv within
+// 2^-23 relative of 1/s, two roundings of 2^-24), so rint gives the same
+// integer for both unless a half-integer lies that close to q.  Inside a
+// group |d/s| <= 1.5 (2^b - 1) (d <= max - min; s is (max - min)/(2^b - 1)
+// rounded to fp16, low by at most a factor 1.5 in the subnormal range), so
+// `near` is set when q is within 2^b 2^-20 -- over 2.6 times the largest
+// bound -- of a half-integer; the caller then encodes again with encode(),
+// for the whole wave (one uniform branch per batch of elements).  q - rint(q)
+// is exact.  s == 0 has inv = 0: q = 0, code 0, never near.
+template <int BITS>
+__device__ __forceinline__ uint32_t encode_fast(float x, const GroupScale& g, bool& near) {
+#pragma clang fp contract(off)
+  constexpr float kQmax = float((1 << BITS) - 1);
+  constexpr float kFar = 0.5f - float(1 << BITS) * 0x1p-20f;   // exact
+  const float q = (x - g.z) * g.inv;
+  const float t = rintf(q);
+  near |= fabsf(q - t) >= kFar;
+  return static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), kQmax));
+}
+
+// true on every lane when any lane of the wave sets x
+__device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
 
 // One decode step's append for stream s, by one wave (KIVI note, Algorithm 1,
 // Decoding): lanes 0..D/8-1 copy the new key row into key-residual row
@@ -92,8 +121,14 @@ __device__ __forceinline__ void append_stream(const AppendParams& p, int64_t s, 
   mx = span_max<LPG>(mx);
   const GroupScale gs = group_scale<BITS>(mn, mx);
   uint32_t unit = 0;
+  bool near = false;
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) unit |= encode<BITS>(xv[k], gs) << (((lane * CPL + k) % KPU) * BITS);
+  for (int k = 0; k < CPL; ++k) unit |= encode_fast<BITS>(xv[k], gs, near) << (((lane * CPL + k) % KPU) * BITS);
+  if (wave_any(near)) {
+    unit = 0;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) unit |= encode<BITS>(xv[k], gs) << (((lane * CPL + k) % KPU) * BITS);
+  }
   unit = group_or<LPU>(unit);
   const int64_t te = p.v_dst_tok;
   const int64_t pair = te >> 1;

@@ -10,7 +10,9 @@
 // Bit-exact contract (include/kvq.h): every step is one IEEE fp32 operation
 // on fp16-exact inputs -- subtract, correctly rounded divide, round half to
 // even -- so this file is built without FMA contraction and with correctly
-// rounded fp32 division.
+// rounded fp32 division.  The wave kernels and the decode-step append take
+// the codes from a reciprocal product and divide only where that could
+// change a code (encode_fast, kvq_quant.h).
 
 #include "kvq_internal.h"
 #include "kvq_device.h"
@@ -153,12 +155,23 @@ __global__ void __launch_bounds__(256) quantize_keys_wave_kernel(QuantParams p) 
     float f[8];
     halves(x[k], f);
     uint32_t lo = 0, hi = 0;
+    bool near = false;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const uint32_t q = encode<BITS>(f[c], gs[c]);
+      const uint32_t q = encode_fast<BITS>(f[c], gs[c], near);
       const int bit = c * BITS;
       if (bit < 32) lo |= q << bit;
       else hi |= q << (bit - 32);
+    }
+    if (wave_any(near)) {                // (uniform, rare) a quotient near a rounding boundary
+      lo = hi = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t q = encode<BITS>(f[c], gs[c]);
+        const int bit = c * BITS;
+        if (bit < 32) lo |= q << bit;
+        else hi |= q << (bit - 32);
+      }
     }
     uint8_t* dst = out + int64_t(p.dst_tok + j * G + k * RPI + r0) * RB;
     if constexpr (BITS == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(lo);
@@ -239,11 +252,22 @@ __global__ void __launch_bounds__(256) quantize_values_pairs_kernel(QuantParams 
     uint32_t w[WPL];
 #pragma unroll
     for (int k = 0; k < WPL; ++k) w[k] = 0;
+    bool near = false;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int k = c / KPU, sh = (c % KPU) * BITS;
-      w[k] |= encode<BITS>(fa[c], ga) << sh;
-      if (vb) w[k] |= encode<BITS>(fb[c], gb) << (16 + sh);
+      w[k] |= encode_fast<BITS>(fa[c], ga, near) << sh;
+      if (vb) w[k] |= encode_fast<BITS>(fb[c], gb, near) << (16 + sh);
+    }
+    if (wave_any(near)) {                // (uniform, rare) a quotient near a rounding boundary
+#pragma unroll
+      for (int k = 0; k < WPL; ++k) w[k] = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int k = c / KPU, sh = (c % KPU) * BITS;
+        w[k] |= encode<BITS>(fa[c], ga) << sh;
+        if (vb) w[k] |= encode<BITS>(fb[c], gb) << (16 + sh);
+      }
     }
     if (P > p_hi) continue;
     uint8_t* blk = codes + P * 2 * RB + c8 * WPL * 4;

@@ -17,7 +17,23 @@ def kvq():
     return m
 
 
+def _ties(n_streams, n, d):
+    """Every key group (G tokens of a channel) and value group (G channels of
+    a token) holds 0 and 3, so 2-bit groups get s = 1 and the codes of the
+    other entries land on, or one fp16 ulp beside, the rounding boundaries
+    k + 1/2 (where the kernels' reciprocal shortcut defers to the division)."""
+    h = np.float16
+    up = lambda v: np.nextafter(h(v), h(9))
+    dn = lambda v: np.nextafter(h(v), h(-9))
+    pat = np.array([0, 3, 0.5, 1.5, 2.5, up(0.5), dn(1.5), up(2.5), 1, 2, 0.25, 2.75,
+                    up(1.5), dn(0.5), dn(2.5), dn(3)], np.float16)
+    t, c = np.meshgrid(np.arange(n), np.arange(d), indexing="ij")
+    return np.broadcast_to(pat[(t + c) % pat.size], (n_streams, n, d)).copy()
+
+
 def _data(rng, n_streams, n, d, kind="normal"):
+    if kind == "ties":
+        return _ties(n_streams, n, d)
     x = rng.standard_normal((n_streams, n, d)).astype(np.float32)
     x[:, :, rng.choice(d, 3, replace=False)] *= 9.0
     if kind == "special":
@@ -91,6 +107,12 @@ def test_values_bit_exact_odd_offsets(kvq, bits, d, G):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_gather_and_special_values(kvq, which, bits):
     _run(kvq, which, bits, 32, 128, n_tok=96, dst_tok=0, gather=True, kind="special")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_codes_on_rounding_boundaries(kvq, which, bits):
+    _run(kvq, which, bits, 32, 128, n_tok=96, dst_tok=0, gather=False, kind="ties")
 
 
 def test_fp16_run_is_a_copy(kvq):
