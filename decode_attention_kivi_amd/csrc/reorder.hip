@@ -5,7 +5,11 @@
 //
 // One workgroup of 1024 threads.  Windows are taken 1024 at a time; a block
 // scan over a 64-bit word holding four 16-bit per-width counters gives every
-// window its rank among the earlier windows of its width in one pass.
+// window its rank among the earlier windows of its width in one pass.  The
+// row gather list (W * S entries) is written by a second, grid-wide kernel
+// from the permutation.
+
+#include <algorithm>
 
 #include "kvq_internal.h"
 #include "../../include/kvq.h"
@@ -21,7 +25,7 @@ __device__ __forceinline__ int width_class(uint32_t bits) {
 
 __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(
     const uint8_t* win_bits, int32_t W, int32_t S, int32_t G, int32_t D,
-    int32_t* perm, kvq_segment* segs, int32_t* n_segs, int32_t* row_gather) {
+    int32_t* perm, kvq_segment* segs, int32_t* n_segs) {
   __shared__ uint64_t scan[kReorderThreads];
   __shared__ int count[4];
   __shared__ int bad;
@@ -60,9 +64,6 @@ __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(
       const int rank = int((excl >> (16 * c)) & 0xffff) + int((before >> (16 * c)) & 0xffff);
       const int pos = start[c] + rank;
       perm[pos] = i;
-      if (row_gather) {
-        for (int k = 0; k < S; ++k) row_gather[int64_t(pos) * S + k] = i * S + k;
-      }
     }
     // per-width totals of this chunk; a window count fits 16 bits per chunk
     uint64_t total = scan[kReorderThreads - 1];
@@ -99,14 +100,28 @@ __global__ void __launch_bounds__(kReorderThreads) reorder_kernel(
   }
 }
 
+// row_gather[p * S + k] = perm[p] * S + k: entry j of the reordered cache
+// reads source row j of window perm[j / S]; nothing when the widths were
+// rejected (n_segs < 0, the permutation incomplete).
+__global__ void __launch_bounds__(256) row_gather_kernel(const int32_t* perm, const int32_t* n_segs, int32_t S,
+                                                         int64_t total, int32_t* row_gather) {
+  if (*n_segs < 0) return;
+  for (int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x; j < total; j += int64_t(gridDim.x) * 256)
+    row_gather[j] = perm[j / S] * S + int32_t(j % S);
+}
+
 }  // namespace
 
 hipError_t launch_reorder(const uint8_t* win_bits, int32_t n_windows, int32_t S,
                           int32_t G, int32_t D, int32_t* perm, void* segs,
                           int32_t* n_segs, int32_t* row_gather, hipStream_t s) {
   hipLaunchKernelGGL(reorder_kernel, dim3(1), dim3(kReorderThreads), 0, s, win_bits,
-                     n_windows, S, G, D, perm, static_cast<kvq_segment*>(segs), n_segs,
-                     row_gather);
+                     n_windows, S, G, D, perm, static_cast<kvq_segment*>(segs), n_segs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !row_gather) return e;
+  const int64_t total = int64_t(n_windows) * S;
+  const unsigned grid = unsigned(std::min<int64_t>((total + 255) / 256, 8192));
+  hipLaunchKernelGGL(row_gather_kernel, dim3(grid), dim3(256), 0, s, perm, n_segs, S, total, row_gather);
   return hipGetLastError();
 }
 

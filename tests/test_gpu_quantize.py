@@ -115,6 +115,24 @@ def test_codes_on_rounding_boundaries(kvq, which, bits):
     _run(kvq, which, bits, 32, 128, n_tok=96, dst_tok=0, gather=False, kind="ties")
 
 
+@pytest.mark.parametrize("which", [0, 1])
+def test_two_runs_bit_identical(kvq, which):
+    """Determinism: quantizing the same rows twice gives the same bytes."""
+    import torch
+    rng = np.random.default_rng([12, which])
+    S, n, d, G = 4, 256, 128, 32
+    x = torch.from_numpy(_data(rng, S, n, d)).cuda()
+    outs = []
+    for _ in range(2):
+        codes = torch.zeros(S, n * d, dtype=torch.uint8, device="cuda")
+        meta = torch.zeros(S, n * d, dtype=torch.uint8, device="cuda")
+        print(f"quantize determinism which={which}", flush=True)
+        kvq.kvq_quantize_append(which, 2, G, S, d, n, x, n * d, d, None, codes, n * d, meta, n * d, 0)
+        torch.cuda.synchronize()
+        outs.append((codes.cpu().numpy(), meta.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+
+
 def test_fp16_run_is_a_copy(kvq):
     import torch
     rng = np.random.default_rng(5)

@@ -59,3 +59,15 @@ def test_reorder_rejects_bad_width_on_device(kvq):
     bits = np.array([2, 4, 3, 8], np.uint8)
     n, _, _, _ = _reorder(kvq, bits, 64, 32, 128)
     assert n == -1
+
+
+def test_two_runs_bit_identical(kvq):
+    """Determinism: the same widths give the same permutation, run table and
+    gather list, run after run (the gather list comes from a grid-wide
+    kernel over W * S entries)."""
+    rng = np.random.default_rng(11)
+    bits = rng.choice([16, 8, 4, 2], size=3000, p=[0.05, 0.1, 0.3, 0.55]).astype(np.uint8)
+    a = _reorder(kvq, bits, 256, 32, 128)
+    b = _reorder(kvq, bits, 256, 32, 128)
+    assert a[0] == b[0] and a[2] == b[2]
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[3], b[3])
