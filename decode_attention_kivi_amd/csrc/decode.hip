@@ -144,6 +144,66 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 }
 
 // ---------------------------------------------------------------------------
+// Page cursor of a paged cache: the buffers that hold a sequence's key (or
+// value) tokens, page by page, for loops that run one load pipeline across
+// page boundaries.  Tokens are sequence tokens; code and meta units are
+// tokens or pairs (codes) and key groups or pairs (meta), 2^lg_cu and 2^lg_mu
+// tokens each.  Lane i holds the pool page of the sequence's page pg0 + i
+// (a wave's range spans far fewer than 64 pages); at(t) moves the cursor
+// forward to the page of token t (calls come in token order) and keeps buffer
+// resources for that page and the next, so that a load batch (at most
+// 64 tokens, a page at least 64) finds every token in one of the two.
+// Tokens of a page past the run's n_valid tokens read as zeros.
+struct PageLoc {
+  const uint8_t* head;                // pool base + kv head block offset
+  int64_t page_bytes;
+  int32_t PT, c_off, m_off, n_valid;
+  int32_t lg_cu, cu_bytes, lg_mu, mu_bytes;
+  int32_t pg0, my_page;
+  int32_t pa, end_a;                  // current page, its end token
+  Rsrc ca, cb, ma, mb;                // codes / meta of page pa and pa + 1
+  __device__ __forceinline__ void start(const int32_t* row, int32_t max_pages, int t0, int lane) {
+    pg0 = t0 / PT;
+    my_page = row[min(pg0 + lane, max_pages - 1)];
+    pa = pg0;
+    end_a = (pg0 + 1) * PT;
+    load(pa);
+  }
+  __device__ __forceinline__ Rsrc page(int pg, int32_t off, int lg, int unit) const {
+    const int k = pg - pg0;
+    const int v = k < 64 ? min(max(n_valid - pg * PT, 0), PT) : 0;   // valid tokens of the page
+    const int32_t id = __builtin_amdgcn_readlane(my_page, min(k, 63));
+    return make_rsrc(head + int64_t(id) * page_bytes + off, uint32_t(((v + (1 << lg) - 1) >> lg) * unit));
+  }
+  __device__ __forceinline__ void load(int pg) {
+    ca = page(pg, c_off, lg_cu, cu_bytes);
+    cb = page(pg + 1, c_off, lg_cu, cu_bytes);
+    ma = page(pg, m_off, lg_mu, mu_bytes);
+    mb = page(pg + 1, m_off, lg_mu, mu_bytes);
+  }
+  __device__ __forceinline__ void at(int t) {
+    if (t >= end_a) {                 // (uniform)
+      do {
+        ++pa;
+        end_a += PT;
+      } while (t >= end_a);
+      load(pa);
+    }
+  }
+  // buffer and byte offset of token t's code unit / meta unit (t in page pa or pa + 1)
+  __device__ __forceinline__ Rsrc code(int t, uint32_t& off) const {
+    const bool nx = t >= end_a;
+    off = uint32_t(((t - (nx ? end_a : end_a - PT)) >> lg_cu) * cu_bytes);
+    return nx ? cb : ca;
+  }
+  __device__ __forceinline__ Rsrc meta(int t, uint32_t& off) const {
+    const bool nx = t >= end_a;
+    off = uint32_t(((t - (nx ? end_a : end_a - PT)) >> lg_mu) * mu_bytes);
+    return nx ? mb : ma;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Keys of run tokens [r0, r1) (bits 2/4/8) -> raw logits q'.k (q' = q * 2^-8)
 // at slots slot0 + (t - r0); cbase / mbase address the run's token 0 (codes)
 // and key group 0 (meta) of this stream.  r0 is a multiple of 32, so every
@@ -163,10 +223,10 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
 // B[8*(l/16) .. +8][l % 16] and D[4*(l/16) .. +4][l % 16].  k-block l/16 of
 // instruction m is code pairs 4m .. 4m+3 of the lane's quarter row (pair P:
 // word P / NP, position P % NP, channels clo and clo + NP).
-template <int D, int GQ, int BITS>
+template <int D, int GQ, int BITS, bool PG = false>
 __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
                                const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int slot0,
-                               int lane, int n_wave) {
+                               int lane, int n_wave, PageLoc* loc = nullptr) {
   using KG = KeyGeo<D, GQ, BITS>;
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = KG::RB, LB = KG::LB, TPI = KG::TPI, WPL = KG::WPL, MF = KG::MF;
@@ -179,8 +239,9 @@ __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const Wave
   const int n_items = (n + TPI - 1) / TPI;
   const int jp = r0 >> lg;                             // first key group of the piece
   const int n_groups = ((r1 - 1) >> lg) - jp + 1;
-  const Rsrc crs = make_rsrc(cbase + int64_t(r0) * RB, uint32_t(n) * RB);
-  const Rsrc mrs = make_rsrc(mbase + int64_t(jp) * D * 4, uint32_t(n_groups) * D * 4);
+  // (paged: the page cursor supplies the buffers; cbase and mbase are null)
+  const Rsrc crs = make_rsrc(cbase + (PG ? 0 : int64_t(r0) * RB), PG ? 0u : uint32_t(n) * RB);
+  const Rsrc mrs = make_rsrc(mbase + (PG ? 0 : int64_t(jp) * D * 4), PG ? 0u : uint32_t(n_groups) * D * 4);
   // matrix role of the lane: B column (token) col, k-block kb; A row col
   const int col = lane & 15, kb = lane >> 4;
   const uint32_t lane_off = uint32_t(col * RB + kb * LB);
@@ -211,14 +272,35 @@ __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const Wave
     uint32_t mlo[MI], mhi[MI];
   };
   auto issue = [&](Batch& B, int i0) {
-    const uint32_t cb = lane_off + uint32_t(i0 * TPI * RB);
+    if constexpr (PG) {
+      // pages: each item and each group lies in one page (pages hold whole
+      // groups and multiples of 64 tokens)
+      static_assert(GPI == 1, "one key group per meta iteration");
+      const int t = r0 + i0 * TPI;
+      loc->at(t);
 #pragma unroll
-    for (int u = 0; u < NB; ++u) B.buf[u] = bload<WPL>(crs, cb + u * TPI * RB);
-    const uint32_t mb = meta_off + uint32_t((((r0 + i0 * TPI) >> lg) - jp) * D * 4);
+      for (int u = 0; u < NB; ++u) {
+        uint32_t o;
+        const Rsrc rs = loc->code(t + u * TPI, o);
+        B.buf[u] = bload<WPL>(rs, o + lane_off);
+      }
 #pragma unroll
-    for (int it = 0; it < MI; ++it) {
-      B.mlo[it] = bload<1>(mrs, mb + it * GPI * D * 4);
-      B.mhi[it] = bload<1>(mrs, mb + it * GPI * D * 4 + NP * 4);
+      for (int it = 0; it < MI; ++it) {
+        uint32_t o;
+        const Rsrc rs = loc->meta(((t >> lg) + it) << lg, o);
+        B.mlo[it] = bload<1>(rs, o + meta_off);
+        B.mhi[it] = bload<1>(rs, o + meta_off + NP * 4);
+      }
+    } else {
+      const uint32_t cb = lane_off + uint32_t(i0 * TPI * RB);
+#pragma unroll
+      for (int u = 0; u < NB; ++u) B.buf[u] = bload<WPL>(crs, cb + u * TPI * RB);
+      const uint32_t mb = meta_off + uint32_t((((r0 + i0 * TPI) >> lg) - jp) * D * 4);
+#pragma unroll
+      for (int it = 0; it < MI; ++it) {
+        B.mlo[it] = bload<1>(mrs, mb + it * GPI * D * 4);
+        B.mhi[it] = bload<1>(mrs, mb + it * GPI * D * 4 + NP * 4);
+      }
     }
   };
   auto consume = [&](const Batch& B, int i0) {
@@ -491,11 +573,13 @@ __device__ __forceinline__ void keys_quantized_dot2(const DecodeParams& P, const
 
 // Quantized keys: matrix cores (the comparison library: v_dot2 for one head
 // at d_h = 128).
-template <int D, int GQ, int BITS>
+template <int D, int GQ, int BITS, bool PG = false>
 __device__ __forceinline__ void keys_q(const DecodeParams& P, const WaveLds& W, const uint16_t* qg, int nh,
                                        const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int slot0,
-                                       int lane, int n_wave) {
-  if constexpr (kKeyLoopDot2 && GQ == 1 && D == 128)
+                                       int lane, int n_wave, PageLoc* loc = nullptr) {
+  if constexpr (PG)
+    keys_quantized<D, GQ, BITS, true>(P, W, qg, nh, cbase, mbase, r0, r1, slot0, lane, n_wave, loc);
+  else if constexpr (kKeyLoopDot2 && GQ == 1 && D == 128)
     keys_quantized_dot2<D, BITS>(P, W, qg, nh, cbase, mbase, r0, r1, slot0, lane, n_wave);
   else
     keys_quantized<D, GQ, BITS>(P, W, qg, nh, cbase, mbase, r0, r1, slot0, lane, n_wave);
@@ -579,10 +663,10 @@ __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], in
 // run is read; the partner's meta is finite.  Pair blocks past the range read
 // zero codes and zero meta, so they add 0.  Unless softmax_done, `softmax`
 // runs after the first loads are issued (it writes W.p16).
-template <int D, int GQ, int BITS, class Softmax>
+template <int D, int GQ, int BITS, class Softmax, bool PG = false>
 __device__ __forceinline__ void values_quantized(const DecodeParams& P, const WaveLds& W,
                                  const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int ps0, int lane,
-                                 Softmax& softmax, bool softmax_done, int ph, int n_wave) {
+                                 Softmax& softmax, bool softmax_done, int ph, int n_wave, PageLoc* loc = nullptr) {
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = D * BITS / 8;
   constexpr int CPP = 2 * RB / 16;        // 16-byte chunks per pair block
@@ -603,12 +687,14 @@ __device__ __forceinline__ void values_quantized(const DecodeParams& P, const Wa
   const int p0 = r0 >> 1;
   const int np = ((r1 - 1) >> 1) - p0 + 1;
   const int n_inst = (np + PPI - 1) / PPI;
-  const Rsrc crs = make_rsrc(cbase + int64_t(p0) * 2 * RB, uint32_t(np) * 2 * RB);
-  const Rsrc mrs = make_rsrc(mbase + int64_t(p0) * NG * 8, uint32_t(np) * NG * 8);
+  // (paged: the page cursor supplies the buffers; cbase and mbase are null)
+  const Rsrc crs = make_rsrc(cbase + (PG ? 0 : int64_t(p0) * 2 * RB), PG ? 0u : uint32_t(np) * 2 * RB);
+  const Rsrc mrs = make_rsrc(mbase + (PG ? 0 : int64_t(p0) * NG * 8), PG ? 0u : uint32_t(np) * NG * 8);
   const uint32_t c_off = uint32_t(my_p * 2 * RB + my_c * 16);
   const uint32_t m_off = uint32_t((my_p * NG + g) * 8);
   const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16) + ps0;
   const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  static_assert(!PG || HPP == GQ, "the page cursor moves forward only: one pass");
 
   uint16_t keep[GQ];
   for (int hp = 0; hp < GQ; hp += HPP) {
@@ -624,10 +710,24 @@ __device__ __forceinline__ void values_quantized(const DecodeParams& P, const Wa
       uint2 mb[NBV];
     };
     auto issue = [&](Batch& B, int i0) {
+      if constexpr (PG) {
+        // an instruction's 32 tokens lie in one page
+        const int t = r0 + 2 * i0 * PPI;
+        loc->at(t);
 #pragma unroll
-      for (int u = 0; u < NBV; ++u) {
-        B.cb[u] = bload<4>(crs, c_off + uint32_t((i0 + u) * PPI * 2 * RB));
-        B.mb[u] = bload<2>(mrs, m_off + uint32_t((i0 + u) * PPI * NG * 8));
+        for (int u = 0; u < NBV; ++u) {
+          uint32_t oc, om;
+          const Rsrc rc = loc->code(t + 2 * u * PPI, oc);
+          const Rsrc rm = loc->meta(t + 2 * u * PPI, om);
+          B.cb[u] = bload<4>(rc, oc + c_off);
+          B.mb[u] = bload<2>(rm, om + m_off);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NBV; ++u) {
+          B.cb[u] = bload<4>(crs, c_off + uint32_t((i0 + u) * PPI * 2 * RB));
+          B.mb[u] = bload<2>(mrs, m_off + uint32_t((i0 + u) * PPI * NG * 8));
+        }
       }
     };
     auto consume = [&](const Batch& B, int i0) {
@@ -730,10 +830,11 @@ __device__ __forceinline__ void values_quantized(const DecodeParams& P, const Wa
 // A block; more heads take a second block against the same B.  sum p * s and
 // sum p * z of each row are kept beside, summed over the four k-blocks at
 // the end and folded in: o = D - offset_j sum(p s) + sum(p z).
-template <int D, int GQ, int BITS, class Softmax>
+template <int D, int GQ, int BITS, class Softmax, bool PG = false>
 __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W,
                                       const uint8_t* cbase, const uint8_t* mbase, int r0, int r1, int ps0, int lane,
-                                      Softmax& softmax, bool softmax_done, int ph, int n_wave) {
+                                      Softmax& softmax, bool softmax_done, int ph, int n_wave,
+                                      PageLoc* loc = nullptr) {
   static_assert(D == 128, "eight channels per lane and column");
   constexpr int LT = wave_slots(GQ);
   constexpr int RB = D * BITS / 8;
@@ -754,8 +855,9 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
   const int p0 = r0 >> 1;
   const int np = ((r1 - 1) >> 1) - p0 + 1;
   const int n_steps = (np + 15) >> 4;
-  const Rsrc crs = make_rsrc(cbase + int64_t(p0) * 2 * RB, uint32_t(np) * 2 * RB);
-  const Rsrc mrs = make_rsrc(mbase + int64_t(p0) * NG * 8, uint32_t(np) * NG * 8);
+  // (paged: the page cursor supplies the buffers; cbase and mbase are null)
+  const Rsrc crs = make_rsrc(cbase + (PG ? 0 : int64_t(p0) * 2 * RB), PG ? 0u : uint32_t(np) * 2 * RB);
+  const Rsrc mrs = make_rsrc(mbase + (PG ? 0 : int64_t(p0) * NG * 8), PG ? 0u : uint32_t(np) * NG * 8);
   const uint32_t c_off = uint32_t(4 * kb * 2 * RB + col * LW);
   const uint32_t m_off = uint32_t((4 * kb * NG + ga) * 8);
   const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16) + ps0;
@@ -779,14 +881,30 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
     uint2 m[NBV][4];
   };
   auto issue = [&](Batch& B, int s0) {
+    if constexpr (PG) {
+      // a step's 32 tokens lie in one page
+      loc->at(r0 + 32 * s0);
 #pragma unroll
-    for (int v = 0; v < NBV; ++v)
+      for (int v = 0; v < NBV; ++v) {
+        uint32_t oc, om;
+        const Rsrc rc = loc->code(r0 + 32 * (s0 + v), oc);
+        const Rsrc rm = loc->meta(r0 + 32 * (s0 + v), om);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pr = 16 * (s0 + v) + u;
-        B.c[v][u] = bload<WPL>(crs, c_off + uint32_t(pr * 2 * RB));
-        B.m[v][u] = bload<2>(mrs, m_off + uint32_t(pr * NG * 8));
+        for (int u = 0; u < 4; ++u) {
+          B.c[v][u] = bload<WPL>(rc, oc + c_off + uint32_t(u * 2 * RB));
+          B.m[v][u] = bload<2>(rm, om + m_off + uint32_t(u * NG * 8));
+        }
       }
+    } else {
+#pragma unroll
+      for (int v = 0; v < NBV; ++v)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int pr = 16 * (s0 + v) + u;
+          B.c[v][u] = bload<WPL>(crs, c_off + uint32_t(pr * 2 * RB));
+          B.m[v][u] = bload<2>(mrs, m_off + uint32_t(pr * NG * 8));
+        }
+    }
   };
   auto consume = [&](const Batch& B, int s0) {
 #pragma unroll
@@ -904,14 +1022,16 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
 
 // Quantized values: matrix cores for grouped heads at d_h = 128, the pair
 // loop otherwise.
-template <int D, int GQ, int BITS, class Softmax>
+template <int D, int GQ, int BITS, bool PG = false, class Softmax>
 __device__ __forceinline__ void values_q(const DecodeParams& P, const WaveLds& W, const uint8_t* cbase,
                                          const uint8_t* mbase, int r0, int r1, int ps0, int lane, Softmax& softmax,
-                                         bool softmax_done, int ph, int n_wave) {
+                                         bool softmax_done, int ph, int n_wave, PageLoc* loc = nullptr) {
   if constexpr (D == 128 && GQ >= 2)
-    values_quantized_mfma<D, GQ, BITS>(P.lg_g, W, cbase, mbase, r0, r1, ps0, lane, softmax, softmax_done, ph, n_wave);
+    values_quantized_mfma<D, GQ, BITS, Softmax, PG>(P.lg_g, W, cbase, mbase, r0, r1, ps0, lane, softmax,
+                                                    softmax_done, ph, n_wave, loc);
   else
-    values_quantized<D, GQ, BITS>(P, W, cbase, mbase, r0, r1, ps0, lane, softmax, softmax_done, ph, n_wave);
+    values_quantized<D, GQ, BITS, Softmax, PG>(P, W, cbase, mbase, r0, r1, ps0, lane, softmax, softmax_done, ph,
+                                               n_wave, loc);
 }
 
 // Values from fp16 rows rows[0..n), probabilities at slots slot0 + i
@@ -1065,7 +1185,40 @@ decode_kernel(const DecodeParams P) {
   // runs start at even tokens, so every value pair block starts at an even slot
   if (n > 0) {
     // key pieces in token order
-    if constexpr (PAGED) {
+    if constexpr (PAGED && D == 128) {
+      // quantized keys: one load pipeline across the pages of the range (a
+      // range inside one page takes the plain run loop)
+      const int kend = min(e, n_kq);
+      if (a < kend && a / P.page_tokens == (kend - 1) / P.page_tokens) {
+        const int pg = a / P.page_tokens;
+        const int p0 = pg * P.page_tokens;
+        const uint8_t* hb = P.pages + int64_t(P.block_table[int64_t(b) * P.max_pages + pg]) * P.page_bytes +
+                            int64_t(hkv) * P.head_bytes;
+        switch (P.bits) {
+          case 2: keys_q<D, GQ, 2>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, a - p0, kend - p0, 0, lane, n); break;
+          case 4: keys_q<D, GQ, 4>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, a - p0, kend - p0, 0, lane, n); break;
+          default: keys_q<D, GQ, 8>(P, W, qg, nh, hb, hb + P.pg_kmeta_off, a - p0, kend - p0, 0, lane, n); break;
+        }
+      } else if (a < kend) {
+        PageLoc loc;
+        loc.head = P.pages + int64_t(hkv) * P.head_bytes;
+        loc.page_bytes = P.page_bytes;
+        loc.PT = P.page_tokens;
+        loc.c_off = 0;
+        loc.m_off = P.pg_kmeta_off;
+        loc.n_valid = n_kq;
+        loc.lg_cu = 0;
+        loc.cu_bytes = D * P.bits / 8;
+        loc.lg_mu = P.lg_g;
+        loc.mu_bytes = D * 4;
+        loc.start(P.block_table + int64_t(b) * P.max_pages, P.max_pages, a, lane);
+        switch (P.bits) {
+          case 2: keys_q<D, GQ, 2, true>(P, W, qg, nh, nullptr, nullptr, a, kend, 0, lane, n, &loc); break;
+          case 4: keys_q<D, GQ, 4, true>(P, W, qg, nh, nullptr, nullptr, a, kend, 0, lane, n, &loc); break;
+          default: keys_q<D, GQ, 8, true>(P, W, qg, nh, nullptr, nullptr, a, kend, 0, lane, n, &loc); break;
+        }
+      }
+    } else if constexpr (PAGED) {
       // quantized keys, one piece per page (pages start on key groups)
       const int kend = min(e, n_kq);
       for (int t0 = a; t0 < kend;) {
@@ -1164,7 +1317,44 @@ decode_kernel(const DecodeParams P) {
   wave_lds_sync();
   if (n > 0) {
     // value pieces in token order
-    if constexpr (PAGED) {
+    if constexpr (PAGED && D == 128) {
+      // quantized values: one load pipeline across the pages of the range;
+      // an odd end is the last quantized value
+      const int vend = min(e, n_vq);
+      if (a < vend && a / P.page_tokens == (vend - 1) / P.page_tokens) {
+        const int pg = a / P.page_tokens;
+        const int p0 = pg * P.page_tokens;
+        const uint8_t* hb = P.pages + int64_t(P.block_table[int64_t(b) * P.max_pages + pg]) * P.page_bytes +
+                            int64_t(hkv) * P.head_bytes;
+        const int ph = ((vend & 1) && vend < e) ? vend - a : -1;
+        const uint8_t* cb = hb + P.pg_vcodes_off;
+        const uint8_t* mb = hb + P.pg_vmeta_off;
+        switch (P.bits) {
+          case 2: values_q<D, GQ, 2>(P, W, cb, mb, a - p0, vend - p0, 0, lane, softmax, softmax_done, ph, n); break;
+          case 4: values_q<D, GQ, 4>(P, W, cb, mb, a - p0, vend - p0, 0, lane, softmax, softmax_done, ph, n); break;
+          default: values_q<D, GQ, 8>(P, W, cb, mb, a - p0, vend - p0, 0, lane, softmax, softmax_done, ph, n); break;
+        }
+      } else if (a < vend) {
+        PageLoc loc;
+        loc.head = P.pages + int64_t(hkv) * P.head_bytes;
+        loc.page_bytes = P.page_bytes;
+        loc.PT = P.page_tokens;
+        loc.c_off = P.pg_vcodes_off;
+        loc.m_off = P.pg_vmeta_off;
+        loc.n_valid = n_vq;
+        loc.lg_cu = 1;
+        loc.cu_bytes = 2 * D * P.bits / 8;
+        loc.lg_mu = 1;
+        loc.mu_bytes = (D >> P.lg_g) * 8;
+        loc.start(P.block_table + int64_t(b) * P.max_pages, P.max_pages, a, lane);
+        const int ph = ((vend & 1) && vend < e) ? vend - a : -1;
+        switch (P.bits) {
+          case 2: values_q<D, GQ, 2, true>(P, W, nullptr, nullptr, a, vend, 0, lane, softmax, softmax_done, ph, n, &loc); break;
+          case 4: values_q<D, GQ, 4, true>(P, W, nullptr, nullptr, a, vend, 0, lane, softmax, softmax_done, ph, n, &loc); break;
+          default: values_q<D, GQ, 8, true>(P, W, nullptr, nullptr, a, vend, 0, lane, softmax, softmax_done, ph, n, &loc); break;
+        }
+      }
+    } else if constexpr (PAGED) {
       const int vend = min(e, n_vq);
       for (int t0 = a; t0 < vend;) {
         const int pg = t0 / P.page_tokens;

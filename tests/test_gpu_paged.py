@@ -93,6 +93,14 @@ def test_ragged_many_query_heads(kvq, hq, hkv, d):
     run_paged([5, 300, 2000], hq, hkv, d, 32, 32, 2, 256, n_out=3, factor=8.0)
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (8, 2)])
+def test_wave_ranges_across_many_pages(kvq, bits, hq, hkv):
+    # 64-token pages at d_h 128: a wave's range crosses several pages, which
+    # one load pipeline walks (page cursor); odd value counts end mid-pair
+    run_paged([3, 701, 1500, 2900], hq, hkv, 128, 32, 64, bits, 64, n_out=3, factor=8.0)
+
+
 def test_page_equals_group(kvq):
     # pages of 128 tokens with groups of 128 tokens: one key group per page
     run_paged([129, 384, 1000], 2, 2, 128, 128, 128, 4, 128)
