@@ -284,6 +284,46 @@ def graph_time_us(stream, calls_per_graph: int, record, reps: int = 40, warm: in
     return e0.elapsed_time(e1) / (reps * calls_per_graph) * 1e3
 
 
+def flush_rate(dev, stream, copies: int = 16, streams: int = 512, d: int = 128, R: int = 128,
+               G: int = 32, bits: int = 2):
+    """The two calls a KIVI cache makes besides the step, at the Llama-2-7B
+    decode shape (16 sequences x 32 heads = 512 streams, d128, G32, R128,
+    int2): the key flush (kvq_quantize_append of the R residual keys, every R
+    steps) and the value-window compaction (kvq_residual_append of R rows back
+    to row 0, every R + 2 steps).  Each call reads the next of `copies`
+    residual copies (16 x 16.8 MB, more than the 256 MB Infinity Cache), one
+    HIP graph per kind.  Algorithmic bytes: the flush reads R fp16 rows and
+    writes their codes and R / G (scale, zero) rows per stream; the
+    compaction reads and writes R fp16 rows per stream."""
+    import torch
+    import decode_attention_kivi_amd as kvq
+    g = torch.Generator(device=dev).manual_seed(7)
+    res = [torch.randn(streams, 2 * R + 2, d, generator=g, device=dev).half() for _ in range(copies)]
+    kc = [torch.empty(streams, R * d * bits // 8, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    km = [torch.empty(streams, R // G * d * 4, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    row = (2 * R + 2) * d
+
+    def flushes():
+        for r, c, m in zip(res, kc, km):
+            kvq.kvq_quantize_append(kvq.KVQ_KEYS, bits, G, streams, d, R, r, row, d, None, c, c.stride(0),
+                                    m, m.stride(0), 0, stream)
+
+    def compactions():
+        for r in res:
+            kvq.kvq_residual_append(streams, d, R, r[:, R + 2:], row, d, r, row, 0, stream)
+    flush_us = graph_time_us(stream, copies, flushes)
+    comp_us = graph_time_us(stream, copies, compactions)
+    fb = streams * (R * d * 2 + R * d * bits // 8 + R // G * d * 4)
+    cb = streams * R * d * 2 * 2
+    del res, kc, km
+    return {"config": f"{streams} streams (16 x 32 heads), d{d}, G{G}, R{R}, int{bits}; "
+                      f"{copies} rotating residual copies",
+            "key_flush": {"us_per_call": round(flush_us, 2), "algorithmic_bytes": fb,
+                          "GBs": round(fb / (flush_us * 1e-6) / 1e9, 1)},
+            "window_compaction": {"us_per_call": round(comp_us, 2), "algorithmic_bytes": cb,
+                                  "GBs": round(cb / (comp_us * 1e-6) / 1e9, 1)}}
+
+
 def config_rate(name: str, dev, stream, min_copies: int = 2):
     """kvq_decode_attn at one of the uniform KIVI workloads' full sizes, in
     the state after prefill and one decode step, over rotating cache copies
@@ -595,12 +635,12 @@ def main():
                     help="seconds of untimed replays before timing (clock ramp-up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--part", choices=("all", "attention", "step", "paged", "pq", "search", "windows", "vq",
-                                       "config"),
+                                       "config", "flush"),
                     default="all",
                     help="profiling runs: time only the attention graph, only the step graph, the paged "
                          "ragged batch, the PQ search, the window search, the mixed-precision "
-                         "window cache, the VQ-cache decode or one workload's attention (--workload; "
-                         "and skip the rest)")
+                         "window cache, the VQ-cache decode, one workload's attention (--workload) "
+                         "or the key flush and window compaction (and skip the rest)")
     ap.add_argument("--page-tokens", type=int, default=256, help="page size of the paged ragged batch")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one fp16 row copy of this many MiB first (counter calibration)")
@@ -631,9 +671,11 @@ def main():
         for rounds in (1, 2):
             print(json.dumps({"part": "vq", **vq_decode_rate(dev, st, rounds)}), flush=True)
         return
-    if args.part in ("paged", "pq", "search", "windows", "config"):
+    if args.part in ("paged", "pq", "search", "windows", "config", "flush"):
         dev, st = torch.device("cuda:0"), torch.cuda.Stream()
-        if args.part == "config":
+        if args.part == "flush":
+            r = flush_rate(dev, st)
+        elif args.part == "config":
             r = {"workload": args.workload, **config_rate(args.workload, dev, st)}
         elif args.part == "paged":
             r = paged_ragged_rate(dev, st, page_tokens=args.page_tokens)
@@ -782,7 +824,7 @@ def main():
         attn_pct = step_pct = (float("nan"),) * 3
         n_steps = 0
         components = ceiling = search_rate = paged_rate = windows_rate = pq_rate = vq_rates = None
-        configs = host_us = None
+        configs = host_us = flush = None
         if attn_graph is not None:
             attn_ms, n_steps, attn_pct = timed(attn_graph, attn_tail, args.steps, args.warmup)
         if step_graph is not None:
@@ -791,6 +833,7 @@ def main():
             components = component_times(w, caches[0], k_new, v_new, q, outs[0], stream)
             host_us = host_call_us(caches[0], q, outs[0], w.sm_scale, stream)
             restore()
+            flush = flush_rate(dev, stream)
             ceiling = streaming_read_ceiling(dev, stream)
             search_rate = window_search_rate(dev, stream)
             paged_rate = paged_ragged_rate(dev, stream, page_tokens=args.page_tokens)
@@ -819,8 +862,8 @@ def main():
                             "tokens_context_per_s": round(w.batch * w.n_tokens / (attn_ms * 1e-3), 1)}
     # a step that also flushes the key residual (every R steps) or compacts
     # the value window (every R + 2 steps) costs those calls on top
-    amortized = step_ms * 1e3 + components["key_flush_R_tokens"] / w.residual + \
-        components["window_compaction_R_rows"] / (w.residual + 2)
+    amortized = step_ms * 1e3 + flush["key_flush"]["us_per_call"] / w.residual + \
+        flush["window_compaction"]["us_per_call"] / (w.residual + 2)
     result = {
         "metric": "decode-attn effective KV GB/s (% of HBM peak) + us/step, int2 Llama-2-7B shape",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
@@ -856,7 +899,8 @@ def main():
                            "(launch latency included); us_per_step is the graph-replayed step",
         "us_per_step_amortized": round(amortized, 2),
         "us_per_step_amortized_note": "us_per_step + key flush / R + window compaction / (R + 2), the "
-                                      "last two from components_us (eager calls: an upper bound)",
+                                      "last two graph-replayed over rotating copies (flush_and_compaction)",
+        "flush_and_compaction": flush,
         "host_us_per_call": host_us,
         "window_search": search_rate,
         "paged_ragged": paged_rate,

@@ -72,6 +72,99 @@ __device__ __forceinline__ uint32_t encode_fast(float x, const GroupScale& g, bo
 // true on every lane when any lane of the wave sets x
 __device__ __forceinline__ bool wave_any(bool x) { return __builtin_amdgcn_ballot_w64(x) != 0; }
 
+// ---------------------------------------------------------------------------
+// Row-batch encoder of the wave quantizers: 8 channels held as fp16 pairs
+// (channel 2e in the low half of word e of a 16-byte row piece).
+
+// Packed fp16 min / max (v_pk_min_f16 / v_pk_max_f16, both halves at once).
+// Exact; the sign of a zero result is not specified, which group_scale's
+// canonicalization makes irrelevant.
+__device__ __forceinline__ uint32_t pk_min_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// fl(x - z) for x the fp16 in the low (HI false) or high half of w, in one
+// v_fma_mix_f32: x widened exactly, times one (1.0), plus -z (the source
+// negate modifier), one rounding -- the same value as converting x and
+// subtracting in fp32.
+template <bool HI>
+__device__ __forceinline__ float sub_half_f32(uint32_t w, float one, float z) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(one), "v"(z));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(one), "v"(z));
+  return r;
+}
+
+// A group whose scale lets the reciprocal path skip the clamp: s = 0 (inv 0,
+// every code 0) or s a normal finite fp16.  Then z = min exactly (the extrema
+// are fp16 values), so d = fl(x - z) >= 0, and with s >= (1 - 2^-11)
+// fl(max - min)/(2^b - 1) the product q stays below (2^b - 1)(1 + 2^-10)
+// < 2^b - 1/2: rint(q) is a code without clamping.  Subnormal scales (rounded
+// by up to a factor 1.5) and infinite ones go through encode().
+__device__ __forceinline__ bool scale_unclamped(uint32_t s16) {
+  return s16 == 0u || (s16 >= 0x0400u && s16 < 0x7C00u);
+}
+
+// Codes of the 8 channels of x, by the reciprocal product and without the
+// clamp (valid for scale_unclamped groups), packed as 16-bit chunks of
+// 16/BITS codes (channel c at bits BITS*(c % (16/BITS)) of chunk
+// c / (16/BITS)).  Each code goes into its chunk by one exact fp32 fma
+// (integers below 2^16).  err collects |q - rint(q)|; a batch with
+// err >= 1/2 - 2^b 2^-20 anywhere in the wave is encoded again by encode()
+// (see encode_fast for the bound).  z[c], inv[c] of channel c's group.
+template <int BITS>
+__device__ __forceinline__ void codes8_fast(const uint4& x, const float (&z)[8], const float (&inv)[8],
+                                            float one, float& err, uint32_t (&chunk)[BITS / 2]) {
+#pragma clang fp contract(off)
+  constexpr int KPC = 16 / BITS;         // codes per 16-bit chunk
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  float acc[BITS / 2];
+  float r[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float d = (c & 1) ? sub_half_f32<true>(w[c / 2], one, z[c]) : sub_half_f32<false>(w[c / 2], one, z[c]);
+    const float q = d * inv[c];
+    const float t = rintf(q);
+    r[c] = q - t;
+    const int j = c % KPC;
+    if (j == 0) acc[c / KPC] = t;
+    else acc[c / KPC] = __builtin_fmaf(t, float(1 << (BITS * j)), acc[c / KPC]);
+  }
+#pragma unroll
+  for (int c = 0; c < 8; c += 2) err = fmaxf(err, fmaxf(fabsf(r[c]), fabsf(r[c + 1])));
+#pragma unroll
+  for (int m = 0; m < BITS / 2; ++m) chunk[m] = static_cast<uint32_t>(acc[m]);
+}
+
+// The same chunks from the definition (encode(): correctly rounded quotient,
+// clamp) -- the path of batches the fast one cannot decide.
+template <int BITS>
+__device__ __forceinline__ void codes8_exact(const uint4& x, const GroupScale (&g)[8], uint32_t (&chunk)[BITS / 2]) {
+  constexpr int KPC = 16 / BITS;
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int m = 0; m < BITS / 2; ++m) chunk[m] = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float f = h2f((c & 1) ? (w[c / 2] >> 16) : (w[c / 2] & 0xffffu));
+    chunk[c / KPC] |= encode<BITS>(f, g[c]) << (BITS * (c % KPC));
+  }
+}
+
+// Bound of the reciprocal path: |q - rint(q)| at or above it may round
+// differently from the correctly rounded quotient.
+template <int BITS>
+constexpr float kFastFar = 0.5f - float(1 << BITS) * 0x1p-20f;
+
 // One decode step's append for stream s, by one wave (KIVI note, Algorithm 1,
 // Decoding): lanes 0..D/8-1 copy the new key row into key-residual row
 // k_row, lanes D/8..D/4-1 the new value row into value-window row v_row (16

@@ -77,39 +77,37 @@ __device__ __forceinline__ uint4 load_row16(const uint16_t* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ void halves(const uint4& x, float (&f)[8]) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    f[2 * e] = h2f(w[e] & 0xffffu);
-    f[2 * e + 1] = h2f(w[e] >> 16);
-  }
+// min / max over the lanes l, l ^ LPR, l ^ 2 LPR, ... (the rows of a load
+// instruction that hold the same 8 channels) of packed fp16 pairs; every
+// lane gets the result.
+template <int LPR>
+__device__ __forceinline__ uint32_t rows_min(uint32_t x) {
+  if constexpr (LPR == 8) x = pk_min_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = pk_min_f16(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return pk_min_f16(b[0], b[1]);
+}
+template <int LPR>
+__device__ __forceinline__ uint32_t rows_max(uint32_t x) {
+  if constexpr (LPR == 8) x = pk_max_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = pk_max_f16(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return pk_max_f16(b[0], b[1]);
 }
 
-// min / max over the lanes l, l ^ LPR, l ^ 2 LPR, ... (the rows of a load
-// instruction that hold the same 8 channels), every lane gets the result.
-template <int LPR>
-__device__ __forceinline__ float rows_min(float x) {
-  if constexpr (LPR == 8) x = fminf(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));  // row_ror:8
-  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
-  x = fminf(bitsf(a[0]), bitsf(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
-  return fminf(bitsf(b[0]), bitsf(b[1]));
-}
-template <int LPR>
-__device__ __forceinline__ float rows_max(float x) {
-  if constexpr (LPR == 8) x = fmaxf(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
-  const auto a = __builtin_amdgcn_permlane16_swap(fbits(x), fbits(x), false, false);
-  x = fmaxf(bitsf(a[0]), bitsf(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(fbits(x), fbits(x), false, false);
-  return fmaxf(bitsf(b[0]), bitsf(b[1]));
+__device__ __forceinline__ uint32_t word(const uint4& x, int e) {
+  return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
 }
 
 // Keys: one wave per (stream, key group of G tokens).  Load instruction k
 // brings rows k*RPI .. k*RPI + RPI-1 of the group, lane l holding channels
 // 8*(l % LPR) .. +7 of row k*RPI + l / LPR.  Channel extrema: over the lane's
-// NL rows, then across the RPI lanes of the same channels.  Every lane
-// encodes its 8 channels of its NL rows into 8*BITS bits per row.
+// NL rows on packed fp16 pairs, then across the RPI lanes of the same
+// channels.  Every lane encodes its 8 channels of its NL rows into 8*BITS
+// bits per row (codes8_fast; a row batch of the wave that it cannot decide,
+// or a wave with a group scale outside scale_unclamped, by codes8_exact).
 template <int BITS, int D, int G>
 __global__ void __launch_bounds__(256) quantize_keys_wave_kernel(QuantParams p) {
   constexpr int LPR = D / 8;
@@ -122,61 +120,58 @@ __global__ void __launch_bounds__(256) quantize_keys_wave_kernel(QuantParams p) 
   const int64_t s = blockIdx.y;
   const int c8 = lane % LPR, r0 = lane / LPR;
   const uint16_t* src = p.src + s * p.src_stream_stride + c8 * 8;
+  // row indices first (one uniform branch), then the NL loads back to back:
+  // a gather read inside the load loop would split it into blocks that each
+  // wait for the previous load
+  int64_t row[NL];
+  if (p.src_rows) {
+#pragma unroll
+    for (int k = 0; k < NL; ++k) row[k] = p.src_rows[j * G + k * RPI + r0];
+  } else {
+#pragma unroll
+    for (int k = 0; k < NL; ++k) row[k] = j * G + k * RPI + r0;
+  }
   uint4 x[NL];
 #pragma unroll
-  for (int k = 0; k < NL; ++k) {
-    const int tok = j * G + k * RPI + r0;
-    const int64_t row = p.src_rows ? p.src_rows[tok] : tok;
-    x[k] = load_row16(src + row * p.src_row_stride);
-  }
-  float mn[8], mx[8];
-  {
-    float f[8];
-    halves(x[0], f);
+  for (int k = 0; k < NL; ++k) x[k] = load_row16(src + row[k] * p.src_row_stride);
+  uint32_t mnw[4], mxw[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) mn[c] = mx[c] = f[c];
-  }
+  for (int e = 0; e < 4; ++e) mnw[e] = mxw[e] = word(x[0], e);
 #pragma unroll
   for (int k = 1; k < NL; ++k) {
-    float f[8];
-    halves(x[k], f);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      mn[c] = fminf(mn[c], f[c]);
-      mx[c] = fmaxf(mx[c], f[c]);
+    for (int e = 0; e < 4; ++e) {
+      mnw[e] = pk_min_f16(mnw[e], word(x[k], e));
+      mxw[e] = pk_max_f16(mxw[e], word(x[k], e));
     }
   }
   GroupScale gs[8];
+  float z[8], inv[8];
+  bool slow = false;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) gs[c] = group_scale<BITS>(rows_min<LPR>(mn[c]), rows_max<LPR>(mx[c]));
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t mn = rows_min<LPR>(mnw[e]), mx = rows_max<LPR>(mxw[e]);
+    gs[2 * e] = group_scale<BITS>(h2f(mn & 0xffffu), h2f(mx & 0xffffu));
+    gs[2 * e + 1] = group_scale<BITS>(h2f(mn >> 16), h2f(mx >> 16));
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    z[c] = gs[c].z;
+    inv[c] = gs[c].inv;
+    slow |= !scale_unclamped(gs[c].s16);
+  }
+  const float one = 1.0f;
   uint8_t* out = p.codes + s * p.codes_stream_stride + c8 * BITS;   // 8 channels = BITS bytes
 #pragma unroll
   for (int k = 0; k < NL; ++k) {
-    float f[8];
-    halves(x[k], f);
-    uint32_t lo = 0, hi = 0;
-    bool near = false;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t q = encode_fast<BITS>(f[c], gs[c], near);
-      const int bit = c * BITS;
-      if (bit < 32) lo |= q << bit;
-      else hi |= q << (bit - 32);
-    }
-    if (wave_any(near)) {                // (uniform, rare) a quotient near a rounding boundary
-      lo = hi = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t q = encode<BITS>(f[c], gs[c]);
-        const int bit = c * BITS;
-        if (bit < 32) lo |= q << bit;
-        else hi |= q << (bit - 32);
-      }
-    }
+    uint32_t ch[BITS / 2];
+    float err = 0.0f;
+    codes8_fast<BITS>(x[k], z, inv, one, err, ch);
+    if (wave_any(slow || err >= kFastFar<BITS>)) codes8_exact<BITS>(x[k], gs, ch);   // uniform, rare
     uint8_t* dst = out + int64_t(p.dst_tok + j * G + k * RPI + r0) * RB;
-    if constexpr (BITS == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(lo);
-    else if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = lo;
-    else *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    if constexpr (BITS == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(ch[0]);
+    else if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = ch[0] | (ch[1] << 16);
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(ch[0] | (ch[1] << 16), ch[2] | (ch[3] << 16));
   }
   if (r0 == 0) {
     uint4* meta = reinterpret_cast<uint4*>(p.meta + s * p.meta_stream_stride +
@@ -214,61 +209,82 @@ __global__ void __launch_bounds__(256) quantize_values_pairs_kernel(QuantParams 
   if (P0 > p_hi) return;                // uniform per wave
   const int c8 = lane % LPR, pl = lane / LPR;
   const uint16_t* src = p.src + s * p.src_stream_stride + c8 * 8;
-  uint4 xa[U], xb[U];
+  // source rows of the pair blocks' tokens (an absent token reads source
+  // row 0, which always exists, and is zeroed after the load), resolved
+  // before the loads so that all 2U of them issue back to back
+  int64_t ia[U], ib[U];
+  bool ha[U], hb[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t P = P0 + u * PPI + pl;
     const int64_t i0 = 2 * P - p.dst_tok, i1 = i0 + 1;
-    xa[u] = make_uint4(0, 0, 0, 0);
-    xb[u] = make_uint4(0, 0, 0, 0);
-    if (P <= p_hi && i0 >= 0) {
-      const int64_t row = p.src_rows ? p.src_rows[i0] : i0;
-      xa[u] = load_row16(src + row * p.src_row_stride);
+    ha[u] = P <= p_hi && i0 >= 0;
+    hb[u] = P <= p_hi && i1 < p.n_tok;
+    ia[u] = ha[u] ? i0 : 0;
+    ib[u] = hb[u] ? i1 : 0;
+  }
+  if (p.src_rows) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      ia[u] = p.src_rows[ia[u]];
+      ib[u] = p.src_rows[ib[u]];
     }
-    if (P <= p_hi && i1 < p.n_tok) {
-      const int64_t row = p.src_rows ? p.src_rows[i1] : i1;
-      xb[u] = load_row16(src + row * p.src_row_stride);
-    }
+  }
+  uint4 xa[U], xb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    xa[u] = load_row16(src + ia[u] * p.src_row_stride);
+    xb[u] = load_row16(src + ib[u] * p.src_row_stride);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!ha[u]) xa[u] = make_uint4(0, 0, 0, 0);
+    if (!hb[u]) xb[u] = make_uint4(0, 0, 0, 0);
   }
   uint8_t* codes = p.codes + s * p.codes_stream_stride;
   uint8_t* meta = p.meta + s * p.meta_stream_stride;
   const int g = c8 / LPG;
+  const float one = 1.0f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t P = P0 + u * PPI + pl;
     const int64_t i0 = 2 * P - p.dst_tok, i1 = i0 + 1;
     const bool va = i0 >= 0, vb = i1 < p.n_tok;   // meaningful only for P <= p_hi
-    float fa[8], fb[8];
-    halves(xa[u], fa);
-    halves(xb[u], fb);
-    float mna = fa[0], mxa = fa[0], mnb = fb[0], mxb = fb[0];
-#pragma unroll
-    for (int c = 1; c < 8; ++c) {
-      mna = fminf(mna, fa[c]); mxa = fmaxf(mxa, fa[c]);
-      mnb = fminf(mnb, fb[c]); mxb = fmaxf(mxb, fb[c]);
-    }
-    const GroupScale ga = group_scale<BITS>(group_min<LPG>(mna), group_max<LPG>(mxa));
-    const GroupScale gb = group_scale<BITS>(group_min<LPG>(mnb), group_max<LPG>(mxb));
-    uint32_t w[WPL];
-#pragma unroll
-    for (int k = 0; k < WPL; ++k) w[k] = 0;
-    bool near = false;
+    // token extrema over the lane's 8 channels (packed pairs, then the two
+    // halves), then over the LPG lanes of the group
+    const uint32_t mna2 = pk_min_f16(pk_min_f16(xa[u].x, xa[u].y), pk_min_f16(xa[u].z, xa[u].w));
+    const uint32_t mxa2 = pk_max_f16(pk_max_f16(xa[u].x, xa[u].y), pk_max_f16(xa[u].z, xa[u].w));
+    const uint32_t mnb2 = pk_min_f16(pk_min_f16(xb[u].x, xb[u].y), pk_min_f16(xb[u].z, xb[u].w));
+    const uint32_t mxb2 = pk_max_f16(pk_max_f16(xb[u].x, xb[u].y), pk_max_f16(xb[u].z, xb[u].w));
+    const float mna = fminf(h2f(mna2 & 0xffffu), h2f(mna2 >> 16));
+    const float mxa = fmaxf(h2f(mxa2 & 0xffffu), h2f(mxa2 >> 16));
+    const float mnb = fminf(h2f(mnb2 & 0xffffu), h2f(mnb2 >> 16));
+    const float mxb = fmaxf(h2f(mxb2 & 0xffffu), h2f(mxb2 >> 16));
+    GroupScale ga[8], gb[8];
+    ga[0] = group_scale<BITS>(group_min<LPG>(mna), group_max<LPG>(mxa));
+    gb[0] = group_scale<BITS>(group_min<LPG>(mnb), group_max<LPG>(mxb));
+    float za[8], inva[8], zb[8], invb[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int k = c / KPU, sh = (c % KPU) * BITS;
-      w[k] |= encode_fast<BITS>(fa[c], ga, near) << sh;
-      if (vb) w[k] |= encode_fast<BITS>(fb[c], gb, near) << (16 + sh);
+      ga[c] = ga[0];
+      gb[c] = gb[0];
+      za[c] = ga[0].z;
+      inva[c] = ga[0].inv;
+      zb[c] = gb[0].z;
+      invb[c] = gb[0].inv;
     }
-    if (wave_any(near)) {                // (uniform, rare) a quotient near a rounding boundary
-#pragma unroll
-      for (int k = 0; k < WPL; ++k) w[k] = 0;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int k = c / KPU, sh = (c % KPU) * BITS;
-        w[k] |= encode<BITS>(fa[c], ga) << sh;
-        if (vb) w[k] |= encode<BITS>(fb[c], gb) << (16 + sh);
-      }
+    uint32_t cha[WPL], chb[WPL];
+    float err = 0.0f;
+    codes8_fast<BITS>(xa[u], za, inva, one, err, cha);
+    codes8_fast<BITS>(xb[u], zb, invb, one, err, chb);
+    const bool slow = !scale_unclamped(ga[0].s16) || !scale_unclamped(gb[0].s16);
+    if (wave_any(slow || err >= kFastFar<BITS>)) {   // uniform, rare
+      codes8_exact<BITS>(xa[u], ga, cha);
+      codes8_exact<BITS>(xb[u], gb, chb);
     }
+    uint32_t w[WPL];
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) w[k] = cha[k] | (vb ? chb[k] << 16 : 0u);
     if (P > p_hi) continue;
     uint8_t* blk = codes + P * 2 * RB + c8 * WPL * 4;
     const bool lead = (c8 % LPG) == 0;
@@ -278,11 +294,12 @@ __global__ void __launch_bounds__(256) quantize_values_pairs_kernel(QuantParams 
       else if constexpr (WPL == 2) *reinterpret_cast<uint2*>(blk) = make_uint2(w[0], w[1]);
       else *reinterpret_cast<uint4*>(blk) = make_uint4(w[0], w[1], w[2], w[3]);
       if (lead)
-        *reinterpret_cast<uint2*>(mp) = make_uint2(ga.s16 | (ga.z16 << 16), vb ? (gb.s16 | (gb.z16 << 16)) : 0u);
+        *reinterpret_cast<uint2*>(mp) =
+            make_uint2(ga[0].s16 | (ga[0].z16 << 16), vb ? (gb[0].s16 | (gb[0].z16 << 16)) : 0u);
     } else {
 #pragma unroll
       for (int k = 0; k < WPL; ++k) reinterpret_cast<uint16_t*>(blk)[2 * k + 1] = static_cast<uint16_t>(w[k] >> 16);
-      if (lead) mp[1] = gb.s16 | (gb.z16 << 16);
+      if (lead) mp[1] = gb[0].s16 | (gb[0].z16 << 16);
     }
   }
 }

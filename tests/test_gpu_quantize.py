@@ -34,6 +34,19 @@ def _ties(n_streams, n, d):
 def _data(rng, n_streams, n, d, kind="normal"):
     if kind == "ties":
         return _ties(n_streams, n, d)
+    if kind == "tiny":
+        # groups whose fp16 scale is subnormal (range below (2^b - 1) 2^-14),
+        # where the kernels' reciprocal path must defer to the clamped
+        # division, beside normal ones: key groups (a channel over G tokens)
+        # of channels c % 3 != 0 and value groups (a token over G channels)
+        # of odd tokens hold only values of about 3e-5, 1e-7 or 4e-8 (by
+        # stream; the smaller ones give scales of a few subnormal ulps, whose
+        # rounding pushes quotients past 2^b - 1)
+        x = rng.standard_normal((n_streams, n, d)).astype(np.float32)
+        x *= np.array([3e-5, 1e-7, 4e-8], np.float32)[np.arange(n_streams) % 3][:, None, None]
+        t, c = np.meshgrid(np.arange(n), np.arange(d), indexing="ij")
+        x = np.where((c % 3 == 0) & (t % 2 == 0), rng.standard_normal((n_streams, n, d)), x)
+        return x.astype(np.float16)
     x = rng.standard_normal((n_streams, n, d)).astype(np.float32)
     x[:, :, rng.choice(d, 3, replace=False)] *= 9.0
     if kind == "special":
@@ -113,6 +126,13 @@ def test_gather_and_special_values(kvq, which, bits):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_codes_on_rounding_boundaries(kvq, which, bits):
     _run(kvq, which, bits, 32, 128, n_tok=96, dst_tok=0, gather=False, kind="ties")
+
+
+@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_subnormal_scales(kvq, which, bits):
+    _run(kvq, which, bits, 32, 128, n_tok=96, dst_tok=0, gather=False, kind="tiny")
+    _run(kvq, which, bits, 64, 64, n_tok=128, dst_tok=64 if which == 0 else 3, gather=False, kind="tiny")
 
 
 @pytest.mark.parametrize("which", [0, 1])

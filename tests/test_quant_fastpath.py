@@ -69,3 +69,30 @@ def test_random_groups_rarely_take_the_division():
         got, slow = _fast(d, s, r, qmax)
         assert np.array_equal(got, _exact(d, s, qmax))
         assert slow.mean() < 1e-3
+
+
+def test_normal_scales_need_no_clamp():
+    """The row-batch encoder (codes8_fast) drops the clamp for groups whose
+    fp16 scale s = fl16(fl32(D / (2^b - 1))), D = fl32(max - min), is normal:
+    d = fl32(x - z) <= D with z = min exactly, so the largest product is
+    fl32(D * r) at the largest D that still rounds to s, with r one ulp above
+    1/s; its rint must not pass 2^b - 1.  Checked for every normal fp16 s."""
+    s16 = np.arange(0x0400, 0x7C00, dtype=np.uint16)
+    s = s16.view(np.float16).astype(F32)
+    nxt = (s16 + 1).view(np.float16).astype(np.float64)          # next fp16 (inf past the last)
+    nxt[-1] = 65520.0                                             # the fp16 overflow threshold
+    for bits in (2, 4, 8):
+        qmax = (1 << bits) - 1
+        hi = ((s.astype(np.float64) + nxt) / 2 * qmax).astype(F32)  # about the largest D for s
+        worst = np.zeros_like(s)
+        for k in range(-6, 7):                                   # fp32 values around it
+            D = hi.copy()
+            for _ in range(abs(k)):
+                D = np.nextafter(D, F32(np.inf) if k > 0 else F32(0)).astype(F32)
+            maps = np.float16((D / F32(qmax)).astype(F32)) == s16.view(np.float16)
+            r = np.nextafter((F32(1) / s).astype(F32), F32(np.inf)).astype(F32)
+            q = (D * r).astype(F32)
+            worst = np.where(maps & (q > worst), q, worst)
+        assert (worst > 0).all()
+        assert np.rint(worst).max() <= qmax, bits
+        assert (worst < qmax + 0.25).all()
