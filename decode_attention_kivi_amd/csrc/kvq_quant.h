@@ -21,17 +21,32 @@ struct GroupScale {
   float inv;              // v_rcp_f32(s), within 1 ulp of 1/s; 0 when s == 0 (all codes 0)
 };
 
+// fl(D / qmax) for qmax = 3, 15 or 255 without a division: q0 = fl(D c) with
+// c = fl(1/qmax), the residual r = D - q0 qmax (exact, one fma) and
+// fl(q0 + r c).  Equal to the correctly rounded quotient for every fp32 D in
+// [2^-24, 2^17) (tried exhaustively, one binade at a time, on the host: the
+// steps scale exactly with D's exponent there), 0 for D = 0 and +inf for
+// D = +inf (an infinite input; the residual would be NaN).
+template <int BITS>
+__device__ __forceinline__ float div_qmax(float D) {
+  constexpr float kQmax = float((1 << BITS) - 1);
+  constexpr float kInv = 1.0f / kQmax;
+  const float q0 = D * kInv;
+  const float r = __builtin_fmaf(-q0, kQmax, D);
+  const float q = __builtin_fmaf(r, kInv, q0);
+  return q0 == __builtin_inff() ? q0 : q;
+}
+
 template <int BITS>
 __device__ __forceinline__ GroupScale group_scale(float mn, float mx) {
 #pragma clang fp contract(off)
-  constexpr float kQmax = float((1 << BITS) - 1);
   GroupScale g;
   mn = mn + 0.0f;
   mx = mx + 0.0f;
-  g.s16 = f2h(__fdiv_rn(mx - mn, kQmax));
+  g.s16 = f2h(div_qmax<BITS>(mx - mn));   // mn, mx fp16 values: mx - mn is 0 or in [2^-24, 131008]
   g.z16 = f2h(mn);
   g.s = h2f(g.s16);
-  g.z = h2f(g.z16);
+  g.z = mn;                  // mn is an fp16 value: z16 holds it exactly
   g.inv = g.s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(g.s);
   return g;
 }
@@ -91,16 +106,16 @@ __device__ __forceinline__ uint32_t pk_max_f16(uint32_t a, uint32_t b) {
 }
 
 // fl(x - z) for x the fp16 in the low (HI false) or high half of w, in one
-// v_fma_mix_f32: x widened exactly, times one (1.0), plus -z (the source
-// negate modifier), one rounding -- the same value as converting x and
-// subtracting in fp32.
+// v_fma_mix_f32: x widened exactly, times one (1.0, held in a scalar
+// register), plus -z (the source negate modifier), one rounding -- the same
+// value as converting x and subtracting in fp32.
 template <bool HI>
 __device__ __forceinline__ float sub_half_f32(uint32_t w, float one, float z) {
   float r;
   if constexpr (HI)
-    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(one), "v"(z));
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "s"(one), "v"(z));
   else
-    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(one), "v"(z));
+    asm("v_fma_mix_f32 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "s"(one), "v"(z));
   return r;
 }
 

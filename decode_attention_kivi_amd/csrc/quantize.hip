@@ -97,6 +97,29 @@ __device__ __forceinline__ uint32_t rows_max(uint32_t x) {
   return pk_max_f16(b[0], b[1]);
 }
 
+// min / max over aligned groups of N consecutive lanes (N = 2 .. 16) of
+// packed fp16 pairs: DPP quad permutations, then half-row and row mirrors.
+template <int N>
+__device__ __forceinline__ uint32_t group_pk_min(uint32_t x) {
+  if (N >= 2) x = pk_min_f16(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+  if (N >= 4) x = pk_min_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+  if (N >= 8) x = pk_min_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+  if (N >= 16) x = pk_min_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
+  return x;
+}
+template <int N>
+__device__ __forceinline__ uint32_t group_pk_max(uint32_t x) {
+  if (N >= 2) x = pk_max_f16(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));
+  if (N >= 4) x = pk_max_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));
+  if (N >= 8) x = pk_max_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));
+  if (N >= 16) x = pk_max_f16(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// (low half of a, low half of b) and (high half of a, high half of b)
+__device__ __forceinline__ uint32_t lows(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t highs(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
 __device__ __forceinline__ uint32_t word(const uint4& x, int e) {
   return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
 }
@@ -123,17 +146,19 @@ __global__ void __launch_bounds__(256) quantize_keys_wave_kernel(QuantParams p) 
   // row indices first (one uniform branch), then the NL loads back to back:
   // a gather read inside the load loop would split it into blocks that each
   // wait for the previous load
-  int64_t row[NL];
+  const uint16_t* rp[NL];
   if (p.src_rows) {
 #pragma unroll
-    for (int k = 0; k < NL; ++k) row[k] = p.src_rows[j * G + k * RPI + r0];
+    for (int k = 0; k < NL; ++k) rp[k] = src + int64_t(p.src_rows[j * G + k * RPI + r0]) * p.src_row_stride;
   } else {
+    const int64_t step = int64_t(RPI) * p.src_row_stride;
+    rp[0] = src + int64_t(j * G + r0) * p.src_row_stride;
 #pragma unroll
-    for (int k = 0; k < NL; ++k) row[k] = j * G + k * RPI + r0;
+    for (int k = 1; k < NL; ++k) rp[k] = rp[k - 1] + step;
   }
   uint4 x[NL];
 #pragma unroll
-  for (int k = 0; k < NL; ++k) x[k] = load_row16(src + row[k] * p.src_row_stride);
+  for (int k = 0; k < NL; ++k) x[k] = load_row16(rp[k]);
   uint32_t mnw[4], mxw[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) mnw[e] = mxw[e] = word(x[0], e);
@@ -161,14 +186,15 @@ __global__ void __launch_bounds__(256) quantize_keys_wave_kernel(QuantParams p) 
     slow |= !scale_unclamped(gs[c].s16);
   }
   const float one = 1.0f;
-  uint8_t* out = p.codes + s * p.codes_stream_stride + c8 * BITS;   // 8 channels = BITS bytes
+  // row k's 8 channels (BITS bytes) at a constant offset from the lane's first row
+  uint8_t* out = p.codes + s * p.codes_stream_stride + c8 * BITS + int64_t(p.dst_tok + j * G + r0) * RB;
 #pragma unroll
   for (int k = 0; k < NL; ++k) {
     uint32_t ch[BITS / 2];
     float err = 0.0f;
     codes8_fast<BITS>(x[k], z, inv, one, err, ch);
     if (wave_any(slow || err >= kFastFar<BITS>)) codes8_exact<BITS>(x[k], gs, ch);   // uniform, rare
-    uint8_t* dst = out + int64_t(p.dst_tok + j * G + k * RPI + r0) * RB;
+    uint8_t* dst = out + k * RPI * RB;
     if constexpr (BITS == 2) *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(ch[0]);
     else if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(dst) = ch[0] | (ch[1] << 16);
     else *reinterpret_cast<uint2*>(dst) = make_uint2(ch[0] | (ch[1] << 16), ch[2] | (ch[3] << 16));
@@ -250,19 +276,18 @@ __global__ void __launch_bounds__(256) quantize_values_pairs_kernel(QuantParams 
     const int64_t P = P0 + u * PPI + pl;
     const int64_t i0 = 2 * P - p.dst_tok, i1 = i0 + 1;
     const bool va = i0 >= 0, vb = i1 < p.n_tok;   // meaningful only for P <= p_hi
-    // token extrema over the lane's 8 channels (packed pairs, then the two
-    // halves), then over the LPG lanes of the group
-    const uint32_t mna2 = pk_min_f16(pk_min_f16(xa[u].x, xa[u].y), pk_min_f16(xa[u].z, xa[u].w));
-    const uint32_t mxa2 = pk_max_f16(pk_max_f16(xa[u].x, xa[u].y), pk_max_f16(xa[u].z, xa[u].w));
-    const uint32_t mnb2 = pk_min_f16(pk_min_f16(xb[u].x, xb[u].y), pk_min_f16(xb[u].z, xb[u].w));
-    const uint32_t mxb2 = pk_max_f16(pk_max_f16(xb[u].x, xb[u].y), pk_max_f16(xb[u].z, xb[u].w));
-    const float mna = fminf(h2f(mna2 & 0xffffu), h2f(mna2 >> 16));
-    const float mxa = fmaxf(h2f(mxa2 & 0xffffu), h2f(mxa2 >> 16));
-    const float mnb = fminf(h2f(mnb2 & 0xffffu), h2f(mnb2 >> 16));
-    const float mxb = fmaxf(h2f(mxb2 & 0xffffu), h2f(mxb2 >> 16));
+    // token extrema on packed fp16 pairs: over the lane's 8 channels (its 4
+    // words, then the two halves, tokens a and b side by side in one word),
+    // then over the LPG lanes of the group
+    const uint32_t ma = pk_min_f16(pk_min_f16(xa[u].x, xa[u].y), pk_min_f16(xa[u].z, xa[u].w));
+    const uint32_t Ma = pk_max_f16(pk_max_f16(xa[u].x, xa[u].y), pk_max_f16(xa[u].z, xa[u].w));
+    const uint32_t mb = pk_min_f16(pk_min_f16(xb[u].x, xb[u].y), pk_min_f16(xb[u].z, xb[u].w));
+    const uint32_t Mb = pk_max_f16(pk_max_f16(xb[u].x, xb[u].y), pk_max_f16(xb[u].z, xb[u].w));
+    const uint32_t mn2 = group_pk_min<LPG>(pk_min_f16(lows(ma, mb), highs(ma, mb)));
+    const uint32_t mx2 = group_pk_max<LPG>(pk_max_f16(lows(Ma, Mb), highs(Ma, Mb)));
     GroupScale ga[8], gb[8];
-    ga[0] = group_scale<BITS>(group_min<LPG>(mna), group_max<LPG>(mxa));
-    gb[0] = group_scale<BITS>(group_min<LPG>(mnb), group_max<LPG>(mxb));
+    ga[0] = group_scale<BITS>(h2f(mn2 & 0xffffu), h2f(mx2 & 0xffffu));
+    gb[0] = group_scale<BITS>(h2f(mn2 >> 16), h2f(mx2 >> 16));
     float za[8], inva[8], zb[8], invb[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
