@@ -72,8 +72,11 @@ __global__ void __launch_bounds__(128) quantize_keys_kernel(QuantParams p) {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+typedef const __attribute__((address_space(1))) u32x4* global_u32x4_ptr;
+
+// 16 bytes of a source row (device memory: a global, not a flat, load)
 __device__ __forceinline__ uint4 load_row16(const uint16_t* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  const u32x4 v = __builtin_nontemporal_load((global_u32x4_ptr)p);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -170,14 +173,18 @@ __global__ void __launch_bounds__(256) quantize_keys_wave_kernel(QuantParams p) 
       mxw[e] = pk_max_f16(mxw[e], word(x[k], e));
     }
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    mnw[e] = rows_min<LPR>(mnw[e]);
+    mxw[e] = rows_max<LPR>(mxw[e]);
+  }
   GroupScale gs[8];
   float z[8], inv[8];
   bool slow = false;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const uint32_t mn = rows_min<LPR>(mnw[e]), mx = rows_max<LPR>(mxw[e]);
-    gs[2 * e] = group_scale<BITS>(h2f(mn & 0xffffu), h2f(mx & 0xffffu));
-    gs[2 * e + 1] = group_scale<BITS>(h2f(mn >> 16), h2f(mx >> 16));
+    gs[2 * e] = group_scale<BITS>(h2f(mnw[e] & 0xffffu), h2f(mxw[e] & 0xffffu));
+    gs[2 * e + 1] = group_scale<BITS>(h2f(mnw[e] >> 16), h2f(mxw[e] >> 16));
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) {

@@ -56,10 +56,9 @@ def _data(rng, n_streams, n, d, kind="normal"):
     return x.astype(np.float16)
 
 
-def _run(kvq, which, bits, G, d, n_tok, dst_tok, gather, kind="normal", seed=0):
+def _run(kvq, which, bits, G, d, n_tok, dst_tok, gather, kind="normal", seed=0, S=3):
     import torch
-    rng = np.random.default_rng([seed, which, bits, G, d, n_tok, dst_tok])
-    S = 3
+    rng = np.random.default_rng([seed, which, bits, G, d, n_tok, dst_tok, S])
     n_src = n_tok + 5
     x = _data(rng, S, n_src, d, kind)
     rows = rng.permutation(n_src)[:n_tok].astype(np.int32) if gather else np.arange(n_tok, dtype=np.int32)
@@ -74,7 +73,8 @@ def _run(kvq, which, bits, G, d, n_tok, dst_tok, gather, kind="normal", seed=0):
     codes = torch.zeros(S, cb, dtype=torch.uint8, device=dev)
     meta = torch.zeros(S, mb, dtype=torch.uint8, device=dev)
     rt = torch.from_numpy(rows).to(dev) if gather else None
-    print(f"quantize which={which} bits={bits} G={G} d={d} n={n_tok} dst={dst_tok} gather={gather}", flush=True)
+    print(f"quantize which={which} bits={bits} G={G} d={d} n={n_tok} dst={dst_tok} gather={gather} S={S}",
+          flush=True)
     kvq.kvq_quantize_append(which, bits, G, S, d, n_tok, xt, n_src * d, d, rt, codes, cb, meta, mb, dst_tok)
     torch.cuda.synchronize()
     got_c, got_m = codes.cpu().numpy(), meta.cpu().numpy()
@@ -107,6 +107,12 @@ def _run(kvq, which, bits, G, d, n_tok, dst_tok, gather, kind="normal", seed=0):
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_keys_bit_exact(kvq, bits, d, G):
     _run(kvq, kvq.KVQ_KEYS, bits, G, d, n_tok=2 * G, dst_tok=G, gather=False)
+
+
+@pytest.mark.parametrize("bits,d,G,gather", [(2, 128, 32, False), (8, 64, 64, True)])
+def test_keys_many_streams(kvq, bits, d, G, gather):
+    """8192 key groups in one launch (256 streams x 32 groups)."""
+    _run(kvq, kvq.KVQ_KEYS, bits, G, d, n_tok=32 * G, dst_tok=G, gather=gather, S=256)
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
