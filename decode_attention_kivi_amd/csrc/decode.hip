@@ -1444,15 +1444,16 @@ decode_kernel(const DecodeParams P) {
 
 // Cross-split merge, one workgroup per (b, hq):
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the stream's
-// workgroup partials, M the largest m_s.  The MT threads split the partials
-// (MT / D threads per channel); each folds its share with a running maximum,
-// CH partials at a time with every load of the chunk issued before any is
-// used (one memory round trip per chunk, not a max pass and then a sum
-// pass), and the shares of a channel meet in LDS.
-constexpr int MT = 1024;                     // merge threads: 64 partials in one round trip at d_h 128
-template <int D, bool PAGED>
-__global__ void __launch_bounds__(MT) merge_kernel(const DecodeParams P) {
-  constexpr int R = MT / D;                  // threads per output channel
+// workgroup partials, M the largest m_s.  R threads per channel (R * D
+// threads, R sized on the host to the partials: one 8-partial chunk per
+// thread where that covers them, at most 1024 threads) split the partials;
+// each folds its share with a running maximum, CH partials at a time with
+// every load of the chunk issued before any is used (one memory round trip
+// per chunk, not a max pass and then a sum pass), and the shares of a
+// channel meet in LDS.
+template <int D, bool PAGED, int R>
+__global__ void __launch_bounds__(R * D) merge_kernel(const DecodeParams P) {
+  constexpr int MT = R * D;
   constexpr int CH = 8;                      // partials per chunk and thread
   __shared__ float share[3][MT];
   const int tid = threadIdx.x;
@@ -1495,6 +1496,10 @@ __global__ void __launch_bounds__(MT) merge_kernel(const DecodeParams P) {
     }
     M = cm;
   }
+  if constexpr (R == 1) {
+    P.out[bhq * D + c] = O / L;
+    return;
+  }
   share[0][tid] = M;
   share[1][tid] = L;
   share[2][tid] = O;
@@ -1515,6 +1520,19 @@ __global__ void __launch_bounds__(MT) merge_kernel(const DecodeParams P) {
   }
 }
 
+// the merge with R threads per channel: enough 8-partial chunks for the
+// stream with the most workgroups in one round, at most 1024 threads
+template <int D, bool PAGED>
+hipError_t launch_merge(const DecodeParams& p, hipStream_t s) {
+  const dim3 grid(unsigned(int64_t(p.B) * p.Hq));
+  const int chunks = (p.wg_per_stream + 7) / 8;
+  if (chunks <= 1) hipLaunchKernelGGL((merge_kernel<D, PAGED, 1>), grid, dim3(D), 0, s, p);
+  else if (chunks <= 2) hipLaunchKernelGGL((merge_kernel<D, PAGED, 2>), grid, dim3(2 * D), 0, s, p);
+  else if (chunks <= 4) hipLaunchKernelGGL((merge_kernel<D, PAGED, 4>), grid, dim3(4 * D), 0, s, p);
+  else hipLaunchKernelGGL((merge_kernel<D, PAGED, 1024 / D>), grid, dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int D, int GQ, int NW, bool PAGED>
 hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
   const size_t lds = size_t(lds_bytes(decode_lds<D, GQ>(), NW));
@@ -1524,8 +1542,7 @@ hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
   hipLaunchKernelGGL((decode_kernel<D, GQ, NW, PAGED>), grid, dim3(NW * 64), lds, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.wg_per_stream == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<D, PAGED>), dim3(unsigned(int64_t(p.B) * p.Hq)), dim3(MT), 0, s, p);
-  return hipGetLastError();
+  return launch_merge<D, PAGED>(p, s);
 }
 
 template <int D, int GQ, bool PAGED>
