@@ -87,8 +87,8 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   for (int64_t s : {a->k_res_stride, a->v_res_stride})
     if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
 
-  // head blocks of up to 8 query heads per workgroup (grid z)
-  const int GQ = kvq::head_block(gq);
+  // head blocks of up to 4 query heads per workgroup (grid z)
+  const int GQ = kvq::decode_head_block(gq);
   const int64_t hblocks = (gq + GQ - 1) / GQ;
   if (kvq::decode_lds_bytes(D, GQ, 4) < 0) return KVQ_EUNSUPPORTED;
   const int64_t streams = int64_t(a->batch) * a->n_kv_heads;
@@ -268,7 +268,7 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   for (int64_t s : {a->k_res_stride, a->v_res_stride})
     if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
   const int D = a->d_h, G = a->group;
-  const int GQ = kvq::head_block(gq);     // head blocks of up to 8 query heads (grid z)
+  const int GQ = kvq::decode_head_block(gq);     // head blocks of up to 4 query heads (grid z)
   if (kvq::decode_lds_bytes(D, GQ, kvq::kWaves) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
   const kvq::PagedCost pc = kvq::paged_cost(D, G, a->bits);
   int wg_max = 1;
@@ -843,11 +843,13 @@ kvq_status kvq_kivi_step(kvq_kivi_cache* cache, int32_t batch, int32_t n_q_heads
   // fused append + attention in one launch when the last wave of each
   // stream's single workgroup holds every token the append writes
   // (tokens the append writes: the new token N-1, key and value, and the
-  // quantized value token with its pair partner)
+  // quantized value token with its pair partner).  With several head blocks
+  // (grid z) every block's last wave performs the same append: the same bytes
+  // from the same inputs, so each block reads what it wrote itself whatever
+  // the order of the other blocks' identical stores.
   int32_t first_written = n.n_kq + st.k_row;
   if (st.v_quant_row >= 0) first_written = std::min(first_written, st.v_dst_tok & ~1);
   const bool fused = !st.compact && !st.flush_keys && pl.p.wg_per_stream == 1 && pl.p.n_bounds > 0 &&
-                     pl.p.gq <= pl.GQ &&
                      pl.p.bounds[pl.p.waves_per_stream - 1] <= first_written;
   if (fused) {
     kvq::AppendParams& ap = pl.p.app;

@@ -1467,7 +1467,7 @@ __global__ void __launch_bounds__(R * D) merge_kernel(const DecodeParams P) {
   if constexpr (PAGED) {
     // the workgroups this stream used (the rest of its slots are not written)
     const int n_kq = P.lens[4 * b], n_vq = P.lens[4 * b + 1];
-    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], head_block(P.gq), kWaves);
+    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], decode_head_block(P.gq), kWaves);
   }
   const int c = tid % D, r = tid / D;
   float M = -INFINITY, L = 0.f, O = 0.f;
@@ -1557,7 +1557,6 @@ hipError_t launch_d(const DecodeParams& p, int GQ, hipStream_t s) {
     case 1: return launch_dg<D, 1, PAGED>(p, s);
     case 2: return launch_dg<D, 2, PAGED>(p, s);
     case 4: return launch_dg<D, 4, PAGED>(p, s);
-    case 8: return launch_dg<D, 8, PAGED>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1585,11 +1584,9 @@ int64_t decode_lds_bytes(int D, int GQ, int waves) {
     case 64 * 16 + 1: return lds_bytes(decode_lds<64, 1>(), waves);
     case 64 * 16 + 2: return lds_bytes(decode_lds<64, 2>(), waves);
     case 64 * 16 + 4: return lds_bytes(decode_lds<64, 4>(), waves);
-    case 64 * 16 + 8: return lds_bytes(decode_lds<64, 8>(), waves);
     case 128 * 16 + 1: return lds_bytes(decode_lds<128, 1>(), waves);
     case 128 * 16 + 2: return lds_bytes(decode_lds<128, 2>(), waves);
     case 128 * 16 + 4: return lds_bytes(decode_lds<128, 4>(), waves);
-    case 128 * 16 + 8: return lds_bytes(decode_lds<128, 8>(), waves);
     default: return -1;
   }
 }

@@ -13,10 +13,17 @@ constexpr int kWaves = 8;              // waves per decode workgroup
 constexpr int kMaxRuns = 8;            // runs per half of the cache
 constexpr int kLdsLimit = 160 * 1024;  // LDS of one gfx950 CU: the most a workgroup can use
 constexpr int kWaveAlign = 32;         // wave token ranges start at multiples of this
-// Query heads per kv head that one decode workgroup serves (its head block);
-// a kv head with more query heads takes several head blocks (grid z).
+// Query heads per kv head that one decode workgroup serves (its head block):
+// 1, 2 or 4; a kv head with more query heads takes several head blocks (grid
+// z), each reading the kv head's cache.  A block of 8 heads needs twice the
+// LDS per token (the logits and probabilities of 8 heads), which holds its
+// waves to 112 tokens and lets the per-wave fixed costs dominate: blocks of 4
+// read the cache two to eight times and still ran 1.2-1.6x faster at 7, 8, 16
+// and 32 query heads per kv head.
+__host__ __device__ constexpr int decode_head_block(int gq) { return gq <= 1 ? 1 : gq <= 2 ? 2 : 4; }
+// The PQ scores kernel's head block of gq query heads per kv head (the query
+// heads whose tables one workgroup holds): the next power of two, at most 8.
 constexpr int kMaxHeadBlock = 8;
-// The head block of gq query heads per kv head: the next power of two, at most 8.
 __host__ __device__ constexpr int head_block(int gq) {
   return gq <= 1 ? 1 : gq <= 2 ? 2 : gq <= 4 ? 4 : kMaxHeadBlock;
 }

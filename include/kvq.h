@@ -546,12 +546,12 @@ kvq_status kvq_kivi_step_workspace(const kvq_kivi_cache* cache, int32_t batch,
  *      groups and appended to the key run (kvq_quantize_append), r_k = 0;
  *   4. kvq_decode_attn of q over the updated cache (split chosen by the
  *      library) writes out.
- * When no compaction and no key flush is due, the kv heads have at most 8
- * query heads each, each stream fits one workgroup and every token the
- * append writes falls in the range of that workgroup's last wave, steps 2
- * and 4 run as one launch: that wave performs
- * the stream's append first, with the same arithmetic, so the result is the
- * same as the separate calls.
+ * When no compaction and no key flush is due, each stream fits one workgroup
+ * per head block (of up to 4 query heads) and every token the append writes
+ * falls in the range of that workgroup's last wave, steps 2 and 4 run as one
+ * launch: that wave performs the stream's append first, with the same
+ * arithmetic, so the result is the same as the separate calls (with several
+ * head blocks each block's last wave writes the same bytes).
  *   k_new, v_new  fp16 rows, stream s at element s * new_stride.
  *   q, out        fp16 [batch][n_q_heads][d_h] and fp32 [batch][n_q_heads][d_h];
  *                 n_streams = batch * n_kv_heads with n_kv_heads dividing

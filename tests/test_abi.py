@@ -147,7 +147,7 @@ def test_decode_needs_workspace():
 
 @pytest.mark.parametrize("hq,hkv", [(32, 1), (16, 2), (12, 1), (64, 4)])
 def test_any_head_ratio_plans(hq, hkv):
-    """More than 8 query heads per kv head run in head blocks of 8 (one more
+    """More than 4 query heads per kv head run in head blocks of 4 (one more
     grid dimension); the partial states still cover every query head."""
     a = _decode(batch=2, n_q_heads=hq, n_kv_heads=hkv)
     # N = 259, 64 tokens per workgroup: 5 workgroups per stream

@@ -89,7 +89,7 @@ def test_ragged_d64(kvq, hq, hkv):
 
 @pytest.mark.parametrize("hq,hkv,d", [(32, 1, 128), (24, 2, 64)])
 def test_ragged_many_query_heads(kvq, hq, hkv, d):
-    # more than 8 query heads per kv head: head blocks of 8
+    # more than 4 query heads per kv head: head blocks of 4
     run_paged([5, 300, 2000], hq, hkv, d, 32, 32, 2, 256, n_out=3, factor=8.0)
 
 
