@@ -122,13 +122,13 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
   }
   const int64_t cost_total = pieces.back().c0 + (N - pieces.back().t0) * pieces.back().cost;
 
-  // Each stream's N tokens are cut into kWaves * n_wg wave ranges of about
-  // equal cost, kWaves waves per workgroup.  The automatic choice takes the
-  // n_wg with the least (rounds of the grid over the chip) x (tokens per
-  // workgroup), ties to fewer workgroups (n_wg = 1: no partial states, no
-  // merge kernel), among the counts whose waves hold at least 64 tokens and
-  // at most wave_cap(GQ); split_tokens > 0 asks for workgroups of that many
-  // tokens (refused when a wave range would exceed wave_cap(GQ)).
+  // Each stream's N tokens are cut into nw * n_wg wave ranges of about
+  // equal cost, nw = decode_waves(D, GQ) waves per workgroup.  The automatic
+  // choice takes the n_wg with the least (rounds of the grid over the chip)
+  // x (tokens per workgroup), ties to fewer workgroups (n_wg = 1: no partial
+  // states, no merge kernel), among the counts whose waves hold at least 64
+  // tokens and at most wave_cap(GQ); split_tokens > 0 asks for workgroups of
+  // that many tokens (refused when a wave range would exceed wave_cap(GQ)).
   auto longest = [&](int64_t nws) {
     int64_t worst = 0;
     int prev = 0;
@@ -139,34 +139,34 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
     }
     return worst;
   };
+  const int nw = kvq::decode_waves(D, GQ);
   int64_t n_wg;
   if (a->split_tokens > 0) {
     n_wg = (N + a->split_tokens - 1) / a->split_tokens;
     if (n_wg > (int64_t(1) << 20)) return KVQ_EUNSUPPORTED;
-    if (longest(kvq::kWaves * n_wg) > kvq::wave_cap(GQ)) return KVQ_EUNSUPPORTED;
+    if (longest(nw * n_wg) > kvq::wave_cap(GQ)) return KVQ_EUNSUPPORTED;
   } else {
     const int64_t fill = 256 * kvq::decode_wgs_per_cu(GQ);   // workgroups resident at once
-    int64_t n_min = std::max<int64_t>(1, (N + int64_t(kvq::kWaves) * kvq::wave_tokens(GQ) * 3 / 2 - 1) /
-                                             (int64_t(kvq::kWaves) * kvq::wave_tokens(GQ) * 3 / 2));
-    while (longest(kvq::kWaves * n_min) > kvq::wave_cap(GQ)) {
+    int64_t n_min = std::max<int64_t>(1, (N + int64_t(nw) * kvq::wave_tokens(GQ) * 3 / 2 - 1) /
+                                             (int64_t(nw) * kvq::wave_tokens(GQ) * 3 / 2));
+    while (longest(nw * n_min) > kvq::wave_cap(GQ)) {
       if (n_min >= (int64_t(1) << 20)) return KVQ_EUNSUPPORTED;
       n_min += std::max<int64_t>(1, n_min / 8);
     }
     n_wg = n_min;
     double best = -1;
     for (int64_t c = n_min; c <= std::min(8 * n_min, n_min + 256); ++c) {
-      if (c > n_min && (N + kvq::kWaves * c - 1) / (kvq::kWaves * c) < 64) break;
+      if (c > n_min && (N + nw * c - 1) / (nw * c) < 64) break;
       const double rounds = double((streams * hblocks * c + fill - 1) / fill);
       const double t = rounds * double(N) / double(c);
       if (best >= 0 && t >= best * (1 - 1e-9)) continue;
       // the wave-length check walks every wave bound: only for a candidate
       // that would be taken
-      if (c > n_min && longest(kvq::kWaves * c) > kvq::wave_cap(GQ)) continue;
+      if (c > n_min && longest(nw * c) > kvq::wave_cap(GQ)) continue;
       best = t;
       n_wg = c;
     }
   }
-  const int nw = kvq::kWaves;
   const int64_t nws = nw * n_wg;
   if (kvq::decode_lds_bytes(D, GQ, nw) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
 
@@ -269,7 +269,8 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
     if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
   const int D = a->d_h, G = a->group;
   const int GQ = kvq::decode_head_block(gq);     // head blocks of up to 4 query heads (grid z)
-  if (kvq::decode_lds_bytes(D, GQ, kvq::kWaves) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
+  const int nw = kvq::decode_waves(D, GQ);
+  if (kvq::decode_lds_bytes(D, GQ, nw) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
   const kvq::PagedCost pc = kvq::paged_cost(D, G, a->bits);
   int wg_max = 1;
   bool any_kres = false, any_vres = false;
@@ -284,7 +285,7 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
     if ((nk + a->page_tokens - 1) / a->page_tokens > a->max_pages) return KVQ_EINVAL;
     any_kres |= rk > 0;
     any_vres |= rv > 0;
-    const int nwg = kvq::paged_wgs(pc, int(nk), int(nv), int(N), GQ, kvq::kWaves);
+    const int nwg = kvq::paged_wgs(pc, int(nk), int(nv), int(N), GQ, nw);
     wg_max = std::max(wg_max, nwg);
     seq_wgs[b] = nwg;
     order.emplace_back(-double(kvq::paged_total(pc, int(nk), int(nv), int(N))) / nwg, b);
@@ -309,7 +310,7 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   p.G = G;
   p.lg_g = G == 32 ? 5 : G == 64 ? 6 : 7;
   p.gq = gq;
-  p.waves_per_wg = kvq::kWaves;
+  p.waves_per_wg = nw;
   p.wg_per_stream = wg_max;
   p.scale_log2 = a->sm_scale * 1.4426950408889634f;
   p.pages = static_cast<const uint8_t*>(a->pages);

@@ -34,9 +34,14 @@
 namespace kvq {
 namespace {
 
-// Loads per batch in the value streaming loops (two batches in flight): grouped
-// heads run at two waves per SIMD whatever their register count, so they
-// keep twice the loads in flight.
+// Waves per SIMD of the decode kernel: four for one query head per kv head,
+// three for head blocks of 4 at d_h = 128 (168 VGPRs), two otherwise.
+constexpr int decode_waves_per_simd(int D, int GQ) { return GQ == 1 ? 4 : decode_waves(D, GQ) == 12 ? 3 : 2; }
+// Load batches in flight per wave in the streaming loops: three at two waves
+// per SIMD (registers to spare), two otherwise.
+template <int D, int GQ> constexpr int stream_batches() { return decode_waves_per_simd(D, GQ) == 2 ? 3 : 2; }
+// Loads per batch in the value pair loop (two batches in flight): grouped
+// heads at two waves per SIMD keep more loads in flight per wave.
 template <int GQ> constexpr int value_batch() { return GQ == 1 ? 2 : 3; }
 
 // Make this wave's LDS writes visible to its own later LDS reads.  LDS
@@ -122,8 +127,9 @@ __device__ __forceinline__ typename LoadType<W>::T bload(Rsrc r, uint32_t off) {
 }
 
 struct WaveLds {
-  float* logit;      // [GQ][LT] logits by token slot; later the value row sums
+  float* logit;      // [GQ][LT] logits by token slot
   uint16_t* p16;     // [GQ][LT] fp16 probabilities, zero outside the wave's tokens
+  float* red;        // the value reduction's row sums (after the softmax)
   uint32_t* qs;      // [NGB][QBLK] A blocks (q*s hi/lo rows) of one load batch
   float* bias;       // [NGB][GQ] key biases per (group, head), after the largest A blocks
   float* ow;         // [GQ][D+2] (m, l, o[D]) of the wave (aliases qs/bias)
@@ -136,7 +142,13 @@ __device__ __forceinline__ WaveLds carve_wave(unsigned char* smem, int wave) {
   unsigned char* base = smem + lay.block + int64_t(wave) * lay.wave;
   WaveLds W;
   W.logit = reinterpret_cast<float*>(base);
-  W.p16 = reinterpret_cast<uint16_t*>(base + lay.logit);
+  if constexpr (p16_over_logits(GQ)) {
+    W.p16 = reinterpret_cast<uint16_t*>(base);
+    W.red = W.logit + GQ * wave_slots(GQ) / 2;
+  } else {
+    W.p16 = reinterpret_cast<uint16_t*>(base + lay.logit);
+    W.red = W.logit;
+  }
   W.qs = reinterpret_cast<uint32_t*>(base + lay.logit + lay.p16);
   W.bias = reinterpret_cast<float*>(W.qs + QSMAX);
   W.ow = reinterpret_cast<float*>(base + lay.logit + lay.p16);
@@ -386,7 +398,7 @@ __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const Wave
 
   Batch A, Bb, Cc;
   issue(A, 0);
-  if constexpr (GQ > 1) issue(Bb, NB);
+  if constexpr (stream_batches<D, GQ>() == 3) issue(Bb, NB);
   // q of the lane's meta pair for the GQ heads (global, cached), loaded while
   // the first batch is in flight; padded heads are zero
 #pragma unroll
@@ -394,9 +406,7 @@ __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const Wave
     const uint32_t q2 = h < nh ? uint32_t(qg[h * D + clo]) | (uint32_t(qg[h * D + chi]) << 16) : 0u;
     qk[h] = as_h2(q2) * as_h2(0x1C001C00u);                       // * 2^-8, exact
   }
-  if constexpr (GQ > 1) {
-    // grouped heads run two waves per SIMD with registers to spare: three
-    // batches in flight
+  if constexpr (stream_batches<D, GQ>() == 3) {
     for (int i0 = 0; i0 < n_items; i0 += 3 * NB) {
       progress_prio(0, slot0 + i0 * TPI, n_wave);
       issue(Cc, i0 + 2 * NB);
@@ -633,7 +643,7 @@ __device__ __forceinline__ void keys_fp16(const DecodeParams& P, const WaveLds& 
 // Cross-lane reduction of value partials.  Lane l holds x[0..NX) for chunk
 // c = l % CPL; lanes with equal l % CPL are summed.  Within each row of 16
 // lanes the sums come from DPP rotations; the four rows' sums are left in
-// W.logit (dead by now) as red[(row * CPL + c) * NX + j].
+// W.red as red[(row * CPL + c) * NX + j].
 template <int CPL, int NX>
 __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], int lane) {
 #pragma unroll
@@ -646,7 +656,7 @@ __device__ __forceinline__ void reduce_rows(const WaveLds& W, float (&x)[NX], in
     x[j] = y;
   }
   // lanes (lane % 16) < CPL now hold their row's sums
-  float* red = W.logit;
+  float* red = W.red;
   const int row = lane >> 4, c = lane & 15;
   if (c < CPL) {
 #pragma unroll
@@ -786,7 +796,7 @@ __device__ __forceinline__ void values_quantized(const DecodeParams& P, const Wa
 #pragma unroll
     for (int hh = 0; hh < HPP; ++hh) {
       reduce_rows<CPP, NX>(W, acc[hh], lane);
-      const float* red = W.logit;
+      const float* red = W.red;
 #pragma unroll
       for (int k = 0; k < D / 64; ++k) {
         const int ch = lane + 64 * k;
@@ -844,7 +854,7 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
   constexpr int NP = UP::NP;              // channels per word
   static_assert(WPL * NP == 8, "eight channels per lane");
   constexpr int NAB = (GQ + 3) / 4;       // A blocks for 32-channel groups
-  constexpr int NBV = BITS == 2 ? 2 : 1;  // steps per load batch (three batches in flight)
+  constexpr int NBV = BITS == 2 ? 2 : 1;  // steps per load batch
   const UP unpack;
   const int lg_ng = 7 - lg_g;
   const int NG = 1 << lg_ng;
@@ -951,7 +961,7 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
 
   Batch A, Bb, Cc;
   issue(A, 0);
-  issue(Bb, NBV);
+  if constexpr (stream_batches<D, GQ>() == 3) issue(Bb, NBV);
   uint16_t keep[GQ];
   // the probabilities are made while the first loads are in flight
   if (!softmax_done) softmax();
@@ -965,18 +975,28 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
     }
     wave_lds_sync();
   }
-  for (int s0 = 0; s0 < n_steps; s0 += 3 * NBV) {
-    progress_prio(1, 2 * (ps0 + 16 * s0), n_wave);
-    issue(Cc, s0 + 2 * NBV);
-    consume(A, s0);
-    issue(A, s0 + 3 * NBV);
-    if (s0 + NBV < n_steps) consume(Bb, s0 + NBV);
-    issue(Bb, s0 + 4 * NBV);
-    if (s0 + 2 * NBV < n_steps) consume(Cc, s0 + 2 * NBV);
+  if constexpr (stream_batches<D, GQ>() == 3) {
+    for (int s0 = 0; s0 < n_steps; s0 += 3 * NBV) {
+      progress_prio(1, 2 * (ps0 + 16 * s0), n_wave);
+      issue(Cc, s0 + 2 * NBV);
+      consume(A, s0);
+      issue(A, s0 + 3 * NBV);
+      if (s0 + NBV < n_steps) consume(Bb, s0 + NBV);
+      issue(Bb, s0 + 4 * NBV);
+      if (s0 + 2 * NBV < n_steps) consume(Cc, s0 + 2 * NBV);
+    }
+  } else {
+    for (int s0 = 0; s0 < n_steps; s0 += 2 * NBV) {
+      progress_prio(1, 2 * (ps0 + 16 * s0), n_wave);
+      issue(Bb, s0 + NBV);
+      consume(A, s0);
+      issue(A, s0 + 2 * NBV);
+      if (s0 + NBV < n_steps) consume(Bb, s0 + NBV);
+    }
   }
 
-  // row sums over the four k-blocks, then to LDS (W.logit is free by now)
-  float* red = W.logit;                   // [NAB][sum p*s of 16 rows | sum p*z of 16 rows]
+  // row sums over the four k-blocks, then to LDS
+  float* red = W.red;                     // [NAB][sum p*s of 16 rows | sum p*z of 16 rows]
 #pragma unroll
   for (int ab = 0; ab < NAB; ++ab) {
     float x = srow[ab], y = zrow[ab];
@@ -1079,7 +1099,7 @@ __device__ __forceinline__ void values_fp16(const DecodeParams& P, const WaveLds
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
     reduce_rows<CPR, 8>(W, acc[h], lane);
-    const float* red = W.logit;
+    const float* red = W.red;
 #pragma unroll
     for (int k = 0; k < D / 64; ++k) {
       const int ch = lane + 64 * k;
@@ -1096,10 +1116,11 @@ __device__ __forceinline__ void values_fp16(const DecodeParams& P, const WaveLds
 // ---------------------------------------------------------------------------
 // Four waves per SIMD (<= 128 VGPRs) for one query head per kv head: 16
 // resident waves per CU (two workgroups) keep enough loads in flight to
-// cover HBM latency.  Grouped heads do GQ times the arithmetic per byte and
-// get 256 VGPRs (one workgroup per CU).
+// cover HBM latency.  Grouped heads do GQ times the arithmetic per byte:
+// two heads get 256 VGPRs (one 8-wave workgroup per CU), head blocks of 4
+// three waves per SIMD at 168 VGPRs (one 12-wave workgroup per CU).
 template <int D, int GQ, int NW, bool PAGED>
-__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(GQ == 1 ? 4 : 2)))
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(D, GQ))))
 decode_kernel(const DecodeParams P) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int LT = wave_slots(GQ);
@@ -1300,6 +1321,10 @@ decode_kernel(const DecodeParams P) {
         }
         *reinterpret_cast<uint2*>(W.p16 + h * LT + s) =
             make_uint2(p16[0] | (p16[1] << 16), p16[2] | (p16[3] << 16));
+        // probabilities over the logits: lane l's store lands on logits that
+        // other lanes read in this or an earlier step, so no LDS access
+        // moves across a step (a wave's LDS accesses run in order)
+        if constexpr (p16_over_logits(GQ)) asm volatile("" ::: "memory");
       }
       mh[h] = mx;
       lh[h] = wave_sum64(sum);
@@ -1467,7 +1492,8 @@ __global__ void __launch_bounds__(R * D) merge_kernel(const DecodeParams P) {
   if constexpr (PAGED) {
     // the workgroups this stream used (the rest of its slots are not written)
     const int n_kq = P.lens[4 * b], n_vq = P.lens[4 * b + 1];
-    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], decode_head_block(P.gq), kWaves);
+    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], decode_head_block(P.gq),
+                    decode_waves(D, decode_head_block(P.gq)));
   }
   const int c = tid % D, r = tid / D;
   float M = -INFINITY, L = 0.f, O = 0.f;
@@ -1547,8 +1573,8 @@ hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
 
 template <int D, int GQ, bool PAGED>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t s) {
-  if (p.waves_per_wg != kWaves) return hipErrorInvalidValue;
-  return launch_dgw<D, GQ, kWaves, PAGED>(p, s);
+  if (p.waves_per_wg != decode_waves(D, GQ)) return hipErrorInvalidValue;
+  return launch_dgw<D, GQ, decode_waves(D, GQ), PAGED>(p, s);
 }
 
 template <int D, bool PAGED>

@@ -28,16 +28,25 @@ __host__ __device__ constexpr int head_block(int gq) {
   return gq <= 1 ? 1 : gq <= 2 ? 2 : gq <= 4 ? 4 : kMaxHeadBlock;
 }
 
+// Waves per decode workgroup: 8, or 12 for head blocks of 4 at d_h = 128
+// (three waves per SIMD in one workgroup per CU: their registers fit 168
+// VGPRs, and their probabilities overwrite the logits, so 12 waves' LDS
+// fits 160 KB).
+__host__ __device__ constexpr int decode_waves(int D, int GQ) { return GQ >= 4 && D >= 128 ? 12 : kWaves; }
 // Target tokens per wave; a wave may get up to wave_cap(GQ) tokens.  Larger
 // GQ needs more LDS per token (logits and probabilities of GQ heads).  With
 // one query head per kv head two workgroups share a CU (48 KB of LDS each);
-// grouped heads run one 8-wave workgroup per CU (their registers), so its
-// waves take the longest ranges whose LDS still fits the CU's 160 KB
-// (96 / 156 / 155 KB at d128 for 2 / 4 / 8 heads): every range restart
+// grouped heads run one workgroup per CU (their registers), so its waves
+// take the longest ranges whose LDS still fits the CU's 160 KB (96 KB at
+// d128 for 2 heads, 156 KB for 12 waves of 4 heads): every range restart
 // drains a wave's load pipeline, and short waves are all restarts.
-__host__ __device__ constexpr int wave_tokens(int GQ) { return GQ <= 2 ? 512 : GQ == 4 ? 384 : 112; }
+__host__ __device__ constexpr int wave_tokens(int GQ) { return GQ <= 2 ? 512 : 320; }
 // workgroups per CU of the decode kernel (its register budget)
 __host__ __device__ constexpr int decode_wgs_per_cu(int GQ) { return GQ == 1 ? 2 : 1; }
+// Head blocks of 4 keep the fp16 probabilities [GQ][LT] in the first half of
+// the logit area (each head's softmax writes over logits already consumed)
+// and the value reduction's row sums after them.
+__host__ __device__ constexpr bool p16_over_logits(int GQ) { return GQ >= 4; }
 __host__ __device__ constexpr int wave_cap(int GQ) { return wave_tokens(GQ) * 3 / 2 + kWaveAlign; }
 // token slots per wave in LDS: the cap plus 32, since the streaming loops
 // read and write whole items (up to 32 tokens) past a range's last token
@@ -94,10 +103,12 @@ __host__ __device__ constexpr int64_t kBiasMax() {
 //   logit  fp32 [GQ][LT]  logits by token slot; reused afterwards for the
 //                          row sums of the value reduction (at most 640 floats)
 //   p16    fp16 [GQ][LT]  probabilities, zero outside the wave's tokens
+//                          (head blocks of 4: over the first half of logit,
+//                          the row sums after them)
 //   area   A blocks (q*s hi/lo rows) and biases of the key groups of one load batch;
 //          afterwards the wave's (m, l, o[D]) per head
 struct DecodeLds {
-  int64_t block, logit, p16, area, wave, total;   // total: for kWaves waves
+  int64_t block, logit, p16, area, wave, total;   // total: for decode_waves(D, GQ) waves
 };
 __host__ __device__ constexpr int64_t lds_bytes(const DecodeLds& l, int waves) {
   return l.block + waves * l.wave;
@@ -106,13 +117,13 @@ template <int D, int GQ>
 __host__ __device__ constexpr DecodeLds decode_lds() {
   const int64_t lt = wave_slots(GQ);
   const int64_t block = 0;
-  const int64_t logit = round16(cmax(int64_t(GQ) * lt * 4, 640 * 4));
-  const int64_t p16 = round16(int64_t(GQ) * lt * 2);
+  const int64_t logit = round16(cmax(int64_t(GQ) * lt * 4, (p16_over_logits(GQ) ? GQ * lt / 2 : 0) * 4 + 640 * 4));
+  const int64_t p16 = p16_over_logits(GQ) ? 0 : round16(int64_t(GQ) * lt * 2);
   // A blocks and zero block, then the per-(group, head) biases (see carve_wave)
   const int64_t qs = (kQsMax<D, GQ>() + kBiasMax<D, GQ>()) * 4;
   const int64_t area = round16(cmax(qs, int64_t(GQ) * (D + 2) * 4));
   const int64_t wave = logit + p16 + area;
-  return DecodeLds{block, logit, p16, area, wave, block + kWaves * wave};
+  return DecodeLds{block, logit, p16, area, wave, block + decode_waves(D, GQ) * wave};
 }
 
 struct Run {            // device copy of kvq_segment
@@ -179,7 +190,7 @@ struct DecodeParams {
   int32_t n_tok;                        // N, tokens attended per stream
   int32_t n_kq, n_vq;                   // tokens held in key runs / value runs
   int32_t waves_per_stream;             // a multiple of waves_per_wg
-  int32_t waves_per_wg;                 // kWaves
+  int32_t waves_per_wg;                 // decode_waves(D, head block)
   int32_t wg_per_stream;
   float scale_log2;                     // sm_scale * log2(e)
   int32_t n_k_runs, n_v_runs;

@@ -340,9 +340,9 @@ def test_paged_rejects(lengths, kw, code):
 
 def test_split_plan_fills_the_chip_once():
     # GQA long context (4 sequences, 32 q / 8 kv heads, 32769 tokens, G64):
-    # 32 streams of 4 query heads run one 8-wave workgroup per CU with waves
-    # of up to 608 tokens; 8 workgroups per stream (256 = one round over 256
-    # CUs) beat 11 (352: two rounds) -- workspace = 32 * 8 partial states
+    # 32 streams of 4 query heads run one 12-wave workgroup per CU with waves
+    # of up to 512 tokens; 8 workgroups per stream (256 = one round over 256
+    # CUs) beat 9 to 16 (two rounds) -- workspace = 32 * 8 partial states
     a = _decode(batch=4, n_q_heads=32, n_kv_heads=8, group=64, k_segs=[(2, 0, 32768, 0, 0)],
                 v_segs=[(2, 0, 32641, 0, 0)], n_k_res=1, n_v_res=128, split_tokens=0)
     assert kvq.kvq_decode_attn_workspace(a) == 32 * 8 * 4 * 130 * 4
