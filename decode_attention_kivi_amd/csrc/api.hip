@@ -272,6 +272,11 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   const int nw = kvq::decode_waves(D, GQ);
   if (kvq::decode_lds_bytes(D, GQ, nw) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
   const kvq::PagedCost pc = kvq::paged_cost(D, G, a->bits);
+  // workgroups per stream: waves of up to wave_cap(GQ) - kWaveAlign tokens
+  // of the cheapest kind (the longest ranges the LDS slots hold: fewer
+  // workgroups and wave restarts; 78.4 against 79.6-80.9 us at 512 tokens
+  // on the ragged bench batch, 88.7 at 256, 109 at 128)
+  const int wt = kvq::wave_cap(GQ) - kvq::kWaveAlign;
   int wg_max = 1;
   bool any_kres = false, any_vres = false;
   std::vector<std::pair<double, int>> order;      // (-cost per workgroup, sequence)
@@ -285,7 +290,7 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
     if ((nk + a->page_tokens - 1) / a->page_tokens > a->max_pages) return KVQ_EINVAL;
     any_kres |= rk > 0;
     any_vres |= rv > 0;
-    const int nwg = kvq::paged_wgs(pc, int(nk), int(nv), int(N), GQ, nw);
+    const int nwg = kvq::paged_wgs(pc, int(nk), int(nv), int(N), wt, nw);
     wg_max = std::max(wg_max, nwg);
     seq_wgs[b] = nwg;
     order.emplace_back(-double(kvq::paged_total(pc, int(nk), int(nv), int(N))) / nwg, b);
@@ -324,6 +329,7 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
   p.pg_vcodes_off = int32_t(L.vcodes_off);
   p.pg_vmeta_off = int32_t(L.vmeta_off);
   p.bits = a->bits;
+  p.pg_wave_tokens = wt;
   if (a->batch <= kvq::kMaxSched) {
     // heaviest workgroups first (longest-processing-time order), so the
     // longest sequences do not start last; stable for equal costs

@@ -1156,7 +1156,7 @@ decode_kernel(const DecodeParams P) {
     n_vq = P.lens[4 * b + 1];
     N = n_kq + P.lens[4 * b + 2];
     const PagedCost pc = paged_cost(D, P.G, P.bits);
-    const int nwg = paged_wgs(pc, n_kq, n_vq, N, GQ, NW);
+    const int nwg = paged_wgs(pc, n_kq, n_vq, N, P.pg_wave_tokens, NW);
     if (wg >= nwg) return;                   // the whole workgroup, before any barrier
     a = paged_bound(pc, n_kq, n_vq, N, gw, nwg * NW);
     e = paged_bound(pc, n_kq, n_vq, N, gw + 1, nwg * NW);
@@ -1492,7 +1492,7 @@ __global__ void __launch_bounds__(R * D) merge_kernel(const DecodeParams P) {
   if constexpr (PAGED) {
     // the workgroups this stream used (the rest of its slots are not written)
     const int n_kq = P.lens[4 * b], n_vq = P.lens[4 * b + 1];
-    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], decode_head_block(P.gq),
+    nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], P.pg_wave_tokens,
                     decode_waves(D, decode_head_block(P.gq)));
   }
   const int c = tid % D, r = tid / D;

@@ -225,6 +225,7 @@ struct DecodeParams {
   const int32_t* lens;
   int64_t page_bytes, head_bytes;
   int32_t page_tokens, max_pages, pg_kmeta_off, pg_vcodes_off, pg_vmeta_off, bits;
+  int32_t pg_wave_tokens;              // paged_wgs's wt (<= wave_cap(GQ) - kWaveAlign)
   // Paged schedule (sched_n > 0, batch <= kMaxSched): a 1-D grid of exactly
   // the workgroups the streams need, heaviest workgroups first.  Sequence
   // sched_seq[k] owns grid workgroups sched_start[k] .. sched_start[k+1]-1:
@@ -250,10 +251,11 @@ __host__ __device__ inline int64_t paged_total(const PagedCost& c, int n_kq, int
   return int64_t(n_vq) * c.both_q + int64_t(n_kq - n_vq) * c.key_q + int64_t(N - n_kq) * c.both_16;
 }
 // Workgroups of a paged stream: enough that a wave's share of the stream's
-// bytes is at most wave_tokens(GQ) tokens of the cheapest kind, so no wave
-// range exceeds wave_cap(GQ) (the starts are rounded down by < 32).
-__host__ __device__ inline int paged_wgs(const PagedCost& c, int n_kq, int n_vq, int N, int GQ, int NW) {
-  const int64_t per_wg = int64_t(NW) * wave_tokens(GQ) * c.both_q;
+// bytes is at most wt tokens of the cheapest kind; with wt <= wave_cap(GQ) -
+// kWaveAlign no wave range exceeds wave_cap(GQ) (the starts are rounded
+// down by < kWaveAlign).
+__host__ __device__ inline int paged_wgs(const PagedCost& c, int n_kq, int n_vq, int N, int wt, int NW) {
+  const int64_t per_wg = int64_t(NW) * wt * c.both_q;
   const int64_t t = paged_total(c, n_kq, n_vq, N);
   const int64_t w = (t + per_wg - 1) / per_wg;
   return int(w < 1 ? 1 : w);

@@ -303,11 +303,14 @@ def test_paged_workspace_sizes():
     # (n_kq, n_vq, n_k_res, n_v_res); one workgroup per stream -> no workspace
     a, lens = _paged([[512, 385, 1, 128], [0, 0, 5, 5]])
     assert kvq.kvq_decode_attn_paged_workspace(a) == 0
-    # with 2 query heads per kv head an 8-wave workgroup covers 8 * 512 tokens
-    # of 2-bit keys and values (96 bytes each); 5000 such tokens plus 120
-    # residual-value tokens (304 bytes) need two: the workspace holds
-    # B * Hkv * 2 partial states of gq * (d + 2) floats
+    # with 2 query heads per kv head an 8-wave workgroup covers 8 * 768
+    # tokens of 2-bit keys and values (96 bytes each; waves up to the LDS
+    # cap of 800 slots less the 32-token alignment): 5000 such tokens plus
+    # 120 residual-value tokens (304 bytes) fit one, 6024 plus 120 need two:
+    # the workspace holds B * Hkv * 2 partial states of gq * (d + 2) floats
     a, lens = _paged([[5120, 5000, 0, 120], [32, 0, 0, 32]], max_pages=20)
+    assert kvq.kvq_decode_attn_paged_workspace(a) == 0
+    a, lens = _paged([[6144, 6024, 0, 120], [32, 0, 0, 32]], max_pages=24)
     assert kvq.kvq_decode_attn_paged_workspace(a) == 2 * 2 * 2 * 2 * 130 * 4
     a.workspace, a.workspace_bytes = A, 100
     with pytest.raises(KvqError) as e:
