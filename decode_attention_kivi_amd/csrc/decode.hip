@@ -260,6 +260,8 @@ __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const Wave
   // LDS dword of the lane's A row in block (m = 0, kb) of a group.  Rows past
   // 2*GQ repeat row col % (2*GQ): they only feed D rows that are never read.
   const int a_pos = kb * BS + (col & (ROWS - 1)) * 4;
+  // the lane's logit slots (token col of each item) for heads 2kb and 2kb + 1
+  float* const lgs = W.logit + (2 * kb) * LT + slot0 + col;
 
   // meta role of the lane: pair pi of a row of group gsub (of the meta
   // iteration): k-block pj, pair pp of it
@@ -389,9 +391,8 @@ __device__ __forceinline__ void keys_quantized(const DecodeParams& P, const Wave
         d = __builtin_amdgcn_mfma_f32_16x16x32_f16(am[m], __builtin_bit_cast(half8_t, bm), d, 0, 0, 0);
       }
       // lane (kb, col) holds rows 4kb .. 4kb+3: heads 2kb and 2kb + 1
-      const int slot = slot0 + i * TPI + col;
-      if (2 * kb < GQ) W.logit[(2 * kb) * LT + slot] = (d[0] + b0) + d[1];
-      if (2 * kb + 1 < GQ) W.logit[(2 * kb + 1) * LT + slot] = (d[2] + b1) + d[3];
+      if (2 * kb < GQ) lgs[i * TPI] = (d[0] + b0) + d[1];
+      if (2 * kb + 1 < GQ) lgs[LT + i * TPI] = (d[2] + b1) + d[3];
     }
     wave_lds_sync();                         // the next batch rewrites the A blocks
   };
@@ -749,9 +750,12 @@ __device__ __forceinline__ void values_quantized(const DecodeParams& P, const Wa
         uint32_t ps[HPP];
 #pragma unroll
         for (int hh = 0; hh < HPP; ++hh) {
-          // pair np (a zero slot, or a probability of the next piece whose
-          // meta here reads as zero) stands in for every pair past the range
-          const half2_t p2 = as_h2(pp[(hp + hh) * (LT / 2) + min((i0 + u) * PPI + my_p, np)]);
+          // pairs past the range hold probabilities of later slots or zeros
+          // (finite) against meta that reads as zero; with more than 16
+          // pairs per instruction they could pass the wave's slots, so pair
+          // np (a zero slot, or a probability of the next piece) stands in
+          const int pi = (i0 + u) * PPI + my_p;
+          const half2_t p2 = as_h2(pp[(hp + hh) * (LT / 2) + (PPI > 16 ? min(pi, np) : pi)]);
           const half2_t psh = p2 * s2;
           ps[hh] = as_u32(psh);
           acc[hh][CPCV] = __builtin_amdgcn_fdot2(psh, one2, acc[hh][CPCV], false);
@@ -872,9 +876,11 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
   const uint32_t m_off = uint32_t((4 * kb * NG + ga) * 8);
   const uint32_t* pp = reinterpret_cast<const uint32_t*>(W.p16) + ps0;
   const half2_t one2 = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
-  int prow[NAB];                          // p16 dword row of the lane's A-row head (padded rows repeat a head)
+  // the lane's p16 pairs: the row of its A-row head (padded rows repeat a
+  // head) from the first pair of its k-block
+  const uint32_t* prow[NAB];
 #pragma unroll
-  for (int ab = 0; ab < NAB; ++ab) prow[ab] = min(ab * hpb + (col >> lg_ng), GQ - 1) * (LT / 2);
+  for (int ab = 0; ab < NAB; ++ab) prow[ab] = pp + min(ab * hpb + (col >> lg_ng), GQ - 1) * (LT / 2) + 4 * kb;
 
   float4_t acc[NAB][8];
   float srow[NAB], zrow[NAB];
@@ -920,7 +926,7 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
 #pragma unroll
     for (int v = 0; v < NBV; ++v) {
       if (s0 + v >= n_steps) continue;    // uniform
-      const int pb = 16 * (s0 + v) + 4 * kb;
+      const int pb = 16 * (s0 + v);       // the step's first pair
       uint32_t s2[4], z2[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -934,9 +940,10 @@ __device__ __forceinline__ void values_quantized_mfma(int lg_g, const WaveLds& W
         uint32_t aw[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          // pair np (zero, or a probability whose meta here reads as zero)
-          // stands in for every pair past the range
-          const half2_t p2 = as_h2(pp[prow[ab] + min(pb + u, np)]);
+          // pairs past the range (at most 15, within the wave's slots) hold
+          // probabilities of later slots or zeros, finite, against meta that
+          // reads as zero
+          const half2_t p2 = as_h2(prow[ab][pb + u]);
           const half2_t psh = p2 * as_h2(s2[u]);
           aw[u] = as_u32(psh);
           srow[ab] = __builtin_amdgcn_fdot2(psh, one2, srow[ab], false);
