@@ -139,7 +139,7 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
     }
     return worst;
   };
-  const int nw = kvq::decode_waves(D, GQ);
+  int nw = kvq::decode_waves(D, GQ);
   int64_t n_wg;
   if (a->split_tokens > 0) {
     n_wg = (N + a->split_tokens - 1) / a->split_tokens;
@@ -166,6 +166,15 @@ kvq_status make_plan(const kvq_decode_args* a, Plan* out) {
       best = t;
       n_wg = c;
     }
+    // One head per kv head, more streams than the chip holds at once, each
+    // in one workgroup: 4-wave workgroups (four per CU instead of two 8-wave
+    // ones) give each wave twice the tokens at the same occupancy, so the
+    // per-wave fixed costs (prologue, load ramps, softmax, combine) are paid
+    // half as often (batch-64 int2, 2049 tokens: 86.5 -> 77.9 us); with the
+    // chip filled once they would only split streams across workgroups.
+    if (GQ == 1 && D == 128 && n_wg == 1 && streams * hblocks > fill &&
+        longest(kvq::kWavesSmall) <= kvq::wave_cap(GQ))
+      nw = kvq::kWavesSmall;
   }
   const int64_t nws = nw * n_wg;
   if (kvq::decode_lds_bytes(D, GQ, nw) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;

@@ -1580,6 +1580,8 @@ hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
 
 template <int D, int GQ, bool PAGED>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t s) {
+  if constexpr (!PAGED && GQ == 1 && D == 128)
+    if (p.waves_per_wg == kWavesSmall) return launch_dgw<D, GQ, kWavesSmall, PAGED>(p, s);
   if (p.waves_per_wg != decode_waves(D, GQ)) return hipErrorInvalidValue;
   return launch_dgw<D, GQ, decode_waves(D, GQ), PAGED>(p, s);
 }

@@ -33,6 +33,9 @@ __host__ __device__ constexpr int head_block(int gq) {
 // VGPRs, and their probabilities overwrite the logits, so 12 waves' LDS
 // fits 160 KB).
 __host__ __device__ constexpr int decode_waves(int D, int GQ) { return GQ >= 4 && D >= 128 ? 12 : kWaves; }
+// The 4-wave workgroup of one query head per kv head at d_h = 128 (four per
+// CU), for calls with more streams than two 8-wave workgroups per CU hold.
+constexpr int kWavesSmall = 4;
 // Target tokens per wave; a wave may get up to wave_cap(GQ) tokens.  Larger
 // GQ needs more LDS per token (logits and probabilities of GQ heads).  With
 // one query head per kv head two workgroups share a CU (48 KB of LDS each);
@@ -190,7 +193,7 @@ struct DecodeParams {
   int32_t n_tok;                        // N, tokens attended per stream
   int32_t n_kq, n_vq;                   // tokens held in key runs / value runs
   int32_t waves_per_stream;             // a multiple of waves_per_wg
-  int32_t waves_per_wg;                 // decode_waves(D, head block)
+  int32_t waves_per_wg;                 // decode_waves(D, head block), or kWavesSmall
   int32_t wg_per_stream;
   float scale_log2;                     // sm_scale * log2(e)
   int32_t n_k_runs, n_v_runs;
