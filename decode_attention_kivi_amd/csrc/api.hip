@@ -278,7 +278,7 @@ kvq_status make_paged_plan(const kvq_paged_args* a, Plan* out) {
     if (s < 0 || (s & 7)) return s < 0 ? KVQ_EINVAL : KVQ_EALIGN;
   const int D = a->d_h, G = a->group;
   const int GQ = kvq::decode_head_block(gq);     // head blocks of up to 4 query heads (grid z)
-  const int nw = kvq::decode_waves(D, GQ);
+  const int nw = GQ == 1 && D == 128 ? kvq::kWavesSmall : kvq::decode_waves(D, GQ);
   if (kvq::decode_lds_bytes(D, GQ, nw) > kvq::kLdsLimit) return KVQ_EUNSUPPORTED;
   const kvq::PagedCost pc = kvq::paged_cost(D, G, a->bits);
   // workgroups per stream: waves of up to wave_cap(GQ) - kWaveAlign tokens

@@ -1500,7 +1500,7 @@ __global__ void __launch_bounds__(R * D) merge_kernel(const DecodeParams P) {
     // the workgroups this stream used (the rest of its slots are not written)
     const int n_kq = P.lens[4 * b], n_vq = P.lens[4 * b + 1];
     nwg = paged_wgs(paged_cost(D, P.G, P.bits), n_kq, n_vq, n_kq + P.lens[4 * b + 2], P.pg_wave_tokens,
-                    decode_waves(D, decode_head_block(P.gq)));
+                    P.waves_per_wg);
   }
   const int c = tid % D, r = tid / D;
   float M = -INFINITY, L = 0.f, O = 0.f;
@@ -1580,7 +1580,7 @@ hipError_t launch_dgw(const DecodeParams& p, hipStream_t s) {
 
 template <int D, int GQ, bool PAGED>
 hipError_t launch_dg(const DecodeParams& p, hipStream_t s) {
-  if constexpr (!PAGED && GQ == 1 && D == 128)
+  if constexpr (GQ == 1 && D == 128)
     if (p.waves_per_wg == kWavesSmall) return launch_dgw<D, GQ, kWavesSmall, PAGED>(p, s);
   if (p.waves_per_wg != decode_waves(D, GQ)) return hipErrorInvalidValue;
   return launch_dgw<D, GQ, decode_waves(D, GQ), PAGED>(p, s);
