@@ -170,6 +170,18 @@ def test_one_call_fused_steps_long_context(kvq, bits, d):
     assert launches.count(1) >= 30, launches
 
 
+def test_one_call_steps_many_streams(kvq):
+    # 20 x 32 streams, more than two 8-wave workgroups per CU hold: the plan
+    # takes 4-wave workgroups, and the fused step's append runs in the last
+    # of the 4 waves; checked after every step through a key flush
+    w = SMALL.scaled(context=100, d_h=128, group=32, residual=32, n_kv_heads=32, n_q_heads=32,
+                     batch=20)
+    launches = []
+    run_kivi(kvq, w, units=[(0, 0), (7, 31), (19, 5)], steps=40, check_every_step=True, one_call=True,
+             launches=launches)
+    assert 1 in launches and max(launches) >= 3
+
+
 @pytest.mark.parametrize("split", [2, 33, 64, 96, 1000])
 def test_forced_split_sizes(kvq, split):
     w = SMALL.scaled(context=700, n_kv_heads=2, n_q_heads=2)
