@@ -239,10 +239,47 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
+// f(t, sc[t]) for every t of one wave's segment [w0, w1) of the scores, the
+// wave's lanes on consecutive tokens with U reads in flight per lane; with
+// V4 (w0 and w1 multiples of 4) a read is 4 consecutive tokens.
+template <int U, bool V4, typename F>
+__device__ __forceinline__ void for_segment(const float* sc, int n, int w0, int w1, F&& f) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (V4) {
+    const float4* s4 = reinterpret_cast<const float4*>(sc);
+    for (int t0 = w0; t0 < w1; t0 += 256 * U) {
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = s4[min(t0 + u * 256 + 4 * lane, n - 4) >> 2];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = t0 + u * 256 + 4 * lane;
+        if (t < w1) {
+          f(t, x[u].x + 0.0f);
+          f(t + 1, x[u].y + 0.0f);
+          f(t + 2, x[u].z + 0.0f);
+          f(t + 3, x[u].w + 0.0f);
+        }
+      }
+    }
+  } else {
+    for (int t0 = w0; t0 < w1; t0 += 64 * U) {
+      float x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (t0 + u * 64 + lane < w1) f(t0 + u * 64 + lane, x[u] + 0.0f);
+    }
+  }
+}
+
 // Candidates of the threshold's bucket kept as a list of keys (in hist past
-// the 256 radix counters) when they are few; more (many equal scores) fall
-// back to radix passes over all n scores.
-constexpr int kCand = kBins - 256;
+// the 256 radix counters), each with the segment (wave) of its token in a
+// byte array after the keys, when they are few; more (many equal scores)
+// fall back to radix passes and a counting pass over all n scores.
+constexpr int kCand = 1408;
+static_assert(kCand * 5 <= (kBins - 256) * 4, "keys and segment bytes fit in hist");
 
 // The k largest of sc[0..n) (LDS or global memory, every score within
 // [lo, hi]) into out[0..k) in ascending token order, ties at the threshold to
@@ -256,6 +293,12 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
                                              bool l1_ready) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float s2 = bucket_scale(lo, hi);
+  // wave w owns the contiguous segment [w0, w1) of the tokens in the
+  // candidate pass and the compaction
+  constexpr int NW = kTopkThreads / 64;
+  constexpr int kSegAlign = V4 ? 256 : 64;
+  const int seg = ((n + NW - 1) / NW + kSegAlign - 1) / kSegAlign * kSegAlign;
+  const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
 
   // level 1 and level 2 buckets narrow the k-th largest score down
   uint32_t k_rem = k, above;
@@ -287,14 +330,30 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
   }
   if (tid == 0) sh[70] = 0;
   __syncthreads();
+  // candidate pass over the wave's segment, which also counts the segment's
+  // tokens in higher buckets (bucket ids are non-decreasing in the score:
+  // those scores exceed every candidate's, the lower buckets' are below)
   uint32_t* cand = hist + 256;
-  for_scores<U, V4>(sc, n, [&](int t, float x) {
+  uint8_t* cseg = reinterpret_cast<uint8_t*>(cand + kCand);
+  uint32_t gt_b = 0;
+  for_segment<U, V4>(sc, n, w0, w1, [&](int t, float x) {
     if (copy) copy[t] = x;
-    if ((bucket_id(x, lo, s2) >> cshift) == target) {
+    const int c = bucket_id(x, lo, s2) >> cshift;
+    gt_b += c > target;
+    if (c == target) {
       const uint32_t slot = atomicAdd(&sh[70], 1u);
-      if (slot < uint32_t(kCand)) cand[slot] = order_key(x);
+      if (slot < uint32_t(kCand)) {
+        cand[slot] = order_key(x);
+        cseg[slot] = uint8_t(wave);
+      }
     }
   });
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) gt_b += __shfl_xor(gt_b, o, 64);
+  if (lane == 0) {
+    sh[32 + wave] = gt_b;
+    sh[48 + wave] = 0;
+  }
   __syncthreads();
   const uint32_t n_cand = sh[70];
   __syncthreads();
@@ -327,40 +386,65 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
 
   // prefix is the threshold key T of score Tf: every score > Tf is selected
   // and the first k_rem scores == Tf by token index (float comparisons agree
-  // with the key order, -0 == +0 included).  Compaction: wave w owns a
-  // contiguous segment of tokens; a first pass counts its greater and equal
-  // scores (ballots), the wave totals are scanned, and a second pass writes
-  // each selected token to the greater tokens before it plus the selected
-  // equal tokens before it.
+  // with the key order, -0 == +0 included).  Compaction: per segment the
+  // greater and equal scores are counted (from the candidate list, or by a
+  // pass of ballots when it overflowed), the segment totals are scanned, and
+  // a pass writes each selected token to the greater tokens before it plus
+  // the selected equal tokens before it.
   const float Tf = __builtin_bit_cast(float, (prefix & 0x80000000u) ? (prefix & 0x7fffffffu) : ~prefix);
+  if (n_cand <= uint32_t(kCand)) {
+    for (int i = tid; i < int(n_cand); i += kTopkThreads) {
+      const uint32_t key = cand[i];
+      if (key >= prefix) atomicAdd(&sh[(key > prefix ? 32 : 48) + cseg[i]], 1u);
+    }
+  } else {
+    uint32_t gt_w = 0, eq_w = 0;
+    if constexpr (V4) {
+      const float4* s4 = reinterpret_cast<const float4*>(sc);
+      for (int t0 = w0; t0 < w1; t0 += 256 * U) {
+        float4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = s4[min(t0 + u * 256 + 4 * lane, n - 4) >> 2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int tb = t0 + u * 256 + 4 * lane;
+          const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bool in = tb + j < w1;
+            gt_w += uint32_t(__popcll(__ballot(in && xs[j] > Tf)));
+            eq_w += uint32_t(__popcll(__ballot(in && xs[j] == Tf)));
+          }
+        }
+      }
+    } else {
+      for (int t0 = w0; t0 < w1; t0 += 64 * U) {
+        float x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const bool in = t0 + u * 64 + lane < w1;
+          gt_w += uint32_t(__popcll(__ballot(in && x[u] > Tf)));
+          eq_w += uint32_t(__popcll(__ballot(in && x[u] == Tf)));
+        }
+      }
+    }
+    if (lane == 0) {
+      sh[32 + wave] = gt_w;
+      sh[48 + wave] = eq_w;
+    }
+  }
+  __syncthreads();
+  uint32_t gb = 0, eb = 0;
+  for (int w = 0; w < wave; ++w) {
+    gb += sh[32 + w];
+    eb += sh[48 + w];
+  }
   if constexpr (V4) {
     // 4 consecutive tokens per lane per read: lane L's token j of a step
     // follows every token of the lower lanes and its own tokens before j
     const float4* s4 = reinterpret_cast<const float4*>(sc);
-    constexpr int NW = kTopkThreads / 64;
-    const int seg = ((n + NW - 1) / NW + 255) / 256 * 256;
-    const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
-    uint32_t gt_w = 0, eq_w = 0;
-    for (int t0 = w0; t0 < w1; t0 += 256 * U) {
-      float4 x[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = s4[min(t0 + u * 256 + 4 * lane, n - 4) >> 2];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int tb = t0 + u * 256 + 4 * lane;
-        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool in = tb + j < w1;
-          gt_w += uint32_t(__popcll(__ballot(in && xs[j] > Tf)));
-          eq_w += uint32_t(__popcll(__ballot(in && xs[j] == Tf)));
-        }
-      }
-    }
-    if (lane == 0) { sh[wave] = gt_w; sh[NW + wave] = eq_w; }
-    __syncthreads();
-    uint32_t gb = 0, eb = 0;
-    for (int w = 0; w < wave; ++w) { gb += sh[w]; eb += sh[NW + w]; }
     for (int t0 = w0; t0 < w1; t0 += 256 * U) {
       float4 x[U];
 #pragma unroll
@@ -398,30 +482,11 @@ __device__ __forceinline__ void select_top_k(const float* sc, int n, uint32_t k,
       }
     }
   } else {
-    constexpr int NW = kTopkThreads / 64;
-    const int seg = ((n + NW - 1) / NW + 63) / 64 * 64;
-    const int w0 = min(n, wave * seg), w1 = min(n, w0 + seg);
-    uint32_t gt_w = 0, eq_w = 0;
     for (int t0 = w0; t0 < w1; t0 += 64 * U) {
       float x[U];
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
-  #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool in = t0 + u * 64 + lane < w1;
-        gt_w += uint32_t(__popcll(__ballot(in && x[u] > Tf)));
-        eq_w += uint32_t(__popcll(__ballot(in && x[u] == Tf)));
-      }
-    }
-    if (lane == 0) { sh[wave] = gt_w; sh[NW + wave] = eq_w; }
-    __syncthreads();
-    uint32_t gb = 0, eb = 0;
-    for (int w = 0; w < wave; ++w) { gb += sh[w]; eb += sh[NW + w]; }
-    for (int t0 = w0; t0 < w1; t0 += 64 * U) {
-      float x[U];
-  #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = sc[min(t0 + u * 64 + lane, n - 1)];
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = t0 + u * 64 + lane;
         const bool gt = t < w1 && x[u] > Tf, eq = t < w1 && x[u] == Tf;
