@@ -13,7 +13,9 @@ Shapes cover 1-8 query heads per kv head (7 included), m = 1..16, 3..8-bit
 codes, k = 1 and k = n_tok, token counts that are not multiples of the
 16-byte code loads, both paths (a head's scores resident in LDS up to about
 38K tokens, scores then Top-k through memory past that), and the GQA
-long-context shape at full size (sampled heads checked).
+long-context shape at full size (sampled heads checked); threshold ties
+beyond the candidate list, and ties within it scattered over every wave's
+token segment with the cut inside one.
 """
 import numpy as np
 import pytest
@@ -134,6 +136,43 @@ def test_pq_search_ties(kvq):
                       torch.from_numpy(padded).to(dev), stride, sc, idx2)
     torch.cuda.synchronize()
     assert idx2.cpu().numpy()[0, 0].tolist() == sorted(list(range(0, 50, 3)) + [1, 2, 4])
+
+
+@pytest.mark.parametrize("n,n_ties", [(5000, 1000), (30000, 1400), (50000, 1000), (50001, 1400)])
+def test_pq_search_ties_across_segments(kvq, n, n_ties):
+    # scores 0, 64 and 96 only: 200 tokens at 96, n_ties tokens at 64 (fewer
+    # than the candidate list holds) scattered over the whole range, so that
+    # every wave's token segment holds some of them, and k takes all of the
+    # 96s and the lower-index part of the 64s: the cut falls inside some
+    # segment; both paths, 16-byte and 4-byte score reads on the memory path
+    import torch
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, m, bits = 1, 1, 1, 64, 2, 1
+    q = np.ones((B, Hq, d), np.float16)
+    c = np.zeros((B, Hkv, m, 2, d // m), np.float16)
+    c[0, 0, 0, 1] = 1.0                                              # sub-space 0, code 1: 32
+    c[0, 0, 1, 1] = 2.0                                              # sub-space 1, code 1: 64
+    perm = np.random.default_rng(n).permutation(n)
+    top, ties = perm[:200], perm[200:200 + n_ties]
+    codes = np.zeros((B, Hkv, n, m), np.uint8)
+    codes[0, 0, top, :] = 1
+    codes[0, 0, ties, 1] = 1
+    k = 200 + n_ties // 2
+    stride = (n * m + 15) // 16 * 16
+    padded = np.zeros((1, stride), np.uint8)
+    padded[:, :n * m] = codes.reshape(1, -1)
+    sc = torch.empty(B, Hq, n, dtype=torch.float32, device=dev)
+    idx = torch.empty(B, Hq, k, dtype=torch.int32, device=dev)
+    print(f"pq ties across segments: n{n} ties{n_ties} k{k}", flush=True)
+    kvq.kvq_pq_search(B, Hq, Hkv, d, m, bits, n, k, torch.from_numpy(q).to(dev), torch.from_numpy(c).to(dev),
+                      torch.from_numpy(padded).to(dev), stride, sc, idx)
+    torch.cuda.synchronize()
+    want_sc = np.zeros(n, np.float32)
+    want_sc[ties] = 64.0
+    want_sc[top] = 96.0
+    assert np.array_equal(sc.cpu().numpy()[0, 0], want_sc)
+    want = sorted(top.tolist() + sorted(ties.tolist())[:n_ties // 2])
+    assert idx.cpu().numpy()[0, 0].tolist() == want
 
 
 def test_pq_search_outlier_score(kvq):
