@@ -30,7 +30,10 @@
 namespace kvq {
 namespace {
 
-constexpr int kPqThreads = 256;
+// threads of a scores workgroup: one round of token loads covers a 4096-token
+// chunk, and the tables take a fraction of an entry per thread; 512 where the
+// tables of 8 heads x 16 sub-spaces need more than 128 registers a lane
+__host__ __device__ constexpr int pq_scores_threads(int GQ, int M) { return GQ * M >= 128 ? 512 : 1024; }
 constexpr int kTopkThreads = 1024;
 
 typedef __amdgpu_buffer_rsrc_t Rsrc;
@@ -42,7 +45,8 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 
 template <int GQ, int M>
-__global__ void __launch_bounds__(kPqThreads) pq_scores_kernel(const PqParams P) {
+__global__ void __launch_bounds__(pq_scores_threads(GQ, M)) pq_scores_kernel(const PqParams P) {
+  constexpr int kPqThreads = pq_scores_threads(GQ, M);
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int m = M;
   const int D = P.D, dm = D / m, nc = 1 << P.bits;
@@ -718,7 +722,8 @@ hipError_t launch_pq_search(const PqParams& p, int GQ, bool fused, hipStream_t s
   const int64_t chunks = (int64_t(p.n_tok) + p.chunk_tokens - 1) / p.chunk_tokens;
   const dim3 grid(unsigned(chunks), unsigned(int64_t(p.B) * p.Hkv), unsigned((p.gq + GQ - 1) / GQ));
   const size_t lds = size_t(pq_scores_lds_bytes(GQ, p.D, p.m, p.bits));
-#define PQ_SCORES(G_, M_) hipLaunchKernelGGL((pq_scores_kernel<G_, M_>), grid, dim3(kPqThreads), lds, s, p)
+#define PQ_SCORES(G_, M_) \
+  hipLaunchKernelGGL((pq_scores_kernel<G_, M_>), grid, dim3(pq_scores_threads(G_, M_)), lds, s, p)
 #define PQ_SCORES_M(G_)                      \
   switch (p.m) {                             \
     case 1: PQ_SCORES(G_, 1); break;         \
