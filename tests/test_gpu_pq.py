@@ -99,6 +99,8 @@ def check_pq(kvq, q, c, codes, B, Hq, Hkv, d, m, bits, n_tok, k, heads=None):
     (1, 32, 1, 128, 2, 8, 3000, 300),
     (1, 32, 1, 128, 2, 8, 40001, 500),
     (2, 24, 2, 64, 4, 6, 40001, 100),
+    # 8 heads x 16 sub-spaces of tables: the scores kernel's 512-thread form
+    (1, 8, 1, 128, 16, 4, 40001, 300),
 ])
 def test_pq_search(kvq, B, Hq, Hkv, d, m, bits, n_tok, k):
     run_pq(kvq, B, Hq, Hkv, d, m, bits, n_tok, k)
